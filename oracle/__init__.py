@@ -1,0 +1,375 @@
+"""CPU oracle of the dropless MoE feed-forward layer — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never imports it
+and the two share no code.
+
+``liboracle.so`` (``oracle.cpp``) holds the arithmetic; this module marshals
+numpy arrays and adds the trivial row-movement definitions (permute, combine
+and their backward, routing backward, router weight gradient) in numpy fp64.
+Page keys ([P1], [P2], [P3]) are those listed in ``oracle.h``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCES = [os.path.join(_HERE, "oracle.cpp")]
+CXXFLAGS = ["-O3", "-march=x86-64-v3", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+            "-std=c++17", "-Wall"]
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with g++ (plain C++17 + OpenMP, no fast-math)."""
+    if force or not os.path.exists(LIB_PATH):
+        tmp = LIB_PATH + ".tmp"
+        subprocess.run(["g++", *CXXFLAGS, *SOURCES, "-o", tmp], check=True)
+        os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+_f = ctypes.POINTER(ctypes.c_float)
+_d = ctypes.POINTER(ctypes.c_double)
+_i = ctypes.POINTER(ctypes.c_int32)
+_u8 = ctypes.POINTER(ctypes.c_uint8)
+_int = ctypes.c_int
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build(force=False)
+        L = ctypes.CDLL(LIB_PATH)
+        for acc in ("f64", "f32"):
+            getattr(L, f"oracle_router_logits_{acc}").argtypes = [_f, _f, _int, _int, _int, _f]
+            getattr(L, f"oracle_route_{acc}").argtypes = [_f, _int, _int, _int, _i, _d, _i, _i, _i, _i]
+            getattr(L, f"oracle_expert_fwd_{acc}").argtypes = [
+                _f, _i, _int, _int, _int, _int, _f, _f, _f, _i, _int, _d, _d, _d, _d]
+            getattr(L, f"oracle_expert_dgrad_{acc}").argtypes = [
+                _f, _f, _i, _int, _int, _int, _int, _f, _f, _f, _i, _int, _d, _d, _d]
+            getattr(L, f"oracle_expert_wgrad_{acc}").argtypes = [
+                _f, _f, _i, _int, _int, _int, _int, _f, _f, _f, _d, _d, _d]
+            getattr(L, f"oracle_layer_fwd_{acc}").argtypes = [
+                _f, _i, _d, _int, _int, _int, _int, _int, _f, _f, _f, _d, _d]
+        L.oracle_expert_wgrad_elems_f64.argtypes = [
+            _f, _f, _i, _int, _int, _int, _int, _f, _f, _f, _int, _i, _int, _d]
+        L.oracle_layer_bwd_f64.argtypes = [
+            _f, _f, _i, _d, _f, _int, _int, _int, _int, _int, _f, _f, _f, _d, _d, _d, _d, _d, _d, _d]
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_float
+        L.oracle_mx_scale_code.argtypes = [ctypes.c_float]
+        L.oracle_mx_scale_code.restype = ctypes.c_uint8
+        L.oracle_mx_quantize.argtypes = [_f, _int, _int, _int, _i, _int, _u8, _u8]
+        _lib = L
+    return _lib
+
+
+def _fp(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a, a.ctypes.data_as(_f)
+
+
+def _ip(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a, a.ctypes.data_as(_i)
+
+
+def _dp(a):
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    return a, a.ctypes.data_as(_d)
+
+
+def _out(shape, dtype=np.float64):
+    a = np.zeros(shape, dtype=dtype)
+    return a, a.ctypes.data_as({np.float64: _d, np.float32: _f, np.int32: _i, np.uint8: _u8}[dtype])
+
+
+# ------------------------------------------------------------------ routing
+def router_logits(x, wr, acc="f64"):
+    """logits = x . W_r rounded once to fp32 ([P2] 2.1)."""
+    T, d = x.shape
+    E = wr.shape[1]
+    x, px = _fp(x)
+    wr, pw = _fp(wr)
+    lg, pl = _out((T, E), np.float32)
+    getattr(lib(), f"oracle_router_logits_{acc}")(px, pw, T, d, E, pl)
+    return lg
+
+
+def route(logits, k, acc="f64"):
+    """Softmax, top-k (lower index first on equal logits), renormalised gates,
+    counts, offsets, row_of, src_tk ([P2] 1.1, 2.1; [P1] 二)."""
+    T, E = logits.shape
+    lg, pl = _fp(logits)
+    topk, p1 = _out((T, k), np.int32)
+    gates, p2 = _out((T, k))
+    counts, p3 = _out((E,), np.int32)
+    offsets, p4 = _out((E + 1,), np.int32)
+    row_of, p5 = _out((T, k), np.int32)
+    src_tk, p6 = _out((T * k,), np.int32)
+    getattr(lib(), f"oracle_route_{acc}")(pl, T, E, k, p1, p2, p3, p4, p5, p6)
+    return dict(topk_idx=topk, gates=gates, counts=counts, offsets=offsets, row_of=row_of,
+                src_tk=src_tk)
+
+
+# ------------------------------------------------------------------ experts
+def expert_fwd(xp, offsets, wg, wu, wd, rows=None, acc="f64"):
+    """Per-row SwiGLU expert over expert-major rows; returns g, u, h, yp for
+    the requested rows (all rows when rows is None)."""
+    R, d = xp.shape
+    E, _, F = wg.shape
+    xp, pxp = _fp(xp)
+    off, poff = _ip(offsets)
+    wg, pg = _fp(wg)
+    wu, pu = _fp(wu)
+    wd, pd = _fp(wd)
+    if rows is None:
+        rw, prw, n = None, None, R
+    else:
+        rw, prw = _ip(rows)
+        n = len(rw)
+    g, p1 = _out((n, F))
+    u, p2 = _out((n, F))
+    h, p3 = _out((n, F))
+    yp, p4 = _out((n, d))
+    getattr(lib(), f"oracle_expert_fwd_{acc}")(pxp, poff, E, R, d, F, pg, pu, pd, prw, n, p1, p2, p3, p4)
+    return dict(g=g, u=u, h=h, yp=yp)
+
+
+def expert_dgrad(xp, dyp, offsets, wg, wu, wd, rows=None, acc="f64"):
+    R, d = xp.shape
+    E, _, F = wg.shape
+    xp, pxp = _fp(xp)
+    dyp, pdy = _fp(dyp)
+    off, poff = _ip(offsets)
+    wg, pg = _fp(wg)
+    wu, pu = _fp(wu)
+    wd, pd = _fp(wd)
+    if rows is None:
+        rw, prw, n = None, None, R
+    else:
+        rw, prw = _ip(rows)
+        n = len(rw)
+    dg, p1 = _out((n, F))
+    du, p2 = _out((n, F))
+    dxp, p3 = _out((n, d))
+    getattr(lib(), f"oracle_expert_dgrad_{acc}")(pxp, pdy, poff, E, R, d, F, pg, pu, pd, prw, n, p1, p2, p3)
+    return dict(dg=dg, du=du, dxp=dxp)
+
+
+def expert_wgrad(xp, dyp, offsets, wg, wu, wd, acc="f64"):
+    R, d = xp.shape
+    E, _, F = wg.shape
+    xp, pxp = _fp(xp)
+    dyp, pdy = _fp(dyp)
+    off, poff = _ip(offsets)
+    wg, pg = _fp(wg)
+    wu, pu = _fp(wu)
+    wd, pd = _fp(wd)
+    dwg, p1 = _out((E, d, F))
+    dwu, p2 = _out((E, d, F))
+    dwd, p3 = _out((E, F, d))
+    getattr(lib(), f"oracle_expert_wgrad_{acc}")(pxp, pdy, poff, E, R, d, F, pg, pu, pd, p1, p2, p3)
+    return dict(dwg=dwg, dwu=dwu, dwd=dwd)
+
+
+def expert_wgrad_elems(xp, dyp, offsets, wg, wu, wd, which, elems):
+    """Selected weight-gradient elements; which 0=dWg, 1=dWu, 2=dWd;
+    elems is an (n,3) int array of (e, a, b) indices into dW[e][a][b]."""
+    R, d = xp.shape
+    E, _, F = wg.shape
+    xp, pxp = _fp(xp)
+    dyp, pdy = _fp(dyp)
+    off, poff = _ip(offsets)
+    wg, pg = _fp(wg)
+    wu, pu = _fp(wu)
+    wd, pd = _fp(wd)
+    el, pel = _ip(np.asarray(elems).reshape(-1, 3))
+    out, po = _out((len(el),))
+    lib().oracle_expert_wgrad_elems_f64(pxp, pdy, poff, E, R, d, F, pg, pu, pd, which, pel, len(el), po)
+    return out
+
+
+# ------------------------------------------------------------------ whole layer
+def layer_fwd(x, topk_idx, gates, wg, wu, wd, acc="f64", want_ytj=False):
+    """Token-by-token layer forward: y_t = sum_j g_tj * expert_{S_tj}(x_t)
+    ([P2] 2.1).  Returns y and optionally Y_tj [T,k,d]."""
+    T, d = x.shape
+    E, _, F = wg.shape
+    k = topk_idx.shape[1]
+    x, px = _fp(x)
+    ti, pti = _ip(topk_idx)
+    ga, pga = _dp(gates)
+    wg, pg = _fp(wg)
+    wu, pu = _fp(wu)
+    wd, pd = _fp(wd)
+    y, py = _out((T, d))
+    if want_ytj:
+        ytj, pyt = _out((T, k, d))
+    else:
+        ytj, pyt = None, None
+    getattr(lib(), f"oracle_layer_fwd_{acc}")(px, pti, pga, T, d, E, k, F, pg, pu, pd, py, pyt)
+    return (y, ytj) if want_ytj else y
+
+
+def layer_bwd(x, wr, topk_idx, gates, dy, wg, wu, wd):
+    """fp64 whole-layer backward ([P2] 1.2): dgates, dlogits_sel, dx, dWg,
+    dWu, dWd, dWr."""
+    T, d = x.shape
+    E, _, F = wg.shape
+    k = topk_idx.shape[1]
+    x, px = _fp(x)
+    wr, pwr = _fp(wr)
+    ti, pti = _ip(topk_idx)
+    ga, pga = _dp(gates)
+    dy, pdy = _fp(dy)
+    wg, pg = _fp(wg)
+    wu, pu = _fp(wu)
+    wd, pd = _fp(wd)
+    dgates, p1 = _out((T, k))
+    dls, p2 = _out((T, k))
+    dx, p3 = _out((T, d))
+    dwg, p4 = _out((E, d, F))
+    dwu, p5 = _out((E, d, F))
+    dwd, p6 = _out((E, F, d))
+    dwr, p7 = _out((d, E))
+    lib().oracle_layer_bwd_f64(px, pwr, pti, pga, pdy, T, d, E, k, F, pg, pu, pd, p1, p2, p3, p4, p5,
+                               p6, p7)
+    return dict(dgates=dgates, dlogits_sel=dls, dx=dx, dwg=dwg, dwu=dwu, dwd=dwd, dwr=dwr)
+
+
+# ------------------------------------------------------------------ row movement (definitions)
+def permute(x, row_of):
+    """Xp[row_of[t,j]] = x_t: each token written into its k expert rows
+    ([P1] 二, rowwise writes into the experts' input buffers)."""
+    T, k = row_of.shape
+    xp = np.zeros((T * k, x.shape[1]), dtype=np.float64)
+    for j in range(k):
+        xp[row_of[:, j]] = x
+    return xp
+
+
+def combine(yp, gates, row_of):
+    """y_t = sum_j gates[t,j] * Yp[row_of[t,j]] in slot order, fp64
+    ([P2] 2.1: results return along the original path and are restored)."""
+    T, k = row_of.shape
+    y = np.zeros((T, yp.shape[1]), dtype=np.float64)
+    for j in range(k):
+        y += gates[:, j:j + 1].astype(np.float64) * yp[row_of[:, j]].astype(np.float64)
+    return y
+
+
+def combine_bwd(dy, yp, gates, row_of):
+    """dYp[row_of[t,j]] = gates[t,j]*dy_t and dgates[t,j] = <dy_t, Yp[row_of[t,j]]>."""
+    T, k = row_of.shape
+    dyp = np.zeros((T * k, dy.shape[1]), dtype=np.float64)
+    dgates = np.zeros((T, k), dtype=np.float64)
+    dy = dy.astype(np.float64)
+    for j in range(k):
+        dyp[row_of[:, j]] = gates[:, j:j + 1].astype(np.float64) * dy
+        dgates[:, j] = np.einsum("td,td->t", dy, yp[row_of[:, j]].astype(np.float64))
+    return dyp, dgates
+
+
+def route_bwd(gates, dgates):
+    """Selected-slot logit gradient of the renormalised softmax gates:
+    dl_tj = g_tj * (dg_tj - sum_i g_ti dg_ti); unselected logits get 0."""
+    g = gates.astype(np.float64)
+    dg = dgates.astype(np.float64)
+    return g * (dg - (g * dg).sum(axis=1, keepdims=True))
+
+
+def permute_bwd(dxp, row_of, topk_idx=None, dlogits_sel=None, wr=None):
+    """dx_t = sum_j dXp[row_of[t,j]] (+ sum_j dl_tj * W_r[:, S_tj] when the
+    router terms are given)."""
+    T, k = row_of.shape
+    dx = np.zeros((T, dxp.shape[1]), dtype=np.float64)
+    for j in range(k):
+        dx += dxp[row_of[:, j]].astype(np.float64)
+    if dlogits_sel is not None:
+        wr = wr.astype(np.float64)
+        for j in range(k):
+            dx += dlogits_sel[:, j:j + 1].astype(np.float64) * wr[:, topk_idx[:, j]].T
+    return dx
+
+
+def router_wgrad(x, dlogits_sel, topk_idx, E):
+    """dW_r[:, e] = sum over (t,j) with S_tj = e of dl_tj * x_t."""
+    T, d = x.shape
+    dwr = np.zeros((d, E), dtype=np.float64)
+    x = x.astype(np.float64)
+    for j in range(topk_idx.shape[1]):
+        for e in range(E):
+            m = topk_idx[:, j] == e
+            if m.any():
+                dwr[:, e] += (dlogits_sel[m, j].astype(np.float64)[:, None] * x[m]).sum(axis=0)
+    return dwr
+
+
+# ------------------------------------------------------------------ MXFP8
+def e4m3_encode(v):
+    return lib().oracle_e4m3_encode(float(v))
+
+
+def e4m3_decode(c):
+    return lib().oracle_e4m3_decode(int(c))
+
+
+def mx_scale_code(amax):
+    return lib().oracle_mx_scale_code(float(amax))
+
+
+def e4m3_values():
+    """Value of each of the 256 codes (NaN codes are NaN)."""
+    return np.array([lib().oracle_e4m3_decode(c) for c in range(256)], dtype=np.float32)
+
+
+def mx_quantize(src, axis, offsets=None):
+    """MX quantisation of a [rows, cols] matrix; returns (codes, scales).  See
+    oracle.h for the block layouts."""
+    rows, cols = src.shape
+    s, ps = _fp(src)
+    codes, pc = _out((rows, cols), np.uint8)
+    if axis == 0:
+        assert cols % 32 == 0
+        scales, psc = _out((rows, cols // 32), np.uint8)
+        lib().oracle_mx_quantize(ps, rows, cols, 0, None, 0, pc, psc)
+    else:
+        if offsets is None:
+            offsets = np.array([0, rows], dtype=np.int32)
+        off, poff = _ip(offsets)
+        nblk = int(sum((int(off[g + 1]) - int(off[g]) + 31) // 32 for g in range(len(off) - 1)))
+        scales, psc = _out((nblk, cols), np.uint8)
+        lib().oracle_mx_quantize(ps, rows, cols, 1, poff, len(off) - 1, pc, psc)
+    return codes, scales
+
+
+def mx_dequantize_rows(codes, scales):
+    """Exact values of axis-0 quantised data: code value * 2^(scale-127)."""
+    vals = e4m3_values().astype(np.float64)[codes]
+    sc = np.ldexp(1.0, scales.astype(np.int32) - 127)
+    return vals * np.repeat(sc, 32, axis=1)
+
+
+def mx_dequantize_cols(codes, scales, offsets):
+    """Exact values of axis-1 quantised data (group-major blocks)."""
+    vals = e4m3_values().astype(np.float64)[codes]
+    out = np.empty_like(vals)
+    blk = 0
+    for g in range(len(offsets) - 1):
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        for b in range((hi - lo + 31) // 32):
+            r0, r1 = lo + 32 * b, min(lo + 32 * b + 32, hi)
+            out[r0:r1] = vals[r0:r1] * np.ldexp(1.0, scales[blk].astype(np.int32) - 127)[None, :]
+            blk += 1
+    return out
