@@ -1,0 +1,180 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) dropless MoE feed-forward layer.
+ *
+ * The layer, as the pages describe it in words:
+ *  - a router scores each token against every expert, the top-k experts are
+ *    selected and only those k run ([P2] sections 1.1 and 2.1);
+ *  - the selection becomes a permutation index and the token rows are packed
+ *    per expert ([P2] 2.1), written straight into each expert's input buffer
+ *    ("rowwise" expert parallelism, [P1] 核心特点 二);
+ *  - routing metadata stays on the GPU so the host never waits on a copy
+ *    back ([P1] 二, GPU-resident routing);
+ *  - the experts run as one device-scheduled grouped GEMM ([P1] 二,
+ *    Grouped GEMM), dropless: no token is dropped when an expert is
+ *    overloaded ([P3] "Как установить Olmo-core");
+ *  - the results return along the original path and are restored to token
+ *    order ([P2] 2.1); forward and backward both move every token ([P2] 1.2);
+ *  - MXFP8 is supported for the expert GEMMs ([P1] 三).
+ * Pages: [P1] "认识 Olmo-core 3" (meetcoding.cn/olmo-core/introduction.html);
+ * [P2] the practitioner article at discosf.com/news/6174547; [P3] vibecoding.ru
+ * news "Обучение MoE ускорилось: Olmo-core 3 дал прирост в 2,7 раза".
+ *
+ * Shapes: T tokens, d = d_model, E experts, k = top-k, F = d_ff, R = T*k rows.
+ * Expert i/o is SwiGLU without biases:  y = (silu(x Wg) * (x Wu)) Wd.
+ * Layouts (row-major): x [T,d]; W_r [d,E]; Wg, Wu [E,d,F]; Wd [E,F,d];
+ * logits [T,E] fp32; topk_idx, row_of [T,k] int32; gates [T,k] fp32;
+ * counts [E], offsets [E+1] int32; src_tk [R] int32; expert buffers
+ * (xp, g, u, h, yp, ...) are expert-major rows [R, *] with the rows of
+ * expert e at offsets[e] .. offsets[e+1]-1, in ascending token order.
+ *
+ * Conventions for every call:
+ *  - Every pointer is a DEVICE pointer unless marked (host).  The caller owns
+ *    every buffer, including the workspace registered with
+ *    moe_set_workspace; the library keeps no pointer after a call returns
+ *    except the registered workspace.
+ *  - No call allocates device memory, copies between host and device, or
+ *    synchronises: each only validates on the host and enqueues kernels on
+ *    the context's stream, so the whole layer can be captured in a HIP graph.
+ *    counts/offsets are never read by the host.
+ *  - Errors: host-side validation returns MOE_ERR_INVALID_ARGUMENT (null or
+ *    misaligned pointers, sizes out of range) or MOE_ERR_UNSUPPORTED, and
+ *    never aborts; launch failures return MOE_ERR_HIP.  moe_last_error gives
+ *    the text.  Device faults surface asynchronously, as in HIP.
+ *  - Limits: 1 <= k <= min(E, 32); E <= 1024; T*k < 2^31; d % 8 == 0 and
+ *    F % 8 == 0 (16-byte bf16 rows); data pointers 16-byte aligned.
+ *    For MXFP8, d and F are multiples of 128.
+ *  - Preconditions: logits are finite (otherwise routing is unspecified but
+ *    memory-safe).  A context is not thread-safe: one context per stream.
+ *  - Gradients overwrite their outputs (no accumulation into them).
+ */
+#ifndef MOE_H
+#define MOE_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_ctx moe_ctx;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+/* Element type of activations and weights.  MOE_F32: fp32 data and fp32
+ * arithmetic.  MOE_BF16: bf16 data, fp32 accumulation, bf16 outputs. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* ---------------------------------------------------------------- context */
+
+/* Create a context on `device` that enqueues on `hip_stream` (a hipStream_t,
+ * NULL = the default stream).  *out (host) receives the context. */
+moe_status moe_create(int device, void* hip_stream, moe_ctx** out);
+moe_status moe_destroy(moe_ctx* ctx);
+moe_status moe_set_stream(moe_ctx* ctx, void* hip_stream);
+/* Static text of a status code. */
+const char* moe_status_string(moe_status s);
+/* Text of the last error on this context (owned by the context). */
+const char* moe_last_error(const moe_ctx* ctx);
+
+/* Device workspace needed by the calls that use it for a layer of this
+ * shape: moe_route (per-block expert histograms) and moe_permute_bwd with
+ * the router term (a transposed copy of W_r).  The calls run in stream order,
+ * so they share one region.  *bytes is a host output. */
+moe_status moe_workspace_size(moe_ctx* ctx, int T, int d, int E, int k, moe_dtype dtype,
+                              size_t* bytes);
+/* Register caller-owned device workspace (256-byte aligned). */
+moe_status moe_set_workspace(moe_ctx* ctx, void* ws, size_t bytes);
+
+/* ---------------------------------------------------------------- forward */
+
+/* Router scores: logits[t,e] = sum_i x[t,i] * w_router[i,e], fp32
+ * accumulation, fp32 output.  [P2] 1.1, 2.1. */
+moe_status moe_router_logits(moe_ctx* ctx, const void* x, const void* w_router, int T, int d,
+                             int E, moe_dtype dtype, float* logits);
+
+/* Routing.  For each token: the k experts with the largest logits, larger
+ * logit first and the lower expert index first among equal logits
+ * (+0 == -0); gates[t,j] = softmax over the k selected logits (equal to the
+ * softmax over all E renormalised over the selection).  Then the expert
+ * histogram counts[e], offsets = exclusive scan of counts (offsets[E] = R),
+ * and the stable expert-major permutation: row_of[t,j] is the row of (t,j)
+ * in the expert buffers, src_tk[row] = t*k + j its inverse.  Rows within an
+ * expert are in ascending t.  Needs the registered workspace
+ * (moe_workspace_size).  [P2] 2.1 (permutation index), [P1] 二
+ * (GPU-resident routing metadata). */
+moe_status moe_route(moe_ctx* ctx, const float* logits, int T, int E, int k, int32_t* topk_idx,
+                     float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                     int32_t* src_tk);
+
+/* Rowwise permute: xp[row_of[t,j]] = x[t] for every (t,j); xp is [T*k, d].
+ * [P1] 二 (rows written straight into the experts' input buffers). */
+moe_status moe_permute(moe_ctx* ctx, const void* x, const int32_t* row_of, int T, int d, int k,
+                       moe_dtype dtype, void* xp);
+
+/* Grouped SwiGLU experts over the R expert-major rows, scheduled on the
+ * device from `offsets` (no host sync): for the rows of expert e,
+ * g = xp Wg[e], u = xp Wu[e], h = silu(g) * u, yp = h Wd[e].  g, u, h
+ * ([R,F]) are saved for the backward; yp is [R,d].  An expert with no rows
+ * does no work.  [P1] 二 (grouped GEMM), [P3] (dropless). */
+moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
+                               const void* w_up, const void* w_down, const int32_t* offsets,
+                               int E, int R, int d, int F, moe_dtype dtype, void* g, void* u,
+                               void* h, void* yp);
+
+/* Gate-weighted unpermute-combine: y[t] = sum_j gates[t,j] * yp[row_of[t,j]],
+ * summed in slot order in fp32, rounded once.  [P2] 2.1 (return and
+ * restore). */
+moe_status moe_combine(moe_ctx* ctx, const void* yp, const float* gates, const int32_t* row_of,
+                       int T, int d, int k, moe_dtype dtype, void* y);
+
+/* --------------------------------------------------------------- backward
+ * [P2] 1.2: the backward moves every token again. */
+
+/* dyp[row_of[t,j]] = gates[t,j] * dy[t];  dgates[t,j] = <dy[t], yp[row_of[t,j]]>
+ * (fp32). */
+moe_status moe_combine_bwd(moe_ctx* ctx, const void* dy, const void* yp, const float* gates,
+                           const int32_t* row_of, int T, int d, int k, moe_dtype dtype,
+                           void* dyp, float* dgates);
+
+/* Logit gradient at the selected slots of the renormalised softmax gates:
+ * dlogits_sel[t,j] = gates[t,j] * (dgates[t,j] - sum_i gates[t,i]*dgates[t,i]).
+ * Unselected logits have gradient exactly 0 (not stored). */
+moe_status moe_route_bwd(moe_ctx* ctx, const float* gates, const float* dgates, int T, int k,
+                         float* dlogits_sel);
+
+/* Backward of moe_grouped_ffn_fwd for upstream rows dyp [R,d]:
+ *   dh = dyp Wd[e]^T;  dg = dh * u * silu'(g);  du = dh * silu(g)
+ *   dxp = dg Wg[e]^T + du Wu[e]^T
+ *   dWd[e] = h_e^T dyp_e;  dWg[e] = xp_e^T dg_e;  dWu[e] = xp_e^T du_e
+ * dg, du ([R,F]) are outputs too.  Weight gradients of an expert with no
+ * rows are exactly zero. */
+moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
+                               const void* w_up, const void* w_down, const int32_t* offsets,
+                               const void* g, const void* u, const void* h, const void* dyp,
+                               int E, int R, int d, int F, moe_dtype dtype, void* dg, void* du,
+                               void* dxp, void* dw_gate, void* dw_up, void* dw_down);
+
+/* dx[t] = sum_j dxp[row_of[t,j]]  (+ sum_j dlogits_sel[t,j] * w_router[:, topk_idx[t,j]]
+ * when dlogits_sel and w_router are both non-NULL), fp32 accumulation. */
+moe_status moe_permute_bwd(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
+                           const int32_t* topk_idx, const float* dlogits_sel,
+                           const void* w_router, int T, int d, int E, int k, moe_dtype dtype,
+                           void* dx);
+
+/* Router weight gradient: dw_router[i,e] = sum over the rows r of expert e
+ * (ascending) of dlogits_sel[src_tk[r]] * x[src_tk[r] / k, i]; fp32
+ * accumulation in a fixed order, stored in dtype. */
+moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_sel,
+                            const int32_t* src_tk, const int32_t* offsets, int T, int d, int E,
+                            int k, moe_dtype dtype, void* dw_router);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,331 @@
+"""Python binding of the MI355X dropless MoE layer library (libmoe.so).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+``libmoe.so``.  PyTorch provides device memory and the current HIP stream.
+The functions carry the C ABI's names (``include/moe.h``) and take torch
+tensors; each raises ``MoeError`` on a non-OK status.  There is no CPU
+fallback: importing works without the library, but any call raises when
+``libmoe.so`` is missing or no GPU is present.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_int = ctypes.c_int
+
+# name -> argument types after the context pointer
+_SIGS = {
+    "moe_router_logits": [_vp, _vp, _int, _int, _int, _int, _vp],
+    "moe_route": [_vp, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_permute": [_vp, _vp, _int, _int, _int, _int, _vp],
+    "moe_grouped_ffn_fwd": [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp, _vp, _vp, _vp],
+    "moe_combine": [_vp, _vp, _vp, _int, _int, _int, _int, _vp],
+    "moe_combine_bwd": [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp, _vp],
+    "moe_route_bwd": [_vp, _vp, _int, _int, _vp],
+    "moe_grouped_ffn_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int,
+                            _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_permute_bwd": [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
+    "moe_router_wgrad": [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
+}
+EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "moe_last_error",
+           "moe_workspace_size", "moe_set_workspace", *_SIGS.keys()]
+
+
+def lib():
+    """Load libmoe.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MoeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m routing_grouped_expert_softmax_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.moe_create.argtypes = [_int, _vp, ctypes.POINTER(_vp)]
+        L.moe_destroy.argtypes = [_vp]
+        L.moe_set_stream.argtypes = [_vp, _vp]
+        L.moe_status_string.argtypes = [_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = [_vp]
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_workspace_size.argtypes = [_vp, _int, _int, _int, _int, _int, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_set_workspace.argtypes = [_vp, _vp, ctypes.c_size_t]
+        for name, sig in _SIGS.items():
+            getattr(L, name).argtypes = [_vp, *sig]
+        _lib = L
+    return _lib
+
+
+class Context:
+    """One library context per (device, stream); owns a torch workspace."""
+
+    def __init__(self, device: int = 0):
+        if not torch.cuda.is_available():
+            raise MoeError("no GPU: the MoE library runs only on the GPU")
+        self.device = device
+        h = _vp()
+        self._check(lib().moe_create(device, None, ctypes.byref(h)), None)
+        self.handle = h
+        self._ws = None
+        self._ws_bytes = 0
+
+    def _check(self, st, handle="self"):
+        if st != 0:
+            msg = ""
+            if handle is not None and getattr(self, "handle", None) is not None:
+                msg = lib().moe_last_error(self.handle).decode()
+            raise MoeError(f"{_STATUS.get(st, st)}: {msg}")
+
+    def bind_stream(self):
+        s = torch.cuda.current_stream(self.device)
+        self._check(lib().moe_set_stream(self.handle, _vp(s.cuda_stream)))
+
+    def ensure_workspace(self, T, d, E, k, dtype):
+        n = ctypes.c_size_t()
+        self._check(lib().moe_workspace_size(self.handle, T, d, E, k, dtype, ctypes.byref(n)))
+        if n.value > self._ws_bytes:
+            self._ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=f"cuda:{self.device}")
+            self._ws_bytes = n.value
+            self._check(lib().moe_set_workspace(self.handle, _vp(self._ws.data_ptr()), n.value))
+
+    def call(self, name, *args):
+        self.bind_stream()
+        self._check(getattr(lib(), name)(self.handle, *args))
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            lib().moe_destroy(self.handle)
+            self.handle = None
+
+
+_ctx = {}
+
+
+def context(device: int | None = None) -> Context:
+    dev = torch.cuda.current_device() if device is None else device
+    if dev not in _ctx:
+        _ctx[dev] = Context(dev)
+    return _ctx[dev]
+
+
+def _p(t):
+    return None if t is None else _vp(t.data_ptr())
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise MoeError(f"unsupported dtype {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise MoeError("tensors must be contiguous GPU tensors")
+
+
+# ------------------------------------------------------------------ ABI calls
+def moe_router_logits(x, w_router, logits=None):
+    _need_cuda(x, w_router)
+    T, d = x.shape
+    E = w_router.shape[1]
+    if logits is None:
+        logits = torch.empty(T, E, dtype=torch.float32, device=x.device)
+    context(x.device.index).call("moe_router_logits", _p(x), _p(w_router), T, d, E, _dt(x), _p(logits))
+    return logits
+
+
+def moe_route(logits, k, out=None):
+    """Returns dict(topk_idx, gates, counts, offsets, row_of, src_tk)."""
+    _need_cuda(logits)
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        out = dict(topk_idx=torch.empty(T, k, dtype=torch.int32, device=dev),
+                   gates=torch.empty(T, k, dtype=torch.float32, device=dev),
+                   counts=torch.empty(E, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   row_of=torch.empty(T, k, dtype=torch.int32, device=dev),
+                   src_tk=torch.empty(max(T * k, 1), dtype=torch.int32, device=dev))
+    ctx = context(dev.index)
+    ctx.ensure_workspace(T, 8, E, k, MOE_F32)
+    ctx.call("moe_route", _p(logits), T, E, k, _p(out["topk_idx"]), _p(out["gates"]), _p(out["counts"]),
+             _p(out["offsets"]), _p(out["row_of"]), _p(out["src_tk"]))
+    return out
+
+
+def moe_permute(x, row_of, xp=None):
+    _need_cuda(x, row_of)
+    T, d = x.shape
+    k = row_of.shape[1]
+    if xp is None:
+        xp = torch.empty(T * k, d, dtype=x.dtype, device=x.device)
+    context(x.device.index).call("moe_permute", _p(x), _p(row_of), T, d, k, _dt(x), _p(xp))
+    return xp
+
+
+def moe_grouped_ffn_fwd(xp, w_gate, w_up, w_down, offsets, out=None):
+    """Returns dict(g, u, h, yp)."""
+    _need_cuda(xp, w_gate, w_up, w_down, offsets)
+    R, d = xp.shape
+    E, _, F = w_gate.shape
+    if out is None:
+        out = dict(g=torch.empty(R, F, dtype=xp.dtype, device=xp.device),
+                   u=torch.empty(R, F, dtype=xp.dtype, device=xp.device),
+                   h=torch.empty(R, F, dtype=xp.dtype, device=xp.device),
+                   yp=torch.empty(R, d, dtype=xp.dtype, device=xp.device))
+    context(xp.device.index).call("moe_grouped_ffn_fwd", _p(xp), _p(w_gate), _p(w_up), _p(w_down),
+                                  _p(offsets), E, R, d, F, _dt(xp), _p(out["g"]), _p(out["u"]),
+                                  _p(out["h"]), _p(out["yp"]))
+    return out
+
+
+def moe_combine(yp, gates, row_of, y=None):
+    _need_cuda(yp, gates, row_of)
+    T, k = row_of.shape
+    d = yp.shape[1]
+    if y is None:
+        y = torch.empty(T, d, dtype=yp.dtype, device=yp.device)
+    context(yp.device.index).call("moe_combine", _p(yp), _p(gates), _p(row_of), T, d, k, _dt(yp), _p(y))
+    return y
+
+
+def moe_combine_bwd(dy, yp, gates, row_of, dyp=None, dgates=None):
+    _need_cuda(dy, yp, gates, row_of)
+    T, k = row_of.shape
+    d = yp.shape[1]
+    if dyp is None:
+        dyp = torch.empty(T * k, d, dtype=yp.dtype, device=yp.device)
+    if dgates is None:
+        dgates = torch.empty(T, k, dtype=torch.float32, device=yp.device)
+    context(yp.device.index).call("moe_combine_bwd", _p(dy), _p(yp), _p(gates), _p(row_of), T, d, k,
+                                  _dt(yp), _p(dyp), _p(dgates))
+    return dyp, dgates
+
+
+def moe_route_bwd(gates, dgates, dlogits_sel=None):
+    _need_cuda(gates, dgates)
+    T, k = gates.shape
+    if dlogits_sel is None:
+        dlogits_sel = torch.empty(T, k, dtype=torch.float32, device=gates.device)
+    context(gates.device.index).call("moe_route_bwd", _p(gates), _p(dgates), T, k, _p(dlogits_sel))
+    return dlogits_sel
+
+
+def moe_grouped_ffn_bwd(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp, out=None):
+    """Returns dict(dg, du, dxp, dw_gate, dw_up, dw_down)."""
+    _need_cuda(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp)
+    R, d = xp.shape
+    E, _, F = w_gate.shape
+    if out is None:
+        dev, dt = xp.device, xp.dtype
+        out = dict(dg=torch.empty(R, F, dtype=dt, device=dev), du=torch.empty(R, F, dtype=dt, device=dev),
+                   dxp=torch.empty(R, d, dtype=dt, device=dev),
+                   dw_gate=torch.empty_like(w_gate), dw_up=torch.empty_like(w_up),
+                   dw_down=torch.empty_like(w_down))
+    context(xp.device.index).call("moe_grouped_ffn_bwd", _p(xp), _p(w_gate), _p(w_up), _p(w_down),
+                                  _p(offsets), _p(g), _p(u), _p(h), _p(dyp), E, R, d, F, _dt(xp),
+                                  _p(out["dg"]), _p(out["du"]), _p(out["dxp"]), _p(out["dw_gate"]),
+                                  _p(out["dw_up"]), _p(out["dw_down"]))
+    return out
+
+
+def moe_permute_bwd(dxp, row_of, topk_idx=None, dlogits_sel=None, w_router=None, dx=None):
+    _need_cuda(dxp, row_of, topk_idx, dlogits_sel, w_router)
+    T, k = row_of.shape
+    d = dxp.shape[1]
+    E = w_router.shape[1] if w_router is not None else 1
+    if dx is None:
+        dx = torch.empty(T, d, dtype=dxp.dtype, device=dxp.device)
+    ctx = context(dxp.device.index)
+    if w_router is not None:
+        ctx.ensure_workspace(T, d, E, min(k, E), _dt(dxp))
+    ctx.call("moe_permute_bwd", _p(dxp), _p(row_of), _p(topk_idx), _p(dlogits_sel), _p(w_router),
+             T, d, E, k, _dt(dxp), _p(dx))
+    return dx
+
+
+def moe_router_wgrad(x, dlogits_sel, src_tk, offsets, E, dw_router=None):
+    _need_cuda(x, dlogits_sel, src_tk, offsets)
+    T, d = x.shape
+    k = dlogits_sel.shape[1]
+    if dw_router is None:
+        dw_router = torch.empty(d, E, dtype=x.dtype, device=x.device)
+    context(x.device.index).call("moe_router_wgrad", _p(x), _p(dlogits_sel), _p(src_tk), _p(offsets),
+                                 T, d, E, k, _dt(x), _p(dw_router))
+    return dw_router
+
+
+# ------------------------------------------------------------------ the layer
+@dataclass
+class LayerBuffers:
+    """Every device buffer of one forward+backward, allocated once."""
+    logits: torch.Tensor
+    route: dict
+    xp: torch.Tensor
+    ffn: dict
+    y: torch.Tensor
+    dyp: torch.Tensor
+    dgates: torch.Tensor
+    dlogits_sel: torch.Tensor
+    bwd: dict
+    dx: torch.Tensor
+    dw_router: torch.Tensor
+
+
+def alloc_layer(T, d, E, k, F, dtype, device):
+    dev = torch.device(device)
+    R = T * k
+    z = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
+    route = dict(topk_idx=z(T, k, dt=torch.int32), gates=z(T, k, dt=torch.float32),
+                 counts=z(E, dt=torch.int32), offsets=z(E + 1, dt=torch.int32),
+                 row_of=z(T, k, dt=torch.int32), src_tk=z(max(R, 1), dt=torch.int32))
+    ffn = dict(g=z(R, F), u=z(R, F), h=z(R, F), yp=z(R, d))
+    bwd = dict(dg=z(R, F), du=z(R, F), dxp=z(R, d), dw_gate=z(E, d, F), dw_up=z(E, d, F),
+               dw_down=z(E, F, d))
+    return LayerBuffers(logits=z(T, E, dt=torch.float32), route=route, xp=z(R, d), ffn=ffn, y=z(T, d),
+                        dyp=z(R, d), dgates=z(T, k, dt=torch.float32),
+                        dlogits_sel=z(T, k, dt=torch.float32), bwd=bwd, dx=z(T, d), dw_router=z(d, E))
+
+
+def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logits_override=None):
+    """Router scores -> route -> permute -> grouped SwiGLU experts -> combine.
+    `logits_override` (optional [T,E] fp32 on the GPU) replaces the router
+    scores as the routing input after the router GEMM has run."""
+    moe_router_logits(x, w_router, buf.logits)
+    moe_route(buf.logits if logits_override is None else logits_override, k, buf.route)
+    moe_permute(x, buf.route["row_of"], buf.xp)
+    moe_grouped_ffn_fwd(buf.xp, w_gate, w_up, w_down, buf.route["offsets"], buf.ffn)
+    moe_combine(buf.ffn["yp"], buf.route["gates"], buf.route["row_of"], buf.y)
+    return buf.y
+
+
+def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers):
+    """combine_bwd -> route_bwd -> grouped FFN bwd -> permute_bwd (+router
+    dgrad) -> router wgrad.  Returns dx; weight grads are in buf.bwd and
+    buf.dw_router."""
+    r = buf.route
+    moe_combine_bwd(dy, buf.ffn["yp"], r["gates"], r["row_of"], buf.dyp, buf.dgates)
+    moe_route_bwd(r["gates"], buf.dgates, buf.dlogits_sel)
+    moe_grouped_ffn_bwd(buf.xp, w_gate, w_up, w_down, r["offsets"], buf.ffn["g"], buf.ffn["u"],
+                        buf.ffn["h"], buf.dyp, buf.bwd)
+    moe_permute_bwd(buf.bwd["dxp"], r["row_of"], r["topk_idx"], buf.dlogits_sel, w_router, buf.dx)
+    moe_router_wgrad(x, buf.dlogits_sel, r["src_tk"], r["offsets"], w_router.shape[1], buf.dw_router)
+    return buf.dx

@@ -1,0 +1,99 @@
+// common.h — internal helpers shared by the HIP sources of the MoE library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+
+struct moe_ctx {
+  int device = 0;
+  hipStream_t stream = nullptr;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  std::string last_error;
+};
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bf16 bits
+
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// fp32 -> bf16 with round-to-nearest-even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Packs two floats into one dword of two bf16 (lo = a).
+__device__ __forceinline__ uint32_t pack2bf(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static __device__ __forceinline__ float ld(const float* p, size_t i) { return p[i]; }
+  static __device__ __forceinline__ void st(float* p, size_t i, float v) { p[i] = v; }
+};
+template <>
+struct Elem<bf16_t> {
+  static __device__ __forceinline__ float ld(const bf16_t* p, size_t i) { return bf2f(p[i]); }
+  static __device__ __forceinline__ void st(bf16_t* p, size_t i, float v) { p[i] = f2bf(v); }
+};
+
+__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+}  // namespace moe
+
+// ---------------------------------------------------------------- host side
+namespace moe_host {
+
+inline moe_status fail(moe_ctx* ctx, moe_status st, const char* fmt, ...) {
+  if (ctx) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    ctx->last_error = buf;
+  }
+  return st;
+}
+
+inline moe_status check_launch(moe_ctx* ctx, const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(ctx, MOE_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t esize(moe_dtype dt) { return dt == MOE_F32 ? 4 : 2; }
+
+}  // namespace moe_host
+
+#define MOE_CHECK_CTX(ctx) \
+  do {                     \
+    if (!(ctx)) return MOE_ERR_INVALID_ARGUMENT; \
+  } while (0)
+
+#define MOE_REQUIRE(ctx, cond, ...)                                               \
+  do {                                                                            \
+    if (!(cond)) return moe_host::fail((ctx), MOE_ERR_INVALID_ARGUMENT, __VA_ARGS__); \
+  } while (0)
+
+#define MOE_REQUIRE_PTR(ctx, p) \
+  MOE_REQUIRE(ctx, (p) != nullptr && moe_host::aligned16(p), "%s: null or not 16-byte aligned", #p)
+
+#define MOE_REQUIRE_DTYPE(ctx, dt) \
+  MOE_REQUIRE(ctx, (dt) == MOE_F32 || (dt) == MOE_BF16, "unsupported dtype %d", (int)(dt))

@@ -1,0 +1,777 @@
+// gemm_bf16.hip — device-scheduled grouped GEMM for the SwiGLU experts on the
+// gfx950 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
+//
+// Pages: many small per-expert GEMMs are merged into one grouped GEMM so the
+// GPU is fed ([P1] 核心特点 二, Grouped GEMM); it is scheduled on the device from
+// GPU-resident routing metadata, with no host synchronisation ([P1] 二); the
+// layer is dropless ([P3]).  The pages' kernel is prior art for another GPU;
+// this one is written for CDNA4:
+//
+//  * Block tile BM x 256 (BM = 256 or 128) x BK = 64, four waves in a 2x2
+//    grid, each wave a (BM/2) x 128 sub-tile of 32x32 MFMA tiles.  One block
+//    per CU (128 KiB of LDS: two stages of A and B tiles).
+//  * Both tiles live in LDS K-contiguous (one 128-byte row per M/N index) with
+//    the 16-byte chunk index XOR-swizzled by (row & 7), so fragment reads
+//    (lanes on 32 consecutive rows, one 16-byte chunk each) are conflict-free.
+//    Operands that are K-strided in HBM (weights in the forward pass,
+//    activations in wgrad) are loaded as 8x8 blocks of 16-byte row pieces and
+//    transposed in registers before the LDS store.
+//  * Global loads for stage k+1 are issued before the MFMAs of stage k; one
+//    barrier per K step.
+//  * The MFMA operands are swapped (weights as the A operand) so each lane ends
+//    with four consecutive output columns per register group: 8-byte stores.
+//  * Scheduling: M-ragged launches (forward, dgrad) size the grid from the host
+//    bound sum_e ceil(n_e/BM) <= R/BM + E; every block scans the per-expert
+//    counts (from `offsets`, read on the device) to find its (expert, m-tile,
+//    n-tile); blocks past the real total exit.  Logical tiles are handed to
+//    the 8 XCDs in contiguous ranges (block b runs on XCD b % 8), and within an
+//    expert the m-tiles sharing one weight tile are consecutive, so they meet
+//    in the same L2.  K-ragged launches (wgrad) have a fixed tile grid per
+//    expert and loop over that expert's own rows; an expert with no rows
+//    writes zeros.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+enum Mode : int {
+  FWD_UP = 0,      // g,u,h = swiglu(xp Wg, xp Wu)            M-ragged, dual B, B N-contig
+  FWD_DOWN = 1,    // yp = h Wd                               M-ragged, B N-contig
+  DGRAD_DOWN = 2,  // dh = dyp Wd^T -> dg, du                  M-ragged, B K-contig
+  DGRAD_UP = 3,    // dxp = dg Wg^T + du Wu^T (two K segments) M-ragged, B K-contig
+  WGRAD_UP = 4,    // dWg, dWu = xp^T (dg | du)                K-ragged, dual B
+  WGRAD_DOWN = 5,  // dWd = h^T dyp                            K-ragged
+  ROUTER = 6       // logits = x W_r (one group, fp32 out)     M = T, B N-contig
+};
+
+template <int MODE>
+struct Traits {
+  static constexpr bool kA_KCONTIG = !(MODE == WGRAD_UP || MODE == WGRAD_DOWN);
+  static constexpr bool kB_KCONTIG = (MODE == DGRAD_DOWN || MODE == DGRAD_UP);
+  static constexpr bool kDUAL = (MODE == FWD_UP || MODE == WGRAD_UP);
+  static constexpr bool kKRAGGED = (MODE == WGRAD_UP || MODE == WGRAD_DOWN);
+  static constexpr bool kSINGLE = (MODE == ROUTER);
+};
+
+struct Params {
+  const bf16_t* a0;  // A operand (segment 0)
+  const bf16_t* a1;  // A operand, second K segment (DGRAD_UP)
+  int lda;
+  const bf16_t* b0;  // B operand (or first of the pair)
+  const bf16_t* b1;  // second B (dual) or second K segment (DGRAD_UP)
+  int ldb;
+  long long b_gstride;  // per-expert stride of B (weights); 0 if B is per-row data
+  void* c0;
+  void* c1;
+  void* c2;
+  int ldc;
+  long long c_gstride;  // per-expert stride of C (wgrad outputs)
+  const bf16_t* aux0;   // saved g (DGRAD_DOWN)
+  const bf16_t* aux1;   // saved u (DGRAD_DOWN)
+  const int32_t* offsets;
+  int E;
+  int M;      // fixed M (K-ragged: output rows; ROUTER: T)
+  int N;      // columns per output matrix
+  int K;      // fixed K (M-ragged)
+  int kseg;   // K of segment 0 (DGRAD_UP), else K
+  int ntiles;  // tiles along N
+  int mtiles;  // tiles along M (K-ragged)
+};
+
+constexpr int BN = 256;
+constexpr int BK = 64;
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 7)); }
+
+// Byte offset inside a K-contiguous LDS tile of the 16-byte chunk (row, chunk).
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * (BK * 2) + swz(row, chunk) * 16;
+}
+
+// 8x8 transpose of bf16: in[i] holds 8 values (i, 0..7); out[r] = (0..7, r).
+__device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
+  uint32_t w[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    w[i][0] = in[i].x;
+    w[i][1] = in[i].y;
+    w[i][2] = in[i].z;
+    w[i][3] = in[i].w;
+  }
+  uint32_t o[8][4];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t a = w[2 * p][r >> 1], b = w[2 * p + 1][r >> 1];
+      o[r][p] = (r & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) out[r] = make_uint4(o[r][0], o[r][1], o[r][2], o[r][3]);
+}
+
+// Column of the N-dim for LDS B-tile row j: which matrix (dual) and its column.
+template <bool DUAL>
+__device__ __forceinline__ void bcol(int nt, int j, int& sel, int& col) {
+  if (DUAL) {
+    const int wn = j >> 7, w = j & 127;
+    sel = w >> 6;
+    col = nt * 128 + wn * 64 + (w & 63);
+  } else {
+    sel = 0;
+    col = nt * BN + j;
+  }
+}
+
+template <int MODE, int BM>
+struct Tile {
+  using TR = Traits<MODE>;
+  static constexpr int WM = BM / 2;        // wave tile rows (M)
+  static constexpr int SM = WM / 32;       // 32-row subtiles per wave
+  static constexpr int A_CHUNKS = BM / 32;  // 16-byte chunks per thread (K-contig A)
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BN * BK * 2;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+};
+
+// Work description of one block.
+struct Work {
+  int e;         // expert (group)
+  int row0;      // first A row of the tile (M-ragged) / first K row of the group
+  int rows;      // valid rows of the tile (M-ragged) / K length of the group (K-ragged)
+  int m0;        // first output M index (K-ragged)
+  int nt;        // n-tile
+};
+
+// Block-wide search of (expert, tile) for logical tile L in an M-ragged launch.
+// Returns false when L is past the real total.
+template <int BM>
+__device__ bool find_mtile(const Params& p, int* sh, Work& w) {
+  const int tid = threadIdx.x;
+  const int per = (p.E + kThreads - 1) / kThreads;  // experts per thread (<= 4)
+  int cnt[4], til[4];
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * per + q;
+    cnt[q] = 0;
+    til[q] = 0;
+    if (q < per && e < p.E) {
+      cnt[q] = p.offsets[e + 1] - p.offsets[e];
+      til[q] = ((cnt[q] + BM - 1) / BM) * p.ntiles;
+    }
+    local += til[q];
+  }
+  // exclusive scan of `local` over the block
+  sh[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int add = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  const int total = sh[kThreads - 1];
+  int run = sh[tid] - local;
+  __syncthreads();
+  // logical tile of this block: contiguous ranges per XCD
+  const int per_xcd = (total + 7) / 8;
+  const int slot = blockIdx.x >> 3;
+  const int L = (blockIdx.x & 7) * per_xcd + slot;
+  const bool live = slot < per_xcd && L < total;
+  if (tid == 0) sh[kThreads] = -1;
+  __syncthreads();
+  if (live) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * per + q;
+      if (q < per && e < p.E && til[q] > 0 && L >= run && L < run + til[q]) {
+        const int mt_e = (cnt[q] + BM - 1) / BM;
+        const int local_t = L - run;
+        sh[kThreads] = e;
+        sh[kThreads + 1] = local_t % mt_e;  // m-tile
+        sh[kThreads + 2] = local_t / mt_e;  // n-tile
+      }
+      run += til[q];
+    }
+  }
+  __syncthreads();
+  const int e = sh[kThreads];
+  if (e < 0) return false;
+  const int mt = sh[kThreads + 1];
+  w.e = e;
+  w.nt = sh[kThreads + 2];
+  const int beg = p.offsets[e], end = p.offsets[e + 1];
+  w.row0 = beg + mt * BM;
+  w.rows = min(BM, end - w.row0);
+  w.m0 = 0;
+  return true;
+}
+
+template <int MODE, int BM>
+__global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
+  using TR = Traits<MODE>;
+  using TL = Tile<MODE, BM>;
+  constexpr int SM = TL::SM;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ int sh[kThreads + 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  // ---------------------------------------------------------------- work
+  Work w;
+  if (TR::kKRAGGED) {
+    // fixed grid: expert-major, then n-tile, then m-tile; XCD-contiguous
+    const int total = p.E * p.ntiles * p.mtiles;
+    const int per_xcd = (total + 7) / 8;
+    const int slot = blockIdx.x >> 3;
+    const int L = (blockIdx.x & 7) * per_xcd + slot;
+    if (slot >= per_xcd || L >= total) return;
+    const int per_e = p.ntiles * p.mtiles;
+    w.e = L / per_e;
+    const int r = L % per_e;
+    w.nt = r / p.mtiles;
+    w.m0 = (r % p.mtiles) * BM;
+    w.row0 = p.offsets[w.e];
+    w.rows = p.offsets[w.e + 1] - w.row0;
+  } else if (TR::kSINGLE) {
+    const int mt_total = (p.M + BM - 1) / BM;
+    const int total = mt_total * p.ntiles;
+    const int per_xcd = (total + 7) / 8;
+    const int slot = blockIdx.x >> 3;
+    const int L = (blockIdx.x & 7) * per_xcd + slot;
+    if (slot >= per_xcd || L >= total) return;
+    w.e = 0;
+    w.nt = L / mt_total;
+    w.row0 = (L % mt_total) * BM;
+    w.rows = min(BM, p.M - w.row0);
+    w.m0 = 0;
+  } else {
+    if (!find_mtile<BM>(p, sh, w)) return;
+  }
+
+  const bf16_t* bbase0 = p.b0 + (size_t)w.e * p.b_gstride;
+  const bf16_t* bbase1 = p.b1 ? p.b1 + (size_t)w.e * p.b_gstride : nullptr;
+  const int nk = TR::kKRAGGED ? (w.rows + BK - 1) / BK : p.K / BK;
+
+  // ---------------------------------------------------------------- loaders
+  uint4 ra[8], rb[8];
+
+  auto load_a = [&](int kt) {
+    const int k0 = kt * BK;
+    if (TR::kA_KCONTIG) {
+      const bf16_t* a = p.a0;
+      int kk = k0;
+      if (MODE == DGRAD_UP && k0 >= p.kseg) {
+        a = p.a1;
+        kk = k0 - p.kseg;
+      }
+#pragma unroll
+      for (int i = 0; i < TL::A_CHUNKS; ++i) {
+        const int q = tid + i * kThreads;
+        const int row = q >> 3, kc = q & 7;
+        if (row < w.rows)
+          ra[i] = *reinterpret_cast<const uint4*>(a + (size_t)(w.row0 + row) * p.lda + kk + kc * 8);
+        else
+          ra[i] = make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      // M-contiguous A (wgrad): block (kc, mc) of 8 k-rows x 8 m values
+      const int kc = tid & 7, mc = tid >> 3;
+      const int m = w.m0 + mc * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = k0 + kc * 8 + i;
+        if (k < w.rows && m < p.M)
+          ra[i] = *reinterpret_cast<const uint4*>(p.a0 + (size_t)(w.row0 + k) * p.lda + m);
+        else
+          ra[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+
+  auto load_b = [&](int kt) {
+    const int k0 = kt * BK;
+    if (TR::kB_KCONTIG) {
+      const bf16_t* b = bbase0;
+      int kk = k0;
+      if (MODE == DGRAD_UP && k0 >= p.kseg) {
+        b = bbase1;
+        kk = k0 - p.kseg;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = tid + i * kThreads;
+        const int j = q >> 3, kc = q & 7;
+        const int col = w.nt * BN + j;
+        if (col < p.N)
+          rb[i] = *reinterpret_cast<const uint4*>(b + (size_t)col * p.ldb + kk + kc * 8);
+        else
+          rb[i] = make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const int kc = tid & 7, nc = tid >> 3;
+      int sel, col;
+      bcol<TR::kDUAL>(w.nt, nc * 8, sel, col);
+      const bf16_t* b = sel ? bbase1 : bbase0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int k = k0 + kc * 8 + i;
+        const bool kvalid = TR::kKRAGGED ? (k < w.rows) : true;
+        if (kvalid && col < p.N) {
+          const size_t krow = TR::kKRAGGED ? (size_t)(w.row0 + k) : (size_t)k;
+          rb[i] = *reinterpret_cast<const uint4*>(b + krow * p.ldb + col);
+        } else {
+          rb[i] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  auto store_tiles = [&](int stage) {
+    unsigned char* As = smem + stage * TL::STAGE;
+    unsigned char* Bs = As + TL::A_BYTES;
+    if (TR::kA_KCONTIG) {
+#pragma unroll
+      for (int i = 0; i < TL::A_CHUNKS; ++i) {
+        const int q = tid + i * kThreads;
+        const int row = q >> 3, kc = q & 7;
+        *reinterpret_cast<uint4*>(As + lds_off(row, kc)) = ra[i];
+      }
+    } else {
+      uint4 t[8];
+      transpose8(ra, t);
+      const int kc = tid & 7, mc = tid >> 3;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(As + lds_off(mc * 8 + r, kc)) = t[r];
+    }
+    if (TR::kB_KCONTIG) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int q = tid + i * kThreads;
+        const int j = q >> 3, kc = q & 7;
+        *reinterpret_cast<uint4*>(Bs + lds_off(j, kc)) = rb[i];
+      }
+    } else {
+      uint4 t[8];
+      transpose8(rb, t);
+      const int kc = tid & 7, nc = tid >> 3;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(Bs + lds_off(nc * 8 + r, kc)) = t[r];
+    }
+  };
+
+  // ---------------------------------------------------------------- main loop
+  f32x16 acc[SM][4];
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int frag_row = lane & 31;
+  const int frag_kc = lane >> 5;
+
+  if (nk > 0) {
+    load_a(0);
+    load_b(0);
+    store_tiles(0);
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) {
+      load_a(kt + 1);
+      load_b(kt + 1);
+    }
+    const unsigned char* As = smem + cur * TL::STAGE;
+    const unsigned char* Bs = As + TL::A_BYTES;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      bf16x8 xb[4], ya[SM];
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn) {
+        const int row = wn * 128 + sn * 32 + frag_row;
+        xb[sn] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(row, kk * 2 + frag_kc));
+      }
+#pragma unroll
+      for (int sm = 0; sm < SM; ++sm) {
+        const int row = wm * TL::WM + sm * 32 + frag_row;
+        ya[sm] = *reinterpret_cast<const bf16x8*>(As + lds_off(row, kk * 2 + frag_kc));
+      }
+#pragma unroll
+      for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+        for (int sn = 0; sn < 4; ++sn)
+          acc[sm][sn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[sn], ya[sm], acc[sm][sn], 0, 0, 0);
+    }
+    if (kt + 1 < nk) store_tiles(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // Lane holds C[m = mbase + (lane&31)][n = nbase + 8*(r/4) + 4*(lane>>5) + r%4].
+  const int ncol4 = 4 * (lane >> 5);
+#pragma unroll
+  for (int sm = 0; sm < SM; ++sm) {
+    const int mloc = wm * TL::WM + sm * 32 + (lane & 31);  // row inside the block tile
+    bool mvalid;
+    size_t crow;
+    if (TR::kKRAGGED) {
+      mvalid = (w.m0 + mloc) < p.M;
+      crow = (size_t)(w.m0 + mloc);
+    } else {
+      mvalid = mloc < w.rows;
+      crow = (size_t)(w.row0 + mloc);
+    }
+    if (!mvalid) continue;
+    if (TR::kDUAL) {
+#pragma unroll
+      for (int sn = 0; sn < 2; ++sn) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = w.nt * 128 + wn * 64 + sn * 32 + 8 * g4 + ncol4;
+          if (col >= p.N) continue;
+          float gv[4], uv[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            gv[r] = acc[sm][sn][g4 * 4 + r];
+            uv[r] = acc[sm][sn + 2][g4 * 4 + r];
+          }
+          if (MODE == FWD_UP) {
+            const size_t off = crow * p.ldc + col;
+            *reinterpret_cast<uint2*>((bf16_t*)p.c0 + off) =
+                make_uint2(pack2bf(gv[0], gv[1]), pack2bf(gv[2], gv[3]));
+            *reinterpret_cast<uint2*>((bf16_t*)p.c1 + off) =
+                make_uint2(pack2bf(uv[0], uv[1]), pack2bf(uv[2], uv[3]));
+            float hv[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) hv[r] = silu_f(gv[r]) * uv[r];
+            *reinterpret_cast<uint2*>((bf16_t*)p.c2 + off) =
+                make_uint2(pack2bf(hv[0], hv[1]), pack2bf(hv[2], hv[3]));
+          } else {  // WGRAD_UP
+            const size_t off = (size_t)w.e * p.c_gstride + crow * p.ldc + col;
+            *reinterpret_cast<uint2*>((bf16_t*)p.c0 + off) =
+                make_uint2(pack2bf(gv[0], gv[1]), pack2bf(gv[2], gv[3]));
+            *reinterpret_cast<uint2*>((bf16_t*)p.c1 + off) =
+                make_uint2(pack2bf(uv[0], uv[1]), pack2bf(uv[2], uv[3]));
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = w.nt * BN + wn * 128 + sn * 32 + 8 * g4 + ncol4;
+          if (col >= p.N) continue;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[sm][sn][g4 * 4 + r];
+          if (MODE == ROUTER) {
+            float* c = (float*)p.c0 + crow * p.ldc + col;
+            *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
+          } else if (MODE == DGRAD_DOWN) {
+            const size_t off = crow * p.ldc + col;
+            const uint2 graw = *reinterpret_cast<const uint2*>(p.aux0 + off);
+            const uint2 uraw = *reinterpret_cast<const uint2*>(p.aux1 + off);
+            const uint32_t gw[2] = {graw.x, graw.y}, uw[2] = {uraw.x, uraw.y};
+            float dg[4], du[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float g = __uint_as_float((r & 1) ? (gw[r >> 1] & 0xffff0000u) : (gw[r >> 1] << 16));
+              const float u = __uint_as_float((r & 1) ? (uw[r >> 1] & 0xffff0000u) : (uw[r >> 1] << 16));
+              const float s = sigmoid_f(g);
+              dg[r] = v[r] * u * s * (1.0f + g * (1.0f - s));
+              du[r] = v[r] * g * s;
+            }
+            *reinterpret_cast<uint2*>((bf16_t*)p.c0 + off) =
+                make_uint2(pack2bf(dg[0], dg[1]), pack2bf(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>((bf16_t*)p.c1 + off) =
+                make_uint2(pack2bf(du[0], du[1]), pack2bf(du[2], du[3]));
+          } else {
+            size_t off = crow * p.ldc + col;
+            if (TR::kKRAGGED) off += (size_t)w.e * p.c_gstride;
+            *reinterpret_cast<uint2*>((bf16_t*)p.c0 + off) =
+                make_uint2(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]));
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, int BM>
+hipError_t launch(const Params& p, int blocks, hipStream_t s) {
+  using TL = Tile<MODE, BM>;
+  const int smem = 2 * TL::STAGE;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_kernel<MODE, BM>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  blocks = (blocks + 7) / 8 * 8;
+  grouped_gemm_kernel<MODE, BM><<<blocks, kThreads, smem, s>>>(p);
+  return hipGetLastError();
+}
+
+// Upper bound of sum_e ceil(n_e / BM) over any split of R rows into E groups.
+int mtile_bound(int R, int E, int BM) { return R / BM + E; }
+
+}  // namespace
+
+// ---------------------------------------------------------------- host API
+using namespace moe_host;
+
+// Row-tile height for an M-ragged launch: 128 when the average expert holds
+// fewer than ~1000 rows (less padding in each expert's last tile), else 256.
+static int pick_bm(int R, int E) { return (R / (E > 0 ? E : 1)) < 1024 ? 128 : 256; }
+
+template <int MODE>
+static hipError_t launch_mragged(Params& p, int R, hipStream_t s) {
+  const int bm = pick_bm(R, p.E);
+  if (bm == 128) return launch<MODE, 128>(p, mtile_bound(R, p.E, 128) * p.ntiles, s);
+  return launch<MODE, 256>(p, mtile_bound(R, p.E, 256) * p.ntiles, s);
+}
+
+moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const void* wr, int T_,
+                                           int d, int E, float* logits) {
+  if (d % BK != 0)
+    return fail(ctx, MOE_ERR_UNSUPPORTED, "moe_router_logits: MFMA path needs d %% 64 == 0");
+  Params p{};
+  p.a0 = (const bf16_t*)x;
+  p.lda = d;
+  p.b0 = (const bf16_t*)wr;
+  p.ldb = E;
+  p.c0 = logits;
+  p.ldc = E;
+  p.M = T_;
+  p.N = E;
+  p.K = d;
+  p.kseg = d;
+  p.ntiles = (E + BN - 1) / BN;
+  p.E = 1;
+  const int blocks = ((T_ + 255) / 256) * p.ntiles;
+  hipError_t e = launch<ROUTER, 256>(p, blocks, ctx->stream);
+  if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "router GEMM: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+// fp32 path (gemm_f32.hip)
+moe_status moe_internal_ffn_fwd_f32(moe_ctx* ctx, const float* xp, const float* wg,
+                                    const float* wu, const float* wd, const int32_t* offsets,
+                                    int E, int R, int d, int F, float* g, float* u, float* h,
+                                    float* yp);
+moe_status moe_internal_ffn_bwd_f32(moe_ctx* ctx, const float* xp, const float* wg,
+                                    const float* wu, const float* wd, const int32_t* offsets,
+                                    const float* g, const float* u, const float* h,
+                                    const float* dyp, int E, int R, int d, int F, float* dg,
+                                    float* du, float* dxp, float* dwg, float* dwu, float* dwd);
+
+static moe_status ffn_validate(moe_ctx* ctx, int E, int R, int d, int F, moe_dtype dtype,
+                               const char* what) {
+  MOE_REQUIRE_DTYPE(ctx, dtype);
+  MOE_REQUIRE(ctx, E >= 1 && E <= 1024 && R >= 0 && d >= 8 && F >= 8 && d % 8 == 0 && F % 8 == 0,
+              "%s: bad shape E=%d R=%d d=%d F=%d", what, E, R, d, F);
+  if (dtype == MOE_BF16 && (d % 64 != 0 || F % 64 != 0))
+    return fail(ctx, MOE_ERR_UNSUPPORTED, "%s: bf16 path needs d and F multiples of 64", what);
+  return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
+                               const void* w_up, const void* w_down, const int32_t* offsets,
+                               int E, int R, int d, int F, moe_dtype dtype, void* g, void* u,
+                               void* h, void* yp) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = ffn_validate(ctx, E, R, d, F, dtype, "moe_grouped_ffn_fwd");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(ctx, xp);
+  MOE_REQUIRE_PTR(ctx, w_gate);
+  MOE_REQUIRE_PTR(ctx, w_up);
+  MOE_REQUIRE_PTR(ctx, w_down);
+  MOE_REQUIRE_PTR(ctx, offsets);
+  MOE_REQUIRE_PTR(ctx, g);
+  MOE_REQUIRE_PTR(ctx, u);
+  MOE_REQUIRE_PTR(ctx, h);
+  MOE_REQUIRE_PTR(ctx, yp);
+  if (R == 0) return MOE_OK;
+  if (dtype == MOE_F32)
+    return moe_internal_ffn_fwd_f32(ctx, (const float*)xp, (const float*)w_gate,
+                                    (const float*)w_up, (const float*)w_down, offsets, E, R, d, F,
+                                    (float*)g, (float*)u, (float*)h, (float*)yp);
+  hipError_t e;
+  {
+    Params p{};
+    p.a0 = (const bf16_t*)xp;
+    p.lda = d;
+    p.b0 = (const bf16_t*)w_gate;
+    p.b1 = (const bf16_t*)w_up;
+    p.ldb = F;
+    p.b_gstride = (long long)d * F;
+    p.c0 = g;
+    p.c1 = u;
+    p.c2 = h;
+    p.ldc = F;
+    p.offsets = offsets;
+    p.E = E;
+    p.N = F;
+    p.K = d;
+    p.kseg = d;
+    p.ntiles = (F + 127) / 128;
+    e = launch_mragged<FWD_UP>(p, R, ctx->stream);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up GEMM: %s", hipGetErrorString(e));
+  }
+  {
+    Params p{};
+    p.a0 = (const bf16_t*)h;
+    p.lda = F;
+    p.b0 = (const bf16_t*)w_down;
+    p.ldb = d;
+    p.b_gstride = (long long)F * d;
+    p.c0 = yp;
+    p.ldc = d;
+    p.offsets = offsets;
+    p.E = E;
+    p.N = d;
+    p.K = F;
+    p.kseg = F;
+    p.ntiles = (d + BN - 1) / BN;
+    e = launch_mragged<FWD_DOWN>(p, R, ctx->stream);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down GEMM: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
+                               const void* w_up, const void* w_down, const int32_t* offsets,
+                               const void* g, const void* u, const void* h, const void* dyp,
+                               int E, int R, int d, int F, moe_dtype dtype, void* dg, void* du,
+                               void* dxp, void* dw_gate, void* dw_up, void* dw_down) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = ffn_validate(ctx, E, R, d, F, dtype, "moe_grouped_ffn_bwd");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(ctx, xp);
+  MOE_REQUIRE_PTR(ctx, w_gate);
+  MOE_REQUIRE_PTR(ctx, w_up);
+  MOE_REQUIRE_PTR(ctx, w_down);
+  MOE_REQUIRE_PTR(ctx, offsets);
+  MOE_REQUIRE_PTR(ctx, g);
+  MOE_REQUIRE_PTR(ctx, u);
+  MOE_REQUIRE_PTR(ctx, h);
+  MOE_REQUIRE_PTR(ctx, dyp);
+  MOE_REQUIRE_PTR(ctx, dg);
+  MOE_REQUIRE_PTR(ctx, du);
+  MOE_REQUIRE_PTR(ctx, dxp);
+  MOE_REQUIRE_PTR(ctx, dw_gate);
+  MOE_REQUIRE_PTR(ctx, dw_up);
+  MOE_REQUIRE_PTR(ctx, dw_down);
+  if (dtype == MOE_F32)
+    return moe_internal_ffn_bwd_f32(ctx, (const float*)xp, (const float*)w_gate,
+                                    (const float*)w_up, (const float*)w_down, offsets,
+                                    (const float*)g, (const float*)u, (const float*)h,
+                                    (const float*)dyp, E, R, d, F, (float*)dg, (float*)du,
+                                    (float*)dxp, (float*)dw_gate, (float*)dw_up, (float*)dw_down);
+  hipError_t e;
+  if (R > 0) {
+    // down dgrad with the SwiGLU backward in the epilogue
+    Params p{};
+    p.a0 = (const bf16_t*)dyp;
+    p.lda = d;
+    p.b0 = (const bf16_t*)w_down;  // B[k=c][n=f] = Wd[f][c]: rows of Wd are K-contiguous
+    p.ldb = d;
+    p.b_gstride = (long long)F * d;
+    p.c0 = dg;
+    p.c1 = du;
+    p.ldc = F;
+    p.aux0 = (const bf16_t*)g;
+    p.aux1 = (const bf16_t*)u;
+    p.offsets = offsets;
+    p.E = E;
+    p.N = F;
+    p.K = d;
+    p.kseg = d;
+    p.ntiles = (F + BN - 1) / BN;
+    e = launch_mragged<DGRAD_DOWN>(p, R, ctx->stream);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down dgrad: %s", hipGetErrorString(e));
+  }
+  {
+    // down wgrad: dWd[e] = h_e^T dyp_e (M = F, N = d, K = rows of e)
+    Params p{};
+    p.a0 = (const bf16_t*)h;
+    p.lda = F;
+    p.b0 = (const bf16_t*)dyp;
+    p.ldb = d;
+    p.c0 = dw_down;
+    p.ldc = d;
+    p.c_gstride = (long long)F * d;
+    p.offsets = offsets;
+    p.E = E;
+    p.M = F;
+    p.N = d;
+    p.ntiles = (d + BN - 1) / BN;
+    p.mtiles = (F + 255) / 256;
+    e = launch<WGRAD_DOWN, 256>(p, E * p.ntiles * p.mtiles, ctx->stream);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down wgrad: %s", hipGetErrorString(e));
+  }
+  if (R > 0) {
+    // gate/up dgrad: dxp = dg Wg^T + du Wu^T (K = 2F in two segments)
+    Params p{};
+    p.a0 = (const bf16_t*)dg;
+    p.a1 = (const bf16_t*)du;
+    p.lda = F;
+    p.b0 = (const bf16_t*)w_gate;  // B[k=f][n=i] = Wg[i][f]: rows of Wg are K-contiguous
+    p.b1 = (const bf16_t*)w_up;
+    p.ldb = F;
+    p.b_gstride = (long long)d * F;
+    p.c0 = dxp;
+    p.ldc = d;
+    p.offsets = offsets;
+    p.E = E;
+    p.N = d;
+    p.K = 2 * F;
+    p.kseg = F;
+    p.ntiles = (d + BN - 1) / BN;
+    e = launch_mragged<DGRAD_UP>(p, R, ctx->stream);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up dgrad: %s", hipGetErrorString(e));
+  }
+  {
+    // gate/up wgrad: dWg[e] = xp_e^T dg_e, dWu[e] = xp_e^T du_e (M = d, N = F each)
+    Params p{};
+    p.a0 = (const bf16_t*)xp;
+    p.lda = d;
+    p.b0 = (const bf16_t*)dg;
+    p.b1 = (const bf16_t*)du;
+    p.ldb = F;
+    p.c0 = dw_gate;
+    p.c1 = dw_up;
+    p.ldc = F;
+    p.c_gstride = (long long)d * F;
+    p.offsets = offsets;
+    p.E = E;
+    p.M = d;
+    p.N = F;
+    p.ntiles = (F + 127) / 128;
+    p.mtiles = (d + 255) / 256;
+    e = launch<WGRAD_UP, 256>(p, E * p.ntiles * p.mtiles, ctx->stream);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up wgrad: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+}  // extern "C"

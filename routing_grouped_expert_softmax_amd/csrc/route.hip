@@ -1,0 +1,489 @@
+// route.hip — router scores, softmax top-k, expert histogram, scan and the
+// stable expert-major permutation; routing backward and router wgrad.
+//
+// Pages: a router scores each token, the top-k experts are chosen and the
+// choice becomes a permutation index ([P2] 1.1, 2.1); the routing metadata
+// stays resident on the GPU ([P1] 核心特点 二, GPU-resident routing).
+//
+// Device layout of the routing workspace: block_counts[E][nblk] int32 with
+// nblk = ceil(T / 256): expert-major, so the scan kernel reads each expert's
+// per-block counts contiguously.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kTokBlock = 256;  // tokens per routing block (one per thread)
+
+// ---------------------------------------------------------------- scores
+// Small-E router scores on the vector ALUs: one wave per token at a time; each
+// lane takes 16-byte chunks of the token's row and the matching rows of W_r
+// (E contiguous values per feature), accumulating all E dot products in
+// registers; the E partial sums are reduced across the wave in a fixed order.
+// (Large E uses the MFMA grouped GEMM with a single group; see gemm_bf16.hip.)
+template <typename T, int EMAX, bool EXACT>
+__global__ void __launch_bounds__(256) router_logits_small_kernel(const T* __restrict__ x,
+                                                                  const T* __restrict__ wr, int T_,
+                                                                  int d, int E,
+                                                                  float* __restrict__ logits) {
+  constexpr int V = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nwaves = (gridDim.x * blockDim.x) >> 6;
+  const int nchunk = d / V;
+  float acc[EMAX];
+  for (int t = wave; t < T_; t += nwaves) {
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) acc[e] = 0.f;
+    const T* xr = x + (size_t)t * d;
+    for (int c = lane; c < nchunk; c += 64) {
+      const uint4 xraw = *reinterpret_cast<const uint4*>(xr + (size_t)c * V);
+      const T* xv = reinterpret_cast<const T*>(&xraw);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float xf = Elem<T>::ld(xv, v);
+        const T* wrow = wr + (size_t)(c * V + v) * E;
+        if constexpr (EXACT) {
+          constexpr int NV = EMAX * sizeof(T) / 16;
+#pragma unroll
+          for (int q = 0; q < NV; ++q) {
+            const uint4 wraw = *reinterpret_cast<const uint4*>(wrow + q * V);
+            const T* wv = reinterpret_cast<const T*>(&wraw);
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[q * V + i] += xf * Elem<T>::ld(wv, i);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < EMAX; ++e)
+            if (e < E) acc[e] += xf * Elem<T>::ld(wrow, e);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      float v = acc[e];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      acc[e] = v;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e)
+        if (e < E) logits[(size_t)t * E + e] = acc[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- top-k
+// One thread per token.  The experts are visited in ascending index; a
+// candidate enters the kept list only if its logit is strictly larger than
+// the k-th kept one, and lands behind every kept expert with an equal or
+// larger logit, so the list is ordered by (logit descending, index
+// ascending).  NaN scores count as -inf.  Gates are the softmax over the k
+// kept logits.  Each block also counts its tokens' experts in LDS and writes
+// its histogram column to the workspace.
+template <int KMAX>
+__global__ void __launch_bounds__(kTokBlock) topk_hist_kernel(
+    const float* __restrict__ logits, int T_, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ gates, int32_t* __restrict__ block_counts, int nblk) {
+  __shared__ int hist[1024];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kTokBlock + threadIdx.x;
+  if (t < T_) {
+    float val[KMAX];
+    int idx[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      val[i] = -INFINITY;
+      idx[i] = -1;
+    }
+    const float* l = logits + (size_t)t * E;
+    for (int e = 0; e < E; ++e) {
+      float v = l[e];
+      if (v != v) v = -INFINITY;
+      // position = number of kept experts that stay ahead of this one
+      int p = 0;
+      bool enter = false;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i) {
+        if (i < k) {
+          bool ahead = idx[i] >= 0 && val[i] >= v;
+          p += ahead ? 1 : 0;
+        }
+      }
+      enter = p < k;
+      if (enter) {
+#pragma unroll
+        for (int i = KMAX - 1; i > 0; --i) {
+          if (i < k && i > p) {
+            val[i] = val[i - 1];
+            idx[i] = idx[i - 1];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i) {
+          if (i == p) {
+            val[i] = v;
+            idx[i] = e;
+          }
+        }
+      }
+    }
+    // softmax over the kept logits (val[0] is the largest)
+    float m = val[0];
+    float z = 0.f;
+    float ex[KMAX];
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      ex[i] = (i < k) ? expf(val[i] - m) : 0.f;
+      z += ex[i];
+    }
+    const float inv = 1.0f / z;
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      if (i < k) {
+        topk_idx[(size_t)t * k + i] = idx[i];
+        gates[(size_t)t * k + i] = ex[i] * inv;
+        atomicAdd(&hist[idx[i]], 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x)
+    block_counts[(size_t)e * nblk + blockIdx.x] = hist[e];
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x == 256).
+__device__ int block_exclusive_scan(int v, int* sh /*[256]*/, int* total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    int add = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  int incl = sh[tid];
+  if (total) *total = sh[255];
+  __syncthreads();
+  return incl - v;
+}
+
+// One block per expert: exclusive scan of the expert's per-block counts (in
+// place: block_counts becomes each block's base row inside the expert) and the
+// expert's total count.
+__global__ void __launch_bounds__(256) expert_scan_kernel(int32_t* __restrict__ block_counts,
+                                                          int nblk, int32_t* __restrict__ counts) {
+  __shared__ int sh[256];
+  const int e = blockIdx.x;
+  int32_t* col = block_counts + (size_t)e * nblk;
+  const int per = (nblk + 255) / 256;
+  const int b0 = threadIdx.x * per;
+  int local = 0;
+  for (int i = 0; i < per; ++i)
+    if (b0 + i < nblk) local += col[b0 + i];
+  int total;
+  int run = block_exclusive_scan(local, sh, &total);
+  for (int i = 0; i < per; ++i) {
+    if (b0 + i < nblk) {
+      int c = col[b0 + i];
+      col[b0 + i] = run;
+      run += c;
+    }
+  }
+  if (threadIdx.x == 0) counts[e] = total;
+}
+
+// Offsets (exclusive scan over experts, recomputed by every block from the
+// counts) and the stable ranks: the row of (t,j) with e = topk[t,j] is
+// offsets[e] + (rows of e in earlier blocks) + (earlier tokens of this block
+// that chose e).  Experts within a token are distinct, so only earlier tokens
+// matter.
+template <int KMAX>
+__global__ void __launch_bounds__(kTokBlock) rank_kernel(
+    const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ block_counts, int nblk,
+    const int32_t* __restrict__ counts, int T_, int E, int k, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_of, int32_t* __restrict__ src_tk) {
+  __shared__ int sh[256];
+  __shared__ int offs[1025];
+  __shared__ int sel[kTokBlock * KMAX];
+  const int tid = threadIdx.x;
+  // offsets: each thread owns up to 4 consecutive experts
+  int c[4];
+  int local = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int e = tid * 4 + q;
+    c[q] = e < E ? counts[e] : 0;
+    local += c[q];
+  }
+  int total;
+  int run = block_exclusive_scan(local, sh, &total);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int e = tid * 4 + q;
+    if (e < E) offs[e] = run;
+    run += c[q];
+  }
+  if (tid == 0) offs[E] = total;
+  const int tbase = blockIdx.x * kTokBlock;
+  const int t = tbase + tid;
+  const int ntok = min(kTokBlock, T_ - tbase);
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (j < k) sel[tid * KMAX + j] = (tid < ntok) ? topk_idx[(size_t)t * k + j] : -1;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
+  if (tid >= ntok) return;
+  int mine[KMAX], rank[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    mine[j] = (j < k) ? sel[tid * KMAX + j] : -2;
+    rank[j] = 0;
+  }
+  for (int tp = 0; tp < tid; ++tp) {
+#pragma unroll
+    for (int jp = 0; jp < KMAX; ++jp) {
+      if (jp < k) {
+        int o = sel[tp * KMAX + jp];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) rank[j] += (o == mine[j]) ? 1 : 0;
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    if (j < k) {
+      const int e = mine[j];
+      const int row = offs[e] + block_counts[(size_t)e * nblk + blockIdx.x] + rank[j];
+      const int flat = t * k + j;
+      row_of[flat] = row;
+      src_tk[row] = flat;
+    }
+  }
+}
+
+template <int KMAX>
+void launch_route(const float* logits, int T_, int E, int k, int32_t* topk_idx, float* gates,
+                  int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_tk,
+                  int32_t* block_counts, int nblk, hipStream_t s) {
+  topk_hist_kernel<KMAX><<<nblk, kTokBlock, 0, s>>>(logits, T_, E, k, topk_idx, gates,
+                                                    block_counts, nblk);
+  expert_scan_kernel<<<E, 256, 0, s>>>(block_counts, nblk, counts);
+  rank_kernel<KMAX><<<nblk, kTokBlock, 0, s>>>(topk_idx, block_counts, nblk, counts, T_, E, k,
+                                               offsets, row_of, src_tk);
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int n, int v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ---------------------------------------------------------------- backward
+__global__ void route_bwd_kernel(const float* __restrict__ gates, const float* __restrict__ dgates,
+                                 int T_, int k, float* __restrict__ dls) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T_) return;
+  const float* g = gates + (size_t)t * k;
+  const float* dg = dgates + (size_t)t * k;
+  float s = 0.f;
+  for (int j = 0; j < k; ++j) s += g[j] * dg[j];
+  for (int j = 0; j < k; ++j) dls[(size_t)t * k + j] = g[j] * (dg[j] - s);
+}
+
+// Router weight gradient.  One block per (expert, 64-feature chunk): the
+// block's row groups walk the expert's rows (fixed stride), each lane
+// accumulating a 16-byte chunk of features in fp32; the row groups are then
+// summed in a fixed order, so the result is deterministic.
+template <typename T>
+__global__ void __launch_bounds__(256) router_wgrad_kernel(
+    const T* __restrict__ x, const float* __restrict__ dls, const int32_t* __restrict__ src_tk,
+    const int32_t* __restrict__ offsets, int d, int E, int k, T* __restrict__ dwr) {
+  constexpr int V = 16 / sizeof(T);       // features per lane
+  constexpr int LPR = 64 / V;             // lanes per 64-feature row chunk
+  constexpr int NG = 256 / LPR;           // row groups
+  __shared__ float part[NG][64];
+  const int e = blockIdx.y;
+  const int f0 = blockIdx.x * 64;
+  const int lane = threadIdx.x % LPR;
+  const int grp = threadIdx.x / LPR;
+  const int r0 = offsets[e], r1 = offsets[e + 1];
+  float acc[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) acc[v] = 0.f;
+  const int fi = f0 + lane * V;
+  if (fi < d) {
+    for (int r = r0 + grp; r < r1; r += NG) {
+      const int flat = src_tk[r];
+      const float w = dls[flat];
+      const T* xr = x + (size_t)(flat / k) * d + fi;
+      const uint4 raw = *reinterpret_cast<const uint4*>(xr);
+      const T* xv = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] += w * Elem<T>::ld(xv, v);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v) part[grp][lane * V + v] = acc[v];
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int f = f0 + threadIdx.x;
+    float s = 0.f;
+    for (int g = 0; g < NG; ++g) s += part[g][threadIdx.x];
+    if (f < d) Elem<T>::st(dwr, (size_t)f * E + e, s);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- C ABI
+using namespace moe_host;
+
+static size_t route_ws_bytes(int T_, int E) {
+  const size_t nblk = (size_t)(T_ + kTokBlock - 1) / kTokBlock;
+  return ((size_t)E * nblk * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+// Router-transpose scratch used by moe_permute_bwd (W_r^T, [E,d]).
+size_t moe_internal_wrt_bytes(int d, int E, moe_dtype dt) {
+  return ((size_t)d * E * esize(dt) + 255) & ~(size_t)255;
+}
+
+// Defined in gemm_bf16.hip: router scores through the MFMA GEMM.
+moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const void* wr, int T_,
+                                           int d, int E, float* logits);
+
+extern "C" {
+
+moe_status moe_workspace_size(moe_ctx* ctx, int T_, int d, int E, int k, moe_dtype dtype,
+                              size_t* bytes) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE_DTYPE(ctx, dtype);
+  MOE_REQUIRE(ctx, bytes != nullptr, "bytes is null");
+  MOE_REQUIRE(ctx, T_ >= 0 && d >= 8 && E >= 1 && E <= 1024 && k >= 1 && k <= E && k <= 32,
+              "bad shape T=%d d=%d E=%d k=%d", T_, d, E, k);
+  const size_t a = route_ws_bytes(T_, E), b = moe_internal_wrt_bytes(d, E, dtype);
+  *bytes = a > b ? a : b;
+  return MOE_OK;
+}
+
+moe_status moe_router_logits(moe_ctx* ctx, const void* x, const void* w_router, int T_, int d,
+                             int E, moe_dtype dtype, float* logits) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE_DTYPE(ctx, dtype);
+  MOE_REQUIRE(ctx, T_ >= 0 && d >= 8 && d % 8 == 0 && E >= 1 && E <= 1024,
+              "moe_router_logits: bad shape T=%d d=%d E=%d", T_, d, E);
+  MOE_REQUIRE_PTR(ctx, x);
+  MOE_REQUIRE_PTR(ctx, w_router);
+  MOE_REQUIRE_PTR(ctx, logits);
+  if (T_ == 0) return MOE_OK;
+  if (dtype == MOE_BF16 && E > 16 && E % 8 == 0)
+    return moe_internal_router_logits_mfma(ctx, x, w_router, T_, d, E, logits);
+  const int blocks = std::min(1024, (T_ + 3) / 4);
+#define RL_LAUNCH(TY, EM, EX)                                                                   \
+  router_logits_small_kernel<TY, EM, EX><<<blocks, 256, 0, ctx->stream>>>(                      \
+      (const TY*)x, (const TY*)w_router, T_, d, E, logits)
+#define RL_CASE(EM)                                                                             \
+  if (E <= EM) {                                                                                \
+    if (dtype == MOE_BF16) {                                                                    \
+      if (E == EM && (EM * 2) % 16 == 0) RL_LAUNCH(bf16_t, EM, (EM * 2) % 16 == 0);             \
+      else RL_LAUNCH(bf16_t, EM, false);                                                        \
+    } else {                                                                                    \
+      if (E == EM && (EM * 4) % 16 == 0) RL_LAUNCH(float, EM, (EM * 4) % 16 == 0);              \
+      else RL_LAUNCH(float, EM, false);                                                         \
+    }                                                                                           \
+    return check_launch(ctx, "moe_router_logits");                                              \
+  }
+  RL_CASE(4)
+  RL_CASE(8)
+  RL_CASE(16)
+  RL_CASE(32)
+  RL_CASE(64)
+#undef RL_CASE
+#undef RL_LAUNCH
+  return fail(ctx, MOE_ERR_UNSUPPORTED,
+              "moe_router_logits: E=%d needs bf16 with E %% 8 == 0 (MFMA path)", E);
+}
+
+moe_status moe_route(moe_ctx* ctx, const float* logits, int T_, int E, int k, int32_t* topk_idx,
+                     float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                     int32_t* src_tk) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, T_ >= 0 && E >= 1 && E <= 1024 && k >= 1 && k <= E && k <= 32,
+              "moe_route: bad shape T=%d E=%d k=%d", T_, E, k);
+  MOE_REQUIRE(ctx, (int64_t)T_ * k < (int64_t)1 << 31, "moe_route: T*k >= 2^31");
+  MOE_REQUIRE_PTR(ctx, logits);
+  MOE_REQUIRE_PTR(ctx, topk_idx);
+  MOE_REQUIRE_PTR(ctx, gates);
+  MOE_REQUIRE_PTR(ctx, counts);
+  MOE_REQUIRE_PTR(ctx, offsets);
+  MOE_REQUIRE_PTR(ctx, row_of);
+  MOE_REQUIRE_PTR(ctx, src_tk);
+  const size_t need = route_ws_bytes(T_, E);
+  if (ctx->ws == nullptr || ctx->ws_bytes < need)
+    return fail(ctx, MOE_ERR_WORKSPACE, "moe_route: workspace %zu bytes < %zu needed",
+                ctx->ws_bytes, need);
+  const int nblk = (T_ + kTokBlock - 1) / kTokBlock;
+  int32_t* bc = reinterpret_cast<int32_t*>(ctx->ws);
+  if (T_ == 0) {
+    // no tokens: every count and offset is zero
+    fill_i32_kernel<<<(E + 256) / 256, 256, 0, ctx->stream>>>(counts, E, 0);
+    fill_i32_kernel<<<(E + 256) / 256, 256, 0, ctx->stream>>>(offsets, E + 1, 0);
+    return check_launch(ctx, "moe_route");
+  }
+  if (k <= 2)
+    launch_route<2>(logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk, bc, nblk,
+                    ctx->stream);
+  else if (k <= 4)
+    launch_route<4>(logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk, bc, nblk,
+                    ctx->stream);
+  else if (k <= 8)
+    launch_route<8>(logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk, bc, nblk,
+                    ctx->stream);
+  else
+    launch_route<32>(logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk, bc, nblk,
+                     ctx->stream);
+  return check_launch(ctx, "moe_route");
+}
+
+moe_status moe_route_bwd(moe_ctx* ctx, const float* gates, const float* dgates, int T_, int k,
+                         float* dlogits_sel) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, T_ >= 0 && k >= 1 && k <= 32, "moe_route_bwd: bad shape T=%d k=%d", T_, k);
+  MOE_REQUIRE_PTR(ctx, gates);
+  MOE_REQUIRE_PTR(ctx, dgates);
+  MOE_REQUIRE_PTR(ctx, dlogits_sel);
+  if (T_ == 0) return MOE_OK;
+  route_bwd_kernel<<<(T_ + 255) / 256, 256, 0, ctx->stream>>>(gates, dgates, T_, k, dlogits_sel);
+  return check_launch(ctx, "moe_route_bwd");
+}
+
+moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_sel,
+                            const int32_t* src_tk, const int32_t* offsets, int T_, int d, int E,
+                            int k, moe_dtype dtype, void* dw_router) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE_DTYPE(ctx, dtype);
+  MOE_REQUIRE(ctx, T_ >= 0 && d >= 8 && d % 8 == 0 && E >= 1 && E <= 1024 && k >= 1 && k <= E,
+              "moe_router_wgrad: bad shape");
+  MOE_REQUIRE_PTR(ctx, x);
+  MOE_REQUIRE_PTR(ctx, dlogits_sel);
+  MOE_REQUIRE_PTR(ctx, src_tk);
+  MOE_REQUIRE_PTR(ctx, offsets);
+  MOE_REQUIRE_PTR(ctx, dw_router);
+  dim3 grid((d + 63) / 64, E);
+  if (dtype == MOE_BF16)
+    router_wgrad_kernel<bf16_t><<<grid, 256, 0, ctx->stream>>>(
+        (const bf16_t*)x, dlogits_sel, src_tk, offsets, d, E, k, (bf16_t*)dw_router);
+  else
+    router_wgrad_kernel<float><<<grid, 256, 0, ctx->stream>>>(
+        (const float*)x, dlogits_sel, src_tk, offsets, d, E, k, (float*)dw_router);
+  return check_launch(ctx, "moe_router_wgrad");
+}
+
+}  // extern "C"

@@ -1,0 +1,381 @@
+// rows.hip — row movement: rowwise permute into the expert buffers, the
+// gate-weighted unpermute-combine, and their backward passes.
+//
+// Pages: routed rows are written straight into the experts' input buffers
+// ([P1] 核心特点 二, rowwise expert parallelism); results return along the
+// original path and are restored to token order ([P2] 2.1); the backward moves
+// every token again ([P2] 1.2).
+//
+// All four kernels are HBM-bound row copies: one wave owns one token at a time
+// and moves its rows in 16-byte lane chunks (1 KiB per wave instruction), so
+// every global access is a fully coalesced 16-byte vector access.  The k row
+// indices of the token are wave-uniform scalar loads.
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+template <typename T>
+struct Vec {
+  static constexpr int N = 16 / sizeof(T);
+};
+
+__device__ __forceinline__ void unpack(const uint4& r, float (&f)[8], bf16_t) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack(const uint4& r, float (&f)[4], float) {
+  f[0] = __uint_as_float(r.x);
+  f[1] = __uint_as_float(r.y);
+  f[2] = __uint_as_float(r.z);
+  f[3] = __uint_as_float(r.w);
+}
+__device__ __forceinline__ uint4 pack(const float (&f)[8], bf16_t) {
+  return make_uint4(pack2bf(f[0], f[1]), pack2bf(f[2], f[3]), pack2bf(f[4], f[5]),
+                    pack2bf(f[6], f[7]));
+}
+__device__ __forceinline__ uint4 pack(const float (&f)[4], float) {
+  return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                    __float_as_uint(f[3]));
+}
+
+constexpr int kWaves = 4;  // waves per block; one token per wave at a time
+
+// xp[row_of[t,j]] = x[t]: read each token row once, write its k copies.
+template <int KMAX>
+__global__ void __launch_bounds__(256) permute_kernel(const uint4* __restrict__ x,
+                                                      const int32_t* __restrict__ row_of, int T_,
+                                                      int nchunk, int k, uint4* __restrict__ xp) {
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int nw = gridDim.x * kWaves;
+  for (int t = wave; t < T_; t += nw) {
+    int rows[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) rows[j] = j < k ? row_of[(size_t)t * k + j] : 0;
+    const uint4* src = x + (size_t)t * nchunk;
+    for (int c = lane; c < nchunk; c += 64) {
+      const uint4 v = src[c];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) xp[(size_t)rows[j] * nchunk + c] = v;
+    }
+  }
+}
+
+// y[t] = sum_j gates[t,j] * yp[row_of[t,j]], slot order, fp32 sums.
+template <typename T, int KMAX>
+__global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ yp,
+                                                      const float* __restrict__ gates,
+                                                      const int32_t* __restrict__ row_of, int T_,
+                                                      int nchunk, int k, uint4* __restrict__ y) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int nw = gridDim.x * kWaves;
+  for (int t = wave; t < T_; t += nw) {
+    int rows[KMAX];
+    float g[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      rows[j] = j < k ? row_of[(size_t)t * k + j] : 0;
+      g[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
+    }
+    for (int c = lane; c < nchunk; c += 64) {
+      float acc[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+          float f[V];
+          unpack(yp[(size_t)rows[j] * nchunk + c], f, T());
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] += g[j] * f[i];
+        }
+      }
+      y[(size_t)t * nchunk + c] = pack(acc, T());
+    }
+  }
+}
+
+// dyp[row_of[t,j]] = gates[t,j] * dy[t];  dgates[t,j] = <dy[t], yp[row_of[t,j]]>.
+// The dot products are lane partials reduced across the wave in a fixed order.
+template <typename T, int KMAX>
+__global__ void __launch_bounds__(256) combine_bwd_kernel(
+    const uint4* __restrict__ dy, const uint4* __restrict__ yp, const float* __restrict__ gates,
+    const int32_t* __restrict__ row_of, int T_, int nchunk, int k, uint4* __restrict__ dyp,
+    float* __restrict__ dgates) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int nw = gridDim.x * kWaves;
+  for (int t = wave; t < T_; t += nw) {
+    int rows[KMAX];
+    float g[KMAX], dot[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      rows[j] = j < k ? row_of[(size_t)t * k + j] : 0;
+      g[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
+      dot[j] = 0.f;
+    }
+    for (int c = lane; c < nchunk; c += 64) {
+      float d[V];
+      unpack(dy[(size_t)t * nchunk + c], d, T());
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+          float f[V], o[V];
+          unpack(yp[(size_t)rows[j] * nchunk + c], f, T());
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            dot[j] += d[i] * f[i];
+            o[i] = g[j] * d[i];
+          }
+          dyp[(size_t)rows[j] * nchunk + c] = pack(o, T());
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      float v = dot[j];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+      dot[j] = v;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k) dgates[(size_t)t * k + j] = dot[j];
+    }
+  }
+}
+
+// dx[t] = sum_j dxp[row_of[t,j]] + sum_j dl[t,j] * W_r^T[topk[t,j]]  (router
+// term optional; W_r^T is [E,d], made by transpose_kernel).
+template <typename T, int KMAX, bool ROUTER>
+__global__ void __launch_bounds__(256) permute_bwd_kernel(
+    const uint4* __restrict__ dxp, const int32_t* __restrict__ row_of,
+    const int32_t* __restrict__ topk, const float* __restrict__ dls,
+    const uint4* __restrict__ wrt, int T_, int nchunk, int k, uint4* __restrict__ dx) {
+  constexpr int V = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int nw = gridDim.x * kWaves;
+  for (int t = wave; t < T_; t += nw) {
+    int rows[KMAX], ex[KMAX];
+    float w[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+      rows[j] = j < k ? row_of[(size_t)t * k + j] : 0;
+      if (ROUTER) {
+        ex[j] = j < k ? topk[(size_t)t * k + j] : 0;
+        w[j] = j < k ? dls[(size_t)t * k + j] : 0.f;
+      }
+    }
+    for (int c = lane; c < nchunk; c += 64) {
+      float acc[V];
+#pragma unroll
+      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k) {
+          float f[V];
+          unpack(dxp[(size_t)rows[j] * nchunk + c], f, T());
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] += f[i];
+        }
+      }
+      if (ROUTER) {
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (j < k) {
+            float f[V];
+            unpack(wrt[(size_t)ex[j] * nchunk + c], f, T());
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[i] += w[j] * f[i];
+          }
+        }
+      }
+      dx[(size_t)t * nchunk + c] = pack(acc, T());
+    }
+  }
+}
+
+// out[e][i] = in[i][e] for a [d,E] matrix (router weights, small).
+template <typename T>
+__global__ void transpose_kernel(const T* __restrict__ in, int d, int E, T* __restrict__ out) {
+  __shared__ T tile[32][33];
+  const int i0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 256 threads: 8 rows at a time
+  for (int r = ty; r < 32; r += 8) {
+    const int i = i0 + r, e = e0 + tx;
+    if (i < d && e < E) tile[r][tx] = in[(size_t)i * E + e];
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int e = e0 + r, i = i0 + tx;
+    if (i < d && e < E) out[(size_t)e * d + i] = tile[tx][r];
+  }
+}
+
+int grid_for(int T_) {
+  const int want = (T_ + kWaves - 1) / kWaves;
+  return want < 8192 ? (want > 0 ? want : 1) : 8192;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- C ABI
+using namespace moe_host;
+
+size_t moe_internal_wrt_bytes(int d, int E, moe_dtype dt);
+
+#define ROWS_DISPATCH_K(KVAR, LAUNCH) \
+  do {                                \
+    if (KVAR <= 2) {                  \
+      constexpr int KM = 2;           \
+      LAUNCH;                         \
+    } else if (KVAR <= 4) {           \
+      constexpr int KM = 4;           \
+      LAUNCH;                         \
+    } else if (KVAR <= 8) {           \
+      constexpr int KM = 8;           \
+      LAUNCH;                         \
+    } else {                          \
+      constexpr int KM = 32;          \
+      LAUNCH;                         \
+    }                                 \
+  } while (0)
+
+static moe_status rows_common(moe_ctx* ctx, int T_, int d, int k, moe_dtype dtype,
+                              const char* what) {
+  MOE_REQUIRE_DTYPE(ctx, dtype);
+  MOE_REQUIRE(ctx, T_ >= 0 && d >= 8 && d % 8 == 0 && k >= 1 && k <= 32,
+              "%s: bad shape T=%d d=%d k=%d", what, T_, d, k);
+  MOE_REQUIRE(ctx, (int64_t)T_ * k < (int64_t)1 << 31, "%s: T*k >= 2^31", what);
+  return MOE_OK;
+}
+
+extern "C" {
+
+moe_status moe_permute(moe_ctx* ctx, const void* x, const int32_t* row_of, int T_, int d, int k,
+                       moe_dtype dtype, void* xp) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = rows_common(ctx, T_, d, k, dtype, "moe_permute");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(ctx, x);
+  MOE_REQUIRE_PTR(ctx, row_of);
+  MOE_REQUIRE_PTR(ctx, xp);
+  if (T_ == 0) return MOE_OK;
+  const int nchunk = (int)(d * esize(dtype) / 16);
+  ROWS_DISPATCH_K(k, (permute_kernel<KM><<<grid_for(T_), 256, 0, ctx->stream>>>(
+                         (const uint4*)x, row_of, T_, nchunk, k, (uint4*)xp)));
+  return check_launch(ctx, "moe_permute");
+}
+
+moe_status moe_combine(moe_ctx* ctx, const void* yp, const float* gates, const int32_t* row_of,
+                       int T_, int d, int k, moe_dtype dtype, void* y) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = rows_common(ctx, T_, d, k, dtype, "moe_combine");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(ctx, yp);
+  MOE_REQUIRE_PTR(ctx, gates);
+  MOE_REQUIRE_PTR(ctx, row_of);
+  MOE_REQUIRE_PTR(ctx, y);
+  if (T_ == 0) return MOE_OK;
+  const int nchunk = (int)(d * esize(dtype) / 16);
+  if (dtype == MOE_BF16)
+    ROWS_DISPATCH_K(k, (combine_kernel<bf16_t, KM><<<grid_for(T_), 256, 0, ctx->stream>>>(
+                           (const uint4*)yp, gates, row_of, T_, nchunk, k, (uint4*)y)));
+  else
+    ROWS_DISPATCH_K(k, (combine_kernel<float, KM><<<grid_for(T_), 256, 0, ctx->stream>>>(
+                           (const uint4*)yp, gates, row_of, T_, nchunk, k, (uint4*)y)));
+  return check_launch(ctx, "moe_combine");
+}
+
+moe_status moe_combine_bwd(moe_ctx* ctx, const void* dy, const void* yp, const float* gates,
+                           const int32_t* row_of, int T_, int d, int k, moe_dtype dtype,
+                           void* dyp, float* dgates) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = rows_common(ctx, T_, d, k, dtype, "moe_combine_bwd");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(ctx, dy);
+  MOE_REQUIRE_PTR(ctx, yp);
+  MOE_REQUIRE_PTR(ctx, gates);
+  MOE_REQUIRE_PTR(ctx, row_of);
+  MOE_REQUIRE_PTR(ctx, dyp);
+  MOE_REQUIRE_PTR(ctx, dgates);
+  if (T_ == 0) return MOE_OK;
+  const int nchunk = (int)(d * esize(dtype) / 16);
+  if (dtype == MOE_BF16)
+    ROWS_DISPATCH_K(k, (combine_bwd_kernel<bf16_t, KM><<<grid_for(T_), 256, 0, ctx->stream>>>(
+                           (const uint4*)dy, (const uint4*)yp, gates, row_of, T_, nchunk, k,
+                           (uint4*)dyp, dgates)));
+  else
+    ROWS_DISPATCH_K(k, (combine_bwd_kernel<float, KM><<<grid_for(T_), 256, 0, ctx->stream>>>(
+                           (const uint4*)dy, (const uint4*)yp, gates, row_of, T_, nchunk, k,
+                           (uint4*)dyp, dgates)));
+  return check_launch(ctx, "moe_combine_bwd");
+}
+
+moe_status moe_permute_bwd(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
+                           const int32_t* topk_idx, const float* dlogits_sel,
+                           const void* w_router, int T_, int d, int E, int k, moe_dtype dtype,
+                           void* dx) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = rows_common(ctx, T_, d, k, dtype, "moe_permute_bwd");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(ctx, dxp);
+  MOE_REQUIRE_PTR(ctx, row_of);
+  MOE_REQUIRE_PTR(ctx, dx);
+  const bool router = dlogits_sel != nullptr && w_router != nullptr;
+  if (router) {
+    MOE_REQUIRE(ctx, E >= 1 && E <= 1024 && k <= E, "moe_permute_bwd: bad E=%d", E);
+    MOE_REQUIRE_PTR(ctx, topk_idx);
+    MOE_REQUIRE_PTR(ctx, dlogits_sel);
+    MOE_REQUIRE_PTR(ctx, w_router);
+    const size_t need = moe_internal_wrt_bytes(d, E, dtype);
+    if (ctx->ws == nullptr || ctx->ws_bytes < need)
+      return fail(ctx, MOE_ERR_WORKSPACE, "moe_permute_bwd: workspace %zu bytes < %zu needed",
+                  ctx->ws_bytes, need);
+  }
+  if (T_ == 0) return MOE_OK;
+  const int nchunk = (int)(d * esize(dtype) / 16);
+  if (router) {
+    dim3 tg((d + 31) / 32, (E + 31) / 32);
+    if (dtype == MOE_BF16)
+      transpose_kernel<bf16_t><<<tg, 256, 0, ctx->stream>>>((const bf16_t*)w_router, d, E,
+                                                            (bf16_t*)ctx->ws);
+    else
+      transpose_kernel<float><<<tg, 256, 0, ctx->stream>>>((const float*)w_router, d, E,
+                                                           (float*)ctx->ws);
+  }
+  const uint4* wrt = (const uint4*)ctx->ws;
+#define PB_LAUNCH(TY)                                                                          \
+  do {                                                                                         \
+    if (router)                                                                                \
+      ROWS_DISPATCH_K(k, (permute_bwd_kernel<TY, KM, true><<<grid_for(T_), 256, 0, ctx->stream>>>( \
+                             (const uint4*)dxp, row_of, topk_idx, dlogits_sel, wrt, T_, nchunk, k, \
+                             (uint4*)dx)));                                                    \
+    else                                                                                       \
+      ROWS_DISPATCH_K(k, (permute_bwd_kernel<TY, KM, false><<<grid_for(T_), 256, 0, ctx->stream>>>( \
+                             (const uint4*)dxp, row_of, nullptr, nullptr, nullptr, T_, nchunk, k, \
+                             (uint4*)dx)));                                                    \
+  } while (0)
+  if (dtype == MOE_BF16)
+    PB_LAUNCH(bf16_t);
+  else
+    PB_LAUNCH(float);
+#undef PB_LAUNCH
+  return check_launch(ctx, "moe_permute_bwd");
+}
+
+}  // extern "C"
