@@ -174,6 +174,40 @@ moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_se
                             const int32_t* src_tk, const int32_t* offsets, int T, int d, int E,
                             int k, moe_dtype dtype, void* dw_router);
 
+/* -------------------------------------------------------------- profiling
+ * Per-kernel timing with HIP events recorded on the context's stream around
+ * each kernel launch, for measurement runs (off by default; costs two event
+ * records per launch when on).  Kernel ids: */
+typedef enum {
+  MOE_K_ROUTER_LOGITS = 0, /* router scores (VALU or MFMA) */
+  MOE_K_TOPK,              /* softmax top-k + block histograms */
+  MOE_K_SCAN,              /* per-expert block scans */
+  MOE_K_RANK,              /* offsets + stable ranks -> row_of, src_tk */
+  MOE_K_PERMUTE,
+  MOE_K_GEMM_UP,           /* gate/up grouped GEMM + SwiGLU */
+  MOE_K_GEMM_DOWN,         /* down grouped GEMM */
+  MOE_K_COMBINE,
+  MOE_K_COMBINE_BWD,
+  MOE_K_ROUTE_BWD,
+  MOE_K_GEMM_DGRAD_DOWN,   /* down dgrad + SwiGLU backward */
+  MOE_K_GEMM_WGRAD_DOWN,
+  MOE_K_GEMM_DGRAD_UP,
+  MOE_K_GEMM_WGRAD_UP,
+  MOE_K_PERMUTE_BWD,       /* incl. the W_r transpose when the router term is on */
+  MOE_K_ROUTER_WGRAD,
+  MOE_K_COUNT
+} moe_kernel_id;
+
+/* Turn event timing on (clears previous records) or off (keeps them for
+ * moe_profile_query). */
+moe_status moe_profile_enable(moe_ctx* ctx, int on);
+/* Launch count and summed duration (ms) of one kernel id since the last
+ * enable.  Waits for the recorded events (host synchronisation: measurement
+ * only).  launches and total_ms are host outputs. */
+moe_status moe_profile_query(moe_ctx* ctx, int kernel_id, int* launches, double* total_ms);
+/* Static name of a kernel id. */
+const char* moe_kernel_name(int kernel_id);
+
 #ifdef __cplusplus
 }
 #endif

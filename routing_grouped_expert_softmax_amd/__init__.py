@@ -45,7 +45,13 @@ _SIGS = {
     "moe_router_wgrad": [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
 }
 EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "moe_last_error",
-           "moe_workspace_size", "moe_set_workspace", *_SIGS.keys()]
+           "moe_workspace_size", "moe_set_workspace", *_SIGS.keys(), "moe_profile_enable",
+           "moe_profile_query", "moe_kernel_name"]
+
+# kernel ids of the profiling hook (moe_kernel_id in include/moe.h)
+KERNELS = ["router_logits", "topk_hist", "expert_scan", "rank", "permute", "gemm_up_swiglu",
+           "gemm_down", "combine", "combine_bwd", "route_bwd", "gemm_dgrad_down_swiglu",
+           "gemm_wgrad_down", "gemm_dgrad_up", "gemm_wgrad_up", "permute_bwd", "router_wgrad"]
 
 
 def lib():
@@ -67,6 +73,10 @@ def lib():
         L.moe_set_workspace.argtypes = [_vp, _vp, ctypes.c_size_t]
         for name, sig in _SIGS.items():
             getattr(L, name).argtypes = [_vp, *sig]
+        L.moe_profile_enable.argtypes = [_vp, _int]
+        L.moe_profile_query.argtypes = [_vp, _int, ctypes.POINTER(_int), ctypes.POINTER(ctypes.c_double)]
+        L.moe_kernel_name.argtypes = [_int]
+        L.moe_kernel_name.restype = ctypes.c_char_p
         _lib = L
     return _lib
 
@@ -106,6 +116,20 @@ class Context:
     def call(self, name, *args):
         self.bind_stream()
         self._check(getattr(lib(), name)(self.handle, *args))
+
+    def profile(self, on: bool):
+        """Turn per-kernel HIP-event timing on (clearing old records) or off."""
+        self._check(lib().moe_profile_enable(self.handle, 1 if on else 0))
+
+    def profile_results(self):
+        """{kernel name: (launches, total ms)} since profiling was enabled."""
+        out = {}
+        for i, name in enumerate(KERNELS):
+            n, ms = _int(), ctypes.c_double()
+            self._check(lib().moe_profile_query(self.handle, i, ctypes.byref(n), ctypes.byref(ms)))
+            if n.value:
+                out[name] = (n.value, ms.value)
+        return out
 
     def close(self):
         if getattr(self, "handle", None) is not None:

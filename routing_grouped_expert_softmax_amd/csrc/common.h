@@ -6,8 +6,16 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "../../include/moe.h"
+
+// Event pairs recorded around the launches of one kernel id while profiling.
+struct moe_prof_slot {
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  int used = 0;
+};
 
 struct moe_ctx {
   int device = 0;
@@ -15,6 +23,33 @@ struct moe_ctx {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   std::string last_error;
+  bool prof = false;
+  moe_prof_slot slots[MOE_K_COUNT];
+};
+
+// Records a start event on construction and a stop event on destruction
+// around a launch of kernel `id`, when the context is profiling.
+struct moe_prof_scope {
+  moe_ctx* c;
+  moe_prof_slot* s = nullptr;
+  moe_prof_scope(moe_ctx* ctx, int id) : c(ctx) {
+    if (!c || !c->prof) return;
+    s = &c->slots[id];
+    if (s->used == (int)s->ev.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+        s = nullptr;
+        return;
+      }
+      s->ev.emplace_back(a, b);
+    }
+    hipEventRecord(s->ev[s->used].first, c->stream);
+  }
+  ~moe_prof_scope() {
+    if (!s) return;
+    hipEventRecord(s->ev[s->used].second, c->stream);
+    s->used++;
+  }
 };
 
 namespace moe {

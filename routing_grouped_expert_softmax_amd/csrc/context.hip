@@ -19,8 +19,48 @@ moe_status moe_create(int device, void* hip_stream, moe_ctx** out) {
 
 moe_status moe_destroy(moe_ctx* ctx) {
   MOE_CHECK_CTX(ctx);
+  for (auto& s : ctx->slots)
+    for (auto& e : s.ev) {
+      hipEventDestroy(e.first);
+      hipEventDestroy(e.second);
+    }
   delete ctx;
   return MOE_OK;
+}
+
+moe_status moe_profile_enable(moe_ctx* ctx, int on) {
+  MOE_CHECK_CTX(ctx);
+  ctx->prof = on != 0;
+  if (ctx->prof)
+    for (auto& s : ctx->slots) s.used = 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_query(moe_ctx* ctx, int id, int* launches, double* total_ms) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, id >= 0 && id < MOE_K_COUNT && launches && total_ms, "bad profile query");
+  const moe_prof_slot& s = ctx->slots[id];
+  double sum = 0;
+  for (int i = 0; i < s.used; ++i) {
+    if (hipEventSynchronize(s.ev[i].second) != hipSuccess)
+      return moe_host::fail(ctx, MOE_ERR_HIP, "profile: event wait failed");
+    float ms = 0;
+    if (hipEventElapsedTime(&ms, s.ev[i].first, s.ev[i].second) != hipSuccess)
+      return moe_host::fail(ctx, MOE_ERR_HIP, "profile: elapsed time failed");
+    sum += ms;
+  }
+  *launches = s.used;
+  *total_ms = sum;
+  return MOE_OK;
+}
+
+const char* moe_kernel_name(int id) {
+  static const char* names[MOE_K_COUNT] = {
+      "router_logits", "topk_hist", "expert_scan", "rank", "permute", "gemm_up_swiglu",
+      "gemm_down", "combine", "combine_bwd", "route_bwd", "gemm_dgrad_down_swiglu",
+      "gemm_wgrad_down", "gemm_dgrad_up", "gemm_wgrad_up", "permute_bwd", "router_wgrad"};
+  if (id < 0 || id >= MOE_K_COUNT) return "unknown";
+  return names[id];
 }
 
 moe_status moe_set_stream(moe_ctx* ctx, void* hip_stream) {

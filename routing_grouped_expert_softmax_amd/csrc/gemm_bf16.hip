@@ -634,7 +634,10 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.K = d;
     p.kseg = d;
     p.ntiles = (F + 127) / 128;
-    e = launch_mragged<FWD_UP>(p, R, ctx->stream);
+    {
+      moe_prof_scope ps(ctx, MOE_K_GEMM_UP);
+      e = launch_mragged<FWD_UP>(p, R, ctx->stream);
+    }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up GEMM: %s", hipGetErrorString(e));
   }
   {
@@ -652,7 +655,10 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.K = F;
     p.kseg = F;
     p.ntiles = (d + BN - 1) / BN;
-    e = launch_mragged<FWD_DOWN>(p, R, ctx->stream);
+    {
+      moe_prof_scope ps(ctx, MOE_K_GEMM_DOWN);
+      e = launch_mragged<FWD_DOWN>(p, R, ctx->stream);
+    }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down GEMM: %s", hipGetErrorString(e));
   }
   return MOE_OK;
@@ -707,7 +713,10 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.K = d;
     p.kseg = d;
     p.ntiles = (F + BN - 1) / BN;
-    e = launch_mragged<DGRAD_DOWN>(p, R, ctx->stream);
+    {
+      moe_prof_scope ps(ctx, MOE_K_GEMM_DGRAD_DOWN);
+      e = launch_mragged<DGRAD_DOWN>(p, R, ctx->stream);
+    }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down dgrad: %s", hipGetErrorString(e));
   }
   {
@@ -726,7 +735,10 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.N = d;
     p.ntiles = (d + BN - 1) / BN;
     p.mtiles = (F + 255) / 256;
-    e = launch<WGRAD_DOWN, 256>(p, E * p.ntiles * p.mtiles, ctx->stream);
+    {
+      moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
+      e = launch<WGRAD_DOWN, 256>(p, E * p.ntiles * p.mtiles, ctx->stream);
+    }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down wgrad: %s", hipGetErrorString(e));
   }
   if (R > 0) {
@@ -747,7 +759,10 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.K = 2 * F;
     p.kseg = F;
     p.ntiles = (d + BN - 1) / BN;
-    e = launch_mragged<DGRAD_UP>(p, R, ctx->stream);
+    {
+      moe_prof_scope ps(ctx, MOE_K_GEMM_DGRAD_UP);
+      e = launch_mragged<DGRAD_UP>(p, R, ctx->stream);
+    }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up dgrad: %s", hipGetErrorString(e));
   }
   {
@@ -768,7 +783,10 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.N = F;
     p.ntiles = (F + 127) / 128;
     p.mtiles = (d + 255) / 256;
-    e = launch<WGRAD_UP, 256>(p, E * p.ntiles * p.mtiles, ctx->stream);
+    {
+      moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
+      e = launch<WGRAD_UP, 256>(p, E * p.ntiles * p.mtiles, ctx->stream);
+    }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up wgrad: %s", hipGetErrorString(e));
   }
   return MOE_OK;

@@ -272,10 +272,18 @@ __global__ void __launch_bounds__(kTokBlock) rank_kernel(
 template <int KMAX>
 void launch_route(const float* logits, int T_, int E, int k, int32_t* topk_idx, float* gates,
                   int32_t* counts, int32_t* offsets, int32_t* row_of, int32_t* src_tk,
-                  int32_t* block_counts, int nblk, hipStream_t s) {
-  topk_hist_kernel<KMAX><<<nblk, kTokBlock, 0, s>>>(logits, T_, E, k, topk_idx, gates,
-                                                    block_counts, nblk);
-  expert_scan_kernel<<<E, 256, 0, s>>>(block_counts, nblk, counts);
+                  int32_t* block_counts, int nblk, moe_ctx* ctx) {
+  hipStream_t s = ctx->stream;
+  {
+    moe_prof_scope ps(ctx, MOE_K_TOPK);
+    topk_hist_kernel<KMAX><<<nblk, kTokBlock, 0, s>>>(logits, T_, E, k, topk_idx, gates,
+                                                      block_counts, nblk);
+  }
+  {
+    moe_prof_scope ps(ctx, MOE_K_SCAN);
+    expert_scan_kernel<<<E, 256, 0, s>>>(block_counts, nblk, counts);
+  }
+  moe_prof_scope ps(ctx, MOE_K_RANK);
   rank_kernel<KMAX><<<nblk, kTokBlock, 0, s>>>(topk_idx, block_counts, nblk, counts, T_, E, k,
                                                offsets, row_of, src_tk);
 }
@@ -383,6 +391,7 @@ moe_status moe_router_logits(moe_ctx* ctx, const void* x, const void* w_router, 
   MOE_REQUIRE_PTR(ctx, w_router);
   MOE_REQUIRE_PTR(ctx, logits);
   if (T_ == 0) return MOE_OK;
+  moe_prof_scope ps(ctx, MOE_K_ROUTER_LOGITS);
   if (dtype == MOE_BF16 && E > 16 && E % 8 == 0)
     return moe_internal_router_logits_mfma(ctx, x, w_router, T_, d, E, logits);
   const int blocks = std::min(1024, (T_ + 3) / 4);
@@ -439,16 +448,16 @@ moe_status moe_route(moe_ctx* ctx, const float* logits, int T_, int E, int k, in
   }
   if (k <= 2)
     launch_route<2>(logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk, bc, nblk,
-                    ctx->stream);
+                    ctx);
   else if (k <= 4)
     launch_route<4>(logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk, bc, nblk,
-                    ctx->stream);
+                    ctx);
   else if (k <= 8)
     launch_route<8>(logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk, bc, nblk,
-                    ctx->stream);
+                    ctx);
   else
     launch_route<32>(logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk, bc, nblk,
-                     ctx->stream);
+                     ctx);
   return check_launch(ctx, "moe_route");
 }
 
@@ -460,6 +469,7 @@ moe_status moe_route_bwd(moe_ctx* ctx, const float* gates, const float* dgates, 
   MOE_REQUIRE_PTR(ctx, dgates);
   MOE_REQUIRE_PTR(ctx, dlogits_sel);
   if (T_ == 0) return MOE_OK;
+  moe_prof_scope ps(ctx, MOE_K_ROUTE_BWD);
   route_bwd_kernel<<<(T_ + 255) / 256, 256, 0, ctx->stream>>>(gates, dgates, T_, k, dlogits_sel);
   return check_launch(ctx, "moe_route_bwd");
 }
@@ -477,6 +487,7 @@ moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_se
   MOE_REQUIRE_PTR(ctx, offsets);
   MOE_REQUIRE_PTR(ctx, dw_router);
   dim3 grid((d + 63) / 64, E);
+  moe_prof_scope ps(ctx, MOE_K_ROUTER_WGRAD);
   if (dtype == MOE_BF16)
     router_wgrad_kernel<bf16_t><<<grid, 256, 0, ctx->stream>>>(
         (const bf16_t*)x, dlogits_sel, src_tk, offsets, d, E, k, (bf16_t*)dw_router);

@@ -276,6 +276,7 @@ moe_status moe_permute(moe_ctx* ctx, const void* x, const int32_t* row_of, int T
   MOE_REQUIRE_PTR(ctx, xp);
   if (T_ == 0) return MOE_OK;
   const int nchunk = (int)(d * esize(dtype) / 16);
+  moe_prof_scope ps(ctx, MOE_K_PERMUTE);
   ROWS_DISPATCH_K(k, (permute_kernel<KM><<<grid_for(T_), 256, 0, ctx->stream>>>(
                          (const uint4*)x, row_of, T_, nchunk, k, (uint4*)xp)));
   return check_launch(ctx, "moe_permute");
@@ -292,6 +293,7 @@ moe_status moe_combine(moe_ctx* ctx, const void* yp, const float* gates, const i
   MOE_REQUIRE_PTR(ctx, y);
   if (T_ == 0) return MOE_OK;
   const int nchunk = (int)(d * esize(dtype) / 16);
+  moe_prof_scope ps(ctx, MOE_K_COMBINE);
   if (dtype == MOE_BF16)
     ROWS_DISPATCH_K(k, (combine_kernel<bf16_t, KM><<<grid_for(T_), 256, 0, ctx->stream>>>(
                            (const uint4*)yp, gates, row_of, T_, nchunk, k, (uint4*)y)));
@@ -315,6 +317,7 @@ moe_status moe_combine_bwd(moe_ctx* ctx, const void* dy, const void* yp, const f
   MOE_REQUIRE_PTR(ctx, dgates);
   if (T_ == 0) return MOE_OK;
   const int nchunk = (int)(d * esize(dtype) / 16);
+  moe_prof_scope ps(ctx, MOE_K_COMBINE_BWD);
   if (dtype == MOE_BF16)
     ROWS_DISPATCH_K(k, (combine_bwd_kernel<bf16_t, KM><<<grid_for(T_), 256, 0, ctx->stream>>>(
                            (const uint4*)dy, (const uint4*)yp, gates, row_of, T_, nchunk, k,
@@ -349,6 +352,7 @@ moe_status moe_permute_bwd(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
   }
   if (T_ == 0) return MOE_OK;
   const int nchunk = (int)(d * esize(dtype) / 16);
+  moe_prof_scope ps(ctx, MOE_K_PERMUTE_BWD);
   if (router) {
     dim3 tg((d + 31) / 32, (E + 31) / 32);
     if (dtype == MOE_BF16)

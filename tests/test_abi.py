@@ -30,6 +30,9 @@ def test_library_exports_every_declared_symbol():
     missing = [n for n in declared_symbols() if not hasattr(L, n)]
     assert not missing, missing
     assert set(declared_symbols()) == set(moe.EXPORTS)
+    names = [L.moe_kernel_name(i).decode() for i in range(len(moe.KERNELS))]
+    assert names == moe.KERNELS
+    assert L.moe_kernel_name(len(moe.KERNELS)) == b"unknown"
 
 
 def test_status_strings_and_null_context():

@@ -1,0 +1,194 @@
+"""End-to-end GPU parity of the whole layer (forward + backward through the C
+ABI) against the CPU oracle, graph capture (no host sync inside the layer),
+determinism, and checks at the benchmark workloads' full sizes on sampled
+outputs the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from tolerance import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import routing_grouped_expert_softmax_amd as m
+    m.context(0)
+    return m
+
+
+def run_layer(moe, cfg, inp):
+    g = {k: inp[k].to(DEV) for k in ("x", "wr", "wg", "wu", "wd", "dy")}
+    override = inp["logits"].to(DEV) if "logits" in inp else None
+    dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
+    buf = moe.alloc_layer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, dt, DEV)
+    moe.layer_forward(g["x"], g["wr"], g["wg"], g["wu"], g["wd"], cfg.k, buf, override)
+    moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf)
+    torch.cuda.synchronize()
+    return g, buf, override
+
+
+def oracle_routing(cfg, inp, acc="f64"):
+    x, wr = mi.f32(inp["x"]), mi.f32(inp["wr"])
+    logits = oracle.router_logits(x, wr, acc)
+    src = inp["logits"].numpy() if "logits" in inp else logits
+    return logits, oracle.route(src, cfg.k, acc)
+
+
+def topk_margin(logits, k):
+    s = -np.sort(-logits.astype(np.float64), axis=1)
+    return s[:, k - 1] - s[:, k] if logits.shape[1] > k else np.full(len(logits), np.inf)
+
+
+@pytest.mark.parametrize("name,over", [("tiny", {}),
+                                       ("tiny", dict(dtype="bf16", T=700, E=16, k=4, x_std=1.0)),
+                                       ("tiny", dict(dtype="bf16", T=1000, d=256, E=8, k=2, F=320,
+                                                     x_std=1.0, routing="zipf", n_dead=2))])
+def test_layer_end_to_end(moe, name, over):
+    cfg = mi.config(name, **over)
+    inp = mi.layer_inputs(cfg)
+    g, buf, _ = run_layer(moe, cfg, inp)
+    logits, r = oracle_routing(cfg, inp)
+    tol = 1e-4 if cfg.dtype == "fp32" else 2e-2
+    assert_close(buf.logits.cpu().numpy(), logits, 1e-5, "logits")
+    # Routing from the GPU's own scores equals the oracle's except where the
+    # k-th and (k+1)-th logits are closer than the two sides' rounding
+    # differences; if such a token flips, the chain is re-run from the
+    # oracle's scores so the rest compares like with like.
+    gt = buf.route["topk_idx"].cpu().numpy()
+    differ = np.any(gt != r["topk_idx"], axis=1)
+    if "logits" not in inp:
+        near = topk_margin(logits, cfg.k) < 1e-6
+        assert not np.any(differ & ~near), "routing differs away from near ties"
+        if differ.any():
+            inp = dict(inp, logits=torch.from_numpy(logits))
+            g, buf, _ = run_layer(moe, cfg, inp)
+    else:
+        assert not differ.any()
+    assert np.array_equal(buf.route["topk_idx"].cpu().numpy(), r["topk_idx"])
+    for key in ("counts", "offsets", "row_of"):
+        assert np.array_equal(buf.route[key].cpu().numpy(), r[key]), key
+    assert np.array_equal(buf.route["src_tk"].cpu().numpy()[:cfg.T * cfg.k], r["src_tk"])
+    x, wr, dy = mi.f32(inp["x"]), mi.f32(inp["wr"]), mi.f32(inp["dy"])
+    wg, wu, wd = mi.f32(inp["wg"]), mi.f32(inp["wu"]), mi.f32(inp["wd"])
+    y = oracle.layer_fwd(x, r["topk_idx"], r["gates"], wg, wu, wd)
+    b = oracle.layer_bwd(x, wr, r["topk_idx"], r["gates"], dy, wg, wu, wd)
+    f = lambda t: t.detach().float().cpu().numpy()  # noqa: E731
+    assert_close(f(buf.y), y, tol, "y")
+    assert_close(f(buf.dgates), b["dgates"], tol, "dgates")
+    assert_close(f(buf.dlogits_sel), b["dlogits_sel"], tol, "dlogits")
+    assert_close(f(buf.dx), b["dx"], tol, "dx")
+    assert_close(f(buf.dw_router), b["dwr"], tol, "dW_r")
+    for name_, ref in [("dw_gate", b["dwg"]), ("dw_up", b["dwu"]), ("dw_down", b["dwd"])]:
+        got = f(buf.bwd[name_])
+        for e in range(cfg.E):
+            assert_close(got[e], ref[e], tol, f"{name_}[{e}]")
+
+
+def test_graph_capture_replay(moe):
+    """The whole forward+backward is captured in one HIP graph (so it issues
+    no host synchronisation) and every replay reproduces the eager result."""
+    cfg = mi.config("tiny", dtype="bf16", T=512, d=256, E=16, k=4, F=256, x_std=1.0)
+    inp = mi.layer_inputs(cfg)
+    g, buf, _ = run_layer(moe, cfg, inp)
+    eager = {"y": buf.y.clone(), "dx": buf.dx.clone(), "dwg": buf.bwd["dw_gate"].clone(),
+             "dwr": buf.dw_router.clone(), "row_of": buf.route["row_of"].clone()}
+    for t in (buf.y, buf.dx, buf.bwd["dw_gate"], buf.dw_router, buf.route["row_of"]):
+        t.zero_()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            moe.layer_forward(g["x"], g["wr"], g["wg"], g["wu"], g["wd"], cfg.k, buf)
+            moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(3):
+        buf.y.zero_()
+        buf.dx.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(buf.y, eager["y"]), rep
+        assert torch.equal(buf.dx, eager["dx"]), rep
+        assert torch.equal(buf.bwd["dw_gate"], eager["dwg"]), rep
+        assert torch.equal(buf.dw_router, eager["dwr"]), rep
+        assert torch.equal(buf.route["row_of"], eager["row_of"]), rep
+
+
+def test_batch_invariance(moe):
+    """Shuffling the tokens permutes the forward output bit-exactly (no
+    position-dependent reduction order in the forward path)."""
+    cfg = mi.config("tiny", dtype="bf16", T=640, d=256, E=8, k=2, F=256, x_std=1.0)
+    inp = mi.layer_inputs(cfg)
+    _, buf, _ = run_layer(moe, cfg, inp)
+    y0 = buf.y.clone()
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(cfg.T))
+    inp2 = dict(inp)
+    inp2["x"] = inp["x"][perm].contiguous()
+    inp2["dy"] = inp["dy"][perm].contiguous()
+    _, buf2, _ = run_layer(moe, cfg, inp2)
+    assert torch.equal(buf2.y, y0[perm.to(DEV)])
+
+
+# ------------------------------------------------------------------ full size
+@pytest.mark.parametrize("name", ["dense8", "uniform128", "zipf128"])
+def test_full_size_sampled(moe, name):
+    """The benchmark workloads at full size, launched exactly as bench.py does:
+    routing checked on every token, outputs and input gradients on a sample of
+    tokens, weight gradients on sampled elements."""
+    cfg = mi.config(name)
+    inp = mi.layer_inputs(cfg)
+    g, buf, _ = run_layer(moe, cfg, inp)
+    rng = np.random.default_rng(123)
+    x, wr, dy = mi.f32(inp["x"]), mi.f32(inp["wr"]), mi.f32(inp["dy"])
+    wg, wu, wd = mi.f32(inp["wg"]), mi.f32(inp["wu"]), mi.f32(inp["wd"])
+    # routing on every token
+    if "logits" in inp:
+        r = oracle.route(inp["logits"].numpy(), cfg.k, "f32")
+        for key in ("topk_idx", "counts", "offsets", "row_of"):
+            assert np.array_equal(buf.route[key].cpu().numpy(), r[key]), key
+        assert np.array_equal(buf.route["src_tk"].cpu().numpy(), r["src_tk"])
+    else:
+        logits = oracle.router_logits(x, wr, "f32")
+        assert_close(buf.logits.cpu().numpy(), logits, 1e-5, "logits")
+        r = oracle.route(logits, cfg.k, "f32")
+        gt = buf.route["topk_idx"].cpu().numpy()
+        differ = np.any(gt != r["topk_idx"], axis=1)
+        near = topk_margin(logits, cfg.k) < 1e-4
+        assert not np.any(differ & ~near), "routing differs away from near ties"
+        if not differ.any():
+            for key in ("counts", "offsets", "row_of"):
+                assert np.array_equal(buf.route[key].cpu().numpy(), r[key]), key
+    gates = r["gates"]
+    tok = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 48, replace=False)]))
+    tok = tok[np.all(buf.route["topk_idx"].cpu().numpy()[tok] == r["topk_idx"][tok], axis=1)]
+    # forward output and input gradient at the sampled tokens
+    y = oracle.layer_fwd(x[tok], r["topk_idx"][tok], gates[tok], wg, wu, wd)
+    assert_close(buf.y.float().cpu().numpy()[tok], y, 2e-2, "y (sampled tokens)")
+    b = oracle.layer_bwd(x[tok], wr, r["topk_idx"][tok], gates[tok], dy[tok], wg, wu, wd)
+    assert_close(buf.dx.float().cpu().numpy()[tok], b["dx"], 2e-2, "dx (sampled tokens)")
+    assert_close(buf.dgates.cpu().numpy()[tok], b["dgates"], 2e-2, "dgates (sampled tokens)")
+    # weight gradients at sampled elements: the oracle needs every row of the
+    # expert, built here from the generated inputs and the oracle's routing
+    src = r["src_tk"]
+    xp = x[src // cfg.k]
+    dyp = (gates.reshape(-1)[src][:, None] * dy[src // cfg.k]).astype(np.float32)
+    counts = r["counts"]
+    live = np.flatnonzero(counts > 0)
+    experts = np.unique(np.concatenate([[live[np.argmax(counts[live])]], rng.choice(live, 3)]))
+    for which, name_, shp in [(0, "dw_gate", (cfg.d, cfg.F)), (1, "dw_up", (cfg.d, cfg.F)),
+                              (2, "dw_down", (cfg.F, cfg.d))]:
+        el = np.stack([np.repeat(experts, 6), rng.integers(0, shp[0], 6 * len(experts)),
+                       rng.integers(0, shp[1], 6 * len(experts))], 1)
+        ref = oracle.expert_wgrad_elems(xp, dyp, r["offsets"], wg, wu, wd, which, el)
+        got = buf.bwd[name_].float().cpu().numpy()[el[:, 0], el[:, 1], el[:, 2]]
+        assert_close(got, ref, 2e-2, f"{name_} (sampled elements)")
+    # experts with no rows have exactly zero weight gradients
+    for e in np.flatnonzero(counts == 0):
+        assert not buf.bwd["dw_gate"][e].any() and not buf.bwd["dw_down"][e].any()
