@@ -261,30 +261,64 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
     if (!find_mtile<BM>(p, sh, w)) return;
   }
 
-  const bf16_t* bbase0 = p.b0 + (size_t)w.e * p.b_gstride;
-  const bf16_t* bbase1 = p.b1 ? p.b1 + (size_t)w.e * p.b_gstride : nullptr;
   const int nk = TR::kKRAGGED ? (w.rows + BK - 1) / BK : p.K / BK;
 
   // ---------------------------------------------------------------- loaders
+  // Every tile load is a raw buffer load through a descriptor whose range
+  // covers exactly the rows this block may use: rows past the range (past the
+  // tile's valid rows, past an expert's K rows, past the end of a weight
+  // matrix) read as zero without any branch.  Columns past N only feed output
+  // columns that are never stored.
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
+  const size_t esz = sizeof(bf16_t);
+  __amdgpu_buffer_rsrc_t ra0, ra1, rb0, rb1;
+  {
+    // A: the tile's (M-ragged) or the expert's (K-ragged) rows
+    const size_t abytes = (size_t)max(w.rows, 0) * p.lda * esz;
+    ra0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a0 + (size_t)w.row0 * p.lda), (short)0,
+                                            (int)abytes, 0x00020000);
+    ra1 = ra0;
+    if (MODE == DGRAD_UP)
+      ra1 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a1 + (size_t)w.row0 * p.lda), (short)0,
+                                              (int)abytes, 0x00020000);
+    if (TR::kKRAGGED) {
+      // B holds per-row data of the same expert rows
+      const size_t bbytes = (size_t)max(w.rows, 0) * p.ldb * esz;
+      rb0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b0 + (size_t)w.row0 * p.ldb), (short)0,
+                                              (int)bbytes, 0x00020000);
+      rb1 = TR::kDUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.b1 + (size_t)w.row0 * p.ldb),
+                                                          (short)0, (int)bbytes, 0x00020000)
+                      : rb0;
+    } else {
+      // B is the expert's weight matrix: K x ldb (N-contiguous) or N x ldb
+      const size_t bbytes =
+          (size_t)(TR::kB_KCONTIG ? p.N : (MODE == ROUTER ? p.K : p.K)) * p.ldb * esz;
+      rb0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b0 + (size_t)w.e * p.b_gstride), (short)0,
+                                              (int)bbytes, 0x00020000);
+      rb1 = (TR::kDUAL || MODE == DGRAD_UP)
+                ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.b1 + (size_t)w.e * p.b_gstride),
+                                                    (short)0, (int)bbytes, 0x00020000)
+                : rb0;
+    }
+  }
+  auto bload = [](__amdgpu_buffer_rsrc_t r, int off) -> uint4 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+  };
+
   uint4 ra[8], rb[8];
 
   auto load_a = [&](int kt) {
     const int k0 = kt * BK;
     if (TR::kA_KCONTIG) {
-      const bf16_t* a = p.a0;
-      int kk = k0;
-      if (MODE == DGRAD_UP && k0 >= p.kseg) {
-        a = p.a1;
-        kk = k0 - p.kseg;
-      }
+      const bool seg1 = (MODE == DGRAD_UP) && k0 >= p.kseg;
+      const int kk = seg1 ? k0 - p.kseg : k0;
+      const __amdgpu_buffer_rsrc_t r = seg1 ? ra1 : ra0;
 #pragma unroll
       for (int i = 0; i < TL::A_CHUNKS; ++i) {
         const int q = tid + i * kThreads;
         const int row = q >> 3, kc = q & 7;
-        if (row < w.rows)
-          ra[i] = *reinterpret_cast<const uint4*>(a + (size_t)(w.row0 + row) * p.lda + kk + kc * 8);
-        else
-          ra[i] = make_uint4(0, 0, 0, 0);
+        ra[i] = bload(r, (int)(((size_t)row * p.lda + kk + kc * 8) * esz));
       }
     } else {
       // M-contiguous A (wgrad): block (kc, mc) of 8 k-rows x 8 m values
@@ -293,10 +327,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int k = k0 + kc * 8 + i;
-        if (k < w.rows && m < p.M)
-          ra[i] = *reinterpret_cast<const uint4*>(p.a0 + (size_t)(w.row0 + k) * p.lda + m);
-        else
-          ra[i] = make_uint4(0, 0, 0, 0);
+        ra[i] = bload(ra0, (int)(((size_t)k * p.lda + m) * esz));
       }
     }
   };
@@ -304,37 +335,32 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   auto load_b = [&](int kt) {
     const int k0 = kt * BK;
     if (TR::kB_KCONTIG) {
-      const bf16_t* b = bbase0;
-      int kk = k0;
-      if (MODE == DGRAD_UP && k0 >= p.kseg) {
-        b = bbase1;
-        kk = k0 - p.kseg;
-      }
+      const bool seg1 = (MODE == DGRAD_UP) && k0 >= p.kseg;
+      const int kk = seg1 ? k0 - p.kseg : k0;
+      const __amdgpu_buffer_rsrc_t r = seg1 ? rb1 : rb0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int q = tid + i * kThreads;
         const int j = q >> 3, kc = q & 7;
         const int col = w.nt * BN + j;
-        if (col < p.N)
-          rb[i] = *reinterpret_cast<const uint4*>(b + (size_t)col * p.ldb + kk + kc * 8);
-        else
-          rb[i] = make_uint4(0, 0, 0, 0);
+        rb[i] = bload(r, (int)(((size_t)col * p.ldb + kk + kc * 8) * esz));
       }
     } else {
-      const int kc = tid & 7, nc = tid >> 3;
-      int sel, col;
-      bcol<TR::kDUAL>(w.nt, nc * 8, sel, col);
-      const bf16_t* b = sel ? bbase1 : bbase0;
+      // N-contiguous B: block (kc, nc) of 8 k-rows x 8 columns.  In the dual
+      // layout each wave's 64 LDS rows come from one matrix (wave & 1).
+      const int kc = tid & 7, nc8 = (tid & 63) >> 3;
+      int col;
+      __amdgpu_buffer_rsrc_t r = rb0;
+      if (TR::kDUAL) {
+        col = w.nt * 128 + (wv >> 1) * 64 + nc8 * 8;
+        if (wv & 1) r = rb1;
+      } else {
+        col = w.nt * BN + (tid >> 3) * 8;
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int k = k0 + kc * 8 + i;
-        const bool kvalid = TR::kKRAGGED ? (k < w.rows) : true;
-        if (kvalid && col < p.N) {
-          const size_t krow = TR::kKRAGGED ? (size_t)(w.row0 + k) : (size_t)k;
-          rb[i] = *reinterpret_cast<const uint4*>(b + krow * p.ldb + col);
-        } else {
-          rb[i] = make_uint4(0, 0, 0, 0);
-        }
+        rb[i] = bload(r, (int)(((size_t)k * p.ldb + col) * esz));
       }
     }
   };
