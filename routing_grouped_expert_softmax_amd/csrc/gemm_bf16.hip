@@ -88,58 +88,33 @@ constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int kThreads = 256;
 
-__device__ __forceinline__ int swz(int row, int chunk) { return (chunk ^ (row & 7)); }
+#define LDS_AS __attribute__((address_space(3)))
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
-// Byte offset inside a K-contiguous LDS tile of the 16-byte chunk (row, chunk).
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * (BK * 2) + swz(row, chunk) * 16;
-}
+// ---------------------------------------------------------------- LDS layouts
+// K-contiguous tile ([rows][64 k], 128-byte rows): the 16-byte chunk index is
+// XOR-swizzled with g(row) = (row ^ row>>3) & 7, so the rows of any 16
+// consecutive fragment lanes hit 16 distinct bank slots.
+__device__ __forceinline__ int swz_kc(int row) { return (row ^ (row >> 3)) & 7; }
+// M/N-contiguous tile ([64 k][cols], 256- or 512-byte rows): chunk index XOR
+// 4*(k & 3), so a transposing fragment read (4 k rows x 32 bytes per 16
+// lanes) covers every bank slot once per 32 lanes.
+__device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 2; }
 
-// 8x8 transpose of bf16: in[i] holds 8 values (i, 0..7); out[r] = (0..7, r).
-__device__ __forceinline__ void transpose8(const uint4 (&in)[8], uint4 (&out)[8]) {
-  uint32_t w[8][4];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    w[i][0] = in[i].x;
-    w[i][1] = in[i].y;
-    w[i][2] = in[i].z;
-    w[i][3] = in[i].w;
-  }
-  uint32_t o[8][4];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t a = w[2 * p][r >> 1], b = w[2 * p + 1][r >> 1];
-      o[r][p] = (r & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 8; ++r) out[r] = make_uint4(o[r][0], o[r][1], o[r][2], o[r][3]);
-}
-
-// Column of the N-dim for LDS B-tile row j: which matrix (dual) and its column.
-template <bool DUAL>
-__device__ __forceinline__ void bcol(int nt, int j, int& sel, int& col) {
-  if (DUAL) {
-    const int wn = j >> 7, w = j & 127;
-    sel = w >> 6;
-    col = nt * 128 + wn * 64 + (w & 63);
-  } else {
-    sel = 0;
-    col = nt * BN + j;
-  }
-}
-
+// Tile geometry of one pipeline stage.
 template <int MODE, int BM>
 struct Tile {
   using TR = Traits<MODE>;
-  static constexpr int WM = BM / 2;        // wave tile rows (M)
-  static constexpr int SM = WM / 32;       // 32-row subtiles per wave
-  static constexpr int A_CHUNKS = BM / 32;  // 16-byte chunks per thread (K-contig A)
+  static constexpr int WM = BM / 2;   // wave tile rows (M)
+  static constexpr int SM = WM / 32;  // 32-row subtiles per wave
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = BN * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_INST = A_BYTES / 1024 / 4;  // 1 KiB direct loads per wave
+  static constexpr int B_INST = B_BYTES / 1024 / 4;
+  static constexpr int A_PITCH = TR::kA_KCONTIG ? 128 : BM * 2;  // LDS row pitch (bytes)
+  // B: K-contiguous [256][64]; N-contiguous [64][256]; dual: two [64][128]
+  static constexpr int B_PITCH = TR::kB_KCONTIG ? 128 : (TR::kDUAL ? 256 : 512);
 };
 
 // Work description of one block.
@@ -216,18 +191,20 @@ __device__ bool find_mtile(const Params& p, int* sh, Work& w) {
   return true;
 }
 
-template <int MODE, int BM>
+template <int MODE, int BM, int S>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using TR = Traits<MODE>;
   using TL = Tile<MODE, BM>;
   constexpr int SM = TL::SM;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
   __shared__ int sh[kThreads + 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   // ---------------------------------------------------------------- work
   Work w;
@@ -260,145 +237,146 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   } else {
     if (!find_mtile<BM>(p, sh, w)) return;
   }
-
   const int nk = TR::kKRAGGED ? (w.rows + BK - 1) / BK : p.K / BK;
 
-  // ---------------------------------------------------------------- loaders
-  // Every tile load is a raw buffer load through a descriptor whose range
-  // covers exactly the rows this block may use: rows past the range (past the
-  // tile's valid rows, past an expert's K rows, past the end of a weight
-  // matrix) read as zero without any branch.  Columns past N only feed output
-  // columns that are never stored.
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, scalar
+  // ---------------------------------------------------------------- sources
+  // Raw buffer descriptors whose ranges cover exactly the rows this block may
+  // read: rows past a tile's valid rows, past an expert's K rows or past a
+  // weight matrix read as zero (the loads below never branch).  Columns past
+  // N only feed output columns that are never stored.
   const size_t esz = sizeof(bf16_t);
-  __amdgpu_buffer_rsrc_t ra0, ra1, rb0, rb1;
+  __amdgpu_buffer_rsrc_t rsa0, rsa1, rsb0, rsb1;
   {
-    // A: the tile's (M-ragged) or the expert's (K-ragged) rows
     const size_t abytes = (size_t)max(w.rows, 0) * p.lda * esz;
-    ra0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a0 + (size_t)w.row0 * p.lda), (short)0,
-                                            (int)abytes, 0x00020000);
-    ra1 = ra0;
+    rsa0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a0 + (size_t)w.row0 * p.lda), (short)0,
+                                             (int)abytes, 0x00020000);
+    rsa1 = rsa0;
     if (MODE == DGRAD_UP)
-      ra1 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a1 + (size_t)w.row0 * p.lda), (short)0,
-                                              (int)abytes, 0x00020000);
+      rsa1 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a1 + (size_t)w.row0 * p.lda), (short)0,
+                                               (int)abytes, 0x00020000);
     if (TR::kKRAGGED) {
-      // B holds per-row data of the same expert rows
       const size_t bbytes = (size_t)max(w.rows, 0) * p.ldb * esz;
-      rb0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b0 + (size_t)w.row0 * p.ldb), (short)0,
-                                              (int)bbytes, 0x00020000);
-      rb1 = TR::kDUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.b1 + (size_t)w.row0 * p.ldb),
-                                                          (short)0, (int)bbytes, 0x00020000)
-                      : rb0;
+      rsb0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b0 + (size_t)w.row0 * p.ldb), (short)0,
+                                               (int)bbytes, 0x00020000);
+      rsb1 = TR::kDUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.b1 + (size_t)w.row0 * p.ldb),
+                                                           (short)0, (int)bbytes, 0x00020000)
+                       : rsb0;
     } else {
-      // B is the expert's weight matrix: K x ldb (N-contiguous) or N x ldb
-      const size_t bbytes =
-          (size_t)(TR::kB_KCONTIG ? p.N : (MODE == ROUTER ? p.K : p.K)) * p.ldb * esz;
-      rb0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b0 + (size_t)w.e * p.b_gstride), (short)0,
-                                              (int)bbytes, 0x00020000);
-      rb1 = (TR::kDUAL || MODE == DGRAD_UP)
-                ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.b1 + (size_t)w.e * p.b_gstride),
-                                                    (short)0, (int)bbytes, 0x00020000)
-                : rb0;
+      const size_t bbytes = (size_t)(TR::kB_KCONTIG ? p.N : p.K) * p.ldb * esz;
+      rsb0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b0 + (size_t)w.e * p.b_gstride), (short)0,
+                                               (int)bbytes, 0x00020000);
+      rsb1 = (TR::kDUAL || MODE == DGRAD_UP)
+                 ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.b1 + (size_t)w.e * p.b_gstride),
+                                                     (short)0, (int)bbytes, 0x00020000)
+                 : rsb0;
     }
   }
-  auto bload = [](__amdgpu_buffer_rsrc_t r, int off) -> uint4 {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-    return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
-  };
 
-  uint4 ra[8], rb[8];
-
-  auto load_a = [&](int kt) {
-    const int k0 = kt * BK;
+  // Per-lane byte offsets of this wave's direct loads (fixed over the K loop;
+  // the K advance goes in the scalar offset).  Each load moves 16 bytes per
+  // lane into LDS at (instruction base + 16 * lane), so the global side picks
+  // the source chunk that belongs at that (swizzled) LDS position.
+  int aoff[TL::A_INST], boff[TL::B_INST];
+#pragma unroll
+  for (int j = 0; j < TL::A_INST; ++j) {
+    const int q = wv * TL::A_INST + j;  // 1 KiB instruction index inside the A tile
     if (TR::kA_KCONTIG) {
-      const bool seg1 = (MODE == DGRAD_UP) && k0 >= p.kseg;
-      const int kk = seg1 ? k0 - p.kseg : k0;
-      const __amdgpu_buffer_rsrc_t r = seg1 ? ra1 : ra0;
-#pragma unroll
-      for (int i = 0; i < TL::A_CHUNKS; ++i) {
-        const int q = tid + i * kThreads;
-        const int row = q >> 3, kc = q & 7;
-        ra[i] = bload(r, (int)(((size_t)row * p.lda + kk + kc * 8) * esz));
-      }
+      const int row = q * 8 + (lane >> 3), pc = lane & 7;
+      aoff[j] = (row * p.lda + ((pc ^ swz_kc(row)) << 3)) * (int)esz;
     } else {
-      // M-contiguous A (wgrad): block (kc, mc) of 8 k-rows x 8 m values
-      const int kc = tid & 7, mc = tid >> 3;
-      const int m = w.m0 + mc * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = k0 + kc * 8 + i;
-        ra[i] = bload(ra0, (int)(((size_t)k * p.lda + m) * esz));
-      }
+      constexpr int CPR = BM / 8;  // 16-byte chunks per k row
+      const int k = (q * 64 + lane) / CPR, pc = (q * 64 + lane) % CPR;
+      aoff[j] = (k * p.lda + w.m0 + ((pc ^ swz_mn(k)) << 3)) * (int)esz;
     }
-  };
-
-  auto load_b = [&](int kt) {
-    const int k0 = kt * BK;
-    if (TR::kB_KCONTIG) {
-      const bool seg1 = (MODE == DGRAD_UP) && k0 >= p.kseg;
-      const int kk = seg1 ? k0 - p.kseg : k0;
-      const __amdgpu_buffer_rsrc_t r = seg1 ? rb1 : rb0;
+  }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = tid + i * kThreads;
-        const int j = q >> 3, kc = q & 7;
-        const int col = w.nt * BN + j;
-        rb[i] = bload(r, (int)(((size_t)col * p.ldb + kk + kc * 8) * esz));
-      }
+  for (int j = 0; j < TL::B_INST; ++j) {
+    const int q = wv * TL::B_INST + j;
+    if (TR::kB_KCONTIG) {
+      const int n = q * 8 + (lane >> 3), pc = lane & 7;
+      boff[j] = ((w.nt * BN + n) * p.ldb + ((pc ^ swz_kc(n)) << 3)) * (int)esz;
+    } else if (TR::kDUAL) {
+      // two sub-tiles of [64 k][128 n]: instructions 0..15 matrix 0, 16..31 matrix 1
+      const int qq = q & 15;
+      const int k = qq * 4 + (lane >> 4), pc = lane & 15;
+      boff[j] = (k * p.ldb + w.nt * 128 + ((pc ^ swz_mn(k)) << 3)) * (int)esz;
     } else {
-      // N-contiguous B: block (kc, nc) of 8 k-rows x 8 columns.  In the dual
-      // layout each wave's 64 LDS rows come from one matrix (wave & 1).
-      const int kc = tid & 7, nc8 = (tid & 63) >> 3;
-      int col;
-      __amdgpu_buffer_rsrc_t r = rb0;
-      if (TR::kDUAL) {
-        col = w.nt * 128 + (wv >> 1) * 64 + nc8 * 8;
-        if (wv & 1) r = rb1;
+      const int k = q * 2 + (lane >> 5), pc = lane & 31;
+      boff[j] = (k * p.ldb + w.nt * BN + ((pc ^ swz_mn(k)) << 3)) * (int)esz;
+    }
+  }
+
+  // Issue the direct loads of K step kt into stage buffer `st`.
+  auto issue = [&](int kt, int st) {
+    const int k0 = kt * BK;
+    LDS_AS unsigned char* base = (LDS_AS unsigned char*)((LDS_AS unsigned char*)smem) + st * TL::STAGE;
+    // A
+    {
+      __amdgpu_buffer_rsrc_t r = rsa0;
+      int soff;
+      if (TR::kA_KCONTIG) {
+        int kk = k0;
+        if (MODE == DGRAD_UP && k0 >= p.kseg) {
+          r = rsa1;
+          kk = k0 - p.kseg;
+        }
+        soff = kk * (int)esz;
       } else {
-        col = w.nt * BN + (tid >> 3) * 8;
+        soff = k0 * p.lda * (int)esz;
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = k0 + kc * 8 + i;
-        rb[i] = bload(r, (int)(((size_t)k * p.ldb + col) * esz));
+      for (int j = 0; j < TL::A_INST; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (LDS_AS void*)(base + (wv * TL::A_INST + j) * 1024), 16, aoff[j], soff, 0, 0);
+    }
+    // B
+    {
+      LDS_AS unsigned char* bbase = base + TL::A_BYTES;
+      __amdgpu_buffer_rsrc_t r = rsb0;
+      int soff;
+      if (TR::kB_KCONTIG) {
+        int kk = k0;
+        if (MODE == DGRAD_UP && k0 >= p.kseg) {
+          r = rsb1;
+          kk = k0 - p.kseg;
+        }
+        soff = kk * (int)esz;
+      } else {
+        soff = k0 * p.ldb * (int)esz;
+        if (TR::kDUAL && wv >= 2) r = rsb1;  // waves 2,3 load the second matrix
       }
+#pragma unroll
+      for (int j = 0; j < TL::B_INST; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (LDS_AS void*)(bbase + (wv * TL::B_INST + j) * 1024), 16, boff[j], soff, 0, 0);
     }
   };
 
-  auto store_tiles = [&](int stage) {
-    unsigned char* As = smem + stage * TL::STAGE;
-    unsigned char* Bs = As + TL::A_BYTES;
-    if (TR::kA_KCONTIG) {
+  // ---------------------------------------------------------------- fragments
+  // K-contiguous tile: one 16-byte read per lane (row = lane & 31).
+  auto frag_kc = [&](const LDS_AS unsigned char* t, int row0, int kk) -> bf16x8 {
+    const int row = row0 + (lane & 31);
+    const int lc = kk * 2 + (lane >> 5);
+    return *(const LDS_AS bf16x8*)(t + row * 128 + ((lc ^ swz_kc(row)) << 4));
+  };
+  // M/N-contiguous tile: two transposing 8-byte reads give each lane 8
+  // consecutive k of column (col0 + lane & 31): in each 16-lane group, lane i
+  // receives element i%4 of the reads of lanes i/4 + 4j, so lane
+  // a + 4b addresses row k0 + b, columns col0 + 16*group + 4a.
+  auto frag_mn = [&](const LDS_AS unsigned char* t, int pitch, int col0, int kk) -> bf16x8 {
+    const int g = (lane >> 4) & 1, half = lane >> 5;
+    const int col = col0 + 16 * g + 4 * (lane & 3);
+    bf16x4 v[2];
 #pragma unroll
-      for (int i = 0; i < TL::A_CHUNKS; ++i) {
-        const int q = tid + i * kThreads;
-        const int row = q >> 3, kc = q & 7;
-        *reinterpret_cast<uint4*>(As + lds_off(row, kc)) = ra[i];
-      }
-    } else {
-      uint4 t[8];
-      transpose8(ra, t);
-      const int kc = tid & 7, mc = tid >> 3;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(As + lds_off(mc * 8 + r, kc)) = t[r];
+    for (int r = 0; r < 2; ++r) {
+      const int k = kk * 16 + 8 * half + 4 * r + ((lane & 15) >> 2);
+      const LDS_AS unsigned char* a =
+          t + k * pitch + (((col >> 3) ^ swz_mn(k)) << 4) + ((col & 7) << 1);
+      v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)a);
     }
-    if (TR::kB_KCONTIG) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = tid + i * kThreads;
-        const int j = q >> 3, kc = q & 7;
-        *reinterpret_cast<uint4*>(Bs + lds_off(j, kc)) = rb[i];
-      }
-    } else {
-      uint4 t[8];
-      transpose8(rb, t);
-      const int kc = tid & 7, nc = tid >> 3;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(Bs + lds_off(nc * 8 + r, kc)) = t[r];
-    }
+    return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
-  // ---------------------------------------------------------------- main loop
   f32x16 acc[SM][4];
 #pragma unroll
   for (int i = 0; i < SM; ++i)
@@ -407,35 +385,29 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int frag_row = lane & 31;
-  const int frag_kc = lane >> 5;
-
-  if (nk > 0) {
-    load_a(0);
-    load_b(0);
-    store_tiles(0);
-    __syncthreads();
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      load_a(kt + 1);
-      load_b(kt + 1);
-    }
-    const unsigned char* As = smem + cur * TL::STAGE;
-    const unsigned char* Bs = As + TL::A_BYTES;
+  auto compute = [&](int st) {
+    const LDS_AS unsigned char* As = (const LDS_AS unsigned char*)((LDS_AS unsigned char*)smem) + st * TL::STAGE;
+    const LDS_AS unsigned char* Bs = As + TL::A_BYTES;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       bf16x8 xb[4], ya[SM];
 #pragma unroll
       for (int sn = 0; sn < 4; ++sn) {
-        const int row = wn * 128 + sn * 32 + frag_row;
-        xb[sn] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(row, kk * 2 + frag_kc));
+        if (TR::kB_KCONTIG) {
+          xb[sn] = frag_kc(Bs, wn * 128 + sn * 32, kk);
+        } else if (TR::kDUAL) {
+          // subtiles 0,1: matrix 0 columns wn*64 + ..; 2,3: matrix 1, same columns
+          xb[sn] = frag_mn(Bs + (sn >> 1) * (BK * 256), 256, wn * 64 + (sn & 1) * 32, kk);
+        } else {
+          xb[sn] = frag_mn(Bs, 512, wn * 128 + sn * 32, kk);
+        }
       }
 #pragma unroll
       for (int sm = 0; sm < SM; ++sm) {
-        const int row = wm * TL::WM + sm * 32 + frag_row;
-        ya[sm] = *reinterpret_cast<const bf16x8*>(As + lds_off(row, kk * 2 + frag_kc));
+        if (TR::kA_KCONTIG)
+          ya[sm] = frag_kc(As, wm * TL::WM + sm * 32, kk);
+        else
+          ya[sm] = frag_mn(As, TL::A_PITCH, wm * TL::WM + sm * 32, kk);
       }
 #pragma unroll
       for (int sm = 0; sm < SM; ++sm)
@@ -443,8 +415,29 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
         for (int sn = 0; sn < 4; ++sn)
           acc[sm][sn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[sn], ya[sm], acc[sm][sn], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_tiles(cur ^ 1);
+  };
+
+  // ---------------------------------------------------------------- main loop
+  // S-stage pipeline: at the top of step kt the wave waits for its own loads
+  // of stage kt (later stages may stay in flight), a barrier makes every
+  // wave's loads visible and frees the buffer read in step kt-1, the loads of
+  // step kt+S-1 go into that buffer, then step kt is computed.
+  constexpr int LPS = TL::A_INST + TL::B_INST;  // direct loads per wave per stage
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s);
+  for (int kt = 0; kt < nk; ++kt) {
+    // loads issued after stage kt so far: stages kt+1 .. min(kt+S-2, nk-1)
+    const int after = min(S - 2, nk - 1 - kt);
+    if (S >= 3 && after >= 1) {
+      // vmcnt(LPS): simm16 = vmcnt[3:0] | expcnt(7)[6:4] | lgkmcnt(15)[11:8] | vmcnt[5:4]<<14
+      __builtin_amdgcn_s_waitcnt((LPS & 15) | (7 << 4) | (15 << 8) | ((LPS >> 4) << 14));
+    } else {
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    }
     __syncthreads();
+    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
+    compute(kt % S);
   }
 
   // ---------------------------------------------------------------- epilogue
@@ -537,21 +530,22 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
       }
     }
   }
+#endif
 }
 
-template <int MODE, int BM>
+template <int MODE, int BM, int S>
 hipError_t launch(const Params& p, int blocks, hipStream_t s) {
   using TL = Tile<MODE, BM>;
-  const int smem = 2 * TL::STAGE;
+  const int smem = S * TL::STAGE;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_kernel<MODE, BM>,
+    hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_kernel<MODE, BM, S>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   blocks = (blocks + 7) / 8 * 8;
-  grouped_gemm_kernel<MODE, BM><<<blocks, kThreads, smem, s>>>(p);
+  grouped_gemm_kernel<MODE, BM, S><<<blocks, kThreads, smem, s>>>(p);
   return hipGetLastError();
 }
 
@@ -570,8 +564,8 @@ static int pick_bm(int R, int E) { return (R / (E > 0 ? E : 1)) < 1024 ? 128 : 2
 template <int MODE>
 static hipError_t launch_mragged(Params& p, int R, hipStream_t s) {
   const int bm = pick_bm(R, p.E);
-  if (bm == 128) return launch<MODE, 128>(p, mtile_bound(R, p.E, 128) * p.ntiles, s);
-  return launch<MODE, 256>(p, mtile_bound(R, p.E, 256) * p.ntiles, s);
+  if (bm == 128) return launch<MODE, 128, 3>(p, mtile_bound(R, p.E, 128) * p.ntiles, s);
+  return launch<MODE, 256, 2>(p, mtile_bound(R, p.E, 256) * p.ntiles, s);
 }
 
 moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const void* wr, int T_,
@@ -592,7 +586,7 @@ moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const vo
   p.ntiles = (E + BN - 1) / BN;
   p.E = 1;
   const int blocks = ((T_ + 255) / 256) * p.ntiles;
-  hipError_t e = launch<ROUTER, 256>(p, blocks, ctx->stream);
+  hipError_t e = launch<ROUTER, 256, 2>(p, blocks, ctx->stream);
   if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "router GEMM: %s", hipGetErrorString(e));
   return MOE_OK;
 }
@@ -763,7 +757,7 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.mtiles = (F + 255) / 256;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
-      e = launch<WGRAD_DOWN, 256>(p, E * p.ntiles * p.mtiles, ctx->stream);
+      e = launch<WGRAD_DOWN, 256, 2>(p, E * p.ntiles * p.mtiles, ctx->stream);
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down wgrad: %s", hipGetErrorString(e));
   }
@@ -811,7 +805,7 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.mtiles = (d + 255) / 256;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
-      e = launch<WGRAD_UP, 256>(p, E * p.ntiles * p.mtiles, ctx->stream);
+      e = launch<WGRAD_UP, 256, 2>(p, E * p.ntiles * p.mtiles, ctx->stream);
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up wgrad: %s", hipGetErrorString(e));
   }

@@ -56,3 +56,16 @@ def test_no_cpu_fallback_without_gpu():
         pytest.skip("a GPU is present")
     with pytest.raises(moe.MoeError):
         moe.context(0)
+
+
+def test_library_has_no_unresolved_kernels():
+    """Every kernel launched from host code is defined in the library (a
+    kernel whose stub the host pass failed to emit would be an undefined
+    symbol that only fails at load time)."""
+    import subprocess
+    import routing_grouped_expert_softmax_amd as m
+    ctypes.CDLL(m.LIB_PATH, mode=os.RTLD_NOW)
+    out = subprocess.run(["nm", "-C", "--undefined-only", m.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    bad = [ln for ln in out.splitlines() if "anonymous namespace" in ln or "moe" in ln]
+    assert not bad, bad
