@@ -31,6 +31,8 @@
 //    writes zeros.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 using namespace moe;
@@ -100,6 +102,21 @@ __device__ __forceinline__ int swz_kc(int row) { return (row ^ (row >> 3)) & 7; 
 // 4*(k & 3), so a transposing fragment read (4 k rows x 32 bytes per 16
 // lanes) covers every bank slot once per 32 lanes.
 __device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 2; }
+
+// 16-byte-per-lane buffer load straight into LDS (lane l writes lds + 16*l).
+// Issued as inline assembly so the compiler's wait-count pass does not treat
+// it as an LDS write that every later LDS read must wait for: the kernel
+// waits for these loads itself (s_waitcnt vmcnt) before the barrier that
+// publishes a stage.  The instruction has no register outputs.  M0 carries
+// the LDS address (one wait state between writing M0 and the load).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, LDS_AS void* lds, int voff,
+                                      int soff) {
+  const unsigned lds_addr = (unsigned)(uintptr_t)lds;
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
+               : "memory");
+}
 
 // Tile geometry of one pipeline stage.
 template <int MODE, int BM>
@@ -197,7 +214,11 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   using TR = Traits<MODE>;
   using TL = Tile<MODE, BM>;
   constexpr int SM = TL::SM;
-  extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+  // One LDS array per pipeline stage: distinct objects let the compiler see
+  // that fragment reads of one stage never alias the loads landing in another.
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds2[S > 2 ? TL::STAGE : 16];
   __shared__ int sh[kThreads + 4];
 
   const int tid = threadIdx.x;
@@ -307,9 +328,15 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   }
 
   // Issue the direct loads of K step kt into stage buffer `st`.
-  auto issue = [&](int kt, int st) {
+  auto stage_ptr = [&](auto st) -> LDS_AS unsigned char* {
+    constexpr int ST = decltype(st)::value;
+    if constexpr (ST == 0) return (LDS_AS unsigned char*)lds0;
+    else if constexpr (ST == 1) return (LDS_AS unsigned char*)lds1;
+    else return (LDS_AS unsigned char*)lds2;
+  };
+  auto issue = [&](int kt, auto st) {
     const int k0 = kt * BK;
-    LDS_AS unsigned char* base = (LDS_AS unsigned char*)((LDS_AS unsigned char*)smem) + st * TL::STAGE;
+    LDS_AS unsigned char* base = stage_ptr(st);
     // A
     {
       __amdgpu_buffer_rsrc_t r = rsa0;
@@ -326,8 +353,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
       }
 #pragma unroll
       for (int j = 0; j < TL::A_INST; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (LDS_AS void*)(base + (wv * TL::A_INST + j) * 1024), 16, aoff[j], soff, 0, 0);
+        dma16(r, (LDS_AS void*)(base + (wv * TL::A_INST + j) * 1024), aoff[j], soff);
     }
     // B
     {
@@ -347,8 +373,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
       }
 #pragma unroll
       for (int j = 0; j < TL::B_INST; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (LDS_AS void*)(bbase + (wv * TL::B_INST + j) * 1024), 16, boff[j], soff, 0, 0);
+        dma16(r, (LDS_AS void*)(bbase + (wv * TL::B_INST + j) * 1024), boff[j], soff);
     }
   };
 
@@ -385,8 +410,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](int st) {
-    const LDS_AS unsigned char* As = (const LDS_AS unsigned char*)((LDS_AS unsigned char*)smem) + st * TL::STAGE;
+  auto compute = [&](auto st) {
+    const LDS_AS unsigned char* As = stage_ptr(st);
     const LDS_AS unsigned char* Bs = As + TL::A_BYTES;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
@@ -423,22 +448,43 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   // wave's loads visible and frees the buffer read in step kt-1, the loads of
   // step kt+S-1 go into that buffer, then step kt is computed.
   constexpr int LPS = TL::A_INST + TL::B_INST;  // direct loads per wave per stage
-#pragma unroll
-  for (int s = 0; s < S - 1; ++s)
-    if (s < nk) issue(s, s);
-  for (int kt = 0; kt < nk; ++kt) {
-    // loads issued after stage kt so far: stages kt+1 .. min(kt+S-2, nk-1)
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (0 < nk) issue(0, I0{});
+  if (S > 2 && 1 < nk) issue(1, I1{});
+  // One K step on stage CUR, loading step kt+S-1 into stage NXT.  The wait
+  // covers only this wave's loads of step kt (later steps stay in flight);
+  // the barrier has no memory fence (a fence would drain every load).
+  auto step = [&](int kt, auto cur, auto nxt) {
     const int after = min(S - 2, nk - 1 - kt);
-    if (S >= 3 && after >= 1) {
-      // vmcnt(LPS): simm16 = vmcnt[3:0] | expcnt(7)[6:4] | lgkmcnt(15)[11:8] | vmcnt[5:4]<<14
+    if (S >= 3 && after >= 1)
+      // vmcnt(LPS): simm16 = vmcnt[3:0] | expcnt(7)<<4 | lgkmcnt(15)<<8 | vmcnt[5:4]<<14
       __builtin_amdgcn_s_waitcnt((LPS & 15) | (7 << 4) | (15 << 8) | ((LPS >> 4) << 14));
-    } else {
+    else
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + S - 1 < nk) issue(kt + S - 1, nxt);
+    compute(cur);
+  };
+  int kt = 0;
+  if constexpr (S == 2) {
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, I0{}, I1{});
+      step(kt + 1, I1{}, I0{});
     }
-    __syncthreads();
-    if (kt + S - 1 < nk) issue(kt + S - 1, (kt + S - 1) % S);
-    compute(kt % S);
+    if (kt < nk) step(kt, I0{}, I1{});
+  } else {
+    for (; kt + 2 < nk; kt += 3) {
+      step(kt, I0{}, I2{});
+      step(kt + 1, I1{}, I0{});
+      step(kt + 2, I2{}, I1{});
+    }
+    if (kt < nk) step(kt, I0{}, I2{});
+    if (kt + 1 < nk) step(kt + 1, I1{}, I0{});
   }
+  // all waves are done with the stage buffers before the block exits
+  asm volatile("s_barrier" ::: "memory");
 
   // ---------------------------------------------------------------- epilogue
   // Lane holds C[m = mbase + (lane&31)][n = nbase + 8*(r/4) + 4*(lane>>5) + r%4].
@@ -535,17 +581,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
 
 template <int MODE, int BM, int S>
 hipError_t launch(const Params& p, int blocks, hipStream_t s) {
-  using TL = Tile<MODE, BM>;
-  const int smem = S * TL::STAGE;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)grouped_gemm_kernel<MODE, BM, S>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   blocks = (blocks + 7) / 8 * 8;
-  grouped_gemm_kernel<MODE, BM, S><<<blocks, kThreads, smem, s>>>(p);
+  grouped_gemm_kernel<MODE, BM, S><<<blocks, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
