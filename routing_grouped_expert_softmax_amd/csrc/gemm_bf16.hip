@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "common.h"
 
@@ -87,20 +88,24 @@ struct Params {
 };
 
 constexpr int BN = 256;
-constexpr int BK = 64;
 constexpr int kThreads = 256;
 
 #define LDS_AS __attribute__((address_space(3)))
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
 // ---------------------------------------------------------------- LDS layouts
-// K-contiguous tile ([rows][64 k], 128-byte rows): the 16-byte chunk index is
-// XOR-swizzled with g(row) = (row ^ row>>3) & 7, so the rows of any 16
-// consecutive fragment lanes hit 16 distinct bank slots.
-__device__ __forceinline__ int swz_kc(int row) { return (row ^ (row >> 3)) & 7; }
-// M/N-contiguous tile ([64 k][cols], 256- or 512-byte rows): chunk index XOR
-// 4*(k & 3), so a transposing fragment read (4 k rows x 32 bytes per 16
-// lanes) covers every bank slot once per 32 lanes.
+// K-contiguous tile: groups of 8 rows, each group 1 KiB laid out as
+// [16-deep K slice][row % 8][32 bytes], the two 16-byte halves of a row
+// swapped when bit 3 of the row is set.  One 1 KiB load instruction fills one
+// group (8 full 128-byte row segments of HBM); the 16 lanes of one LDS pass
+// (16 consecutive rows, same half) hit 16 distinct bank slots; a fragment
+// address is one per-lane base plus a compile-time offset per row block and
+// slice.
+__device__ __forceinline__ int kc_half(int row, int h) { return h ^ ((row >> 3) & 1); }
+// M/N-contiguous tile ([64 k][cols], 256- or 512-byte rows): the 16-byte
+// chunk index is XOR-ed with 4*(k & 3), so a transposing fragment read
+// (4 k rows x 32 bytes per 16 lanes, two groups side by side) covers every
+// bank slot once per 32 lanes.
 __device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 2; }
 
 // 16-byte-per-lane buffer load straight into LDS (lane l writes lds + 16*l).
@@ -118,8 +123,23 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, LDS_AS void* lds
                : "memory");
 }
 
+// Scheduling hint for one K slice: one MFMA, then its share of the DS reads
+// of the next slice, repeated (the groups are compile-time constants).
+template <int I, int NM, int NR>
+__device__ __forceinline__ void sched_step() {
+  constexpr int per = (NR + NM - 1) / NM;
+  constexpr int done = I * per;
+  constexpr int n = NR - done < 0 ? 0 : (NR - done < per ? NR - done : per);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+  if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // DS reads
+}
+template <int NM, int NR, int... I>
+__device__ __forceinline__ void sched_interleave(std::integer_sequence<int, I...>) {
+  (sched_step<I, NM, NR>(), ...);
+}
+
 // Tile geometry of one pipeline stage.
-template <int MODE, int BM>
+template <int MODE, int BM, int BK>
 struct Tile {
   using TR = Traits<MODE>;
   static constexpr int WM = BM / 2;   // wave tile rows (M)
@@ -208,17 +228,18 @@ __device__ bool find_mtile(const Params& p, int* sh, Work& w) {
   return true;
 }
 
-template <int MODE, int BM, int S>
+template <int MODE, int BM, int S, int BK>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using TR = Traits<MODE>;
-  using TL = Tile<MODE, BM>;
+  using TL = Tile<MODE, BM, BK>;
   constexpr int SM = TL::SM;
   // One LDS array per pipeline stage: distinct objects let the compiler see
   // that fragment reads of one stage never alias the loads landing in another.
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char lds2[S > 2 ? TL::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds3[S > 3 ? TL::STAGE : 16];
   __shared__ int sh[kThreads + 4];
 
   const int tid = threadIdx.x;
@@ -302,8 +323,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   for (int j = 0; j < TL::A_INST; ++j) {
     const int q = wv * TL::A_INST + j;  // 1 KiB instruction index inside the A tile
     if (TR::kA_KCONTIG) {
-      const int row = q * 8 + (lane >> 3), pc = lane & 7;
-      aoff[j] = (row * p.lda + ((pc ^ swz_kc(row)) << 3)) * (int)esz;
+      // instruction q fills rows 8q..8q+7; lane = slice*16 + (row%8)*2 + half
+      const int kk = lane >> 4, row = q * 8 + ((lane & 15) >> 1), hp = lane & 1;
+      aoff[j] = (row * p.lda + (kk * 2 + kc_half(row, hp)) * 8) * (int)esz;
     } else {
       constexpr int CPR = BM / 8;  // 16-byte chunks per k row
       const int k = (q * 64 + lane) / CPR, pc = (q * 64 + lane) % CPR;
@@ -314,11 +336,12 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   for (int j = 0; j < TL::B_INST; ++j) {
     const int q = wv * TL::B_INST + j;
     if (TR::kB_KCONTIG) {
-      const int n = q * 8 + (lane >> 3), pc = lane & 7;
-      boff[j] = ((w.nt * BN + n) * p.ldb + ((pc ^ swz_kc(n)) << 3)) * (int)esz;
+      const int kk = lane >> 4, n = q * 8 + ((lane & 15) >> 1), hp = lane & 1;
+      boff[j] = ((w.nt * BN + n) * p.ldb + (kk * 2 + kc_half(n, hp)) * 8) * (int)esz;
     } else if (TR::kDUAL) {
-      // two sub-tiles of [64 k][128 n]: instructions 0..15 matrix 0, 16..31 matrix 1
-      const int qq = q & 15;
+      // two sub-tiles of [BK k][128 n]: the first BK/4 instructions fill
+      // matrix 0 (waves 0,1), the rest matrix 1 (waves 2,3)
+      const int qq = q % (BK / 4);
       const int k = qq * 4 + (lane >> 4), pc = lane & 15;
       boff[j] = (k * p.ldb + w.nt * 128 + ((pc ^ swz_mn(k)) << 3)) * (int)esz;
     } else {
@@ -332,7 +355,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
     constexpr int ST = decltype(st)::value;
     if constexpr (ST == 0) return (LDS_AS unsigned char*)lds0;
     else if constexpr (ST == 1) return (LDS_AS unsigned char*)lds1;
-    else return (LDS_AS unsigned char*)lds2;
+    else if constexpr (ST == 2) return (LDS_AS unsigned char*)lds2;
+    else return (LDS_AS unsigned char*)lds3;
   };
   auto issue = [&](int kt, auto st) {
     const int k0 = kt * BK;
@@ -378,28 +402,30 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   };
 
   // ---------------------------------------------------------------- fragments
-  // K-contiguous tile: one 16-byte read per lane (row = lane & 31).
+  // K-contiguous tile: lane reads row (row0 + lane & 31), half (lane >> 5) of
+  // slice kk.  The per-lane part is computed once; row0 (a multiple of 32)
+  // and kk fold into the instruction's immediate offset.
+  const int kc_lane = ((lane & 31) >> 3) * 1024 + (lane & 7) * 32 +
+                      (kc_half(lane & 31, lane >> 5) << 4);
   auto frag_kc = [&](const LDS_AS unsigned char* t, int row0, int kk) -> bf16x8 {
-    const int row = row0 + (lane & 31);
-    const int lc = kk * 2 + (lane >> 5);
-    return *(const LDS_AS bf16x8*)(t + row * 128 + ((lc ^ swz_kc(row)) << 4));
+    return *(const LDS_AS bf16x8*)(t + (row0 >> 3) * 1024 + kk * 256 + kc_lane);
   };
   // M/N-contiguous tile: two transposing 8-byte reads give each lane 8
   // consecutive k of column (col0 + lane & 31): in each 16-lane group, lane i
-  // receives element i%4 of the reads of lanes i/4 + 4j, so lane
-  // a + 4b addresses row k0 + b, columns col0 + 16*group + 4a.
+  // receives element i%4 of the reads of lanes i/4 + 4j, so lane a + 4b
+  // addresses row 8*half + 4r + b, columns col0 + 16*group + 4a.  The k of a
+  // lane is kk*16 + 8*half + 4r + b, so the swizzle depends on b only and kk,
+  // r fold into the immediate offset.
+  const int mn_b = (lane & 15) >> 2, mn_g = (lane >> 4) & 1, mn_half = lane >> 5;
+  const int mn_x = 2 * mn_g + ((lane & 3) >> 1);   // chunk within the 32-column group
+  const int mn_sub = (lane & 1) * 8;               // 8-byte half of the chunk
   auto frag_mn = [&](const LDS_AS unsigned char* t, int pitch, int col0, int kk) -> bf16x8 {
-    const int g = (lane >> 4) & 1, half = lane >> 5;
-    const int col = col0 + 16 * g + 4 * (lane & 3);
-    bf16x4 v[2];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int k = kk * 16 + 8 * half + 4 * r + ((lane & 15) >> 2);
-      const LDS_AS unsigned char* a =
-          t + k * pitch + (((col >> 3) ^ swz_mn(k)) << 4) + ((col & 7) << 1);
-      v[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)a);
-    }
-    return __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    // (col0/8 + x) ^ 4*b with col0 a multiple of 32: bits 2.. come from col0
+    const int chunk = ((col0 >> 3) ^ swz_mn(mn_b)) + mn_x;
+    const LDS_AS unsigned char* a = t + (8 * mn_half + mn_b) * pitch + (chunk << 4) + mn_sub;
+    bf16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(a + (kk * 16) * pitch));
+    bf16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((LDS_AS bf16x4*)(a + (kk * 16 + 4) * pitch));
+    return __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
   f32x16 acc[SM][4];
@@ -410,36 +436,62 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](auto st) {
-    const LDS_AS unsigned char* As = stage_ptr(st);
+  // Fragments of one 16-deep K slice.
+  struct Frags {
+    bf16x8 xb[4], ya[SM];
+  };
+  auto load_frags = [&](const LDS_AS unsigned char* As, int kk, Frags& f) {
     const LDS_AS unsigned char* Bs = As + TL::A_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 xb[4], ya[SM];
-#pragma unroll
-      for (int sn = 0; sn < 4; ++sn) {
-        if (TR::kB_KCONTIG) {
-          xb[sn] = frag_kc(Bs, wn * 128 + sn * 32, kk);
-        } else if (TR::kDUAL) {
-          // subtiles 0,1: matrix 0 columns wn*64 + ..; 2,3: matrix 1, same columns
-          xb[sn] = frag_mn(Bs + (sn >> 1) * (BK * 256), 256, wn * 64 + (sn & 1) * 32, kk);
-        } else {
-          xb[sn] = frag_mn(Bs, 512, wn * 128 + sn * 32, kk);
-        }
+    for (int sn = 0; sn < 4; ++sn) {
+      if (TR::kB_KCONTIG) {
+        f.xb[sn] = frag_kc(Bs, wn * 128 + sn * 32, kk);
+      } else if (TR::kDUAL) {
+        // subtiles 0,1: matrix 0 columns wn*64 + ..; 2,3: matrix 1, same columns
+        f.xb[sn] = frag_mn(Bs + (sn >> 1) * (BK * 256), 256, wn * 64 + (sn & 1) * 32, kk);
+      } else {
+        f.xb[sn] = frag_mn(Bs, 512, wn * 128 + sn * 32, kk);
       }
-#pragma unroll
-      for (int sm = 0; sm < SM; ++sm) {
-        if (TR::kA_KCONTIG)
-          ya[sm] = frag_kc(As, wm * TL::WM + sm * 32, kk);
-        else
-          ya[sm] = frag_mn(As, TL::A_PITCH, wm * TL::WM + sm * 32, kk);
-      }
-#pragma unroll
-      for (int sm = 0; sm < SM; ++sm)
-#pragma unroll
-        for (int sn = 0; sn < 4; ++sn)
-          acc[sm][sn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xb[sn], ya[sm], acc[sm][sn], 0, 0, 0);
     }
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm) {
+      if (TR::kA_KCONTIG)
+        f.ya[sm] = frag_kc(As, wm * TL::WM + sm * 32, kk);
+      else
+        f.ya[sm] = frag_mn(As, TL::A_PITCH, wm * TL::WM + sm * 32, kk);
+    }
+  };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn)
+        acc[sm][sn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.xb[sn], f.ya[sm], acc[sm][sn], 0, 0, 0);
+  };
+  // LDS read instructions per K slice and MFMAs per K slice.
+  constexpr int kReads = (TR::kB_KCONTIG ? 4 : 8) + (TR::kA_KCONTIG ? SM : 2 * SM);
+  constexpr int kMfma = SM * 4;
+  // Scheduling hint: alternate the MFMAs of one slice with the LDS reads of
+  // the next, so the matrix pipe never waits on a just-issued read.
+  auto interleave = [&]() { sched_interleave<kMfma, kReads>(std::make_integer_sequence<int, kMfma>{}); };
+  // One stage: the fragments of slice kk+1 are read while the MFMAs of slice
+  // kk run.
+  auto compute = [&](auto st) {
+    const LDS_AS unsigned char* As = stage_ptr(st);
+    Frags f0, f1;
+    load_frags(As, 0, f0);
+    load_frags(As, 1, f1);
+    mma(f0);
+    interleave();
+    if constexpr (BK == 64) {
+      load_frags(As, 2, f0);
+      mma(f1);
+      interleave();
+      load_frags(As, 3, f1);
+      mma(f0);
+      interleave();
+    }
+    mma(f1);
   };
 
   // ---------------------------------------------------------------- main loop
@@ -451,15 +503,19 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
   if (0 < nk) issue(0, I0{});
   if (S > 2 && 1 < nk) issue(1, I1{});
+  if (S > 3 && 2 < nk) issue(2, I2{});
   // One K step on stage CUR, loading step kt+S-1 into stage NXT.  The wait
   // covers only this wave's loads of step kt (later steps stay in flight);
   // the barrier has no memory fence (a fence would drain every load).
   auto step = [&](int kt, auto cur, auto nxt) {
-    const int after = min(S - 2, nk - 1 - kt);
-    if (S >= 3 && after >= 1)
-      // vmcnt(LPS): simm16 = vmcnt[3:0] | expcnt(7)<<4 | lgkmcnt(15)<<8 | vmcnt[5:4]<<14
+    const int after = min(S - 2, nk - 1 - kt);  // stages issued after kt so far
+    // vmcnt(n): simm16 = vmcnt[3:0] | expcnt(7)<<4 | lgkmcnt(15)<<8 | vmcnt[5:4]<<14
+    if (S >= 4 && after >= 2)
+      __builtin_amdgcn_s_waitcnt(((2 * LPS) & 15) | (7 << 4) | (15 << 8) | (((2 * LPS) >> 4) << 14));
+    else if (S >= 3 && after >= 1)
       __builtin_amdgcn_s_waitcnt((LPS & 15) | (7 << 4) | (15 << 8) | ((LPS >> 4) << 14));
     else
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
@@ -474,7 +530,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
       step(kt + 1, I1{}, I0{});
     }
     if (kt < nk) step(kt, I0{}, I1{});
-  } else {
+  } else if constexpr (S == 3) {
     for (; kt + 2 < nk; kt += 3) {
       step(kt, I0{}, I2{});
       step(kt + 1, I1{}, I0{});
@@ -482,6 +538,16 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
     }
     if (kt < nk) step(kt, I0{}, I2{});
     if (kt + 1 < nk) step(kt + 1, I1{}, I0{});
+  } else {
+    for (; kt + 3 < nk; kt += 4) {
+      step(kt, I0{}, I3{});
+      step(kt + 1, I1{}, I0{});
+      step(kt + 2, I2{}, I1{});
+      step(kt + 3, I3{}, I2{});
+    }
+    if (kt < nk) step(kt, I0{}, I3{});
+    if (kt + 1 < nk) step(kt + 1, I1{}, I0{});
+    if (kt + 2 < nk) step(kt + 2, I2{}, I1{});
   }
   // all waves are done with the stage buffers before the block exits
   asm volatile("s_barrier" ::: "memory");
@@ -579,12 +645,17 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
 #endif
 }
 
-template <int MODE, int BM, int S>
+template <int MODE, int BM, int S, int BK>
 hipError_t launch(const Params& p, int blocks, hipStream_t s) {
   blocks = (blocks + 7) / 8 * 8;
-  grouped_gemm_kernel<MODE, BM, S><<<blocks, kThreads, 0, s>>>(p);
+  grouped_gemm_kernel<MODE, BM, S, BK><<<blocks, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
+
+#ifndef GEMM_BK
+#define GEMM_BK 64
+#define GEMM_S 2
+#endif
 
 // Upper bound of sum_e ceil(n_e / BM) over any split of R rows into E groups.
 int mtile_bound(int R, int E, int BM) { return R / BM + E; }
@@ -594,20 +665,18 @@ int mtile_bound(int R, int E, int BM) { return R / BM + E; }
 // ---------------------------------------------------------------- host API
 using namespace moe_host;
 
-// Row-tile height for an M-ragged launch: 128 when the average expert holds
-// fewer than ~1000 rows (less padding in each expert's last tile), else 256.
-static int pick_bm(int R, int E) { return (R / (E > 0 ? E : 1)) < 1024 ? 128 : 256; }
-
+// Row-tile height of an M-ragged launch.  256-row tiles halve the weight
+// traffic per FLOP and win even when experts hold only ~500 rows; the down
+// dgrad, whose epilogue also streams the saved g and u, runs best with 128.
 template <int MODE>
 static hipError_t launch_mragged(Params& p, int R, hipStream_t s) {
-  const int bm = pick_bm(R, p.E);
-  if (bm == 128) return launch<MODE, 128, 3>(p, mtile_bound(R, p.E, 128) * p.ntiles, s);
-  return launch<MODE, 256, 2>(p, mtile_bound(R, p.E, 256) * p.ntiles, s);
+  if (MODE == DGRAD_DOWN) return launch<MODE, 128, 3, 64>(p, mtile_bound(R, p.E, 128) * p.ntiles, s);
+  return launch<MODE, 256, GEMM_S, GEMM_BK>(p, mtile_bound(R, p.E, 256) * p.ntiles, s);
 }
 
 moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const void* wr, int T_,
                                            int d, int E, float* logits) {
-  if (d % BK != 0)
+  if (d % 64 != 0)
     return fail(ctx, MOE_ERR_UNSUPPORTED, "moe_router_logits: MFMA path needs d %% 64 == 0");
   Params p{};
   p.a0 = (const bf16_t*)x;
@@ -623,7 +692,7 @@ moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const vo
   p.ntiles = (E + BN - 1) / BN;
   p.E = 1;
   const int blocks = ((T_ + 255) / 256) * p.ntiles;
-  hipError_t e = launch<ROUTER, 256, 2>(p, blocks, ctx->stream);
+  hipError_t e = launch<ROUTER, 256, 2, 64>(p, blocks, ctx->stream);
   if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "router GEMM: %s", hipGetErrorString(e));
   return MOE_OK;
 }
@@ -794,7 +863,7 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.mtiles = (F + 255) / 256;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
-      e = launch<WGRAD_DOWN, 256, 2>(p, E * p.ntiles * p.mtiles, ctx->stream);
+      e = launch<WGRAD_DOWN, 256, GEMM_S, GEMM_BK>(p, E * p.ntiles * p.mtiles, ctx->stream);
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down wgrad: %s", hipGetErrorString(e));
   }
@@ -842,7 +911,7 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.mtiles = (d + 255) / 256;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
-      e = launch<WGRAD_UP, 256, 2>(p, E * p.ntiles * p.mtiles, ctx->stream);
+      e = launch<WGRAD_UP, 256, GEMM_S, GEMM_BK>(p, E * p.ntiles * p.mtiles, ctx->stream);
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up wgrad: %s", hipGetErrorString(e));
   }
