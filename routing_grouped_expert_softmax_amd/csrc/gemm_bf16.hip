@@ -7,19 +7,21 @@
 // layer is dropless ([P3]).  The pages' kernel is prior art for another GPU;
 // this one is written for CDNA4:
 //
-//  * Block tile BM x 256 (BM = 256 or 128) x BK = 64, four waves in a 2x2
-//    grid, each wave a (BM/2) x 128 sub-tile of 32x32 MFMA tiles.  One block
-//    per CU (128 KiB of LDS: two stages of A and B tiles).
-//  * Both tiles live in LDS K-contiguous (one 128-byte row per M/N index) with
-//    the 16-byte chunk index XOR-swizzled by (row & 7), so fragment reads
-//    (lanes on 32 consecutive rows, one 16-byte chunk each) are conflict-free.
-//    Operands that are K-strided in HBM (weights in the forward pass,
-//    activations in wgrad) are loaded as 8x8 blocks of 16-byte row pieces and
-//    transposed in registers before the LDS store.
-//  * Global loads for stage k+1 are issued before the MFMAs of stage k; one
-//    barrier per K step.
-//  * The MFMA operands are swapped (weights as the A operand) so each lane ends
-//    with four consecutive output columns per register group: 8-byte stores.
+//  * Block tile BM x 256 x BK (BM = 256, or 128 for the down dgrad; BK = 64),
+//    four waves in a 2x2 grid, each wave a (BM/2) x 128 sub-tile of 32x32
+//    MFMA tiles with its accumulators in AGPRs.  One block per CU.
+//  * Tiles move HBM -> LDS with buffer loads that write LDS directly (16 bytes
+//    per lane), S stages deep, one static LDS array per stage, explicit vmcnt
+//    waits and a fence-free barrier; no VGPR staging, no VALU transposes.
+//  * K-contiguous operands (activations in the forward pass and dgrad, weight
+//    rows in dgrad) feed the MFMA with ds_read_b128; M/N-contiguous operands
+//    (weights in the forward pass, both operands in wgrad) with two
+//    ds_read_b64_tr_b16 (hardware transpose) per fragment.  Both LDS layouts
+//    are swizzled so the direct-load writes and the fragment reads are free of
+//    bank conflicts (measured: zero).
+//  * The MFMA operands are swapped (B fragment as the A operand) so each lane
+//    ends with four consecutive output columns per register group: 8-byte
+//    stores, with the SwiGLU forward/backward fused into the epilogue.
 //  * Scheduling: M-ragged launches (forward, dgrad) size the grid from the host
 //    bound sum_e ceil(n_e/BM) <= R/BM + E; every block scans the per-expert
 //    counts (from `offsets`, read on the device) to find its (expert, m-tile,
@@ -121,21 +123,6 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, LDS_AS void* lds
                :
                : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
                : "memory");
-}
-
-// Scheduling hint for one K slice: one MFMA, then its share of the DS reads
-// of the next slice, repeated (the groups are compile-time constants).
-template <int I, int NM, int NR>
-__device__ __forceinline__ void sched_step() {
-  constexpr int per = (NR + NM - 1) / NM;
-  constexpr int done = I * per;
-  constexpr int n = NR - done < 0 ? 0 : (NR - done < per ? NR - done : per);
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-  if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);  // DS reads
-}
-template <int NM, int NR, int... I>
-__device__ __forceinline__ void sched_interleave(std::integer_sequence<int, I...>) {
-  (sched_step<I, NM, NR>(), ...);
 }
 
 // Tile geometry of one pipeline stage.
@@ -468,28 +455,19 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
       for (int sn = 0; sn < 4; ++sn)
         acc[sm][sn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.xb[sn], f.ya[sm], acc[sm][sn], 0, 0, 0);
   };
-  // LDS read instructions per K slice and MFMAs per K slice.
-  constexpr int kReads = (TR::kB_KCONTIG ? 4 : 8) + (TR::kA_KCONTIG ? SM : 2 * SM);
-  constexpr int kMfma = SM * 4;
-  // Scheduling hint: alternate the MFMAs of one slice with the LDS reads of
-  // the next, so the matrix pipe never waits on a just-issued read.
-  auto interleave = [&]() { sched_interleave<kMfma, kReads>(std::make_integer_sequence<int, kMfma>{}); };
   // One stage: the fragments of slice kk+1 are read while the MFMAs of slice
-  // kk run.
+  // kk run (the compiler interleaves the two).
   auto compute = [&](auto st) {
     const LDS_AS unsigned char* As = stage_ptr(st);
     Frags f0, f1;
     load_frags(As, 0, f0);
     load_frags(As, 1, f1);
     mma(f0);
-    interleave();
     if constexpr (BK == 64) {
       load_frags(As, 2, f0);
       mma(f1);
-      interleave();
       load_frags(As, 3, f1);
       mma(f0);
-      interleave();
     }
     mma(f1);
   };
