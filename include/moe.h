@@ -41,8 +41,8 @@
  *    never aborts; launch failures return MOE_ERR_HIP.  moe_last_error gives
  *    the text.  Device faults surface asynchronously, as in HIP.
  *  - Limits: 1 <= k <= min(E, 32); E <= 1024; T*k < 2^31; d % 8 == 0 and
- *    F % 8 == 0 (16-byte bf16 rows); data pointers 16-byte aligned.
- *    For MXFP8, d and F are multiples of 128.
+ *    F % 8 == 0 (16-byte bf16 rows); data pointers 16-byte aligned.  The bf16
+ *    grouped FFN needs d, F % 64 == 0; MXFP8 needs d, F % 128 == 0.
  *  - Preconditions: logits are finite (otherwise routing is unspecified but
  *    memory-safe).  A context is not thread-safe: one context per stream.
  *  - Gradients overwrite their outputs (no accumulation into them).
@@ -67,8 +67,13 @@ typedef enum {
 } moe_status;
 
 /* Element type of activations and weights.  MOE_F32: fp32 data and fp32
- * arithmetic.  MOE_BF16: bf16 data, fp32 accumulation, bf16 outputs. */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+ * arithmetic.  MOE_BF16: bf16 data, fp32 accumulation, bf16 outputs.
+ * MOE_MXFP8: (grouped FFN only) bf16 data in and out; every GEMM operand is
+ * quantised to MXFP8 along its reduction axis (E4M3 elements, 32-element
+ * blocks, e8m0 scales, see moe_mx_quantize), fp32 accumulation, bf16 outputs;
+ * g and u are bf16 and SwiGLU and its backward run in fp32 on those values,
+ * h, dyp, dg and du are quantised again where a GEMM consumes them.  [P1] 三 */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP8 = 2 } moe_dtype;
 
 /* ---------------------------------------------------------------- context */
 
@@ -88,6 +93,10 @@ const char* moe_last_error(const moe_ctx* ctx);
  * so they share one region.  *bytes is a host output. */
 moe_status moe_workspace_size(moe_ctx* ctx, int T, int d, int E, int k, moe_dtype dtype,
                               size_t* bytes);
+/* Device workspace of an MXFP8 grouped FFN call (moe_grouped_ffn_fwd/bwd with
+ * MOE_MXFP8: the quantised operands); *bytes is a host output.  Register
+ * max(this, moe_workspace_size(...)). */
+moe_status moe_mx_workspace_size(moe_ctx* ctx, int E, int R, int d, int F, size_t* bytes);
 /* Register caller-owned device workspace (256-byte aligned). */
 moe_status moe_set_workspace(moe_ctx* ctx, void* ws, size_t bytes);
 
@@ -174,6 +183,27 @@ moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_se
                             const int32_t* src_tk, const int32_t* offsets, int T, int d, int E,
                             int k, moe_dtype dtype, void* dw_router);
 
+/* ----------------------------------------------------------------- MXFP8
+ * MX quantisation of a bf16 [rows, cols] matrix ([P1] 三: MXFP8).  Blocks of
+ * 32 elements share the scale byte s + 127 with s = floor(log2(max |v|)) - 8
+ * clamped to [-127, 127] (byte 0 for an all-zero block); each element is the
+ * E4M3 value nearest to v / 2^s (ties to even, saturating at +-448, sign
+ * kept, NaN -> 0x7f).
+ *  axis 0: blocks along each row (cols % 32 == 0): codes [rows, cols],
+ *          scales [rows, cols/32]; kpad_ld is ignored.
+ *  axis 1: blocks of 32 consecutive rows of one column, restarting at every
+ *          group of rows (group_offsets[groups+1] on the device; NULL means
+ *          one group of all rows), the last block of a group zero-padded.
+ *          Output transposed and K-contiguous: codes [cols, kpad_ld] and
+ *          scales [cols, kpad_ld/32]; group g starts at K position
+ *          sum_{g'<g} roundup(n_g', 128) and its positions up to
+ *          roundup(n_g, 128) are written (padding as zero codes and zero
+ *          scales).  kpad_ld % 128 == 0 and kpad_ld >= rows + 127*groups.
+ * codes/scales are caller-owned device buffers. */
+moe_status moe_mx_quantize(moe_ctx* ctx, const void* src_bf16, int rows, int cols, int axis,
+                           const int32_t* group_offsets, int groups, uint8_t* codes,
+                           uint8_t* scales_e8m0, int kpad_ld);
+
 /* -------------------------------------------------------------- profiling
  * Per-kernel timing with HIP events recorded on the context's stream around
  * each kernel launch, for measurement runs (off by default; costs two event
@@ -195,6 +225,7 @@ typedef enum {
   MOE_K_GEMM_WGRAD_UP,
   MOE_K_PERMUTE_BWD,       /* incl. the W_r transpose when the router term is on */
   MOE_K_ROUTER_WGRAD,
+  MOE_K_MX_QUANT,          /* MXFP8 quantisation (moe_mx_quantize and the MX FFN) */
   MOE_K_COUNT
 } moe_kernel_id;
 

@@ -373,3 +373,171 @@ def mx_dequantize_cols(codes, scales, offsets):
             out[r0:r1] = vals[r0:r1] * np.ldexp(1.0, scales[blk].astype(np.int32) - 127)[None, :]
             blk += 1
     return out
+
+
+# ------------------------------------------------------------------ MXFP8 expert chain
+def _bf16_round(a):
+    """Round float64 values to bf16 (nearest even) and return them as float64."""
+    a32 = np.ascontiguousarray(a, dtype=np.float32)
+    u = a32.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def mx_rows(a):
+    """Exact values of `a` after MX quantisation along its rows (axis 0)."""
+    c, s = mx_quantize(np.ascontiguousarray(a, dtype=np.float32), axis=0)
+    return mx_dequantize_rows(c, s)
+
+
+def mx_cols(a, offsets):
+    """Exact values of `a` after MX quantisation down its columns in blocks
+    restarting at each group of rows."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if offsets is None:
+        offsets = np.array([0, a.shape[0]], dtype=np.int32)
+    c, s = mx_quantize(a, axis=1, offsets=offsets)
+    return mx_dequantize_cols(c, s, offsets)
+
+
+def mx_expert_fwd(xp, offsets, wg, wu, wd):
+    """MXFP8 forward of the grouped SwiGLU experts ([P1] 三).  Each GEMM takes
+    its operands quantised along its reduction axis (activations rowwise,
+    weights down their columns, one block set per expert), dequantised
+    exactly, summed in fp64; g and u are rounded to bf16, h = silu(g)*u is
+    formed in fp64 from those values, rounded to bf16 and quantised again
+    for the down projection.  Returns g, u, h (bf16 values) and yp."""
+    R, d = xp.shape
+    E, _, F = wg.shape
+    xq = mx_rows(xp)
+    g = np.zeros((R, F))
+    u = np.zeros((R, F))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        g[lo:hi] = xq[lo:hi] @ mx_cols(wg[e], None)
+        u[lo:hi] = xq[lo:hi] @ mx_cols(wu[e], None)
+    g = _bf16_round(g)
+    u = _bf16_round(u)
+    h = _bf16_round(g / (1.0 + np.exp(-g)) * u)
+    hq = mx_rows(h)
+    yp = np.zeros((R, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            yp[lo:hi] = hq[lo:hi] @ mx_cols(wd[e], None)
+    return dict(g=g, u=u, h=h, yp=yp)
+
+
+def mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, g, u, h):
+    """MXFP8 backward for upstream rows dyp, given the forward's bf16 g, u and
+    h: dh = Q(dyp) Q(Wd^T) (blocks along d), dg/du from bf16 g, u in fp64
+    then rounded to bf16, dxp = Q(dg) Q(Wg^T) + Q(du) Q(Wu^T) (blocks along F),
+    and per expert dWd = Qc(h)^T Qc(dyp), dWg = Qc(xp)^T Qc(dg),
+    dWu = Qc(xp)^T Qc(du) with blocks along that expert's rows."""
+    R, d = xp.shape
+    E, _, F = wg.shape
+    dyq = mx_rows(dyp)
+    dh = np.zeros((R, F))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            dh[lo:hi] = dyq[lo:hi] @ mx_rows(wd[e]).T
+    s = 1.0 / (1.0 + np.exp(-g))
+    dg = _bf16_round(dh * u * s * (1.0 + g * (1.0 - s)))
+    du = _bf16_round(dh * g * s)
+    dgq, duq = mx_rows(dg), mx_rows(du)
+    dxp = np.zeros((R, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            dxp[lo:hi] = dgq[lo:hi] @ mx_rows(wg[e]).T + duq[lo:hi] @ mx_rows(wu[e]).T
+    off = np.asarray(offsets, dtype=np.int32)
+    xc, hc, yc = mx_cols(xp, off), mx_cols(h, off), mx_cols(dyp, off)
+    gc, uc = mx_cols(dg, off), mx_cols(du, off)
+    dwg = np.zeros((E, d, F))
+    dwu = np.zeros((E, d, F))
+    dwd = np.zeros((E, F, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            dwg[e] = xc[lo:hi].T @ gc[lo:hi]
+            dwu[e] = xc[lo:hi].T @ uc[lo:hi]
+            dwd[e] = hc[lo:hi].T @ yc[lo:hi]
+    return dict(dg=dg, du=du, dxp=dxp, dwg=dwg, dwu=dwu, dwd=dwd)
+
+
+def _expert_of(offsets, r):
+    return int(np.searchsorted(np.asarray(offsets), r, side="right") - 1)
+
+
+def mx_expert_rows(xp, dyp, offsets, wg, wu, wd, rows):
+    """The MX chain's per-row outputs (g, u, h, yp, dg, du, dxp) for the
+    selected rows only: every one of them depends on its own row and its
+    expert's weights, since rowwise blocks never span rows."""
+    E, d, F = wg.shape
+    rows = np.asarray(rows)
+    out = {k: np.zeros((len(rows), F)) for k in ("g", "u", "h", "dg", "du")}
+    out["yp"] = np.zeros((len(rows), d))
+    out["dxp"] = np.zeros((len(rows), d))
+    ex = np.array([_expert_of(offsets, r) for r in rows])
+    for e in np.unique(ex):
+        sel = np.nonzero(ex == e)[0]
+        r = rows[sel]
+        xq = mx_rows(xp[r])
+        g = _bf16_round(xq @ mx_cols(wg[e], None))
+        u = _bf16_round(xq @ mx_cols(wu[e], None))
+        h = _bf16_round(g / (1.0 + np.exp(-g)) * u)
+        yp = mx_rows(h) @ mx_cols(wd[e], None)
+        dh = mx_rows(dyp[r]) @ mx_rows(wd[e]).T
+        s = 1.0 / (1.0 + np.exp(-g))
+        dg = _bf16_round(dh * u * s * (1.0 + g * (1.0 - s)))
+        du = _bf16_round(dh * g * s)
+        dxp = mx_rows(dg) @ mx_rows(wg[e]).T + mx_rows(du) @ mx_rows(wu[e]).T
+        for k, v in (("g", g), ("u", u), ("h", h), ("yp", yp), ("dg", dg), ("du", du), ("dxp", dxp)):
+            out[k][sel] = v
+    return out
+
+
+def mx_expert_wgrad_elems(xp, dyp, offsets, wg, wu, wd, which, elems):
+    """Selected elements of the MX chain's weight gradients; which 0=dWg,
+    1=dWu, 2=dWd, elems (n,3) of (e, a, b) into dW[e][a][b].  Needs only the
+    columns a and b of the two operands over expert e's rows; column blocks
+    restart at the expert's first row."""
+    E, d, F = wg.shape
+    elems = np.asarray(elems).reshape(-1, 3)
+    out = np.zeros(len(elems))
+    for e in np.unique(elems[:, 0]):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        sel = np.nonzero(elems[:, 0] == e)[0]
+        one = np.array([0, hi - lo], dtype=np.int32)
+        xq = mx_rows(xp[lo:hi])
+        dyq = mx_rows(dyp[lo:hi])
+        wgc, wuc, wdc = mx_cols(wg[e], None), mx_cols(wu[e], None), mx_cols(wd[e], None)
+        wdr = mx_rows(wd[e])
+
+        def gu(c):
+            g = _bf16_round(xq @ wgc[:, c])
+            u = _bf16_round(xq @ wuc[:, c])
+            return g, u
+
+        def col(v):  # column quantisation of one column over the expert's rows
+            return mx_cols(v.reshape(-1, 1), one)[:, 0]
+
+        for i in sel:
+            _, a, b = (int(t) for t in elems[i])
+            if which == 2:  # dWd[a][b] = sum_r Qc(h)[r,a] Qc(dyp)[r,b]
+                g, u = gu(a)
+                h = _bf16_round(g / (1.0 + np.exp(-g)) * u)
+                out[i] = col(h) @ col(dyp[lo:hi, b].astype(np.float64))
+            else:  # dWg/dWu[a][b] = sum_r Qc(xp)[r,a] Qc(dg or du)[r,b]
+                g, u = gu(b)
+                dh = dyq @ wdr[b, :]
+                s = 1.0 / (1.0 + np.exp(-g))
+                v = dh * u * s * (1.0 + g * (1.0 - s)) if which == 0 else dh * g * s
+                out[i] = col(xp[lo:hi, a].astype(np.float64)) @ col(_bf16_round(v))
+        del xq, dyq, wgc, wuc, wdc, wdr
+    return out

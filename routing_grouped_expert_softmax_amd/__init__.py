@@ -18,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 _STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace", 4: "HIP error"}
 
 
@@ -43,15 +43,17 @@ _SIGS = {
                             _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_permute_bwd": [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
     "moe_router_wgrad": [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
+    "moe_mx_quantize": [_vp, _int, _int, _int, _vp, _int, _vp, _vp, _int],
 }
 EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "moe_last_error",
            "moe_workspace_size", "moe_set_workspace", *_SIGS.keys(), "moe_profile_enable",
-           "moe_profile_query", "moe_kernel_name"]
+           "moe_profile_query", "moe_kernel_name", "moe_mx_workspace_size"]
 
 # kernel ids of the profiling hook (moe_kernel_id in include/moe.h)
 KERNELS = ["router_logits", "topk_hist", "expert_scan", "rank", "permute", "gemm_up_swiglu",
            "gemm_down", "combine", "combine_bwd", "route_bwd", "gemm_dgrad_down_swiglu",
-           "gemm_wgrad_down", "gemm_dgrad_up", "gemm_wgrad_up", "permute_bwd", "router_wgrad"]
+           "gemm_wgrad_down", "gemm_dgrad_up", "gemm_wgrad_up", "permute_bwd", "router_wgrad",
+           "mx_quantize"]
 
 
 def lib():
@@ -71,6 +73,7 @@ def lib():
         L.moe_last_error.restype = ctypes.c_char_p
         L.moe_workspace_size.argtypes = [_vp, _int, _int, _int, _int, _int, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_set_workspace.argtypes = [_vp, _vp, ctypes.c_size_t]
+        L.moe_mx_workspace_size.argtypes = [_vp, _int, _int, _int, _int, ctypes.POINTER(ctypes.c_size_t)]
         for name, sig in _SIGS.items():
             getattr(L, name).argtypes = [_vp, *sig]
         L.moe_profile_enable.argtypes = [_vp, _int]
@@ -108,6 +111,15 @@ class Context:
     def ensure_workspace(self, T, d, E, k, dtype):
         n = ctypes.c_size_t()
         self._check(lib().moe_workspace_size(self.handle, T, d, E, k, dtype, ctypes.byref(n)))
+        self._grow(n.value)
+
+    def ensure_mx_workspace(self, E, R, d, F):
+        n = ctypes.c_size_t()
+        self._check(lib().moe_mx_workspace_size(self.handle, E, R, d, F, ctypes.byref(n)))
+        self._grow(n.value)
+
+    def _grow(self, nbytes):
+        n = ctypes.c_size_t(nbytes)
         if n.value > self._ws_bytes:
             self._ws = torch.empty(max(n.value, 256), dtype=torch.uint8, device=f"cuda:{self.device}")
             self._ws_bytes = n.value
@@ -205,18 +217,22 @@ def moe_permute(x, row_of, xp=None):
     return xp
 
 
-def moe_grouped_ffn_fwd(xp, w_gate, w_up, w_down, offsets, out=None):
-    """Returns dict(g, u, h, yp)."""
+def moe_grouped_ffn_fwd(xp, w_gate, w_up, w_down, offsets, out=None, mxfp8=False):
+    """Returns dict(g, u, h, yp).  mxfp8=True runs the MXFP8 GEMMs on the bf16
+    tensors (quantised inside the call)."""
     _need_cuda(xp, w_gate, w_up, w_down, offsets)
     R, d = xp.shape
     E, _, F = w_gate.shape
+    dt = MOE_MXFP8 if mxfp8 else _dt(xp)
+    if mxfp8:
+        context(xp.device.index).ensure_mx_workspace(E, R, d, F)
     if out is None:
         out = dict(g=torch.empty(R, F, dtype=xp.dtype, device=xp.device),
                    u=torch.empty(R, F, dtype=xp.dtype, device=xp.device),
                    h=torch.empty(R, F, dtype=xp.dtype, device=xp.device),
                    yp=torch.empty(R, d, dtype=xp.dtype, device=xp.device))
     context(xp.device.index).call("moe_grouped_ffn_fwd", _p(xp), _p(w_gate), _p(w_up), _p(w_down),
-                                  _p(offsets), E, R, d, F, _dt(xp), _p(out["g"]), _p(out["u"]),
+                                  _p(offsets), E, R, d, F, dt, _p(out["g"]), _p(out["u"]),
                                   _p(out["h"]), _p(out["yp"]))
     return out
 
@@ -253,19 +269,22 @@ def moe_route_bwd(gates, dgates, dlogits_sel=None):
     return dlogits_sel
 
 
-def moe_grouped_ffn_bwd(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp, out=None):
+def moe_grouped_ffn_bwd(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp, out=None, mxfp8=False):
     """Returns dict(dg, du, dxp, dw_gate, dw_up, dw_down)."""
     _need_cuda(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp)
     R, d = xp.shape
     E, _, F = w_gate.shape
+    dt = MOE_MXFP8 if mxfp8 else _dt(xp)
+    if mxfp8:
+        context(xp.device.index).ensure_mx_workspace(E, R, d, F)
     if out is None:
-        dev, dt = xp.device, xp.dtype
-        out = dict(dg=torch.empty(R, F, dtype=dt, device=dev), du=torch.empty(R, F, dtype=dt, device=dev),
-                   dxp=torch.empty(R, d, dtype=dt, device=dev),
+        dev, tdt = xp.device, xp.dtype
+        out = dict(dg=torch.empty(R, F, dtype=tdt, device=dev), du=torch.empty(R, F, dtype=tdt, device=dev),
+                   dxp=torch.empty(R, d, dtype=tdt, device=dev),
                    dw_gate=torch.empty_like(w_gate), dw_up=torch.empty_like(w_up),
                    dw_down=torch.empty_like(w_down))
     context(xp.device.index).call("moe_grouped_ffn_bwd", _p(xp), _p(w_gate), _p(w_up), _p(w_down),
-                                  _p(offsets), _p(g), _p(u), _p(h), _p(dyp), E, R, d, F, _dt(xp),
+                                  _p(offsets), _p(g), _p(u), _p(h), _p(dyp), E, R, d, F, dt,
                                   _p(out["dg"]), _p(out["du"]), _p(out["dxp"]), _p(out["dw_gate"]),
                                   _p(out["dw_up"]), _p(out["dw_down"]))
     return out
@@ -295,6 +314,31 @@ def moe_router_wgrad(x, dlogits_sel, src_tk, offsets, E, dw_router=None):
     context(x.device.index).call("moe_router_wgrad", _p(x), _p(dlogits_sel), _p(src_tk), _p(offsets),
                                  T, d, E, k, _dt(x), _p(dw_router))
     return dw_router
+
+
+def mx_kpad(rows, groups):
+    """Leading dimension of a column-quantised MXFP8 operand."""
+    return (rows + 127 * groups + 127 + 127) // 128 * 128
+
+
+def moe_mx_quantize(src, axis, group_offsets=None, groups=1):
+    """MXFP8 quantisation of a bf16 [rows, cols] tensor.  axis 0 -> (codes
+    [rows, cols], scales [rows, cols/32]); axis 1 -> (codes [cols, kpad],
+    scales [cols, kpad/32]) with per-group 128-padded K positions."""
+    _need_cuda(src, group_offsets)
+    rows, cols = src.shape
+    dev = src.device
+    if axis == 0:
+        kp = 0
+        codes = torch.empty(rows, cols, dtype=torch.uint8, device=dev)
+        scales = torch.empty(rows, cols // 32, dtype=torch.uint8, device=dev)
+    else:
+        kp = mx_kpad(rows, groups)
+        codes = torch.empty(cols, kp, dtype=torch.uint8, device=dev)
+        scales = torch.empty(cols, kp // 32, dtype=torch.uint8, device=dev)
+    context(dev.index).call("moe_mx_quantize", _p(src), rows, cols, axis, _p(group_offsets), groups,
+                            _p(codes), _p(scales), kp)
+    return codes, scales
 
 
 # ------------------------------------------------------------------ the layer

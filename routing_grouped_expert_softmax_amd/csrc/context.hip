@@ -58,7 +58,8 @@ const char* moe_kernel_name(int id) {
   static const char* names[MOE_K_COUNT] = {
       "router_logits", "topk_hist", "expert_scan", "rank", "permute", "gemm_up_swiglu",
       "gemm_down", "combine", "combine_bwd", "route_bwd", "gemm_dgrad_down_swiglu",
-      "gemm_wgrad_down", "gemm_dgrad_up", "gemm_wgrad_up", "permute_bwd", "router_wgrad"};
+      "gemm_wgrad_down", "gemm_dgrad_up", "gemm_wgrad_up", "permute_bwd", "router_wgrad",
+      "mx_quantize"};
   if (id < 0 || id >= MOE_K_COUNT) return "unknown";
   return names[id];
 }

@@ -37,32 +37,14 @@
 #include <utility>
 
 #include "common.h"
+#include "gemm_common.h"
 
 using namespace moe;
+using namespace moe_gemm;
 
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
-
-enum Mode : int {
-  FWD_UP = 0,      // g,u,h = swiglu(xp Wg, xp Wu)            M-ragged, dual B, B N-contig
-  FWD_DOWN = 1,    // yp = h Wd                               M-ragged, B N-contig
-  DGRAD_DOWN = 2,  // dh = dyp Wd^T -> dg, du                  M-ragged, B K-contig
-  DGRAD_UP = 3,    // dxp = dg Wg^T + du Wu^T (two K segments) M-ragged, B K-contig
-  WGRAD_UP = 4,    // dWg, dWu = xp^T (dg | du)                K-ragged, dual B
-  WGRAD_DOWN = 5,  // dWd = h^T dyp                            K-ragged
-  ROUTER = 6       // logits = x W_r (one group, fp32 out)     M = T, B N-contig
-};
-
-template <int MODE>
-struct Traits {
-  static constexpr bool kA_KCONTIG = !(MODE == WGRAD_UP || MODE == WGRAD_DOWN);
-  static constexpr bool kB_KCONTIG = (MODE == DGRAD_DOWN || MODE == DGRAD_UP);
-  static constexpr bool kDUAL = (MODE == FWD_UP || MODE == WGRAD_UP);
-  static constexpr bool kKRAGGED = (MODE == WGRAD_UP || MODE == WGRAD_DOWN);
-  static constexpr bool kSINGLE = (MODE == ROUTER);
-};
 
 struct Params {
   const bf16_t* a0;  // A operand (segment 0)
@@ -89,10 +71,6 @@ struct Params {
   int mtiles;  // tiles along M (K-ragged)
 };
 
-constexpr int BN = 256;
-constexpr int kThreads = 256;
-
-#define LDS_AS __attribute__((address_space(3)))
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
 // ---------------------------------------------------------------- LDS layouts
@@ -110,21 +88,6 @@ __device__ __forceinline__ int kc_half(int row, int h) { return h ^ ((row >> 3) 
 // bank slot once per 32 lanes.
 __device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 2; }
 
-// 16-byte-per-lane buffer load straight into LDS (lane l writes lds + 16*l).
-// Issued as inline assembly so the compiler's wait-count pass does not treat
-// it as an LDS write that every later LDS read must wait for: the kernel
-// waits for these loads itself (s_waitcnt vmcnt) before the barrier that
-// publishes a stage.  The instruction has no register outputs.  M0 carries
-// the LDS address (one wait state between writing M0 and the load).
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, LDS_AS void* lds, int voff,
-                                      int soff) {
-  const unsigned lds_addr = (unsigned)(uintptr_t)lds;
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
-}
-
 // Tile geometry of one pipeline stage.
 template <int MODE, int BM, int BK>
 struct Tile {
@@ -140,80 +103,6 @@ struct Tile {
   // B: K-contiguous [256][64]; N-contiguous [64][256]; dual: two [64][128]
   static constexpr int B_PITCH = TR::kB_KCONTIG ? 128 : (TR::kDUAL ? 256 : 512);
 };
-
-// Work description of one block.
-struct Work {
-  int e;         // expert (group)
-  int row0;      // first A row of the tile (M-ragged) / first K row of the group
-  int rows;      // valid rows of the tile (M-ragged) / K length of the group (K-ragged)
-  int m0;        // first output M index (K-ragged)
-  int nt;        // n-tile
-};
-
-// Block-wide search of (expert, tile) for logical tile L in an M-ragged launch.
-// Returns false when L is past the real total.
-template <int BM>
-__device__ bool find_mtile(const Params& p, int* sh, Work& w) {
-  const int tid = threadIdx.x;
-  const int per = (p.E + kThreads - 1) / kThreads;  // experts per thread (<= 4)
-  int cnt[4], til[4];
-  int local = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid * per + q;
-    cnt[q] = 0;
-    til[q] = 0;
-    if (q < per && e < p.E) {
-      cnt[q] = p.offsets[e + 1] - p.offsets[e];
-      til[q] = ((cnt[q] + BM - 1) / BM) * p.ntiles;
-    }
-    local += til[q];
-  }
-  // exclusive scan of `local` over the block
-  sh[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int add = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
-  }
-  const int total = sh[kThreads - 1];
-  int run = sh[tid] - local;
-  __syncthreads();
-  // logical tile of this block: contiguous ranges per XCD
-  const int per_xcd = (total + 7) / 8;
-  const int slot = blockIdx.x >> 3;
-  const int L = (blockIdx.x & 7) * per_xcd + slot;
-  const bool live = slot < per_xcd && L < total;
-  if (tid == 0) sh[kThreads] = -1;
-  __syncthreads();
-  if (live) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = tid * per + q;
-      if (q < per && e < p.E && til[q] > 0 && L >= run && L < run + til[q]) {
-        const int mt_e = (cnt[q] + BM - 1) / BM;
-        const int local_t = L - run;
-        sh[kThreads] = e;
-        sh[kThreads + 1] = local_t % mt_e;  // m-tile
-        sh[kThreads + 2] = local_t / mt_e;  // n-tile
-      }
-      run += til[q];
-    }
-  }
-  __syncthreads();
-  const int e = sh[kThreads];
-  if (e < 0) return false;
-  const int mt = sh[kThreads + 1];
-  w.e = e;
-  w.nt = sh[kThreads + 2];
-  const int beg = p.offsets[e], end = p.offsets[e + 1];
-  w.row0 = beg + mt * BM;
-  w.rows = min(BM, end - w.row0);
-  w.m0 = 0;
-  return true;
-}
 
 template <int MODE, int BM, int S, int BK>
 __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
@@ -264,7 +153,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
     w.rows = min(BM, p.M - w.row0);
     w.m0 = 0;
   } else {
-    if (!find_mtile<BM>(p, sh, w)) return;
+    if (!find_mtile<BM>(p.E, p.offsets, p.ntiles, sh, w)) return;
   }
   const int nk = TR::kKRAGGED ? (w.rows + BK - 1) / BK : p.K / BK;
 
@@ -274,29 +163,22 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   // weight matrix read as zero (the loads below never branch).  Columns past
   // N only feed output columns that are never stored.
   const size_t esz = sizeof(bf16_t);
-  __amdgpu_buffer_rsrc_t rsa0, rsa1, rsb0, rsb1;
+  rsrc_t rsa0, rsa1, rsb0, rsb1;
   {
     const size_t abytes = (size_t)max(w.rows, 0) * p.lda * esz;
-    rsa0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a0 + (size_t)w.row0 * p.lda), (short)0,
-                                             (int)abytes, 0x00020000);
+    rsa0 = make_rsrc((void*)(p.a0 + (size_t)w.row0 * p.lda), abytes);
     rsa1 = rsa0;
     if (MODE == DGRAD_UP)
-      rsa1 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.a1 + (size_t)w.row0 * p.lda), (short)0,
-                                               (int)abytes, 0x00020000);
+      rsa1 = make_rsrc((void*)(p.a1 + (size_t)w.row0 * p.lda), abytes);
     if (TR::kKRAGGED) {
       const size_t bbytes = (size_t)max(w.rows, 0) * p.ldb * esz;
-      rsb0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b0 + (size_t)w.row0 * p.ldb), (short)0,
-                                               (int)bbytes, 0x00020000);
-      rsb1 = TR::kDUAL ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.b1 + (size_t)w.row0 * p.ldb),
-                                                           (short)0, (int)bbytes, 0x00020000)
-                       : rsb0;
+      rsb0 = make_rsrc((void*)(p.b0 + (size_t)w.row0 * p.ldb), bbytes);
+      rsb1 = TR::kDUAL ? make_rsrc((void*)(p.b1 + (size_t)w.row0 * p.ldb), bbytes) : rsb0;
     } else {
       const size_t bbytes = (size_t)(TR::kB_KCONTIG ? p.N : p.K) * p.ldb * esz;
-      rsb0 = __builtin_amdgcn_make_buffer_rsrc((void*)(p.b0 + (size_t)w.e * p.b_gstride), (short)0,
-                                               (int)bbytes, 0x00020000);
+      rsb0 = make_rsrc((void*)(p.b0 + (size_t)w.e * p.b_gstride), bbytes);
       rsb1 = (TR::kDUAL || MODE == DGRAD_UP)
-                 ? __builtin_amdgcn_make_buffer_rsrc((void*)(p.b1 + (size_t)w.e * p.b_gstride),
-                                                     (short)0, (int)bbytes, 0x00020000)
+                 ? make_rsrc((void*)(p.b1 + (size_t)w.e * p.b_gstride), bbytes)
                  : rsb0;
     }
   }
@@ -350,7 +232,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
     LDS_AS unsigned char* base = stage_ptr(st);
     // A
     {
-      __amdgpu_buffer_rsrc_t r = rsa0;
+      rsrc_t r = rsa0;
       int soff;
       if (TR::kA_KCONTIG) {
         int kk = k0;
@@ -369,7 +251,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
     // B
     {
       LDS_AS unsigned char* bbase = base + TL::A_BYTES;
-      __amdgpu_buffer_rsrc_t r = rsb0;
+      rsrc_t r = rsb0;
       int soff;
       if (TR::kB_KCONTIG) {
         int kk = k0;
@@ -531,95 +413,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   asm volatile("s_barrier" ::: "memory");
 
   // ---------------------------------------------------------------- epilogue
-  // Lane holds C[m = mbase + (lane&31)][n = nbase + 8*(r/4) + 4*(lane>>5) + r%4].
-  const int ncol4 = 4 * (lane >> 5);
-#pragma unroll
-  for (int sm = 0; sm < SM; ++sm) {
-    const int mloc = wm * TL::WM + sm * 32 + (lane & 31);  // row inside the block tile
-    bool mvalid;
-    size_t crow;
-    if (TR::kKRAGGED) {
-      mvalid = (w.m0 + mloc) < p.M;
-      crow = (size_t)(w.m0 + mloc);
-    } else {
-      mvalid = mloc < w.rows;
-      crow = (size_t)(w.row0 + mloc);
-    }
-    if (!mvalid) continue;
-    if (TR::kDUAL) {
-#pragma unroll
-      for (int sn = 0; sn < 2; ++sn) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = w.nt * 128 + wn * 64 + sn * 32 + 8 * g4 + ncol4;
-          if (col >= p.N) continue;
-          float gv[4], uv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            gv[r] = acc[sm][sn][g4 * 4 + r];
-            uv[r] = acc[sm][sn + 2][g4 * 4 + r];
-          }
-          if (MODE == FWD_UP) {
-            const size_t off = crow * p.ldc + col;
-            *reinterpret_cast<uint2*>((bf16_t*)p.c0 + off) =
-                make_uint2(pack2bf(gv[0], gv[1]), pack2bf(gv[2], gv[3]));
-            *reinterpret_cast<uint2*>((bf16_t*)p.c1 + off) =
-                make_uint2(pack2bf(uv[0], uv[1]), pack2bf(uv[2], uv[3]));
-            float hv[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) hv[r] = silu_f(gv[r]) * uv[r];
-            *reinterpret_cast<uint2*>((bf16_t*)p.c2 + off) =
-                make_uint2(pack2bf(hv[0], hv[1]), pack2bf(hv[2], hv[3]));
-          } else {  // WGRAD_UP
-            const size_t off = (size_t)w.e * p.c_gstride + crow * p.ldc + col;
-            *reinterpret_cast<uint2*>((bf16_t*)p.c0 + off) =
-                make_uint2(pack2bf(gv[0], gv[1]), pack2bf(gv[2], gv[3]));
-            *reinterpret_cast<uint2*>((bf16_t*)p.c1 + off) =
-                make_uint2(pack2bf(uv[0], uv[1]), pack2bf(uv[2], uv[3]));
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int sn = 0; sn < 4; ++sn) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = w.nt * BN + wn * 128 + sn * 32 + 8 * g4 + ncol4;
-          if (col >= p.N) continue;
-          float v[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = acc[sm][sn][g4 * 4 + r];
-          if (MODE == ROUTER) {
-            float* c = (float*)p.c0 + crow * p.ldc + col;
-            *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
-          } else if (MODE == DGRAD_DOWN) {
-            const size_t off = crow * p.ldc + col;
-            const uint2 graw = *reinterpret_cast<const uint2*>(p.aux0 + off);
-            const uint2 uraw = *reinterpret_cast<const uint2*>(p.aux1 + off);
-            const uint32_t gw[2] = {graw.x, graw.y}, uw[2] = {uraw.x, uraw.y};
-            float dg[4], du[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float g = __uint_as_float((r & 1) ? (gw[r >> 1] & 0xffff0000u) : (gw[r >> 1] << 16));
-              const float u = __uint_as_float((r & 1) ? (uw[r >> 1] & 0xffff0000u) : (uw[r >> 1] << 16));
-              const float s = sigmoid_f(g);
-              dg[r] = v[r] * u * s * (1.0f + g * (1.0f - s));
-              du[r] = v[r] * g * s;
-            }
-            *reinterpret_cast<uint2*>((bf16_t*)p.c0 + off) =
-                make_uint2(pack2bf(dg[0], dg[1]), pack2bf(dg[2], dg[3]));
-            *reinterpret_cast<uint2*>((bf16_t*)p.c1 + off) =
-                make_uint2(pack2bf(du[0], du[1]), pack2bf(du[2], du[3]));
-          } else {
-            size_t off = crow * p.ldc + col;
-            if (TR::kKRAGGED) off += (size_t)w.e * p.c_gstride;
-            *reinterpret_cast<uint2*>((bf16_t*)p.c0 + off) =
-                make_uint2(pack2bf(v[0], v[1]), pack2bf(v[2], v[3]));
-          }
-        }
-      }
-    }
-  }
+  EpiArgs ea{p.c0, p.c1, p.c2, p.ldc, p.c_gstride, p.aux0, p.aux1, p.N, p.M};
+  store_tile<MODE, BM, SM, false>(acc, ea, w, lane, wm, wn);
 #endif
 }
 
@@ -686,17 +481,46 @@ moe_status moe_internal_ffn_bwd_f32(moe_ctx* ctx, const float* xp, const float* 
                                     const float* dyp, int E, int R, int d, int F, float* dg,
                                     float* du, float* dxp, float* dwg, float* dwu, float* dwd);
 
+// MXFP8 path (gemm_mx.hip)
+size_t moe_internal_mx_fwd_bytes(int E, int R, int d, int F);
+size_t moe_internal_mx_bwd_bytes(int E, int R, int d, int F);
+moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t* wg,
+                                   const bf16_t* wu, const bf16_t* wd, const int32_t* offsets,
+                                   int E, int R, int d, int F, bf16_t* g, bf16_t* u, bf16_t* h,
+                                   bf16_t* yp);
+moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t* wg,
+                                   const bf16_t* wu, const bf16_t* wd, const int32_t* offsets,
+                                   const bf16_t* g, const bf16_t* u, const bf16_t* h,
+                                   const bf16_t* dyp, int E, int R, int d, int F, bf16_t* dg,
+                                   bf16_t* du, bf16_t* dxp, bf16_t* dwg, bf16_t* dwu,
+                                   bf16_t* dwd);
+
 static moe_status ffn_validate(moe_ctx* ctx, int E, int R, int d, int F, moe_dtype dtype,
                                const char* what) {
-  MOE_REQUIRE_DTYPE(ctx, dtype);
+  MOE_REQUIRE(ctx, dtype == MOE_F32 || dtype == MOE_BF16 || dtype == MOE_MXFP8,
+              "%s: unsupported dtype %d", what, (int)dtype);
   MOE_REQUIRE(ctx, E >= 1 && E <= 1024 && R >= 0 && d >= 8 && F >= 8 && d % 8 == 0 && F % 8 == 0,
               "%s: bad shape E=%d R=%d d=%d F=%d", what, E, R, d, F);
   if (dtype == MOE_BF16 && (d % 64 != 0 || F % 64 != 0))
     return fail(ctx, MOE_ERR_UNSUPPORTED, "%s: bf16 path needs d and F multiples of 64", what);
+  if (dtype == MOE_MXFP8 && (d % 128 != 0 || F % 128 != 0))
+    return fail(ctx, MOE_ERR_UNSUPPORTED, "%s: MXFP8 path needs d and F multiples of 128", what);
+  MOE_REQUIRE(ctx, (int64_t)R * (d > F ? d : F) * 2 < ((int64_t)1 << 31),
+              "%s: R * max(d, F) too large for 32-bit buffer offsets", what);
   return MOE_OK;
 }
 
 extern "C" {
+
+moe_status moe_mx_workspace_size(moe_ctx* ctx, int E, int R, int d, int F, size_t* bytes) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, bytes != nullptr, "bytes is null");
+  moe_status st = ffn_validate(ctx, E, R, d, F, MOE_MXFP8, "moe_mx_workspace_size");
+  if (st != MOE_OK) return st;
+  const size_t a = moe_internal_mx_fwd_bytes(E, R, d, F), b = moe_internal_mx_bwd_bytes(E, R, d, F);
+  *bytes = a > b ? a : b;
+  return MOE_OK;
+}
 
 moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
                                const void* w_up, const void* w_down, const int32_t* offsets,
@@ -715,6 +539,10 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
   MOE_REQUIRE_PTR(ctx, h);
   MOE_REQUIRE_PTR(ctx, yp);
   if (R == 0) return MOE_OK;
+  if (dtype == MOE_MXFP8)
+    return moe_internal_ffn_fwd_mx(ctx, (const bf16_t*)xp, (const bf16_t*)w_gate,
+                                   (const bf16_t*)w_up, (const bf16_t*)w_down, offsets, E, R, d, F,
+                                   (bf16_t*)g, (bf16_t*)u, (bf16_t*)h, (bf16_t*)yp);
   if (dtype == MOE_F32)
     return moe_internal_ffn_fwd_f32(ctx, (const float*)xp, (const float*)w_gate,
                                     (const float*)w_up, (const float*)w_down, offsets, E, R, d, F,
@@ -791,6 +619,13 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
   MOE_REQUIRE_PTR(ctx, dw_gate);
   MOE_REQUIRE_PTR(ctx, dw_up);
   MOE_REQUIRE_PTR(ctx, dw_down);
+  if (dtype == MOE_MXFP8)
+    return moe_internal_ffn_bwd_mx(ctx, (const bf16_t*)xp, (const bf16_t*)w_gate,
+                                   (const bf16_t*)w_up, (const bf16_t*)w_down, offsets,
+                                   (const bf16_t*)g, (const bf16_t*)u, (const bf16_t*)h,
+                                   (const bf16_t*)dyp, E, R, d, F, (bf16_t*)dg, (bf16_t*)du,
+                                   (bf16_t*)dxp, (bf16_t*)dw_gate, (bf16_t*)dw_up,
+                                   (bf16_t*)dw_down);
   if (dtype == MOE_F32)
     return moe_internal_ffn_bwd_f32(ctx, (const float*)xp, (const float*)w_gate,
                                     (const float*)w_up, (const float*)w_down, offsets,

@@ -1,0 +1,570 @@
+// gemm_mx.hip — device-scheduled grouped GEMM on MXFP8 operands (E4M3 codes
+// with one e8m0 scale per 32 elements along K) for the SwiGLU experts, on the
+// gfx950 scaled matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4), fp32
+// accumulation, bf16 outputs.  MXFP8 for the expert FFN follows the first
+// page, section 三 (MXFP8 for selected operations; the gain comes from the
+// FFN and expert data movement).
+//
+// Every operand arrives K-contiguous from the quantiser (weights are
+// quantised along their GEMM's K and stored transposed where needed), so one
+// tile layout serves all modes: 8-row groups of 1 KiB, [16-byte chunk][row %
+// 8][16 bytes], the chunk index XOR-ed with bit 3 of the row (conflict-free 16
+// lane passes).  A tile row holds 128 K values (4 scale blocks); its four
+// scale bytes arrive with it as one 32-bit LDS word per row.
+//
+// Operand layout of the scaled MFMA (checked on the device): lane l supplies
+// row (l & 31), and its bytes 0-15 / 16-31 hold K = 16*(l>>5) + 0..15 and
+// 32 + 16*(l>>5) + 0..15 of the 64-wide step; the scale of K block 0 comes
+// from the lanes with l < 32, of block 1 from the lanes with l >= 32.  So a
+// lane reads chunks (4kk + half) and (4kk + 2 + half) and scale byte
+// (2kk + half) of its row.
+//
+// Scheduling, stages and the epilogue are the bf16 kernel's (gemm_common.h).
+// Wgrad operands are the column-quantised per-expert token blocks: expert e's
+// K range starts at the exclusive scan of roundup(n_e, 128).
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "common.h"
+#include "gemm_common.h"
+#include "mx.h"
+
+using namespace moe;
+using namespace moe_gemm;
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+struct MxParams {
+  const uint8_t* a0;   // A codes (segment 0)
+  const uint8_t* a1;   // A codes, second K segment (gate/up dgrad)
+  const uint8_t* sa0;  // A scales
+  const uint8_t* sa1;
+  int lda;              // bytes per A row
+  const uint8_t* b0;   // B codes (or first of the pair / first K segment)
+  const uint8_t* b1;
+  const uint8_t* sb0;
+  const uint8_t* sb1;
+  int ldb;              // bytes per B row
+  long long b_row_e;    // per-expert row offset of B (row-quantised weights)
+  long long b_k_e;      // per-expert K offset of B (column-quantised weights)
+  void* c0;
+  void* c1;
+  void* c2;
+  int ldc;
+  long long c_gstride;
+  const bf16_t* aux0;
+  const bf16_t* aux1;
+  const int32_t* offsets;
+  int E;
+  int M;
+  int N;
+  int K;
+  int kseg;
+  int ntiles;
+  int mtiles;
+};
+
+constexpr int BK = 128;  // K bytes (= fp8 values) per stage
+
+template <int BM>
+struct MxTile {
+  static constexpr int WM = BM / 2;
+  static constexpr int SM = WM / 32;
+  static constexpr int A_BYTES = BM * BK;
+  static constexpr int B_BYTES = BN * BK;
+  static constexpr int AS_BYTES = BM * 4;  // one 32-bit scale word per row
+  static constexpr int BS_BYTES = BN * 4;
+  static constexpr int STAGE = A_BYTES + B_BYTES + AS_BYTES + BS_BYTES;
+  static constexpr int A_INST = A_BYTES / 1024 / 4;  // 16-byte loads per wave
+  static constexpr int B_INST = B_BYTES / 1024 / 4;
+  static constexpr int AS_INST = AS_BYTES / 256 / 4;  // 4-byte loads per wave
+  static constexpr int BS_INST = BS_BYTES / 256 / 4;
+};
+
+template <int MODE, int BM, int S>
+__global__ void __launch_bounds__(kThreads, 1) grouped_gemm_mx_kernel(MxParams p) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
+  using TR = Traits<MODE>;
+  using TL = MxTile<BM>;
+  constexpr int SM = TL::SM;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds1[TL::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds2[S > 2 ? TL::STAGE : 16];
+  __shared__ int sh[kThreads + 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+
+  // ---------------------------------------------------------------- work
+  Work w;
+  int kbase = 0;  // K-ragged: first K byte of the expert in the padded layout
+  if (TR::kKRAGGED) {
+    const int total = p.E * p.ntiles * p.mtiles;
+    const int per_xcd = (total + 7) / 8;
+    const int slot = blockIdx.x >> 3;
+    const int L = (blockIdx.x & 7) * per_xcd + slot;
+    if (slot >= per_xcd || L >= total) return;
+    const int per_e = p.ntiles * p.mtiles;
+    w.e = L / per_e;
+    const int r = L % per_e;
+    w.nt = r / p.mtiles;
+    w.m0 = (r % p.mtiles) * BM;
+    // padded K base: exclusive scan of roundup(n_e, 128) over the experts
+    int local = 0;
+    for (int e = tid; e < w.e; e += kThreads)
+      local += (p.offsets[e + 1] - p.offsets[e] + 127) / 128 * 128;
+    sh[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int add = tid >= off ? sh[tid - off] : 0;
+      __syncthreads();
+      sh[tid] += add;
+      __syncthreads();
+    }
+    kbase = __builtin_amdgcn_readfirstlane(sh[kThreads - 1]);
+    const int n = p.offsets[w.e + 1] - p.offsets[w.e];
+    w.row0 = kbase;
+    w.rows = (n + 127) / 128 * 128;  // padded K of the expert (padding is zero)
+  } else {
+    if (!find_mtile<BM>(p.E, p.offsets, p.ntiles, sh, w)) return;
+  }
+  const int nk = TR::kKRAGGED ? w.rows / BK : p.K / BK;
+
+  // ---------------------------------------------------------------- sources
+  rsrc_t ra0, ra1, rsa0, rsa1, rb0, rb1, rsb0, rsb1;
+  if (TR::kKRAGGED) {
+    // codes [M][lda] and [N][ldb] from K byte kbase on; rows m0.. of A
+    ra0 = make_rsrc(p.a0 + kbase, (unsigned long long)p.M * p.lda - kbase);
+    rsa0 = make_rsrc(p.sa0 + kbase / 32, (unsigned long long)p.M * (p.lda / 32) - kbase / 32);
+    rb0 = make_rsrc(p.b0 + kbase, (unsigned long long)p.N * p.ldb - kbase);
+    rsb0 = make_rsrc(p.sb0 + kbase / 32, (unsigned long long)p.N * (p.ldb / 32) - kbase / 32);
+    rb1 = TR::kDUAL ? make_rsrc(p.b1 + kbase, (unsigned long long)p.N * p.ldb - kbase) : rb0;
+    rsb1 = TR::kDUAL
+               ? make_rsrc(p.sb1 + kbase / 32, (unsigned long long)p.N * (p.ldb / 32) - kbase / 32)
+               : rsb0;
+    ra1 = ra0;
+    rsa1 = rsa0;
+  } else {
+    // A: the tile's rows; B: the expert's weights (row and/or K offset)
+    const unsigned long long ab = (unsigned long long)w.rows * p.lda;
+    ra0 = make_rsrc(p.a0 + (size_t)w.row0 * p.lda, ab);
+    rsa0 = make_rsrc(p.sa0 + (size_t)w.row0 * (p.lda / 32), ab / 32);
+    ra1 = ra0;
+    rsa1 = rsa0;
+    if (MODE == DGRAD_UP) {
+      ra1 = make_rsrc(p.a1 + (size_t)w.row0 * p.lda, ab);
+      rsa1 = make_rsrc(p.sa1 + (size_t)w.row0 * (p.lda / 32), ab / 32);
+    }
+    const size_t bo = (size_t)w.e * p.b_row_e * p.ldb + (size_t)w.e * p.b_k_e;
+    const unsigned long long bb = (unsigned long long)p.N * p.ldb - (size_t)w.e * p.b_k_e;
+    rb0 = make_rsrc(p.b0 + bo, bb);
+    rsb0 = make_rsrc(p.sb0 + bo / 32, bb / 32);
+    const bool two = TR::kDUAL || MODE == DGRAD_UP;
+    rb1 = two ? make_rsrc(p.b1 + bo, bb) : rb0;
+    rsb1 = two ? make_rsrc(p.sb1 + bo / 32, bb / 32) : rsb0;
+  }
+
+  // Per-lane offsets of this wave's direct loads.  Code tiles: instruction q
+  // fills rows 8q..8q+7; lane = physical chunk * 8 + row % 8, and the source
+  // chunk is the physical one XOR bit 3 of the row.  Scale tiles: 64 rows per
+  // instruction, one 32-bit word (4 scale blocks) per lane.
+  const int lda_s = p.lda / 32, ldb_s = p.ldb / 32;
+  int aoff[TL::A_INST], boff[TL::B_INST], asoff[TL::AS_INST], bsoff[TL::BS_INST];
+#pragma unroll
+  for (int j = 0; j < TL::A_INST; ++j) {
+    const int q = wv * TL::A_INST + j;
+    const int row = q * 8 + (lane & 7), c = (lane >> 3) ^ ((row >> 3) & 1);
+    aoff[j] = (TR::kKRAGGED ? (w.m0 + row) : row) * p.lda + c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < TL::AS_INST; ++j) {
+    const int row = (wv * TL::AS_INST + j) * 64 + lane;
+    asoff[j] = (TR::kKRAGGED ? (w.m0 + row) : row) * lda_s;
+  }
+#pragma unroll
+  for (int j = 0; j < TL::B_INST; ++j) {
+    const int q = wv * TL::B_INST + j;
+    const int row = q * 8 + (lane & 7), c = (lane >> 3) ^ ((row >> 3) & 1);
+    // dual: rows 0..127 of the tile from matrix 0, 128..255 from matrix 1
+    const int n = TR::kDUAL ? w.nt * 128 + (row & 127) : w.nt * BN + row;
+    boff[j] = n * p.ldb + c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < TL::BS_INST; ++j) {
+    const int row = (wv * TL::BS_INST + j) * 64 + lane;
+    const int n = TR::kDUAL ? w.nt * 128 + (row & 127) : w.nt * BN + row;
+    bsoff[j] = n * ldb_s;
+  }
+
+  auto stage_ptr = [&](auto st) -> LDS_AS unsigned char* {
+    constexpr int ST = decltype(st)::value;
+    if constexpr (ST == 0) return (LDS_AS unsigned char*)lds0;
+    else if constexpr (ST == 1) return (LDS_AS unsigned char*)lds1;
+    else return (LDS_AS unsigned char*)lds2;
+  };
+  auto issue = [&](int kt, auto st) {
+    const int k0 = kt * BK;
+    LDS_AS unsigned char* base = stage_ptr(st);
+    const bool seg1 = (MODE == DGRAD_UP) && k0 >= p.kseg;
+    const int kk = seg1 ? k0 - p.kseg : k0;
+    const rsrc_t ra = seg1 ? ra1 : ra0, rsa = seg1 ? rsa1 : rsa0;
+    rsrc_t rb = seg1 ? rb1 : rb0, rsb = seg1 ? rsb1 : rsb0;
+    if (TR::kDUAL && wv >= 2) {  // waves 2,3 fill the second matrix's rows
+      rb = rb1;
+      rsb = rsb1;
+    }
+#pragma unroll
+    for (int j = 0; j < TL::A_INST; ++j)
+      dma16(ra, (LDS_AS void*)(base + (wv * TL::A_INST + j) * 1024), aoff[j], kk);
+#pragma unroll
+    for (int j = 0; j < TL::B_INST; ++j)
+      dma16(rb, (LDS_AS void*)(base + TL::A_BYTES + (wv * TL::B_INST + j) * 1024), boff[j], kk);
+    // dual scale rows: waves 0,1 rows 0..127 (matrix 0), 2,3 rows 128..255
+#pragma unroll
+    for (int j = 0; j < TL::AS_INST; ++j)
+      dma4(rsa, (LDS_AS void*)(base + TL::A_BYTES + TL::B_BYTES + (wv * TL::AS_INST + j) * 256),
+           asoff[j], kk / 32);
+#pragma unroll
+    for (int j = 0; j < TL::BS_INST; ++j)
+      dma4(rsb,
+           (LDS_AS void*)(base + TL::A_BYTES + TL::B_BYTES + TL::AS_BYTES +
+                          (wv * TL::BS_INST + j) * 256),
+           bsoff[j], kk / 32);
+  };
+
+  // ---------------------------------------------------------------- fragments
+  // Code fragment of 32 rows (row0 + lane & 31) for 64-wide step kk: chunks
+  // 4kk + half and 4kk + 2 + half, each XOR-ed with bit 3 of the row.
+  const int h = lane >> 5;
+  const int cl = ((lane & 31) >> 3) * 1024 + ((h ^ (((lane & 31) >> 3) & 1)) * 128) + (lane & 7) * 16;
+  auto frag = [&](const LDS_AS unsigned char* t, int row0, int kk) -> i32x8 {
+    const LDS_AS unsigned char* a = t + (row0 >> 3) * 1024 + kk * 512 + cl;
+    const uint4 lo = *(const LDS_AS uint4*)(a);
+    const uint4 hi = *(const LDS_AS uint4*)(a + 256);
+    i32x8 r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+  };
+  // Scale word of the lane's row, shifted so byte 2kk is block 2kk + half.
+  auto sword = [&](const LDS_AS unsigned char* s, int row0) -> int {
+    const unsigned v = *(const LDS_AS unsigned*)(s + (row0 + (lane & 31)) * 4);
+    return (int)(v >> (8 * h));
+  };
+
+  f32x16 acc[SM][4];
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](auto st) {
+    const LDS_AS unsigned char* As = stage_ptr(st);
+    const LDS_AS unsigned char* Bs = As + TL::A_BYTES;
+    const LDS_AS unsigned char* Ass = Bs + TL::B_BYTES;
+    const LDS_AS unsigned char* Bss = Ass + TL::AS_BYTES;
+    int sx[4], sy[SM];
+#pragma unroll
+    for (int sn = 0; sn < 4; ++sn) {
+      const int row0 = TR::kDUAL ? (sn >> 1) * 128 + wn * 64 + (sn & 1) * 32 : wn * 128 + sn * 32;
+      sx[sn] = sword(Bss, row0);
+    }
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm) sy[sm] = sword(Ass, wm * TL::WM + sm * 32);
+    // one 64-wide step; the opsel byte index must be a compile-time constant
+    auto mstep = [&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      i32x8 xb[4], ya[SM];
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn) {
+        const int row0 = TR::kDUAL ? (sn >> 1) * 128 + wn * 64 + (sn & 1) * 32 : wn * 128 + sn * 32;
+        xb[sn] = frag(Bs, row0, kk);
+      }
+#pragma unroll
+      for (int sm = 0; sm < SM; ++sm) ya[sm] = frag(As, wm * TL::WM + sm * 32, kk);
+#pragma unroll
+      for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+        for (int sn = 0; sn < 4; ++sn)
+          acc[sm][sn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              xb[sn], ya[sm], acc[sm][sn], 0, 0, 2 * kk, sx[sn], 2 * kk, sy[sm]);
+    };
+    mstep(std::integral_constant<int, 0>{});
+    mstep(std::integral_constant<int, 1>{});
+  };
+
+  // ---------------------------------------------------------------- main loop
+  constexpr int LPS = TL::A_INST + TL::B_INST + TL::AS_INST + TL::BS_INST;
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if (0 < nk) issue(0, I0{});
+  if (S > 2 && 1 < nk) issue(1, I1{});
+  auto step = [&](int kt, auto cur, auto nxt) {
+    const int after = min(S - 2, nk - 1 - kt);
+    if (S >= 3 && after >= 1)
+      __builtin_amdgcn_s_waitcnt((LPS & 15) | (7 << 4) | (15 << 8) | ((LPS >> 4) << 14));
+    else
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    if (kt + S - 1 < nk) issue(kt + S - 1, nxt);
+    compute(cur);
+  };
+  int kt = 0;
+  if constexpr (S == 2) {
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, I0{}, I1{});
+      step(kt + 1, I1{}, I0{});
+    }
+    if (kt < nk) step(kt, I0{}, I1{});
+  } else {
+    for (; kt + 2 < nk; kt += 3) {
+      step(kt, I0{}, I2{});
+      step(kt + 1, I1{}, I0{});
+      step(kt + 2, I2{}, I1{});
+    }
+    if (kt < nk) step(kt, I0{}, I2{});
+    if (kt + 1 < nk) step(kt + 1, I1{}, I0{});
+  }
+  asm volatile("s_barrier" ::: "memory");
+
+  EpiArgs ea{p.c0, p.c1, p.c2, p.ldc, p.c_gstride, p.aux0, p.aux1, p.N, p.M};
+  Work wo = w;
+  if (TR::kKRAGGED) wo.row0 = 0;  // outputs of wgrad are indexed by m0 + row
+  store_tile<MODE, BM, SM, true>(acc, ea, wo, lane, wm, wn);
+#endif
+}
+
+template <int MODE, int BM, int S>
+hipError_t launch_mx(const MxParams& p, int blocks, hipStream_t s) {
+  blocks = (blocks + 7) / 8 * 8;
+  grouped_gemm_mx_kernel<MODE, BM, S><<<blocks, kThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- host side
+using namespace moe_host;
+
+// Layout of the MXFP8 workspace of one forward or backward call: byte ranges
+// (all 256-byte aligned) for every quantised operand.
+namespace {
+struct MxLayout {
+  size_t total = 0;
+  size_t put(size_t bytes) {
+    const size_t at = total;
+    total += (bytes + 255) & ~(size_t)255;
+    return at;
+  }
+};
+int kpad_ld_for(int R, int E) { return (int)((mx_kpad_bound(R, E) + 127) / 128 * 128); }
+}  // namespace
+
+size_t moe_internal_mx_fwd_bytes(int E, int R, int d, int F) {
+  MxLayout L;
+  L.put((size_t)R * d);            // xp codes
+  L.put((size_t)R * d / 32);       // xp scales
+  L.put((size_t)E * d * F * 2);    // wg, wu codes (K = d, transposed)
+  L.put((size_t)E * d * F * 2 / 32);
+  L.put((size_t)R * F);            // h codes
+  L.put((size_t)R * F / 32);
+  L.put((size_t)E * F * d);        // wd codes (K = F, transposed)
+  L.put((size_t)E * F * d / 32);
+  return L.total;
+}
+
+size_t moe_internal_mx_bwd_bytes(int E, int R, int d, int F) {
+  const size_t kp = (size_t)kpad_ld_for(R, E);
+  MxLayout L;
+  L.put((size_t)R * d);            // dyp codes (rowwise along d)
+  L.put((size_t)R * d / 32);
+  L.put((size_t)E * F * d);        // wd rowwise along d
+  L.put((size_t)E * F * d / 32);
+  L.put((size_t)R * F * 2);        // dg, du rowwise along F
+  L.put((size_t)R * F * 2 / 32);
+  L.put((size_t)E * d * F * 2);    // wg, wu rowwise along F
+  L.put((size_t)E * d * F * 2 / 32);
+  L.put((size_t)d * kp);           // xp^T per-expert column blocks
+  L.put((size_t)d * kp / 32);
+  L.put((size_t)F * kp * 3);       // dg^T, du^T, h^T
+  L.put((size_t)F * kp * 3 / 32);
+  L.put((size_t)d * kp);           // dyp^T
+  L.put((size_t)d * kp / 32);
+  return L.total;
+}
+
+moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t* wg,
+                                   const bf16_t* wu, const bf16_t* wd, const int32_t* offsets,
+                                   int E, int R, int d, int F, bf16_t* g, bf16_t* u, bf16_t* h,
+                                   bf16_t* yp) {
+  const size_t need = moe_internal_mx_fwd_bytes(E, R, d, F);
+  if (ctx->ws == nullptr || ctx->ws_bytes < need)
+    return fail(ctx, MOE_ERR_WORKSPACE, "MXFP8 forward: workspace %zu bytes < %zu needed",
+                ctx->ws_bytes, need);
+  uint8_t* ws = (uint8_t*)ctx->ws;
+  MxLayout L;
+  uint8_t* xq = ws + L.put((size_t)R * d);
+  uint8_t* xs = ws + L.put((size_t)R * d / 32);
+  uint8_t* wgq = ws + L.put((size_t)E * d * F * 2);
+  uint8_t* wgs = ws + L.put((size_t)E * d * F * 2 / 32);
+  uint8_t* wuq = wgq + (size_t)E * d * F;
+  uint8_t* wus = wgs + (size_t)E * d * F / 32;
+  uint8_t* hq = ws + L.put((size_t)R * F);
+  uint8_t* hs = ws + L.put((size_t)R * F / 32);
+  uint8_t* wdq = ws + L.put((size_t)E * F * d);
+  uint8_t* wds = ws + L.put((size_t)E * F * d / 32);
+  hipStream_t s = ctx->stream;
+  hipError_t e;
+  {
+    moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
+    // activations along d; weights along d per column, transposed to [F][E*d]
+    e = mx_quantize_rows(xp, R, d, xq, xs, s);
+    if (e == hipSuccess) e = mx_quantize_cols(wg, E * d, F, nullptr, d, E, wgq, wgs, E * d, s);
+    if (e == hipSuccess) e = mx_quantize_cols(wu, E * d, F, nullptr, d, E, wuq, wus, E * d, s);
+    if (e == hipSuccess) e = mx_quantize_cols(wd, E * F, d, nullptr, F, E, wdq, wds, E * F, s);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise: %s", hipGetErrorString(e));
+  }
+  {
+    MxParams p{};
+    p.a0 = xq; p.sa0 = xs; p.lda = d;
+    p.b0 = wgq; p.sb0 = wgs; p.b1 = wuq; p.sb1 = wus; p.ldb = E * d; p.b_k_e = d;
+    p.c0 = g; p.c1 = u; p.c2 = h; p.ldc = F;
+    p.offsets = offsets; p.E = E; p.N = F; p.K = d; p.kseg = d;
+    p.ntiles = (F + 127) / 128;
+    moe_prof_scope ps(ctx, MOE_K_GEMM_UP);
+    e = launch_mx<FWD_UP, 256, 2>(p, (R / 256 + E) * p.ntiles, s);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX gate/up: %s", hipGetErrorString(e));
+  }
+  {
+    moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
+    e = mx_quantize_rows(h, R, F, hq, hs, s);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise h: %s", hipGetErrorString(e));
+  }
+  {
+    MxParams p{};
+    p.a0 = hq; p.sa0 = hs; p.lda = F;
+    p.b0 = wdq; p.sb0 = wds; p.ldb = E * F; p.b_k_e = F;
+    p.c0 = yp; p.ldc = d;
+    p.offsets = offsets; p.E = E; p.N = d; p.K = F; p.kseg = F;
+    p.ntiles = (d + BN - 1) / BN;
+    moe_prof_scope ps(ctx, MOE_K_GEMM_DOWN);
+    e = launch_mx<FWD_DOWN, 256, 2>(p, (R / 256 + E) * p.ntiles, s);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX down: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t* wg,
+                                   const bf16_t* wu, const bf16_t* wd, const int32_t* offsets,
+                                   const bf16_t* g, const bf16_t* u, const bf16_t* h,
+                                   const bf16_t* dyp, int E, int R, int d, int F, bf16_t* dg,
+                                   bf16_t* du, bf16_t* dxp, bf16_t* dwg, bf16_t* dwu,
+                                   bf16_t* dwd) {
+  const size_t need = moe_internal_mx_bwd_bytes(E, R, d, F);
+  if (ctx->ws == nullptr || ctx->ws_bytes < need)
+    return fail(ctx, MOE_ERR_WORKSPACE, "MXFP8 backward: workspace %zu bytes < %zu needed",
+                ctx->ws_bytes, need);
+  const int kp = kpad_ld_for(R, E);
+  uint8_t* ws = (uint8_t*)ctx->ws;
+  MxLayout L;
+  uint8_t* dyq = ws + L.put((size_t)R * d);
+  uint8_t* dys = ws + L.put((size_t)R * d / 32);
+  uint8_t* wdq = ws + L.put((size_t)E * F * d);
+  uint8_t* wds = ws + L.put((size_t)E * F * d / 32);
+  uint8_t* dgq = ws + L.put((size_t)R * F * 2);
+  uint8_t* dgs = ws + L.put((size_t)R * F * 2 / 32);
+  uint8_t* duq = dgq + (size_t)R * F;
+  uint8_t* dus = dgs + (size_t)R * F / 32;
+  uint8_t* wgq = ws + L.put((size_t)E * d * F * 2);
+  uint8_t* wgs = ws + L.put((size_t)E * d * F * 2 / 32);
+  uint8_t* wuq = wgq + (size_t)E * d * F;
+  uint8_t* wus = wgs + (size_t)E * d * F / 32;
+  uint8_t* xtq = ws + L.put((size_t)d * kp);
+  uint8_t* xts = ws + L.put((size_t)d * kp / 32);
+  uint8_t* gtq = ws + L.put((size_t)F * kp * 3);
+  uint8_t* gts = ws + L.put((size_t)F * kp * 3 / 32);
+  uint8_t* utq = gtq + (size_t)F * kp;
+  uint8_t* uts = gts + (size_t)F * kp / 32;
+  uint8_t* htq = utq + (size_t)F * kp;
+  uint8_t* hts = uts + (size_t)F * kp / 32;
+  uint8_t* ytq = ws + L.put((size_t)d * kp);
+  uint8_t* yts = ws + L.put((size_t)d * kp / 32);
+  hipStream_t s = ctx->stream;
+  hipError_t e;
+  {
+    moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
+    e = mx_quantize_rows(dyp, R, d, dyq, dys, s);
+    if (e == hipSuccess) e = mx_quantize_rows(wd, E * F, d, wdq, wds, s);
+    if (e == hipSuccess) e = mx_quantize_rows(wg, E * d, F, wgq, wgs, s);
+    if (e == hipSuccess) e = mx_quantize_rows(wu, E * d, F, wuq, wus, s);
+    if (e == hipSuccess) e = mx_quantize_cols(xp, R, d, offsets, 0, E, xtq, xts, kp, s);
+    if (e == hipSuccess) e = mx_quantize_cols(h, R, F, offsets, 0, E, htq, hts, kp, s);
+    if (e == hipSuccess) e = mx_quantize_cols(dyp, R, d, offsets, 0, E, ytq, yts, kp, s);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise: %s", hipGetErrorString(e));
+  }
+  if (R > 0) {
+    MxParams p{};
+    p.a0 = dyq; p.sa0 = dys; p.lda = d;
+    p.b0 = wdq; p.sb0 = wds; p.ldb = d; p.b_row_e = F;
+    p.c0 = dg; p.c1 = du; p.ldc = F; p.aux0 = g; p.aux1 = u;
+    p.offsets = offsets; p.E = E; p.N = F; p.K = d; p.kseg = d;
+    p.ntiles = (F + BN - 1) / BN;
+    moe_prof_scope ps(ctx, MOE_K_GEMM_DGRAD_DOWN);
+    e = launch_mx<DGRAD_DOWN, 256, 2>(p, (R / 256 + E) * p.ntiles, s);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX down dgrad: %s", hipGetErrorString(e));
+  }
+  {
+    MxParams p{};
+    p.a0 = htq; p.sa0 = hts; p.lda = kp;
+    p.b0 = ytq; p.sb0 = yts; p.ldb = kp;
+    p.c0 = dwd; p.ldc = d; p.c_gstride = (long long)F * d;
+    p.offsets = offsets; p.E = E; p.M = F; p.N = d;
+    p.ntiles = (d + BN - 1) / BN;
+    p.mtiles = (F + 255) / 256;
+    moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
+    e = launch_mx<WGRAD_DOWN, 256, 2>(p, E * p.ntiles * p.mtiles, s);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX down wgrad: %s", hipGetErrorString(e));
+  }
+  {
+    moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
+    e = mx_quantize_rows(dg, R, F, dgq, dgs, s);
+    if (e == hipSuccess) e = mx_quantize_rows(du, R, F, duq, dus, s);
+    if (e == hipSuccess) e = mx_quantize_cols(dg, R, F, offsets, 0, E, gtq, gts, kp, s);
+    if (e == hipSuccess) e = mx_quantize_cols(du, R, F, offsets, 0, E, utq, uts, kp, s);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise dg/du: %s", hipGetErrorString(e));
+  }
+  if (R > 0) {
+    MxParams p{};
+    p.a0 = dgq; p.sa0 = dgs; p.a1 = duq; p.sa1 = dus; p.lda = F;
+    p.b0 = wgq; p.sb0 = wgs; p.b1 = wuq; p.sb1 = wus; p.ldb = F; p.b_row_e = d;
+    p.c0 = dxp; p.ldc = d;
+    p.offsets = offsets; p.E = E; p.N = d; p.K = 2 * F; p.kseg = F;
+    p.ntiles = (d + BN - 1) / BN;
+    moe_prof_scope ps(ctx, MOE_K_GEMM_DGRAD_UP);
+    e = launch_mx<DGRAD_UP, 256, 2>(p, (R / 256 + E) * p.ntiles, s);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX gate/up dgrad: %s", hipGetErrorString(e));
+  }
+  {
+    MxParams p{};
+    p.a0 = xtq; p.sa0 = xts; p.lda = kp;
+    p.b0 = gtq; p.sb0 = gts; p.b1 = utq; p.sb1 = uts; p.ldb = kp;
+    p.c0 = dwg; p.c1 = dwu; p.ldc = F; p.c_gstride = (long long)d * F;
+    p.offsets = offsets; p.E = E; p.M = d; p.N = F;
+    p.ntiles = (F + 127) / 128;
+    p.mtiles = (d + 255) / 256;
+    moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
+    e = launch_mx<WGRAD_UP, 256, 2>(p, E * p.ntiles * p.mtiles, s);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX gate/up wgrad: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}

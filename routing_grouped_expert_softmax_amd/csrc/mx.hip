@@ -1,0 +1,270 @@
+// mx.hip — MXFP8 quantisation: E4M3 elements in 32-element blocks sharing an
+// e8m0 (power-of-two) scale, for the expert GEMMs ([P1] 三, MXFP8).
+//
+// Scale rule (OCP MX): s = floor(log2(amax)) - 8, clamped to [-127, 127]
+// (8 is the exponent of E4M3's largest normal 448 = 1.75 * 2^8); the scale
+// byte is s + 127, so a zero block gets byte 0.  Elements are v / 2^s rounded
+// to the nearest E4M3 value (ties to even), saturating at +-448, sign kept.
+//
+// Two layouts, both K-contiguous for the GEMM that consumes them:
+//  * rowwise:  blocks along each row  -> codes [rows][cols], scales [rows][cols/32]
+//  * columns:  blocks of 32 consecutive rows of one column, restarting at each
+//    group of rows (an expert's tokens, or one expert's weight matrix), the
+//    last block of a group zero-padded.  Output transposed:
+//    codes [cols][Kpad], scales [cols][Kpad/32], where group g owns K
+//    positions [P_g, P_g + roundup(n_g, 128)) and P is the exclusive scan of
+//    the padded group sizes (128-padding keeps every 4-block scale word
+//    aligned; padding blocks are zero).
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+#include "mx.h"
+
+using namespace moe;
+
+namespace {
+
+// Scale byte of a block from its largest magnitude: the float exponent field
+// of amax minus 8, clamped to [0, 254] (0 also for amax == 0 or subnormal).
+__device__ __forceinline__ int mx_scale_byte(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xff);
+  const int c = ef - 8;
+  return c < 0 ? 0 : (c > 254 ? 254 : c);
+}
+
+// E4M3 code of x (already divided by the block scale): round to the grid of
+// the value's binade with rintf (ties to even), computed in float.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (!(a == a)) return 0x7fu;
+  if (a >= 448.0f) return sign | 0x7eu;
+  // binade exponent e (>= -6: below 2^-6 the grid step stays 2^-9)
+  int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;
+  if (e < -6) e = -6;
+  const float m = rintf(ldexpf(a, 3 - e));  // grid units of 2^(e-3)
+  int mi = (int)m;                          // 0..16
+  if (mi < 8) return sign | (uint32_t)mi;   // subnormal (e == -6)
+  if (mi == 16) {                           // rounded up into the next binade
+    mi = 8;
+    e += 1;
+  }
+  uint32_t code = ((uint32_t)(e + 7) << 3) | (uint32_t)(mi - 8);
+  if (code > 0x7eu) code = 0x7eu;
+  return sign | code;
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// One thread per 32-element block along a row.
+__global__ void mx_rows_kernel(const uint4* __restrict__ src, long long nblocks, int bpr,
+                               uint4* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = src[b * 4 + i];
+  float f[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f[i * 8 + 2 * j] = bf_lo(w[j]);
+      f[i * 8 + 2 * j + 1] = bf_hi(w[j]);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  const int sb = mx_scale_byte(amax);
+  const int s = sb - 127;
+  uint32_t out[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) word |= e4m3_code(ldexpf(f[q * 4 + j], -s)) << (8 * j);
+    out[q] = word;
+  }
+  codes[b * 2] = make_uint4(out[0], out[1], out[2], out[3]);
+  codes[b * 2 + 1] = make_uint4(out[4], out[5], out[6], out[7]);
+  scales[b] = (uint8_t)sb;
+  (void)bpr;
+}
+
+// Column blocks with groups.  Block (x = 256-column tile, y = logical row
+// block); each thread owns one column.  The (group, block-in-group) of y comes
+// from a block-wide scan of the padded group sizes (groups from `offsets`, or
+// `urows` rows each when offsets is null).
+__global__ void __launch_bounds__(256) mx_cols_kernel(
+    const bf16_t* __restrict__ src, int rows, int cols, const int32_t* __restrict__ offsets,
+    int urows, int G, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad_ld) {
+  __shared__ int sh[256 + 4];
+  const int tid = threadIdx.x;
+  const int per = (G + 255) / 256;
+  int nb[4], pb[4];  // 32-row blocks (data) and 128-row padded blocks per group
+  int local = 0, plocal = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = tid * per + q;
+    nb[q] = 0;
+    pb[q] = 0;
+    if (q < per && g < G) {
+      const int n = offsets ? offsets[g + 1] - offsets[g] : urows;
+      nb[q] = (n + 31) / 32;
+      pb[q] = (n + 127) / 128;
+    }
+    local += nb[q];
+    plocal += pb[q];
+  }
+  // scan of data blocks (to find this y's group) and of padded blocks (K base)
+  sh[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  int run = sh[tid] - local;
+  const int total = sh[255];
+  __syncthreads();
+  sh[tid] = plocal;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? sh[tid - off] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  int prun = sh[tid] - plocal;
+  __syncthreads();
+  const int y = blockIdx.y;
+  if (tid == 0) sh[256] = -1;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int g = tid * per + q;
+    if (q < per && g < G && y >= run && y < run + nb[q]) {
+      sh[256] = g;
+      sh[257] = y - run;   // block within the group
+      sh[258] = prun * 128;  // K base of the group
+    }
+    run += nb[q];
+    prun += pb[q];
+  }
+  __syncthreads();
+  if (y >= total || sh[256] < 0) return;
+  const int g = sh[256], blk = sh[257], kbase = sh[258];
+  const int gstart = offsets ? offsets[g] : g * urows;
+  const int gend = offsets ? offsets[g + 1] : (g + 1) * urows;
+  const int c = blockIdx.x * 256 + tid;
+  if (c >= cols) return;
+  const int r0 = gstart + blk * 32;
+  float f[32];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int r = r0 + i;
+    f[i] = (r < gend) ? __uint_as_float(((uint32_t)src[(size_t)r * cols + c]) << 16) : 0.f;
+    amax = fmaxf(amax, fabsf(f[i]));
+  }
+  const int sb = mx_scale_byte(amax);
+  const int s = sb - 127;
+  uint32_t out[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) word |= e4m3_code(ldexpf(f[q * 4 + j], -s)) << (8 * j);
+    out[q] = word;
+  }
+  const size_t k = (size_t)kbase + (size_t)blk * 32;
+  uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)c * kpad_ld + k);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  scales[(size_t)c * (kpad_ld / 32) + k / 32] = (uint8_t)sb;
+  (void)rows;
+}
+
+// Zero the padding blocks of a column-quantised operand: for each group, the
+// K positions past its last 32-row block up to its 128 boundary.  One thread
+// per (column, group); only runs over groups whose size is not a multiple of
+// 128.
+__global__ void mx_cols_pad_kernel(const int32_t* __restrict__ offsets, int urows, int G, int cols,
+                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                   int kpad_ld) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= cols) return;
+  int kbase = 0;
+  for (int g = 0; g < G; ++g) {
+    const int n = offsets ? offsets[g + 1] - offsets[g] : urows;
+    const int data = (n + 31) / 32 * 32, padded = (n + 127) / 128 * 128;
+    for (int k = kbase + data; k < kbase + padded; k += 32) {
+      uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)c * kpad_ld + k);
+      dst[0] = make_uint4(0, 0, 0, 0);
+      dst[1] = make_uint4(0, 0, 0, 0);
+      scales[(size_t)c * (kpad_ld / 32) + k / 32] = 0;
+    }
+    kbase += padded;
+  }
+}
+
+}  // namespace
+
+using namespace moe_host;
+
+// Upper bound of the padded K of a column-quantised operand.
+long long mx_kpad_bound(int rows, int groups) { return (long long)rows + 127LL * groups + 127; }
+
+hipError_t mx_quantize_rows(const void* src, int rows, int cols, uint8_t* codes, uint8_t* scales,
+                            hipStream_t s) {
+  const long long nb = (long long)rows * (cols / 32);
+  if (nb == 0) return hipSuccess;
+  mx_rows_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, s>>>((const uint4*)src, nb, cols / 32,
+                                                             (uint4*)codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t mx_quantize_cols(const void* src, int rows, int cols, const int32_t* offsets, int urows,
+                            int groups, uint8_t* codes, uint8_t* scales, int kpad_ld,
+                            hipStream_t s) {
+  const int yb = rows / 32 + groups + 1;
+  dim3 grid((cols + 255) / 256, yb);
+  mx_cols_kernel<<<grid, 256, 0, s>>>((const bf16_t*)src, rows, cols, offsets, urows, groups, codes,
+                                      scales, kpad_ld);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  mx_cols_pad_kernel<<<(cols + 255) / 256, 256, 0, s>>>(offsets, urows, groups, cols, codes, scales,
+                                                        kpad_ld);
+  return hipGetLastError();
+}
+
+extern "C" moe_status moe_mx_quantize(moe_ctx* ctx, const void* src_bf16, int rows, int cols,
+                                      int axis, const int32_t* group_offsets, int groups,
+                                      uint8_t* codes, uint8_t* scales_e8m0, int kpad_ld) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, rows >= 0 && cols >= 32 && cols % 32 == 0, "moe_mx_quantize: bad shape");
+  MOE_REQUIRE(ctx, axis == 0 || axis == 1, "moe_mx_quantize: axis must be 0 or 1");
+  MOE_REQUIRE_PTR(ctx, src_bf16);
+  MOE_REQUIRE_PTR(ctx, codes);
+  MOE_REQUIRE(ctx, scales_e8m0 != nullptr, "moe_mx_quantize: scales is null");
+  if (rows == 0) return MOE_OK;
+  moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
+  hipError_t e;
+  if (axis == 0) {
+    e = mx_quantize_rows(src_bf16, rows, cols, codes, scales_e8m0, ctx->stream);
+  } else {
+    MOE_REQUIRE(ctx, groups >= 1 && groups <= 1024, "moe_mx_quantize: 1 <= groups <= 1024");
+    MOE_REQUIRE(ctx, group_offsets != nullptr || groups == 1,
+                "moe_mx_quantize: group_offsets is null with groups > 1");
+    MOE_REQUIRE(ctx, kpad_ld % 128 == 0 && kpad_ld >= mx_kpad_bound(rows, groups) - 127,
+                "moe_mx_quantize: kpad_ld %d too small or not a multiple of 128", kpad_ld);
+    e = mx_quantize_cols(src_bf16, rows, cols, group_offsets, group_offsets ? 0 : rows, groups,
+                         codes, scales_e8m0, kpad_ld, ctx->stream);
+  }
+  if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "moe_mx_quantize: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
