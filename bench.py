@@ -10,8 +10,15 @@ router weight gradient.  Inputs are resident in HBM before timing starts.
 Prints ONE JSON line.  `value` is tokens/s over the timed steps.  `roofline`
 describes the dominant kernel (largest total time): its algorithmic FLOPs per
 launch over its average launch time, measured with HIP events recorded on the
-library's stream around every launch in the timed region.  `cpu_baseline` is
-the CPU oracle timed on a bounded sample of the same workload.
+library's stream around every launch in the timed region; `traffic` is its
+HBM bytes per launch from the committed rocprofv3 counter summary when that
+was taken on the current kernel source.  `cpu_baseline` is the CPU oracle
+timed on a bounded sample of the same workload.
+
+Two more legs ride on the default run: `e_scaling` times the same layer at
+E=8 (learned-style routing) for the expert-count scaling loss, and `mxfp8`
+times the MXFP8 grouped experts (quantisation included) on 65536 pre-routed
+rows of a 16-expert, d_model 4096, d_ff 1536 share.
 """
 from __future__ import annotations
 
@@ -26,6 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA (MXFP8 operands)
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "MoE-layer tokens/sec fwd+bwd at E=128 top-4; grouped-GEMM % of MFMA peak"
 GEMM_KERNELS = {  # algorithmic FLOPs per launch in units of R*d*F
@@ -33,7 +42,8 @@ GEMM_KERNELS = {  # algorithmic FLOPs per launch in units of R*d*F
     "gemm_dgrad_up": 4, "gemm_wgrad_up": 4,
 }
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-GEMM_SOURCE = os.path.join(ROOT, "routing_grouped_expert_softmax_amd", "csrc", "gemm_bf16.hip")
+GEMM_SOURCES = [os.path.join(ROOT, "routing_grouped_expert_softmax_amd", "csrc", f)
+                for f in ("gemm_bf16.hip", "gemm_common.h")]
 
 
 def row_bytes(name, T, d, k, F, E, esz=2):
@@ -48,9 +58,13 @@ def row_bytes(name, T, d, k, F, E, esz=2):
     }.get(name)
 
 
-def source_hash(path):
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+def source_hash(paths=None):
+    """First 16 hex digits of the SHA-256 of the bf16 grouped-GEMM sources."""
+    h = hashlib.sha256()
+    for path in paths or GEMM_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kernel, workload):
@@ -64,7 +78,7 @@ def read_traffic(kernel, workload):
         if ":" in line and not line.startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("source_sha256_16") != source_hash(GEMM_SOURCE):
+    if kv.get("source_sha256_16") != source_hash():
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -105,29 +119,58 @@ def cpu_baseline(cfg, inp, sample_tokens):
                       f"weights; fp32-accumulating oracle, fwd+bwd, {dt:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="uniform128",
-                    choices=["uniform128", "dense8", "zipf128", "tiny"])
-    ap.add_argument("--cpu-sample", type=int, default=1024,
-                    help="tokens of the workload the CPU oracle baseline runs on (0 = skip)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's share of the layer; runs on more than one GPU "
-              "are not part of this build (use --gpus 1).", file=sys.stderr)
-        sys.exit(2)
+def time_steps(ctx, step, steps, warmup):
+    """Run `warmup` untimed steps, then time exactly `steps` steps between two
+    synchronisations with events on the current stream, per-kernel HIP events
+    on (recorded by the library on its stream around every launch)."""
+    import torch
 
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ctx.profile(True)
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ctx.profile(False)
+    return e0.elapsed_time(e1), wall, ctx.profile_results()
+
+
+def gemm_summary(prof, unit, peak):
+    """Dominant grouped-GEMM kernel (largest total time) and the six GEMMs
+    together: algorithmic FLOPs over the HIP-event kernel times."""
+    gemm_ms = sum(prof[n][1] / prof[n][0] for n in GEMM_KERNELS if n in prof)
+    gemm_flops = 18.0 * unit
+    dom = max((n for n in GEMM_KERNELS if n in prof), key=lambda n: prof[n][1])
+    launches, total_ms = prof[dom]
+    avg_s = total_ms / launches / 1e3
+    flops = GEMM_KERNELS[dom] * unit
+    achieved = flops / avg_s / 1e12
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "flops_per_launch": flops,
+            "avg_launch_ms": round(avg_s * 1e3, 4)}
+    agg = {"tflops": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 1),
+           "frac_of_peak": round(gemm_flops / (gemm_ms / 1e3) / 1e12 / peak, 4),
+           "ms": round(gemm_ms, 4), "flops": gemm_flops}
+    return roof, agg
+
+
+def layer_leg(cfg, steps, warmup, keep_inputs=False):
+    """Time the whole layer forward+backward on one workload."""
     import torch
 
     import moe_inputs as mi
     import routing_grouped_expert_softmax_amd as moe
 
-    cfg = mi.config(args.workload)
     dev = "cuda:0"
-    torch.cuda.set_device(0)
     inp = mi.layer_inputs(cfg)
     g = {k: inp[k].to(dev) for k in ("x", "wr", "wg", "wu", "wd", "dy")}
     override = inp["logits"].to(dev) if "logits" in inp else None
@@ -140,40 +183,111 @@ def main():
         moe.layer_forward(g["x"], g["wr"], g["wg"], g["wu"], g["wd"], cfg.k, buf, override)
         moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    gpu_ms, wall, prof = time_steps(ctx, step, steps, warmup)
+    counts = buf.route["counts"].cpu()
+    out = dict(cfg=cfg, gpu_ms=gpu_ms, wall=wall, prof=prof,
+               tokens_per_s=cfg.T * steps / (gpu_ms / 1e3), ms_per_step=gpu_ms / steps,
+               load={"max": int(counts.max()), "mean": float(counts.float().mean()),
+                     "empty": int((counts == 0).sum())})
+    if keep_inputs:
+        out["inp"] = inp
+    del g, buf, override
+    torch.cuda.empty_cache()
+    return out
 
-    ctx.profile(True)
-    stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ctx.profile(False)
-    gpu_ms = e0.elapsed_time(e1)
-    prof = ctx.profile_results()
 
-    ms_per_step = gpu_ms / args.steps
-    tokens_per_s = cfg.T * args.steps / (gpu_ms / 1e3)
+def mx_leg(steps, warmup):
+    """Time the MXFP8 grouped experts (quantisation included) forward+backward
+    on the pre-routed 16-expert workload."""
+    import torch
+
+    import moe_inputs as mi
+    import routing_grouped_expert_softmax_amd as moe
+
+    dev = "cuda:0"
+    cfg = mi.MX_CONFIG
+    inp = mi.mx_inputs(cfg)
+    g = {k: inp[k].to(dev) for k in ("xp", "dyp", "wg", "wu", "wd")}
+    off = torch.from_numpy(inp["offsets"]).to(dev)
+    R, d, F, E = cfg.rows, cfg.d, cfg.F, cfg.E
+    z = lambda *s: torch.empty(*s, dtype=torch.bfloat16, device=dev)  # noqa: E731
+    fo = dict(g=z(R, F), u=z(R, F), h=z(R, F), yp=z(R, d))
+    bo = dict(dg=z(R, F), du=z(R, F), dxp=z(R, d), dw_gate=z(E, d, F), dw_up=z(E, d, F),
+              dw_down=z(E, F, d))
+    ctx = moe.context(0)
+    ctx.ensure_mx_workspace(E, R, d, F)
+
+    def step():
+        moe.moe_grouped_ffn_fwd(g["xp"], g["wg"], g["wu"], g["wd"], off, fo, mxfp8=True)
+        moe.moe_grouped_ffn_bwd(g["xp"], g["wg"], g["wu"], g["wd"], off, fo["g"], fo["u"], fo["h"],
+                                g["dyp"], bo, mxfp8=True)
+
+    gpu_ms, wall, prof = time_steps(ctx, step, steps, warmup)
+    roof, agg = gemm_summary(prof, R * d * F, PEAK_FP8_TFLOPS)
+    counts = inp["counts"]
+    res = {"workload": f"{cfg.name}: {R} pre-routed rows, d={d}, {E} experts, d_ff={F}, "
+                       f"Zipf({cfg.zipf_s}) counts; MXFP8 E4M3 + e8m0 per 32, fp32 accumulate",
+           "rows_per_s": round(R * steps / (gpu_ms / 1e3), 1), "ms_per_step": round(gpu_ms / steps, 4),
+           "steps": steps, "warmup": warmup, "roofline": roof, "grouped_gemm": agg,
+           "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in prof.items()},
+           "expert_load": {"max": int(counts.max()), "mean": float(counts.mean()), "empty": 0}}
+    del g, fo, bo, off
+    torch.cuda.empty_cache()
+    return res
+
+
+def copy_calibration(mib, reps):
+    """A plain device copy of `mib` MiB, `reps` times: the known-size kernel
+    that scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="uniform128",
+                    choices=["uniform128", "dense8", "zipf128", "tiny"])
+    ap.add_argument("--cpu-sample", type=int, default=8192,
+                    help="tokens of the workload the CPU oracle baseline runs on (0 = skip)")
+    ap.add_argument("--no-escaling", action="store_true",
+                    help="skip the E=8 leg that gives the expert-count scaling loss")
+    ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 grouped-expert leg")
+    ap.add_argument("--mx-steps", type=int, default=10)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the layer; runs on more than one GPU "
+              "are not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import moe_inputs as mi
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 4)
+        return
+
+    cfg = mi.config(args.workload)
+    main_leg = layer_leg(cfg, args.steps, args.warmup, keep_inputs=args.cpu_sample > 0)
+    prof = main_leg["prof"]
     R = cfg.T * cfg.k
     unit = R * cfg.d * cfg.F
-    counts = buf.route["counts"].cpu()
-
-    breakdown = {name: round(ms / n, 4) for name, (n, ms) in prof.items()}
-    gemm_ms = sum(prof[n][1] / prof[n][0] for n in GEMM_KERNELS if n in prof)
-    gemm_flops = 18.0 * unit
-    dom = max((n for n in GEMM_KERNELS if n in prof), key=lambda n: prof[n][1])
-    dom_launches, dom_total_ms = prof[dom]
-    dom_avg_s = dom_total_ms / dom_launches / 1e3
-    dom_flops = GEMM_KERNELS[dom] * unit
-    achieved = dom_flops / dom_avg_s / 1e12
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
+    roof, agg = gemm_summary(prof, unit, peak)
+    roof["traffic"] = read_traffic(roof["kernel"], cfg.name)
     rows = {}
     for name in ("permute", "combine", "combine_bwd", "permute_bwd"):
         if name in prof and cfg.dtype == "bf16":
@@ -183,12 +297,12 @@ def main():
 
     result = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": round(main_leg["tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(main_leg["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -198,23 +312,25 @@ def main():
                                f"{cfg.dtype} SwiGLU experts, routing={cfg.routing}",
                    "tokens": cfg.T, "experts": cfg.E, "top_k": cfg.k, "d_model": cfg.d, "d_ff": cfg.F,
                    "parallelism": "single GPU (one GPU's share; no collectives)"},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": read_traffic(dom, cfg.name),
-                     "flops_per_launch": dom_flops,
-                     "avg_launch_ms": round(dom_avg_s * 1e3, 4)},
-        "grouped_gemm": {"tflops": round(gemm_flops / (gemm_ms / 1e3) / 1e12, 1),
-                         "frac_of_peak": round(gemm_flops / (gemm_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                         "ms": round(gemm_ms, 4), "flops": gemm_flops},
+        "roofline": roof,
+        "grouped_gemm": agg,
         "row_movers": rows,
-        "kernel_ms": breakdown,
-        "expert_load": {"max": int(counts.max()), "mean": float(counts.float().mean()),
-                        "empty": int((counts == 0).sum())},
-        "wall_s_timed": round(wall, 3),
+        "kernel_ms": {name: round(ms / n, 4) for name, (n, ms) in prof.items()},
+        "expert_load": main_leg["load"],
+        "wall_s_timed": round(main_leg["wall"], 3),
     }
+    if not args.no_escaling and cfg.name == "uniform128":
+        base = layer_leg(mi.config("dense8"), args.steps, args.warmup)
+        result["e_scaling"] = {
+            "dense8_tokens_per_s": round(base["tokens_per_s"], 1),
+            "uniform128_tokens_per_s": round(main_leg["tokens_per_s"], 1),
+            "loss": round(1.0 - main_leg["tokens_per_s"] / base["tokens_per_s"], 4),
+            "dense8_grouped_gemm_tflops": gemm_summary(base["prof"], 16384 * 4 * 2048 * 1024,
+                                                       PEAK_BF16_TFLOPS)[1]["tflops"]}
+    if not args.no_mx:
+        result["mxfp8"] = mx_leg(args.mx_steps, 3)
     if args.cpu_sample > 0:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
+        result["cpu_baseline"] = cpu_baseline(cfg, main_leg["inp"], args.cpu_sample)
     print(json.dumps(result), flush=True)
 
 
