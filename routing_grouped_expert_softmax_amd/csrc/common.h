@@ -84,8 +84,11 @@ struct Elem<bf16_t> {
   static __device__ __forceinline__ void st(bf16_t* p, size_t i, float v) { p[i] = f2bf(v); }
 };
 
-__device__ __forceinline__ float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// v_rcp_f32 (about 1 ulp) instead of an IEEE divide: the divide expansion
+// needs several temporaries per element, which the epilogues cannot afford
+// with a full accumulator tile live.
+__device__ __forceinline__ float silu_f(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+__device__ __forceinline__ float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 }  // namespace moe
 

@@ -74,13 +74,13 @@ struct Params {
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
 // ---------------------------------------------------------------- LDS layouts
-// K-contiguous tile: groups of 8 rows, each group 1 KiB laid out as
+// K-contiguous tile: groups of 8 rows, each group 16*BK bytes laid out as
 // [16-deep K slice][row % 8][32 bytes], the two 16-byte halves of a row
-// swapped when bit 3 of the row is set.  One 1 KiB load instruction fills one
-// group (8 full 128-byte row segments of HBM); the 16 lanes of one LDS pass
-// (16 consecutive rows, same half) hit 16 distinct bank slots; a fragment
-// address is one per-lane base plus a compile-time offset per row block and
-// slice.
+// swapped when bit 3 of the row is set.  One 1 KiB load instruction fills
+// 1024 / (16*BK) whole groups (8 full row segments of HBM each); the 16 lanes
+// of one LDS pass (16 consecutive rows, same half) hit 16 distinct bank
+// slots; a fragment address is one per-lane base plus a compile-time offset
+// per row block and slice.
 __device__ __forceinline__ int kc_half(int row, int h) { return h ^ ((row >> 3) & 1); }
 // M/N-contiguous tile ([64 k][cols], 256- or 512-byte rows): the 16-byte
 // chunk index is XOR-ed with 4*(k & 3), so a transposing fragment read
@@ -94,6 +94,9 @@ struct Tile {
   using TR = Traits<MODE>;
   static constexpr int WM = BM / 2;   // wave tile rows (M)
   static constexpr int SM = WM / 32;  // 32-row subtiles per wave
+  static constexpr int GROUP = 16 * BK;     // bytes of one 8-row K-contiguous group
+  static constexpr int SLICES = BK / 16;    // 16-deep K slices per stage
+  static constexpr int GPI = 1024 / GROUP;  // groups filled by one 1 KiB load
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = BN * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -104,8 +107,8 @@ struct Tile {
   static constexpr int B_PITCH = TR::kB_KCONTIG ? 128 : (TR::kDUAL ? 256 : 512);
 };
 
-template <int MODE, int BM, int S, int BK>
-__global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
+template <int MODE, int BM, int S, int BK, int OCC>
+__global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using TR = Traits<MODE>;
   using TL = Tile<MODE, BM, BK>;
@@ -192,8 +195,9 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   for (int j = 0; j < TL::A_INST; ++j) {
     const int q = wv * TL::A_INST + j;  // 1 KiB instruction index inside the A tile
     if (TR::kA_KCONTIG) {
-      // instruction q fills rows 8q..8q+7; lane = slice*16 + (row%8)*2 + half
-      const int kk = lane >> 4, row = q * 8 + ((lane & 15) >> 1), hp = lane & 1;
+      // instruction q fills groups q*GPI..; lane = (group, slice, row % 8, half)
+      const int kk = (lane >> 4) % TL::SLICES, gi = (lane >> 4) / TL::SLICES;
+      const int row = (q * TL::GPI + gi) * 8 + ((lane & 15) >> 1), hp = lane & 1;
       aoff[j] = (row * p.lda + (kk * 2 + kc_half(row, hp)) * 8) * (int)esz;
     } else {
       constexpr int CPR = BM / 8;  // 16-byte chunks per k row
@@ -205,7 +209,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   for (int j = 0; j < TL::B_INST; ++j) {
     const int q = wv * TL::B_INST + j;
     if (TR::kB_KCONTIG) {
-      const int kk = lane >> 4, n = q * 8 + ((lane & 15) >> 1), hp = lane & 1;
+      const int kk = (lane >> 4) % TL::SLICES, gi = (lane >> 4) / TL::SLICES;
+      const int n = (q * TL::GPI + gi) * 8 + ((lane & 15) >> 1), hp = lane & 1;
       boff[j] = ((w.nt * BN + n) * p.ldb + (kk * 2 + kc_half(n, hp)) * 8) * (int)esz;
     } else if (TR::kDUAL) {
       // two sub-tiles of [BK k][128 n]: the first BK/4 instructions fill
@@ -274,10 +279,10 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
   // K-contiguous tile: lane reads row (row0 + lane & 31), half (lane >> 5) of
   // slice kk.  The per-lane part is computed once; row0 (a multiple of 32)
   // and kk fold into the instruction's immediate offset.
-  const int kc_lane = ((lane & 31) >> 3) * 1024 + (lane & 7) * 32 +
+  const int kc_lane = ((lane & 31) >> 3) * TL::GROUP + (lane & 7) * 32 +
                       (kc_half(lane & 31, lane >> 5) << 4);
   auto frag_kc = [&](const LDS_AS unsigned char* t, int row0, int kk) -> bf16x8 {
-    return *(const LDS_AS bf16x8*)(t + (row0 >> 3) * 1024 + kk * 256 + kc_lane);
+    return *(const LDS_AS bf16x8*)(t + (row0 >> 3) * TL::GROUP + kk * 256 + kc_lane);
   };
   // M/N-contiguous tile: two transposing 8-byte reads give each lane 8
   // consecutive k of column (col0 + lane & 31): in each 16-lane group, lane i
@@ -414,21 +419,55 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_kernel(Params p) {
 
   // ---------------------------------------------------------------- epilogue
   EpiArgs ea{p.c0, p.c1, p.c2, p.ldc, p.c_gstride, p.aux0, p.aux1, p.N, p.M};
-  store_tile<MODE, BM, SM, false>(acc, ea, w, lane, wm, wn);
+  if constexpr (epi_staged<MODE>(TL::STAGE, S)) {
+    constexpr int CH = epi_chunk<MODE>(TL::STAGE, S);
+    constexpr int REG = epi_region_bytes<MODE>(CH);
+    constexpr int PER = TL::STAGE / REG;
+    static_assert(S * PER >= 4, "epilogue staging regions do not fit the stage buffers");
+    const int sel = wave / PER;
+    LDS_AS unsigned char* wbuf =
+        (sel == 0 ? (LDS_AS unsigned char*)lds0 : sel == 1 ? (LDS_AS unsigned char*)lds1
+         : sel == 2 ? (LDS_AS unsigned char*)lds2 : (LDS_AS unsigned char*)lds3) + (wave % PER) * REG;
+    store_tile<MODE, BM, SM, false, CH>(acc, ea, w, lane, wm, wn, wbuf);
+  } else {
+    store_tile_direct<MODE, BM, SM, false>(acc, ea, w, lane, wm, wn);
+  }
 #endif
 }
 
-template <int MODE, int BM, int S, int BK>
+template <int MODE, int BM, int S, int BK, int OCC = 1>
 hipError_t launch(const Params& p, int blocks, hipStream_t s) {
   blocks = (blocks + 7) / 8 * 8;
-  grouped_gemm_kernel<MODE, BM, S, BK><<<blocks, kThreads, 0, s>>>(p);
+  grouped_gemm_kernel<MODE, BM, S, BK, OCC><<<blocks, kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 
-#ifndef GEMM_BK
-#define GEMM_BK 64
-#define GEMM_S 2
+// Tile configurations: rows per tile, pipeline stages, K step, blocks per
+// CU.  Two resident blocks per CU (128x256 tiles, 32-deep K steps, 72 KiB of
+// LDS and at most 256 registers per wave) let one block's prologue, barriers
+// and output stores overlap the other block's MFMAs on the same SIMDs; the
+// down dgrad, whose epilogue also reads the saved g and u, keeps one block of
+// 128x256 tiles with 64-deep K steps.
+#ifndef GEMM_M_CFG
+#define GEMM_M_CFG 128, 3, 32, 2   // forward gate/up and down
 #endif
+#ifndef GEMM_DU_CFG
+#define GEMM_DU_CFG 128, 2, 32, 2  // gate/up dgrad
+#endif
+#ifndef GEMM_DD_CFG
+#define GEMM_DD_CFG 128, 3, 64, 1  // down dgrad
+#endif
+#ifndef GEMM_W_CFG
+#define GEMM_W_CFG 128, 3, 32, 2   // both wgrads
+#endif
+template <int BM_, int S_, int BK_, int OCC_>
+struct Cfg {
+  static constexpr int BM = BM_, S = S_, BK = BK_, OCC = OCC_;
+};
+using CfgM = Cfg<GEMM_M_CFG>;
+using CfgDU = Cfg<GEMM_DU_CFG>;
+using CfgDD = Cfg<GEMM_DD_CFG>;
+using CfgW = Cfg<GEMM_W_CFG>;
 
 // Upper bound of sum_e ceil(n_e / BM) over any split of R rows into E groups.
 int mtile_bound(int R, int E, int BM) { return R / BM + E; }
@@ -438,13 +477,13 @@ int mtile_bound(int R, int E, int BM) { return R / BM + E; }
 // ---------------------------------------------------------------- host API
 using namespace moe_host;
 
-// Row-tile height of an M-ragged launch.  256-row tiles halve the weight
-// traffic per FLOP and win even when experts hold only ~500 rows; the down
-// dgrad, whose epilogue also streams the saved g and u, runs best with 128.
+// Launch of a row-ragged mode with its tile configuration; the grid is the
+// bound on sum_e ceil(n_e / BM) tiles, found on the device.
 template <int MODE>
 static hipError_t launch_mragged(Params& p, int R, hipStream_t s) {
-  if (MODE == DGRAD_DOWN) return launch<MODE, 128, 3, 64>(p, mtile_bound(R, p.E, 128) * p.ntiles, s);
-  return launch<MODE, 256, GEMM_S, GEMM_BK>(p, mtile_bound(R, p.E, 256) * p.ntiles, s);
+  using C = std::conditional_t<MODE == DGRAD_DOWN, CfgDD,
+                               std::conditional_t<MODE == DGRAD_UP, CfgDU, CfgM>>;
+  return launch<MODE, C::BM, C::S, C::BK, C::OCC>(p, mtile_bound(R, p.E, C::BM) * p.ntiles, s);
 }
 
 moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const void* wr, int T_,
@@ -673,10 +712,11 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.M = F;
     p.N = d;
     p.ntiles = (d + BN - 1) / BN;
-    p.mtiles = (F + 255) / 256;
+    p.mtiles = (F + CfgW::BM - 1) / CfgW::BM;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
-      e = launch<WGRAD_DOWN, 256, GEMM_S, GEMM_BK>(p, E * p.ntiles * p.mtiles, ctx->stream);
+      e = launch<WGRAD_DOWN, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(p, E * p.ntiles * p.mtiles,
+                                                                    ctx->stream);
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down wgrad: %s", hipGetErrorString(e));
   }
@@ -721,10 +761,11 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.M = d;
     p.N = F;
     p.ntiles = (F + 127) / 128;
-    p.mtiles = (d + 255) / 256;
+    p.mtiles = (d + CfgW::BM - 1) / CfgW::BM;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
-      e = launch<WGRAD_UP, 256, GEMM_S, GEMM_BK>(p, E * p.ntiles * p.mtiles, ctx->stream);
+      e = launch<WGRAD_UP, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(p, E * p.ntiles * p.mtiles,
+                                                                  ctx->stream);
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up wgrad: %s", hipGetErrorString(e));
   }

@@ -167,15 +167,16 @@ struct EpiArgs {
   int M;
 };
 
-// Stores one block tile.  Lane holds
+// Direct epilogue: every lane stores its own 4-column pieces straight from
+// the accumulators (each store covers 16 bytes of 32 rows), used where the
+// staging regions below do not fit.  Lane holds
 // C[m = mbase + (lane&31)][n = nbase + 8*(r/4) + 4*(lane>>5) + r%4] of each
 // 32x32 subtile; dual modes hold g (subtiles 0,1) and u (2,3) of the same
-// columns.  SWIGLU_FROM_BF16: the forward's h (and the dgrad's silu terms)
-// are computed from the bf16-rounded g and u instead of the fp32 sums.
+// columns.
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 template <int MODE, int BM, int SM, bool SWIGLU_FROM_BF16>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const EpiArgs& a,
-                                           const Work& w, int lane, int wm, int wn) {
+__device__ __forceinline__ void store_tile_direct(const f32x16 (&acc)[SM][4], const EpiArgs& a,
+                                                  const Work& w, int lane, int wm, int wn) {
   constexpr int WM = BM / 2;
   // Lane holds C[m = mbase + (lane&31)][n = nbase + 8*(r/4) + 4*(lane>>5) + r%4].
   const int ncol4 = 4 * (lane >> 5);
@@ -268,6 +269,210 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const Epi
           }
         }
       }
+    }
+  }
+}
+
+
+// Epilogue staging region of a wave: inside stage buffer wave / PER at
+// offset (wave % PER) * REG, where PER regions fit in one stage buffer.
+// Callers static_assert that S * PER >= 4.
+// Epilogue staging.  Each wave owns a private LDS region (inside the stage
+// buffers, free once the main loop's last barrier has passed) and writes its
+// outputs through it CH rows at a time: accumulators go into LDS in the MFMA
+// layout, then every lane reads 16 contiguous bytes of a row and stores them,
+// so each store instruction writes whole row segments instead of 16 bytes in
+// each of 32 rows.  The down dgrad reads the saved g and u the same way in
+// reverse.  Rows of a region are WNO bf16 wide; 16-byte chunks are XOR-
+// swizzled with the row so that column-wise MFMA-layout writes and row-wise
+// reads both spread over the banks.
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 bf4(const float (&v)[4]) {
+  u32x2 r;
+  r.x = pack2bf(v[0], v[1]);
+  r.y = pack2bf(v[2], v[3]);
+  return r;
+}
+
+template <int MODE>
+constexpr int epi_nout() {
+  return MODE == FWD_UP ? 3 : (Traits<MODE>::kDUAL || MODE == DGRAD_DOWN) ? 2 : 1;
+}
+template <int MODE>
+constexpr int epi_wno() { return Traits<MODE>::kDUAL ? 64 : 128; }
+template <int MODE>
+constexpr int epi_region_bytes(int ch) { return epi_nout<MODE>() * ch * epi_wno<MODE>() * 2; }
+// Whether four wave regions of CH = 32 rows fit in the stage buffers.
+template <int MODE>
+constexpr bool epi_staged(int stage_bytes, int stages) {
+  return MODE != ROUTER && stages * (stage_bytes / epi_region_bytes<MODE>(32)) >= 4;
+}
+// Rows per chunk: 64 when four wave regions fit in the stage buffers, else 32.
+template <int MODE>
+constexpr int epi_chunk(int stage_bytes, int stages) {
+  return stages * (stage_bytes / epi_region_bytes<MODE>(64)) >= 4 ? 64 : 32;
+}
+
+// Stores one block tile.  Lane holds
+// C[m = mbase + (lane&31)][n = nbase + 8*(r/4) + 4*(lane>>5) + r%4] of each
+// 32x32 subtile; dual modes hold g (subtiles 0,1) and u (2,3) of the same
+// columns.  SWIGLU_FROM_BF16: the forward's h (and the dgrad's silu terms)
+// are computed from the bf16-rounded g and u instead of the fp32 sums.
+// wbuf: this wave's staging region, epi_region_bytes<MODE>(CH) bytes.
+template <int MODE, int BM, int SM, bool SWIGLU_FROM_BF16, int CH>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const EpiArgs& a,
+                                           const Work& w, int lane, int wm, int wn,
+                                           LDS_AS unsigned char* wbuf) {
+  constexpr int WM = BM / 2;
+  const int ncol4 = 4 * (lane >> 5);
+  if constexpr (MODE == ROUTER) {
+    // fp32 scores, E columns: direct stores (small output)
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm) {
+      const int mloc = wm * WM + sm * 32 + (lane & 31);
+      if (mloc >= w.rows) continue;
+      const size_t crow = (size_t)(w.row0 + mloc);
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int col = w.nt * BN + wn * 128 + sn * 32 + 8 * g4 + ncol4;
+          if (col >= a.N) continue;
+          float* c = (float*)a.c0 + crow * a.ldc + col;
+          *reinterpret_cast<float4*>(c) = make_float4(acc[sm][sn][g4 * 4], acc[sm][sn][g4 * 4 + 1],
+                                                      acc[sm][sn][g4 * 4 + 2], acc[sm][sn][g4 * 4 + 3]);
+        }
+    }
+    return;
+  } else {
+    constexpr bool DUAL = Traits<MODE>::kDUAL;
+    constexpr int WNO = epi_wno<MODE>();
+    constexpr int NOUT = epi_nout<MODE>();
+    constexpr int PITCH = WNO * 2;      // bytes per staged row
+    constexpr int CPR = PITCH / 16;     // 16-byte chunks per row
+    constexpr int MAT = CH * PITCH;     // bytes per staged matrix
+    constexpr int RPI = 1024 / PITCH;   // rows per wave-wide 16-byte access
+    constexpr int SMC = CH / 32;
+    static_assert(WM % CH == 0, "chunk must divide the wave tile");
+    const int col0 = DUAL ? w.nt * 128 + wn * 64 : w.nt * BN + wn * 128;
+    const size_t gbase = Traits<MODE>::kKRAGGED ? (size_t)w.e * a.c_gstride : 0;
+    // staged byte offset of (row, 4-column group) in MFMA layout
+    auto frag_off = [&](int row, int col) {
+      return row * PITCH + (((col >> 3) ^ (row & (CPR - 1))) << 4) + (((col >> 2) & 1) << 3);
+    };
+    // row-wise access: lane -> (row within the access, chunk)
+    const int rw_row = lane / CPR, rw_chunk = lane % CPR;
+    auto row_ok = [&](int mloc, size_t& crow) {
+      if (Traits<MODE>::kKRAGGED) {
+        crow = (size_t)(w.m0 + mloc);
+        return (w.m0 + mloc) < a.M;
+      }
+      crow = (size_t)(w.row0 + mloc);
+      return mloc < w.rows;
+    };
+#pragma unroll
+    for (int q = 0; q < WM / CH; ++q) {
+      const int mbase = wm * WM + q * CH;  // first block-tile row of this chunk
+      if (MODE == DGRAD_DOWN) {
+        // saved g, u rows -> LDS (coalesced 16-byte loads)
+#pragma unroll
+        for (int it = 0; it < CH / RPI; ++it) {
+          const int row = it * RPI + rw_row;
+          size_t crow;
+          const int col = col0 + rw_chunk * 8;
+          if (row_ok(mbase + row, crow) && col < a.N) {
+            const size_t off = crow * a.ldc + col;
+            const u32x4 gv = *reinterpret_cast<const u32x4*>(a.aux0 + off);
+            const u32x4 uv = *reinterpret_cast<const u32x4*>(a.aux1 + off);
+            const int lo = row * PITCH + ((rw_chunk ^ (row & (CPR - 1))) << 4);
+            *reinterpret_cast<LDS_AS u32x4*>(wbuf + lo) = gv;
+            *reinterpret_cast<LDS_AS u32x4*>(wbuf + MAT + lo) = uv;
+          }
+        }
+      }
+      asm volatile("" ::: "memory");
+      // accumulators -> LDS
+#pragma unroll
+      for (int s = 0; s < SMC; ++s) {
+        const int sm = q * SMC + s;
+        const int row = s * 32 + (lane & 31);
+        if (DUAL) {
+#pragma unroll
+          for (int sn = 0; sn < 2; ++sn)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int off = frag_off(row, sn * 32 + 8 * g4 + ncol4);
+              float gv[4], uv[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                gv[r] = acc[sm][sn][g4 * 4 + r];
+                uv[r] = acc[sm][sn + 2][g4 * 4 + r];
+              }
+              *reinterpret_cast<LDS_AS u32x2*>(wbuf + off) = bf4(gv);
+              *reinterpret_cast<LDS_AS u32x2*>(wbuf + MAT + off) = bf4(uv);
+              if (MODE == FWD_UP) {
+                float hv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const float gg = SWIGLU_FROM_BF16 ? moe::bf2f(moe::f2bf(gv[r])) : gv[r];
+                  const float uu = SWIGLU_FROM_BF16 ? moe::bf2f(moe::f2bf(uv[r])) : uv[r];
+                  hv[r] = silu_f(gg) * uu;
+                }
+                *reinterpret_cast<LDS_AS u32x2*>(wbuf + 2 * MAT + off) = bf4(hv);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+          for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const int off = frag_off(row, sn * 32 + 8 * g4 + ncol4);
+              float v[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) v[r] = acc[sm][sn][g4 * 4 + r];
+              if (MODE == DGRAD_DOWN) {
+                const u32x2 gw = *reinterpret_cast<const LDS_AS u32x2*>(wbuf + off);
+                const u32x2 uw = *reinterpret_cast<const LDS_AS u32x2*>(wbuf + MAT + off);
+                const uint32_t gq[2] = {gw.x, gw.y}, uq[2] = {uw.x, uw.y};
+                float dg[4], du[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const float g = __uint_as_float((r & 1) ? (gq[r >> 1] & 0xffff0000u) : (gq[r >> 1] << 16));
+                  const float u = __uint_as_float((r & 1) ? (uq[r >> 1] & 0xffff0000u) : (uq[r >> 1] << 16));
+                  const float sg = sigmoid_f(g);
+                  dg[r] = v[r] * u * sg * (1.0f + g * (1.0f - sg));
+                  du[r] = v[r] * g * sg;
+                }
+                *reinterpret_cast<LDS_AS u32x2*>(wbuf + off) = bf4(dg);
+                *reinterpret_cast<LDS_AS u32x2*>(wbuf + MAT + off) = bf4(du);
+              } else {
+                *reinterpret_cast<LDS_AS u32x2*>(wbuf + off) = bf4(v);
+              }
+            }
+        }
+      }
+      asm volatile("" ::: "memory");
+      // LDS -> global, whole row segments per access
+      void* const outs[3] = {a.c0, a.c1, a.c2};
+#pragma unroll
+      for (int it = 0; it < CH / RPI; ++it) {
+        const int row = it * RPI + rw_row;
+        size_t crow;
+        const int col = col0 + rw_chunk * 8;
+        const bool ok = row_ok(mbase + row, crow) && col < a.N;
+        const int lo = row * PITCH + ((rw_chunk ^ (row & (CPR - 1))) << 4);
+#pragma unroll
+        for (int m = 0; m < NOUT; ++m) {
+          const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(wbuf + m * MAT + lo);
+          // streaming store: the output is not re-read by this kernel
+          if (ok)
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<u32x4*>((bf16_t*)outs[m] + gbase + crow * a.ldc + col));
+        }
+      }
+      asm volatile("" ::: "memory");
     }
   }
 }

@@ -340,7 +340,16 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_mx_kernel(MxParams p
   EpiArgs ea{p.c0, p.c1, p.c2, p.ldc, p.c_gstride, p.aux0, p.aux1, p.N, p.M};
   Work wo = w;
   if (TR::kKRAGGED) wo.row0 = 0;  // outputs of wgrad are indexed by m0 + row
-  store_tile<MODE, BM, SM, true>(acc, ea, wo, lane, wm, wn);
+  constexpr int CH = epi_chunk<MODE>(TL::STAGE, S);
+  constexpr int REG = epi_region_bytes<MODE>(CH);
+  constexpr int PER = TL::STAGE / REG;
+  static_assert(S * PER >= 4, "epilogue staging regions do not fit the stage buffers");
+  const int sel = wave / PER;
+  LDS_AS unsigned char* wbuf =
+      (sel == 0 ? (LDS_AS unsigned char*)lds0 : sel == 1 ? (LDS_AS unsigned char*)lds1
+                                                         : (LDS_AS unsigned char*)lds2) +
+      (wave % PER) * REG;
+  store_tile<MODE, BM, SM, true, CH>(acc, ea, wo, lane, wm, wn, wbuf);
 #endif
 }
 
