@@ -503,8 +503,11 @@ moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const vo
   p.kseg = d;
   p.ntiles = (E + BN - 1) / BN;
   p.E = 1;
-  const int blocks = ((T_ + 255) / 256) * p.ntiles;
-  hipError_t e = launch<ROUTER, 256, 2, 64>(p, blocks, ctx->stream);
+  // 64-row tiles: T/64 blocks fill the chip for the token counts the layer
+  // runs at (the scores GEMM is bound by reading x once)
+  constexpr int kRouterBM = 64;
+  const int blocks = ((T_ + kRouterBM - 1) / kRouterBM) * p.ntiles;
+  hipError_t e = launch<ROUTER, kRouterBM, 2, 64, 1>(p, blocks, ctx->stream);
   if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "router GEMM: %s", hipGetErrorString(e));
   return MOE_OK;
 }

@@ -16,7 +16,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int kTokBlock = 256;  // tokens per routing block (one per thread)
+constexpr int kTokBlock = 64;  // tokens per routing block (one wave, one token per lane)
 
 // ---------------------------------------------------------------- scores
 // Small-E router scores on the vector ALUs: one wave per token at a time; each
@@ -78,82 +78,156 @@ __global__ void __launch_bounds__(256) router_logits_small_kernel(const T* __res
 }
 
 // ---------------------------------------------------------------- top-k
-// One thread per token.  The experts are visited in ascending index; a
-// candidate enters the kept list only if its logit is strictly larger than
-// the k-th kept one, and lands behind every kept expert with an equal or
-// larger logit, so the list is ordered by (logit descending, index
-// ascending).  NaN scores count as -inf.  Gates are the softmax over the k
-// kept logits.  Each block also counts its tokens' experts in LDS and writes
-// its histogram column to the workspace.
+// A block of 256 threads takes 64 tokens, four lanes per token.  The block's
+// logits are staged in LDS a chunk of experts at a time (coalesced loads,
+// sixteen in flight per thread; the odd row pitch spreads the column walks
+// over the banks).  Each lane keeps a sorted list of its quarter of every
+// chunk: experts are visited in ascending index, a candidate enters only if
+// its logit is strictly larger than the k-th kept one and lands behind every
+// kept expert with an equal or larger logit, so each list is ordered by
+// (logit descending, index ascending).  The four lists are then merged with
+// k rounds of a shuffle reduction under the same order.  NaN scores count as
+// -inf.  Gates are the softmax over the k kept logits.  The block also counts
+// its tokens' experts in LDS and writes its histogram column to the workspace.
+constexpr int kTopkChunk = 128;   // experts staged per pass
+constexpr int kTopkThreads = 256; // four lanes per token
 template <int KMAX>
-__global__ void __launch_bounds__(kTokBlock) topk_hist_kernel(
+__global__ void __launch_bounds__(kTopkThreads) topk_hist_kernel(
     const float* __restrict__ logits, int T_, int E, int k, int32_t* __restrict__ topk_idx,
     float* __restrict__ gates, int32_t* __restrict__ block_counts, int nblk) {
+  __shared__ float stage[kTokBlock * (kTopkChunk + 1)];
   __shared__ int hist[1024];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[e] = 0;
-  __syncthreads();
-  const int t = blockIdx.x * kTokBlock + threadIdx.x;
-  if (t < T_) {
-    float val[KMAX];
-    int idx[KMAX];
+  const int tid = threadIdx.x;
+  const int tl = tid >> 2, sub = tid & 3;
+  for (int e = tid; e < E; e += kTopkThreads) hist[e] = 0;
+  const int tbase = blockIdx.x * kTokBlock;
+  const int ntok = min(kTokBlock, T_ - tbase);
+  float val[KMAX];
+  int idx[KMAX];
 #pragma unroll
-    for (int i = 0; i < KMAX; ++i) {
-      val[i] = -INFINITY;
-      idx[i] = -1;
-    }
-    const float* l = logits + (size_t)t * E;
-    for (int e = 0; e < E; ++e) {
-      float v = l[e];
-      if (v != v) v = -INFINITY;
-      // position = number of kept experts that stay ahead of this one
-      int p = 0;
-      bool enter = false;
+  for (int i = 0; i < KMAX; ++i) {
+    val[i] = -INFINITY;
+    idx[i] = -1;
+  }
+  for (int c0 = 0; c0 < E; c0 += kTopkChunk) {
+    const int ce = min(kTopkChunk, E - c0);
+    __syncthreads();  // the previous chunk has been consumed
+    // element i of the [ntok][ce] chunk goes to stage[r][c]
+    const int n = ntok * ce;
+    const float inv_ce = 1.0f / (float)ce;
+    for (int base = 0; base < n; base += 16 * kTopkThreads) {
+      float v[16];
+      int pos[16];
 #pragma unroll
-      for (int i = 0; i < KMAX; ++i) {
-        if (i < k) {
-          bool ahead = idx[i] >= 0 && val[i] >= v;
-          p += ahead ? 1 : 0;
+      for (int j = 0; j < 16; ++j) {
+        const int i = base + j * kTopkThreads + tid;
+        int r = (int)((float)i * inv_ce);
+        int c = i - r * ce;
+        if (c < 0) {
+          --r;
+          c += ce;
+        } else if (c >= ce) {
+          ++r;
+          c -= ce;
         }
+        pos[j] = i < n ? r * (kTopkChunk + 1) + c : -1;
+        v[j] = i < n ? logits[(size_t)(tbase + r) * E + c0 + c] : 0.f;
       }
-      enter = p < k;
-      if (enter) {
 #pragma unroll
-        for (int i = KMAX - 1; i > 0; --i) {
-          if (i < k && i > p) {
-            val[i] = val[i - 1];
-            idx[i] = idx[i - 1];
+      for (int j = 0; j < 16; ++j)
+        if (pos[j] >= 0) stage[pos[j]] = v[j];
+    }
+    __syncthreads();
+    if (tl < ntok) {
+      const int q = (ce + 3) >> 2;
+      const int lo = sub * q, hi = min(lo + q, ce);
+      const float* row = stage + tl * (kTopkChunk + 1);
+      for (int c = lo; c < hi; ++c) {
+        float v = row[c];
+        if (v != v) v = -INFINITY;
+        // position = number of kept experts that stay ahead of this one
+        int p = 0;
+#pragma unroll
+        for (int i = 0; i < KMAX; ++i)
+          if (i < k) p += (idx[i] >= 0 && val[i] >= v) ? 1 : 0;
+        if (p < k) {
+#pragma unroll
+          for (int i = KMAX - 1; i > 0; --i) {
+            if (i < k && i > p) {
+              val[i] = val[i - 1];
+              idx[i] = idx[i - 1];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < KMAX; ++i) {
+            if (i == p) {
+              val[i] = v;
+              idx[i] = c0 + c;
+            }
           }
         }
-#pragma unroll
-        for (int i = 0; i < KMAX; ++i) {
-          if (i == p) {
-            val[i] = v;
-            idx[i] = e;
-          }
-        }
       }
     }
-    // softmax over the kept logits (val[0] is the largest)
-    float m = val[0];
+  }
+  // merge the four lists: k rounds, each taking the best head of the four
+  float mv[KMAX];
+  int mi[KMAX];
+  int h = 0;  // next entry of this lane's own list
+#pragma unroll
+  for (int r = 0; r < KMAX; ++r) {
+    mv[r] = -INFINITY;
+    mi[r] = -1;
+    if (r < k) {
+      float bv = -INFINITY;
+      int bi = -1;
+#pragma unroll
+      for (int i = 0; i < KMAX; ++i)
+        if (i == h) {
+          bv = val[i];
+          bi = idx[i];
+        }
+      int bs = sub;
+#pragma unroll
+      for (int off = 1; off < 4; off <<= 1) {
+        const float ov = __shfl_xor(bv, off, 4);
+        const int oi = __shfl_xor(bi, off, 4);
+        const int os = __shfl_xor(bs, off, 4);
+        // (ov, oi) precedes (bv, bi): larger logit, then lower index; empty last
+        const bool take = oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi));
+        if (take) {
+          bv = ov;
+          bi = oi;
+          bs = os;
+        }
+      }
+      mv[r] = bv;
+      mi[r] = bi;
+      if (bs == sub) ++h;
+    }
+  }
+  if (tl < ntok && sub == 0) {
+    const int t = tbase + tl;
+    // softmax over the kept logits (mv[0] is the largest)
+    const float m = mv[0];
     float z = 0.f;
     float ex[KMAX];
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
-      ex[i] = (i < k) ? expf(val[i] - m) : 0.f;
+      ex[i] = (i < k) ? expf(mv[i] - m) : 0.f;
       z += ex[i];
     }
     const float inv = 1.0f / z;
 #pragma unroll
     for (int i = 0; i < KMAX; ++i) {
       if (i < k) {
-        topk_idx[(size_t)t * k + i] = idx[i];
+        topk_idx[(size_t)t * k + i] = mi[i];
         gates[(size_t)t * k + i] = ex[i] * inv;
-        atomicAdd(&hist[idx[i]], 1);
+        atomicAdd(&hist[mi[i]], 1);
       }
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x)
+  for (int e = tid; e < E; e += kTopkThreads)
     block_counts[(size_t)e * nblk + blockIdx.x] = hist[e];
 }
 
@@ -200,35 +274,39 @@ __global__ void __launch_bounds__(256) expert_scan_kernel(int32_t* __restrict__ 
 }
 
 // Offsets (exclusive scan over experts, recomputed by every block from the
-// counts) and the stable ranks: the row of (t,j) with e = topk[t,j] is
-// offsets[e] + (rows of e in earlier blocks) + (earlier tokens of this block
-// that chose e).  Experts within a token are distinct, so only earlier tokens
-// matter.
+// counts with a wave scan) and the stable ranks: the row of (t,j) with
+// e = topk[t,j] is offsets[e] + (rows of e in earlier blocks) + (earlier
+// tokens of this block that chose e).  Experts within a token are distinct,
+// so only earlier tokens matter.
 template <int KMAX>
 __global__ void __launch_bounds__(kTokBlock) rank_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ block_counts, int nblk,
     const int32_t* __restrict__ counts, int T_, int E, int k, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_of, int32_t* __restrict__ src_tk) {
-  __shared__ int sh[256];
   __shared__ int offs[1025];
   __shared__ int sel[kTokBlock * KMAX];
   const int tid = threadIdx.x;
-  // offsets: each thread owns up to 4 consecutive experts
-  int c[4];
+  // offsets: each lane owns `per` consecutive experts (per <= 16)
+  const int per = (E + kTokBlock - 1) / kTokBlock;
   int local = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int e = tid * 4 + q;
-    c[q] = e < E ? counts[e] : 0;
-    local += c[q];
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) local += counts[e];
   }
-  int total;
-  int run = block_exclusive_scan(local, sh, &total);
+  int incl = local;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    int e = tid * 4 + q;
-    if (e < E) offs[e] = run;
-    run += c[q];
+  for (int off = 1; off < kTokBlock; off <<= 1) {
+    const int y = __shfl_up(incl, off, kTokBlock);
+    if (tid >= off) incl += y;
+  }
+  const int total = __shfl(incl, kTokBlock - 1, kTokBlock);
+  int run = incl - local;
+  for (int q = 0; q < per; ++q) {
+    const int e = tid * per + q;
+    if (e < E) {
+      offs[e] = run;
+      run += counts[e];
+    }
   }
   if (tid == 0) offs[E] = total;
   const int tbase = blockIdx.x * kTokBlock;
@@ -239,7 +317,7 @@ __global__ void __launch_bounds__(kTokBlock) rank_kernel(
     if (j < k) sel[tid * KMAX + j] = (tid < ntok) ? topk_idx[(size_t)t * k + j] : -1;
   __syncthreads();
   if (blockIdx.x == 0)
-    for (int e = tid; e <= E; e += blockDim.x) offsets[e] = offs[e];
+    for (int e = tid; e <= E; e += kTokBlock) offsets[e] = offs[e];
   if (tid >= ntok) return;
   int mine[KMAX], rank[KMAX];
 #pragma unroll
@@ -251,7 +329,7 @@ __global__ void __launch_bounds__(kTokBlock) rank_kernel(
 #pragma unroll
     for (int jp = 0; jp < KMAX; ++jp) {
       if (jp < k) {
-        int o = sel[tp * KMAX + jp];
+        const int o = sel[tp * KMAX + jp];
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) rank[j] += (o == mine[j]) ? 1 : 0;
       }
@@ -276,8 +354,8 @@ void launch_route(const float* logits, int T_, int E, int k, int32_t* topk_idx, 
   hipStream_t s = ctx->stream;
   {
     moe_prof_scope ps(ctx, MOE_K_TOPK);
-    topk_hist_kernel<KMAX><<<nblk, kTokBlock, 0, s>>>(logits, T_, E, k, topk_idx, gates,
-                                                      block_counts, nblk);
+    topk_hist_kernel<KMAX><<<nblk, kTopkThreads, 0, s>>>(logits, T_, E, k, topk_idx, gates,
+                                                         block_counts, nblk);
   }
   {
     moe_prof_scope ps(ctx, MOE_K_SCAN);
@@ -305,48 +383,63 @@ __global__ void route_bwd_kernel(const float* __restrict__ gates, const float* _
   for (int j = 0; j < k; ++j) dls[(size_t)t * k + j] = g[j] * (dg[j] - s);
 }
 
-// Router weight gradient.  One block per (expert, 64-feature chunk): the
-// block's row groups walk the expert's rows (fixed stride), each lane
-// accumulating a 16-byte chunk of features in fp32; the row groups are then
-// summed in a fixed order, so the result is deterministic.
+// Router weight gradient.  One block per (expert, 64*V-feature chunk), V
+// features (16 bytes) per lane: wave w walks the expert's rows r0+w, r0+w+4,
+// ... with eight independent row gathers in flight per step, accumulating in
+// fp32 in row order; the four waves are then summed in a fixed order, so the
+// result is deterministic.
 template <typename T>
 __global__ void __launch_bounds__(256) router_wgrad_kernel(
     const T* __restrict__ x, const float* __restrict__ dls, const int32_t* __restrict__ src_tk,
     const int32_t* __restrict__ offsets, int d, int E, int k, T* __restrict__ dwr) {
-  constexpr int V = 16 / sizeof(T);       // features per lane
-  constexpr int LPR = 64 / V;             // lanes per 64-feature row chunk
-  constexpr int NG = 256 / LPR;           // row groups
-  __shared__ float part[NG][64];
+  constexpr int V = 16 / sizeof(T);  // features per lane
+  constexpr int FC = 64 * V;         // features per block
+  constexpr int U = 8;               // rows in flight per wave
+  __shared__ float part[4][FC];
   const int e = blockIdx.y;
-  const int f0 = blockIdx.x * 64;
-  const int lane = threadIdx.x % LPR;
-  const int grp = threadIdx.x / LPR;
+  const int f0 = blockIdx.x * FC;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
   const int r0 = offsets[e], r1 = offsets[e + 1];
   float acc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.f;
   const int fi = f0 + lane * V;
-  if (fi < d) {
-    for (int r = r0 + grp; r < r1; r += NG) {
-      const int flat = src_tk[r];
-      const float w = dls[flat];
-      const T* xr = x + (size_t)(flat / k) * d + fi;
-      const uint4 raw = *reinterpret_cast<const uint4*>(xr);
+  if (fi < d) {  // d % 8 == 0: a lane's 16-byte chunk is wholly inside or outside
+    auto add = [&](float wt, const uint4& raw) {
       const T* xv = reinterpret_cast<const T*>(&raw);
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] += w * Elem<T>::ld(xv, v);
+      for (int v = 0; v < V; ++v) acc[v] += wt * Elem<T>::ld(xv, v);
+    };
+    int r = r0 + w;
+    for (; r + 4 * (U - 1) < r1; r += 4 * U) {
+      int flat[U];
+      float wt[U];
+      uint4 raw[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) flat[j] = src_tk[r + 4 * j];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        wt[j] = dls[flat[j]];
+        raw[j] = *reinterpret_cast<const uint4*>(x + (size_t)(flat[j] / k) * d + fi);
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) add(wt[j], raw[j]);
+    }
+    for (; r < r1; r += 4) {
+      const int flat = src_tk[r];
+      add(dls[flat], *reinterpret_cast<const uint4*>(x + (size_t)(flat / k) * d + fi));
     }
   }
 #pragma unroll
-  for (int v = 0; v < V; ++v) part[grp][lane * V + v] = acc[v];
+  for (int v = 0; v < V; ++v) part[w][lane * V + v] = acc[v];
   __syncthreads();
-  if (threadIdx.x < 64) {
-    const int f = f0 + threadIdx.x;
-    float s = 0.f;
-    for (int g = 0; g < NG; ++g) s += part[g][threadIdx.x];
-    if (f < d) Elem<T>::st(dwr, (size_t)f * E + e, s);
+  for (int f = threadIdx.x; f < FC; f += 256) {
+    const float s = ((part[0][f] + part[1][f]) + part[2][f]) + part[3][f];
+    if (f0 + f < d) Elem<T>::st(dwr, (size_t)(f0 + f) * E + e, s);
   }
 }
+
 
 }  // namespace
 
@@ -486,7 +579,8 @@ moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_se
   MOE_REQUIRE_PTR(ctx, src_tk);
   MOE_REQUIRE_PTR(ctx, offsets);
   MOE_REQUIRE_PTR(ctx, dw_router);
-  dim3 grid((d + 63) / 64, E);
+  const int fc = dtype == MOE_BF16 ? 512 : 256;  // features per block (64 lanes x 16 bytes)
+  dim3 grid((d + fc - 1) / fc, E);
   moe_prof_scope ps(ctx, MOE_K_ROUTER_WGRAD);
   if (dtype == MOE_BF16)
     router_wgrad_kernel<bf16_t><<<grid, 256, 0, ctx->stream>>>(

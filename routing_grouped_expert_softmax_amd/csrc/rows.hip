@@ -47,12 +47,17 @@ __device__ __forceinline__ uint4 pack(const float (&f)[4], float) {
 }
 
 constexpr int kWaves = 4;  // waves per block; one token per wave at a time
+// Chunks per lane loaded before any is used: every gather of a token (CPL
+// chunks of each of its k rows) is in flight at once.
+template <int KMAX>
+constexpr int chunks_per_lane() { return KMAX >= 16 ? 1 : 16 / KMAX; }
 
 // xp[row_of[t,j]] = x[t]: read each token row once, write its k copies.
 template <int KMAX>
 __global__ void __launch_bounds__(256) permute_kernel(const uint4* __restrict__ x,
                                                       const int32_t* __restrict__ row_of, int T_,
                                                       int nchunk, int k, uint4* __restrict__ xp) {
+  constexpr int CPL = 8;
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int nw = gridDim.x * kWaves;
@@ -61,11 +66,20 @@ __global__ void __launch_bounds__(256) permute_kernel(const uint4* __restrict__ 
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) rows[j] = j < k ? row_of[(size_t)t * k + j] : 0;
     const uint4* src = x + (size_t)t * nchunk;
-    for (int c = lane; c < nchunk; c += 64) {
-      const uint4 v = src[c];
+    for (int cb = lane; cb < nchunk; cb += 64 * CPL) {
+      uint4 v[CPL];
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j)
-        if (j < k) xp[(size_t)rows[j] * nchunk + c] = v;
+      for (int u = 0; u < CPL; ++u)
+        v[u] = cb + 64 * u < nchunk ? src[cb + 64 * u] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int c = cb + 64 * u;
+        if (c < nchunk) {
+#pragma unroll
+          for (int j = 0; j < KMAX; ++j)
+            if (j < k) xp[(size_t)rows[j] * nchunk + c] = v[u];
+        }
+      }
     }
   }
 }
@@ -77,6 +91,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ 
                                                       const int32_t* __restrict__ row_of, int T_,
                                                       int nchunk, int k, uint4* __restrict__ y) {
   constexpr int V = Vec<T>::N;
+  constexpr int CPL = chunks_per_lane<KMAX>();
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int nw = gridDim.x * kWaves;
@@ -88,32 +103,45 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ 
       rows[j] = j < k ? row_of[(size_t)t * k + j] : 0;
       g[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
     }
-    for (int c = lane; c < nchunk; c += 64) {
-      float acc[V];
+    for (int cb = lane; cb < nchunk; cb += 64 * CPL) {
+      uint4 raw[CPL][KMAX];
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+      for (int u = 0; u < CPL; ++u)
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (j < k) {
-          float f[V];
-          unpack(yp[(size_t)rows[j] * nchunk + c], f, T());
+        for (int j = 0; j < KMAX; ++j)
+          if (j < k && cb + 64 * u < nchunk) raw[u][j] = yp[(size_t)rows[j] * nchunk + cb + 64 * u];
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] += g[j] * f[i];
+      for (int u = 0; u < CPL; ++u) {
+        const int c = cb + 64 * u;
+        if (c >= nchunk) continue;
+        float acc[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (j < k) {
+            float f[V];
+            unpack(raw[u][j], f, T());
+#pragma unroll
+            for (int i = 0; i < V; ++i) acc[i] += g[j] * f[i];
+          }
         }
+        y[(size_t)t * nchunk + c] = pack(acc, T());
       }
-      y[(size_t)t * nchunk + c] = pack(acc, T());
     }
   }
 }
 
 // dyp[row_of[t,j]] = gates[t,j] * dy[t];  dgates[t,j] = <dy[t], yp[row_of[t,j]]>.
-// The dot products are lane partials reduced across the wave in a fixed order.
+// The dot products are lane partials (chunk order) reduced across the wave in
+// a fixed order.
 template <typename T, int KMAX>
 __global__ void __launch_bounds__(256) combine_bwd_kernel(
     const uint4* __restrict__ dy, const uint4* __restrict__ yp, const float* __restrict__ gates,
     const int32_t* __restrict__ row_of, int T_, int nchunk, int k, uint4* __restrict__ dyp,
     float* __restrict__ dgates) {
   constexpr int V = Vec<T>::N;
+  constexpr int CPL = chunks_per_lane<KMAX>();
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
   const int nw = gridDim.x * kWaves;
@@ -126,20 +154,36 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(
       g[j] = j < k ? gates[(size_t)t * k + j] : 0.f;
       dot[j] = 0.f;
     }
-    for (int c = lane; c < nchunk; c += 64) {
-      float d[V];
-      unpack(dy[(size_t)t * nchunk + c], d, T());
+    for (int cb = lane; cb < nchunk; cb += 64 * CPL) {
+      uint4 draw[CPL], raw[CPL][KMAX];
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (j < k) {
-          float f[V], o[V];
-          unpack(yp[(size_t)rows[j] * nchunk + c], f, T());
+      for (int u = 0; u < CPL; ++u) {
+        const int c = cb + 64 * u;
+        if (c < nchunk) {
+          draw[u] = dy[(size_t)t * nchunk + c];
 #pragma unroll
-          for (int i = 0; i < V; ++i) {
-            dot[j] += d[i] * f[i];
-            o[i] = g[j] * d[i];
+          for (int j = 0; j < KMAX; ++j)
+            if (j < k) raw[u][j] = yp[(size_t)rows[j] * nchunk + c];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int c = cb + 64 * u;
+        if (c >= nchunk) continue;
+        float d[V];
+        unpack(draw[u], d, T());
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+          if (j < k) {
+            float f[V], o[V];
+            unpack(raw[u][j], f, T());
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+              dot[j] += d[i] * f[i];
+              o[i] = g[j] * d[i];
+            }
+            dyp[(size_t)rows[j] * nchunk + c] = pack(o, T());
           }
-          dyp[(size_t)rows[j] * nchunk + c] = pack(o, T());
         }
       }
     }
@@ -180,31 +224,51 @@ __global__ void __launch_bounds__(256) permute_bwd_kernel(
         w[j] = j < k ? dls[(size_t)t * k + j] : 0.f;
       }
     }
-    for (int c = lane; c < nchunk; c += 64) {
-      float acc[V];
+    constexpr int CPL = ROUTER ? (KMAX >= 8 ? 1 : 8 / KMAX) : chunks_per_lane<KMAX>();
+    for (int cb = lane; cb < nchunk; cb += 64 * CPL) {
+      uint4 raw[CPL][KMAX], wraw[CPL][ROUTER ? KMAX : 1];
 #pragma unroll
-      for (int i = 0; i < V; ++i) acc[i] = 0.f;
+      for (int u = 0; u < CPL; ++u) {
+        const int c = cb + 64 * u;
+        if (c < nchunk) {
 #pragma unroll
-      for (int j = 0; j < KMAX; ++j) {
-        if (j < k) {
-          float f[V];
-          unpack(dxp[(size_t)rows[j] * nchunk + c], f, T());
-#pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] += f[i];
+          for (int j = 0; j < KMAX; ++j) {
+            if (j < k) {
+              raw[u][j] = dxp[(size_t)rows[j] * nchunk + c];
+              if (ROUTER) wraw[u][ROUTER ? j : 0] = wrt[(size_t)ex[j] * nchunk + c];
+            }
+          }
         }
       }
-      if (ROUTER) {
+#pragma unroll
+      for (int u = 0; u < CPL; ++u) {
+        const int c = cb + 64 * u;
+        if (c >= nchunk) continue;
+        float acc[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = 0.f;
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
           if (j < k) {
             float f[V];
-            unpack(wrt[(size_t)ex[j] * nchunk + c], f, T());
+            unpack(raw[u][j], f, T());
 #pragma unroll
-            for (int i = 0; i < V; ++i) acc[i] += w[j] * f[i];
+            for (int i = 0; i < V; ++i) acc[i] += f[i];
           }
         }
+        if (ROUTER) {
+#pragma unroll
+          for (int j = 0; j < KMAX; ++j) {
+            if (j < k) {
+              float f[V];
+              unpack(wraw[u][ROUTER ? j : 0], f, T());
+#pragma unroll
+              for (int i = 0; i < V; ++i) acc[i] += w[j] * f[i];
+            }
+          }
+        }
+        dx[(size_t)t * nchunk + c] = pack(acc, T());
       }
-      dx[(size_t)t * nchunk + c] = pack(acc, T());
     }
   }
 }
