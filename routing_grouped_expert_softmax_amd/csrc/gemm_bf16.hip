@@ -33,6 +33,7 @@
 //    writes zeros.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -128,14 +129,32 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   // ---------------------------------------------------------------- work
+  // Logical tiles are split into eight contiguous ranges, one per XCD (block
+  // b runs on XCD b % 8), so the blocks of one XCD share operands in its L2.
+  // A block takes tiles slot, slot + nslot, ... of its XCD's range: one tile
+  // when the grid covers every tile, several when the grid is one resident
+  // set of blocks (then each tile's output stores drain while the next tile
+  // loads instead of at block exit).
+  MTileSched<BM> ms;
+  int total;
+  if (TR::kKRAGGED) {
+    total = p.E * p.ntiles * p.mtiles;
+  } else if (TR::kSINGLE) {
+    total = ((p.M + BM - 1) / BM) * p.ntiles;
+  } else {
+    ms.init(p.E, p.offsets, p.ntiles, sh);
+    total = ms.total;
+  }
+  const int per_xcd = (total + 7) / 8;
+  const int nslot = gridDim.x >> 3;
+  for (int slot = blockIdx.x >> 3; slot < per_xcd; slot += nslot) {
+  const int L = (blockIdx.x & 7) * per_xcd + slot;
+  if (L >= total) break;
+  // the previous tile's epilogue has finished with the LDS stage buffers
+  if (slot != (int)(blockIdx.x >> 3)) lds_barrier();
   Work w;
   if (TR::kKRAGGED) {
-    // fixed grid: expert-major, then n-tile, then m-tile; XCD-contiguous
-    const int total = p.E * p.ntiles * p.mtiles;
-    const int per_xcd = (total + 7) / 8;
-    const int slot = blockIdx.x >> 3;
-    const int L = (blockIdx.x & 7) * per_xcd + slot;
-    if (slot >= per_xcd || L >= total) return;
+    // expert-major, then n-tile, then m-tile
     const int per_e = p.ntiles * p.mtiles;
     w.e = L / per_e;
     const int r = L % per_e;
@@ -145,18 +164,13 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
     w.rows = p.offsets[w.e + 1] - w.row0;
   } else if (TR::kSINGLE) {
     const int mt_total = (p.M + BM - 1) / BM;
-    const int total = mt_total * p.ntiles;
-    const int per_xcd = (total + 7) / 8;
-    const int slot = blockIdx.x >> 3;
-    const int L = (blockIdx.x & 7) * per_xcd + slot;
-    if (slot >= per_xcd || L >= total) return;
     w.e = 0;
     w.nt = L / mt_total;
     w.row0 = (L % mt_total) * BM;
     w.rows = min(BM, p.M - w.row0);
     w.m0 = 0;
   } else {
-    if (!find_mtile<BM>(p.E, p.offsets, p.ntiles, sh, w)) return;
+    ms.lookup(L, p.offsets, sh, w);
   }
   const int nk = TR::kKRAGGED ? (w.rows + BK - 1) / BK : p.K / BK;
 
@@ -432,11 +446,36 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
   } else {
     store_tile_direct<MODE, BM, SM, false>(acc, ea, w, lane, wm, wn);
   }
+  }  // tiles of this block
 #endif
 }
 
+// GEMM_PERSIST=1 caps the grid at one resident set of blocks so each block
+// walks several tiles.  Measured neutral: the first K step of a block's next
+// tile waits on the vector-memory counter, which also counts the previous
+// tile's output stores, so they are not hidden.  Off by default.
+#ifndef GEMM_PERSIST
+#define GEMM_PERSIST 0
+#endif
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Launch with at most one resident set of blocks (OCC per CU): each block
+// then walks several tiles.  `blocks` is the tile bound of the launch.
 template <int MODE, int BM, int S, int BK, int OCC = 1>
 hipError_t launch(const Params& p, int blocks, hipStream_t s) {
+  if (GEMM_PERSIST) blocks = std::min(blocks, device_cus() / 8 * 8 * OCC);
   blocks = (blocks + 7) / 8 * 8;
   grouped_gemm_kernel<MODE, BM, S, BK, OCC><<<blocks, kThreads, 0, s>>>(p);
   return hipGetLastError();

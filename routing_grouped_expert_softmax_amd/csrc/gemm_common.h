@@ -50,6 +50,10 @@ struct Work {
 
 // Block-wide search of (expert, tile) for logical tile L in an M-ragged launch.
 // Returns false when L is past the real total.
+// Tile of a one-tile-per-block row-ragged launch: expert e owns
+// ceil(n_e / BM) * ntiles logical tiles (m-tile fastest, experts in order),
+// split into eight contiguous ranges, one per XCD.  Returns false for blocks
+// past the last tile.
 template <int BM>
 __device__ bool find_mtile(int E, const int32_t* offsets, int ntiles, int* sh, Work& w) {
   const int tid = threadIdx.x;
@@ -113,6 +117,77 @@ __device__ bool find_mtile(int E, const int32_t* offsets, int ntiles, int* sh, W
   w.m0 = 0;
   return true;
 }
+
+// Barrier without a memory fence: waits only for this wave's LDS traffic, so
+// output stores still in flight are not drained (a fence would wait for them).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Tile table of a row-ragged launch: expert e owns ceil(n_e / BM) * ntiles
+// logical tiles, m-tile fastest, experts in order.  Each thread keeps the
+// exclusive scan of the tile counts of its (up to four) experts.
+template <int BM>
+struct MTileSched {
+  int cnt[4], til[4];
+  int run;    // first logical tile of this thread's experts
+  int per;    // experts per thread
+  int total;  // tiles of the launch (block-uniform)
+  __device__ void init(int E, const int32_t* offsets, int ntiles, int* sh) {
+    const int tid = threadIdx.x;
+    per = (E + kThreads - 1) / kThreads;  // <= 4
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * per + q;
+      cnt[q] = 0;
+      til[q] = 0;
+      if (q < per && e < E) {
+        cnt[q] = offsets[e + 1] - offsets[e];
+        til[q] = ((cnt[q] + BM - 1) / BM) * ntiles;
+      }
+      local += til[q];
+    }
+    sh[tid] = local;
+    lds_barrier();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const int add = tid >= off ? sh[tid - off] : 0;
+      lds_barrier();
+      sh[tid] += add;
+      lds_barrier();
+    }
+    total = __builtin_amdgcn_readfirstlane(sh[kThreads - 1]);
+    run = sh[tid] - local;
+    lds_barrier();
+  }
+  // Work of logical tile L < total.  The owning thread publishes it through
+  // sh[kThreads..+2]; the caller keeps a barrier between one call's reads and
+  // the next call's write (every K step has one).
+  __device__ void lookup(int L, const int32_t* offsets, int* sh, Work& w) const {
+    const int tid = threadIdx.x;
+    int r = run;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * per + q;
+      if (q < per && til[q] > 0 && L >= r && L < r + til[q]) {
+        const int mt_e = (cnt[q] + BM - 1) / BM;
+        const int local_t = L - r;
+        sh[kThreads] = e;
+        sh[kThreads + 1] = local_t % mt_e;  // m-tile
+        sh[kThreads + 2] = local_t / mt_e;  // n-tile
+      }
+      r += til[q];
+    }
+    lds_barrier();
+    // block-uniform values: keep them in scalar registers
+    const int e = __builtin_amdgcn_readfirstlane(sh[kThreads]);
+    const int mt = __builtin_amdgcn_readfirstlane(sh[kThreads + 1]);
+    w.e = e;
+    w.nt = __builtin_amdgcn_readfirstlane(sh[kThreads + 2]);
+    const int beg = offsets[e], end = offsets[e + 1];
+    w.row0 = beg + mt * BM;
+    w.rows = min(BM, end - w.row0);
+    w.m0 = 0;
+  }
+};
 
 
 // Raw buffer descriptor (V#) of `bytes` bytes at `base`: dword0/1 base address
