@@ -129,32 +129,40 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   // ---------------------------------------------------------------- work
-  // Logical tiles are split into eight contiguous ranges, one per XCD (block
-  // b runs on XCD b % 8), so the blocks of one XCD share operands in its L2.
-  // A block takes tiles slot, slot + nslot, ... of its XCD's range: one tile
-  // when the grid covers every tile, several when the grid is one resident
-  // set of blocks (then each tile's output stores drain while the next tile
-  // loads instead of at block exit).
+  // Logical tiles are split into eight contiguous ranges of equal tile count,
+  // one per XCD (block b runs on XCD b % 8), so the blocks of one XCD share
+  // operands in its L2.  Block b takes tiles first + b / 8, + nslot, ... of
+  // its XCD's range.
   MTileSched<BM> ms;
-  int total;
+  int first, end;  // this XCD's range of logical tiles
   if (TR::kKRAGGED) {
-    total = p.E * p.ntiles * p.mtiles;
-  } else if (TR::kSINGLE) {
-    total = ((p.M + BM - 1) / BM) * p.ntiles;
+    // equal tile counts per XCD: at the short K of a uniformly loaded layer
+    // (a few hundred rows per expert) computing cost-balanced ranges in every
+    // block costs more than the imbalance they remove
+    const int total = p.E * p.ntiles * p.mtiles;
+    const int per_xcd = (total + 7) / 8;
+    first = min((int)(blockIdx.x & 7) * per_xcd, total);
+    end = min(first + per_xcd, total);
   } else {
-    ms.init(p.E, p.offsets, p.ntiles, sh);
-    total = ms.total;
+    int total;
+    if (TR::kSINGLE) {
+      total = ((p.M + BM - 1) / BM) * p.ntiles;
+    } else {
+      ms.init(p.E, p.offsets, p.ntiles, sh);
+      total = ms.total;
+    }
+    const int per_xcd = (total + 7) / 8;
+    first = (blockIdx.x & 7) * per_xcd;
+    end = min(first + per_xcd, total);
   }
-  const int per_xcd = (total + 7) / 8;
   const int nslot = gridDim.x >> 3;
-  for (int slot = blockIdx.x >> 3; slot < per_xcd; slot += nslot) {
-  const int L = (blockIdx.x & 7) * per_xcd + slot;
-  if (L >= total) break;
+  const int L0 = first + (int)(blockIdx.x >> 3);
+  for (int L = L0; L < end; L += nslot) {
   // the previous tile's epilogue has finished with the LDS stage buffers
-  if (slot != (int)(blockIdx.x >> 3)) lds_barrier();
+  if (L != L0) lds_barrier();
   Work w;
   if (TR::kKRAGGED) {
-    // expert-major, then n-tile, then m-tile
+    // expert-major, then n-tile, then m-tile (m fastest)
     const int per_e = p.ntiles * p.mtiles;
     w.e = L / per_e;
     const int r = L % per_e;

@@ -122,6 +122,99 @@ __device__ bool find_mtile(int E, const int32_t* offsets, int ntiles, int* sh, W
 // output stores still in flight are not drained (a fence would wait for them).
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// XCD ranges of a K-ragged (wgrad) launch.  Every expert owns per_e output
+// tiles (expert-major order); a tile of expert e costs ceil(n_e / BK) + 2 K
+// steps (the 2 stand for its prologue and its stores), so the experts' costs
+// differ as much as their row counts.  XCD x takes the tiles whose cost
+// midpoint lies in [x C/8, (x+1) C/8), C the total cost: eight contiguous
+// ranges of nearly equal cost, so one hot expert's tiles spread over several
+// XCDs instead of loading one.  Sets [first, end) of this block's XCD; the
+// caller's blocks loop over ranges longer than their slots.
+template <int BK>
+__device__ void kragged_xcd_range(const int32_t* offsets, int E, int per_e, int xcd, int& first,
+                                  int& end) {
+  // every wave computes the same result with shuffles: no LDS, no barrier
+  const int lane = threadIdx.x & 63;
+  const int per = (E + 63) / 64;  // experts per lane (<= 16)
+  int cq[16];                     // K-step cost of this lane's experts
+  long long local = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int e = lane * per + q;
+    cq[q] = (q < per && e < E) ? (offsets[e + 1] - offsets[e] + BK - 1) / BK + 2 : 0;
+    local += (long long)cq[q] * per_e;
+  }
+  long long incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  const long long C = __shfl(incl, 63, 64);
+  const long long P0 = incl - local;  // cost before this lane's first expert
+  // Equal tile counts per XCD fill a one-tile-per-block grid exactly; keep
+  // them unless their costs are more than 10% out of balance.  The cost of
+  // the tiles before tile t = e * per_e + j is P_e + j c_e; P_e and c_e come
+  // from the lane that owns expert e.
+  const int total = E * per_e, per_xcd = (total + 7) / 8;
+  auto cost_before = [&](int t) -> long long {
+    if (t >= total) return C;
+    const int e = t / per_e, j = t - e * per_e;
+    const int owner = e / per, qe = e - owner * per;
+    long long pe = P0;
+    int ce = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (q < qe) pe += (long long)cq[q] * per_e;
+      if (q == qe) ce = cq[q];
+    }
+    pe = __shfl(pe, owner, 64);
+    ce = __shfl(ce, owner, 64);
+    return pe + (long long)j * ce;
+  };
+  long long worst = 0;
+  for (int x = 0; x < 8; ++x) {
+    const long long cx =
+        cost_before(min((x + 1) * per_xcd, total)) - cost_before(min(x * per_xcd, total));
+    worst = cx > worst ? cx : worst;
+  }
+  // (worst and C are the same in every lane: make the branch wave-uniform)
+  if (__builtin_amdgcn_readfirstlane((int)(worst * 80 <= C * 11))) {  // worst <= 1.1 C / 8
+    first = __builtin_amdgcn_readfirstlane(min(xcd * per_xcd, total));
+    end = __builtin_amdgcn_readfirstlane(min(first + per_xcd, total));
+    return;
+  }
+  // Otherwise tile j of expert e goes to XCD floor(8 * mid / C), mid =
+  // P_e + (j + 1/2) c_e.  Counting the tiles below a boundary B in float is
+  // exact enough: every block evaluates the same expressions, so the ranges
+  // tile [0, E * per_e) without gaps or overlaps, and the count is monotone
+  // in B.
+  const float b0 = (float)C * (float)xcd * 0.125f, b1 = (float)C * (float)(xcd + 1) * 0.125f;
+  int n0 = 0, n1 = 0;
+  long long P = P0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    if (cq[q] > 0) {
+      const float pf = (float)P, cf = (float)cq[q];
+      auto below = [&](float b) -> int {
+        const float n = ceilf((b - pf) / cf - 0.5f);  // j < (B - P) / c - 1/2
+        return n <= 0.f ? 0 : (n >= (float)per_e ? per_e : (int)n);
+      };
+      n0 += below(b0);
+      n1 += xcd == 7 ? per_e : below(b1);
+      P += (long long)cq[q] * per_e;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    n0 += __shfl_xor(n0, off, 64);
+    n1 += __shfl_xor(n1, off, 64);
+  }
+  first = __builtin_amdgcn_readfirstlane(n0);
+  end = __builtin_amdgcn_readfirstlane(n1);
+}
+
+
 // Tile table of a row-ragged launch: expert e owns ceil(n_e / BM) * ntiles
 // logical tiles, m-tile fastest, experts in order.  Each thread keeps the
 // exclusive scan of the tile counts of its (up to four) experts.

@@ -24,6 +24,7 @@
 // K range starts at the exclusive scan of roundup(n_e, 128).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -103,14 +104,25 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_mx_kernel(MxParams p
   const int wv = __builtin_amdgcn_readfirstlane(wave);
 
   // ---------------------------------------------------------------- work
-  Work w;
+  // Row-ragged modes: one tile per block from eight equal-count XCD ranges.
+  // K-ragged modes: eight equal-cost XCD ranges (tiles cost as much as their
+  // expert's rows); block b takes tiles first + b / 8, + nslot, ... of its
+  // XCD's range.
+  Work w0;
+  int first = 0, end = 1, nslot = 1, L0 = 0;
+  if (TR::kKRAGGED) {
+    kragged_xcd_range<BK>(p.offsets, p.E, p.ntiles * p.mtiles, blockIdx.x & 7, first, end);
+    nslot = gridDim.x >> 3;
+    L0 = first + (int)(blockIdx.x >> 3);
+  } else {
+    if (!find_mtile<BM>(p.E, p.offsets, p.ntiles, sh, w0)) return;
+  }
+  for (int L = L0; L < end; L += nslot) {
+  Work w = w0;
   int kbase = 0;  // K-ragged: first K byte of the expert in the padded layout
   if (TR::kKRAGGED) {
-    const int total = p.E * p.ntiles * p.mtiles;
-    const int per_xcd = (total + 7) / 8;
-    const int slot = blockIdx.x >> 3;
-    const int L = (blockIdx.x & 7) * per_xcd + slot;
-    if (slot >= per_xcd || L >= total) return;
+    // the previous tile's epilogue has finished with the LDS stage buffers
+    if (L != L0) lds_barrier();
     const int per_e = p.ntiles * p.mtiles;
     w.e = L / per_e;
     const int r = L % per_e;
@@ -121,19 +133,18 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_mx_kernel(MxParams p
     for (int e = tid; e < w.e; e += kThreads)
       local += (p.offsets[e + 1] - p.offsets[e] + 127) / 128 * 128;
     sh[tid] = local;
-    __syncthreads();
+    lds_barrier();
     for (int off = 1; off < kThreads; off <<= 1) {
       const int add = tid >= off ? sh[tid - off] : 0;
-      __syncthreads();
+      lds_barrier();
       sh[tid] += add;
-      __syncthreads();
+      lds_barrier();
     }
     kbase = __builtin_amdgcn_readfirstlane(sh[kThreads - 1]);
+    lds_barrier();  // sh is rewritten by the next tile's scan
     const int n = p.offsets[w.e + 1] - p.offsets[w.e];
     w.row0 = kbase;
     w.rows = (n + 127) / 128 * 128;  // padded K of the expert (padding is zero)
-  } else {
-    if (!find_mtile<BM>(p.E, p.offsets, p.ntiles, sh, w)) return;
   }
   const int nk = TR::kKRAGGED ? w.rows / BK : p.K / BK;
 
@@ -350,6 +361,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_mx_kernel(MxParams p
                                                          : (LDS_AS unsigned char*)lds2) +
       (wave % PER) * REG;
   store_tile<MODE, BM, SM, true, CH>(acc, ea, wo, lane, wm, wn, wbuf);
+  }  // tiles of this block
 #endif
 }
 

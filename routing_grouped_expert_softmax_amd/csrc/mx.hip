@@ -14,7 +14,7 @@
 //    codes [cols][Kpad], scales [cols][Kpad/32], where group g owns K
 //    positions [P_g, P_g + roundup(n_g, 128)) and P is the exclusive scan of
 //    the padded group sizes (128-padding keeps every 4-block scale word
-//    aligned; padding blocks are zero).
+//    aligned; padding blocks are zero codes with scale byte 0).
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -94,43 +94,34 @@ __global__ void mx_rows_kernel(const uint4* __restrict__ src, long long nblocks,
   (void)bpr;
 }
 
-// Column blocks with groups.  Block (x = 256-column tile, y = logical row
-// block); each thread owns one column.  The (group, block-in-group) of y comes
+// Column blocks with groups.  Block (x = 256-column tile, y = 128-deep slice
+// of the padded K space).  The slice's 128 x 256 bf16 source tile is staged in
+// LDS with 16-byte row loads (sixteen in flight per thread); then each thread
+// walks one column of it: four 32-row blocks, one full 128-byte line of codes
+// and one 4-byte scale word.  Group g occupies padded K
+// [P_g, P_g + roundup(n_g, 128)), so a slice lies in exactly one group; its
+// rows past n_g are zeros (code 0, scale byte 0).  The slice's group comes
 // from a block-wide scan of the padded group sizes (groups from `offsets`, or
 // `urows` rows each when offsets is null).
 __global__ void __launch_bounds__(256) mx_cols_kernel(
     const bf16_t* __restrict__ src, int rows, int cols, const int32_t* __restrict__ offsets,
     int urows, int G, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad_ld) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * 256];
   __shared__ int sh[256 + 4];
   const int tid = threadIdx.x;
   const int per = (G + 255) / 256;
-  int nb[4], pb[4];  // 32-row blocks (data) and 128-row padded blocks per group
-  int local = 0, plocal = 0;
+  int ps[4];  // 128-row slices per group
+  int plocal = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int g = tid * per + q;
-    nb[q] = 0;
-    pb[q] = 0;
+    ps[q] = 0;
     if (q < per && g < G) {
       const int n = offsets ? offsets[g + 1] - offsets[g] : urows;
-      nb[q] = (n + 31) / 32;
-      pb[q] = (n + 127) / 128;
+      ps[q] = (n + 127) / 128;
     }
-    local += nb[q];
-    plocal += pb[q];
+    plocal += ps[q];
   }
-  // scan of data blocks (to find this y's group) and of padded blocks (K base)
-  sh[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
-  }
-  int run = sh[tid] - local;
-  const int total = sh[255];
-  __syncthreads();
   sh[tid] = plocal;
   __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {
@@ -140,6 +131,7 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(
     __syncthreads();
   }
   int prun = sh[tid] - plocal;
+  const int total = sh[255];
   __syncthreads();
   const int y = blockIdx.y;
   if (tid == 0) sh[256] = -1;
@@ -147,68 +139,77 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int g = tid * per + q;
-    if (q < per && g < G && y >= run && y < run + nb[q]) {
+    if (q < per && g < G && y >= prun && y < prun + ps[q]) {
       sh[256] = g;
-      sh[257] = y - run;   // block within the group
-      sh[258] = prun * 128;  // K base of the group
+      sh[257] = y - prun;  // slice within the group
     }
-    run += nb[q];
-    prun += pb[q];
+    prun += ps[q];
   }
   __syncthreads();
   if (y >= total || sh[256] < 0) return;
-  const int g = sh[256], blk = sh[257], kbase = sh[258];
+  const int g = sh[256], sl = sh[257];
   const int gstart = offsets ? offsets[g] : g * urows;
   const int gend = offsets ? offsets[g + 1] : (g + 1) * urows;
-  const int c = blockIdx.x * 256 + tid;
-  if (c >= cols) return;
-  const int r0 = gstart + blk * 32;
-  float f[32];
-  float amax = 0.f;
+  const int c0 = blockIdx.x * 256;
+  const int r0 = gstart + sl * 128;
+  const int nvalid = min(128, gend - r0);  // >= 1
+  // stage: chunk i = (row i / 32, 8 columns (i % 32) * 8), zeros outside
+  {
+    uint4 v[16];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const int r = r0 + i;
-    f[i] = (r < gend) ? __uint_as_float(((uint32_t)src[(size_t)r * cols + c]) << 16) : 0.f;
-    amax = fmaxf(amax, fabsf(f[i]));
-  }
-  const int sb = mx_scale_byte(amax);
-  const int s = sb - 127;
-  uint32_t out[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) word |= e4m3_code(ldexpf(f[q * 4 + j], -s)) << (8 * j);
-    out[q] = word;
-  }
-  const size_t k = (size_t)kbase + (size_t)blk * 32;
-  uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)c * kpad_ld + k);
-  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
-  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
-  scales[(size_t)c * (kpad_ld / 32) + k / 32] = (uint8_t)sb;
-  (void)rows;
-}
-
-// Zero the padding blocks of a column-quantised operand: for each group, the
-// K positions past its last 32-row block up to its 128 boundary.  One thread
-// per (column, group); only runs over groups whose size is not a multiple of
-// 128.
-__global__ void mx_cols_pad_kernel(const int32_t* __restrict__ offsets, int urows, int G, int cols,
-                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                   int kpad_ld) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= cols) return;
-  int kbase = 0;
-  for (int g = 0; g < G; ++g) {
-    const int n = offsets ? offsets[g + 1] - offsets[g] : urows;
-    const int data = (n + 31) / 32 * 32, padded = (n + 127) / 128 * 128;
-    for (int k = kbase + data; k < kbase + padded; k += 32) {
-      uint4* dst = reinterpret_cast<uint4*>(codes + (size_t)c * kpad_ld + k);
-      dst[0] = make_uint4(0, 0, 0, 0);
-      dst[1] = make_uint4(0, 0, 0, 0);
-      scales[(size_t)c * (kpad_ld / 32) + k / 32] = 0;
+    for (int j = 0; j < 16; ++j) {
+      const int i = tid + 256 * j;
+      const int row = i >> 5, col = c0 + (i & 31) * 8;
+      v[j] = (row < nvalid && col < cols)
+                 ? *reinterpret_cast<const uint4*>(src + (size_t)(r0 + row) * cols + col)
+                 : make_uint4(0, 0, 0, 0);
     }
-    kbase += padded;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) reinterpret_cast<uint4*>(tile)[tid + 256 * j] = v[j];
+  }
+  __syncthreads();
+  const int c = c0 + tid;
+  uint32_t code_words[32];
+  uint32_t sword = 0;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    float f[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      f[i] = __uint_as_float(((uint32_t)tile[(blk * 32 + i) * 256 + tid]) << 16);
+      amax = fmaxf(amax, fabsf(f[i]));
+    }
+    const int sb = mx_scale_byte(amax);
+    const int s = sb - 127;
+    sword |= (uint32_t)sb << (8 * blk);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) word |= e4m3_code(ldexpf(f[q * 4 + j], -s)) << (8 * j);
+      code_words[blk * 8 + q] = word;
+    }
+  }
+  const size_t k = (size_t)y * 128;  // padded K position of the slice
+  if (c < cols) *reinterpret_cast<uint32_t*>(scales + (size_t)c * (kpad_ld / 32) + k / 32) = sword;
+  // codes go back through LDS (144-byte line pitch against bank conflicts) so
+  // that each store instruction writes eight whole 128-byte lines
+  constexpr int LP = 144;
+  __syncthreads();  // every column has been read out of the tile
+  unsigned char* lines = reinterpret_cast<unsigned char*>(tile);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    *reinterpret_cast<uint4*>(lines + tid * LP + 16 * i) =
+        make_uint4(code_words[4 * i], code_words[4 * i + 1], code_words[4 * i + 2],
+                   code_words[4 * i + 3]);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int piece = tid + 256 * j, line = piece >> 3, part = piece & 7;
+    if (c0 + line < cols)
+      *reinterpret_cast<uint4*>(codes + (size_t)(c0 + line) * kpad_ld + k + 16 * part) =
+          *reinterpret_cast<const uint4*>(lines + line * LP + 16 * part);
   }
 }
 
@@ -231,14 +232,11 @@ hipError_t mx_quantize_rows(const void* src, int rows, int cols, uint8_t* codes,
 hipError_t mx_quantize_cols(const void* src, int rows, int cols, const int32_t* offsets, int urows,
                             int groups, uint8_t* codes, uint8_t* scales, int kpad_ld,
                             hipStream_t s) {
-  const int yb = rows / 32 + groups + 1;
+  // bound on the padded slices: sum_g ceil(n_g / 128) <= rows / 128 + groups
+  const int yb = rows / 128 + groups + 1;
   dim3 grid((cols + 255) / 256, yb);
   mx_cols_kernel<<<grid, 256, 0, s>>>((const bf16_t*)src, rows, cols, offsets, urows, groups, codes,
                                       scales, kpad_ld);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  mx_cols_pad_kernel<<<(cols + 255) / 256, 256, 0, s>>>(offsets, urows, groups, cols, codes, scales,
-                                                        kpad_ld);
   return hipGetLastError();
 }
 
