@@ -336,8 +336,15 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
   struct Frags {
     bf16x8 xb[4], ya[SM];
   };
-  auto load_frags = [&](const LDS_AS unsigned char* As, int kk, Frags& f) {
+  // 32-row subtiles of this wave that hold at least one valid row: fewer
+  // than SM only in an expert's last row tile, whose empty subtiles then
+  // skip their fragment reads and MFMAs (wave-uniform branches, in a second
+  // copy of the loop so full tiles run branch-free).
+  const int nvsm = TR::kKRAGGED ? SM
+                                : max(0, min(SM, (w.rows - (wv >> 1) * TL::WM + 31) / 32));
+  auto load_frags = [&](const LDS_AS unsigned char* As, int kk, Frags& f, auto full) {
     const LDS_AS unsigned char* Bs = As + TL::A_BYTES;
+    if (!decltype(full)::value && nvsm == 0) return;
 #pragma unroll
     for (int sn = 0; sn < 4; ++sn) {
       if (TR::kB_KCONTIG) {
@@ -351,34 +358,37 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
     }
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm) {
+      if (!decltype(full)::value && sm >= nvsm) continue;
       if (TR::kA_KCONTIG)
         f.ya[sm] = frag_kc(As, wm * TL::WM + sm * 32, kk);
       else
         f.ya[sm] = frag_mn(As, TL::A_PITCH, wm * TL::WM + sm * 32, kk);
     }
   };
-  auto mma = [&](const Frags& f) {
+  auto mma = [&](const Frags& f, auto full) {
 #pragma unroll
-    for (int sm = 0; sm < SM; ++sm)
+    for (int sm = 0; sm < SM; ++sm) {
+      if (!decltype(full)::value && sm >= nvsm) continue;
 #pragma unroll
       for (int sn = 0; sn < 4; ++sn)
         acc[sm][sn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.xb[sn], f.ya[sm], acc[sm][sn], 0, 0, 0);
+    }
   };
   // One stage: the fragments of slice kk+1 are read while the MFMAs of slice
   // kk run (the compiler interleaves the two).
-  auto compute = [&](auto st) {
+  auto compute = [&](auto st, auto full) {
     const LDS_AS unsigned char* As = stage_ptr(st);
     Frags f0, f1;
-    load_frags(As, 0, f0);
-    load_frags(As, 1, f1);
-    mma(f0);
+    load_frags(As, 0, f0, full);
+    load_frags(As, 1, f1, full);
+    mma(f0, full);
     if constexpr (BK == 64) {
-      load_frags(As, 2, f0);
-      mma(f1);
-      load_frags(As, 3, f1);
-      mma(f0);
+      load_frags(As, 2, f0, full);
+      mma(f1, full);
+      load_frags(As, 3, f1, full);
+      mma(f0, full);
     }
-    mma(f1);
+    mma(f1, full);
   };
 
   // ---------------------------------------------------------------- main loop
@@ -397,7 +407,7 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
   // One K step on stage CUR, loading step kt+S-1 into stage NXT.  The wait
   // covers only this wave's loads of step kt (later steps stay in flight);
   // the barrier has no memory fence (a fence would drain every load).
-  auto step = [&](int kt, auto cur, auto nxt) {
+  auto step = [&](int kt, auto cur, auto nxt, auto full) {
     const int after = min(S - 2, nk - 1 - kt);  // stages issued after kt so far
     // vmcnt(n): simm16 = vmcnt[3:0] | expcnt(7)<<4 | lgkmcnt(15)<<8 | vmcnt[5:4]<<14
     if (S >= 4 && after >= 2)
@@ -408,34 +418,40 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
       __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
     asm volatile("s_barrier" ::: "memory");
     if (kt + S - 1 < nk) issue(kt + S - 1, nxt);
-    compute(cur);
+    compute(cur, full);
   };
-  int kt = 0;
-  if constexpr (S == 2) {
-    for (; kt + 1 < nk; kt += 2) {
-      step(kt, I0{}, I1{});
-      step(kt + 1, I1{}, I0{});
+  auto main_loop = [&](auto full) {
+    int kt = 0;
+    if constexpr (S == 2) {
+      for (; kt + 1 < nk; kt += 2) {
+        step(kt, I0{}, I1{}, full);
+        step(kt + 1, I1{}, I0{}, full);
+      }
+      if (kt < nk) step(kt, I0{}, I1{}, full);
+    } else if constexpr (S == 3) {
+      for (; kt + 2 < nk; kt += 3) {
+        step(kt, I0{}, I2{}, full);
+        step(kt + 1, I1{}, I0{}, full);
+        step(kt + 2, I2{}, I1{}, full);
+      }
+      if (kt < nk) step(kt, I0{}, I2{}, full);
+      if (kt + 1 < nk) step(kt + 1, I1{}, I0{}, full);
+    } else {
+      for (; kt + 3 < nk; kt += 4) {
+        step(kt, I0{}, I3{}, full);
+        step(kt + 1, I1{}, I0{}, full);
+        step(kt + 2, I2{}, I1{}, full);
+        step(kt + 3, I3{}, I2{}, full);
+      }
+      if (kt < nk) step(kt, I0{}, I3{}, full);
+      if (kt + 1 < nk) step(kt + 1, I1{}, I0{}, full);
+      if (kt + 2 < nk) step(kt + 2, I2{}, I1{}, full);
     }
-    if (kt < nk) step(kt, I0{}, I1{});
-  } else if constexpr (S == 3) {
-    for (; kt + 2 < nk; kt += 3) {
-      step(kt, I0{}, I2{});
-      step(kt + 1, I1{}, I0{});
-      step(kt + 2, I2{}, I1{});
-    }
-    if (kt < nk) step(kt, I0{}, I2{});
-    if (kt + 1 < nk) step(kt + 1, I1{}, I0{});
-  } else {
-    for (; kt + 3 < nk; kt += 4) {
-      step(kt, I0{}, I3{});
-      step(kt + 1, I1{}, I0{});
-      step(kt + 2, I2{}, I1{});
-      step(kt + 3, I3{}, I2{});
-    }
-    if (kt < nk) step(kt, I0{}, I3{});
-    if (kt + 1 < nk) step(kt + 1, I1{}, I0{});
-    if (kt + 2 < nk) step(kt + 2, I2{}, I1{});
-  }
+  };
+  if (TR::kKRAGGED || nvsm == SM)
+    main_loop(std::true_type{});
+  else
+    main_loop(std::false_type{});
   // all waves are done with the stage buffers before the block exits
   asm volatile("s_barrier" ::: "memory");
 
