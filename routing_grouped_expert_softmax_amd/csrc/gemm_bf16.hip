@@ -459,14 +459,15 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
   EpiArgs ea{p.c0, p.c1, p.c2, p.ldc, p.c_gstride, p.aux0, p.aux1, p.N, p.M};
   if constexpr (epi_staged<MODE>(TL::STAGE, S)) {
     constexpr int CH = epi_chunk<MODE>(TL::STAGE, S);
-    constexpr int REG = epi_region_bytes<MODE>(CH);
+    constexpr int NCS = epi_ncs<MODE>(TL::STAGE, S);
+    constexpr int REG = epi_region_bytes<MODE>(CH, NCS);
     constexpr int PER = TL::STAGE / REG;
     static_assert(S * PER >= 4, "epilogue staging regions do not fit the stage buffers");
     const int sel = wave / PER;
     LDS_AS unsigned char* wbuf =
         (sel == 0 ? (LDS_AS unsigned char*)lds0 : sel == 1 ? (LDS_AS unsigned char*)lds1
          : sel == 2 ? (LDS_AS unsigned char*)lds2 : (LDS_AS unsigned char*)lds3) + (wave % PER) * REG;
-    store_tile<MODE, BM, SM, false, CH>(acc, ea, w, lane, wm, wn, wbuf);
+    store_tile<MODE, BM, SM, false, CH, NCS>(acc, ea, w, lane, wm, wn, wbuf);
   } else {
     store_tile_direct<MODE, BM, SM, false>(acc, ea, w, lane, wm, wn);
   }
@@ -508,9 +509,9 @@ hipError_t launch(const Params& p, int blocks, hipStream_t s) {
 // Tile configurations: rows per tile, pipeline stages, K step, blocks per
 // CU.  Two resident blocks per CU (128x256 tiles, 32-deep K steps, 72 KiB of
 // LDS and at most 256 registers per wave) let one block's prologue, barriers
-// and output stores overlap the other block's MFMAs on the same SIMDs; the
-// down dgrad, whose epilogue also reads the saved g and u, keeps one block of
-// 128x256 tiles with 64-deep K steps.
+// and output stores overlap the other block's MFMAs on the same SIMDs.  (The
+// down dgrad's epilogue, which also streams the saved g and u, then stages
+// its columns in two passes to fit.)
 #ifndef GEMM_M_CFG
 #define GEMM_M_CFG 128, 3, 32, 2   // forward gate/up and down
 #endif
@@ -518,7 +519,7 @@ hipError_t launch(const Params& p, int blocks, hipStream_t s) {
 #define GEMM_DU_CFG 128, 2, 32, 2  // gate/up dgrad
 #endif
 #ifndef GEMM_DD_CFG
-#define GEMM_DD_CFG 128, 3, 64, 1  // down dgrad
+#define GEMM_DD_CFG 128, 3, 32, 2  // down dgrad
 #endif
 #ifndef GEMM_W_CFG
 #define GEMM_W_CFG 128, 3, 32, 2   // both wgrads

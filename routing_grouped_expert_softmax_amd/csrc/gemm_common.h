@@ -467,19 +467,31 @@ template <int MODE>
 constexpr int epi_nout() {
   return MODE == FWD_UP ? 3 : (Traits<MODE>::kDUAL || MODE == DGRAD_DOWN) ? 2 : 1;
 }
+// Staged row width: a wave's 128 output columns (64 per matrix in the dual
+// modes), or half of them per pass when the region must shrink (NCS = 2).
 template <int MODE>
-constexpr int epi_wno() { return Traits<MODE>::kDUAL ? 64 : 128; }
+constexpr int epi_wno(int ncs) { return Traits<MODE>::kDUAL ? 64 : 128 / ncs; }
 template <int MODE>
-constexpr int epi_region_bytes(int ch) { return epi_nout<MODE>() * ch * epi_wno<MODE>() * 2; }
-// Whether four wave regions of CH = 32 rows fit in the stage buffers.
-template <int MODE>
-constexpr bool epi_staged(int stage_bytes, int stages) {
-  return MODE != ROUTER && stages * (stage_bytes / epi_region_bytes<MODE>(32)) >= 4;
+constexpr int epi_region_bytes(int ch, int ncs) {
+  return epi_nout<MODE>() * ch * epi_wno<MODE>(ncs) * 2;
 }
+// Column passes of the staged epilogue: 1 or 2 (whichever lets four wave
+// regions of 32 rows fit in the stage buffers), 0 = direct epilogue.
+template <int MODE>
+constexpr int epi_ncs(int stage_bytes, int stages) {
+  if (MODE == ROUTER) return 0;
+  if (stages * (stage_bytes / epi_region_bytes<MODE>(32, 1)) >= 4) return 1;
+  if (!Traits<MODE>::kDUAL && stages * (stage_bytes / epi_region_bytes<MODE>(32, 2)) >= 4) return 2;
+  return 0;
+}
+template <int MODE>
+constexpr bool epi_staged(int stage_bytes, int stages) { return epi_ncs<MODE>(stage_bytes, stages) > 0; }
 // Rows per chunk: 64 when four wave regions fit in the stage buffers, else 32.
 template <int MODE>
 constexpr int epi_chunk(int stage_bytes, int stages) {
-  return stages * (stage_bytes / epi_region_bytes<MODE>(64)) >= 4 ? 64 : 32;
+  return stages * (stage_bytes / epi_region_bytes<MODE>(64, epi_ncs<MODE>(stage_bytes, stages))) >= 4
+             ? 64
+             : 32;
 }
 
 // Stores one block tile.  Lane holds
@@ -487,8 +499,8 @@ constexpr int epi_chunk(int stage_bytes, int stages) {
 // 32x32 subtile; dual modes hold g (subtiles 0,1) and u (2,3) of the same
 // columns.  SWIGLU_FROM_BF16: the forward's h (and the dgrad's silu terms)
 // are computed from the bf16-rounded g and u instead of the fp32 sums.
-// wbuf: this wave's staging region, epi_region_bytes<MODE>(CH) bytes.
-template <int MODE, int BM, int SM, bool SWIGLU_FROM_BF16, int CH>
+// wbuf: this wave's staging region, epi_region_bytes<MODE>(CH, NCS) bytes.
+template <int MODE, int BM, int SM, bool SWIGLU_FROM_BF16, int CH, int NCS = 1>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const EpiArgs& a,
                                            const Work& w, int lane, int wm, int wn,
                                            LDS_AS unsigned char* wbuf) {
@@ -515,7 +527,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const Epi
     return;
   } else {
     constexpr bool DUAL = Traits<MODE>::kDUAL;
-    constexpr int WNO = epi_wno<MODE>();
+    static_assert(!DUAL || NCS == 1, "dual epilogues stage all columns at once");
+    constexpr int WNO = epi_wno<MODE>(NCS);
+    constexpr int SNH = 4 / NCS;        // 32-column subtiles per pass (non-dual)
     constexpr int NOUT = epi_nout<MODE>();
     constexpr int PITCH = WNO * 2;      // bytes per staged row
     constexpr int CPR = PITCH / 16;     // 16-byte chunks per row
@@ -523,7 +537,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const Epi
     constexpr int RPI = 1024 / PITCH;   // rows per wave-wide 16-byte access
     constexpr int SMC = CH / 32;
     static_assert(WM % CH == 0, "chunk must divide the wave tile");
-    const int col0 = DUAL ? w.nt * 128 + wn * 64 : w.nt * BN + wn * 128;
+    const int colw = DUAL ? w.nt * 128 + wn * 64 : w.nt * BN + wn * 128;  // wave's first column
     const size_t gbase = Traits<MODE>::kKRAGGED ? (size_t)w.e * a.c_gstride : 0;
     // staged byte offset of (row, 4-column group) in MFMA layout
     auto frag_off = [&](int row, int col) {
@@ -540,8 +554,11 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const Epi
       return mloc < w.rows;
     };
 #pragma unroll
-    for (int q = 0; q < WM / CH; ++q) {
+    for (int q = 0; q < WM / CH; ++q)
+#pragma unroll
+    for (int h = 0; h < NCS; ++h) {
       const int mbase = wm * WM + q * CH;  // first block-tile row of this chunk
+      const int col0 = colw + h * WNO;      // first column of this pass
       if (MODE == DGRAD_DOWN) {
         // saved g, u rows -> LDS (coalesced 16-byte loads)
 #pragma unroll
@@ -593,10 +610,11 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const Epi
             }
         } else {
 #pragma unroll
-          for (int sn = 0; sn < 4; ++sn)
+          for (int sn = 0; sn < 4; ++sn) {
+            if (sn / SNH != h) continue;
 #pragma unroll
             for (int g4 = 0; g4 < 4; ++g4) {
-              const int off = frag_off(row, sn * 32 + 8 * g4 + ncol4);
+              const int off = frag_off(row, (sn % SNH) * 32 + 8 * g4 + ncol4);
               float v[4];
 #pragma unroll
               for (int r = 0; r < 4; ++r) v[r] = acc[sm][sn][g4 * 4 + r];
@@ -619,6 +637,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const Epi
                 *reinterpret_cast<LDS_AS u32x2*>(wbuf + off) = bf4(v);
               }
             }
+          }
         }
       }
       asm volatile("" ::: "memory");

@@ -352,7 +352,8 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_mx_kernel(MxParams p
   Work wo = w;
   if (TR::kKRAGGED) wo.row0 = 0;  // outputs of wgrad are indexed by m0 + row
   constexpr int CH = epi_chunk<MODE>(TL::STAGE, S);
-  constexpr int REG = epi_region_bytes<MODE>(CH);
+  constexpr int NCS = epi_ncs<MODE>(TL::STAGE, S);
+  constexpr int REG = epi_region_bytes<MODE>(CH, NCS);
   constexpr int PER = TL::STAGE / REG;
   static_assert(S * PER >= 4, "epilogue staging regions do not fit the stage buffers");
   const int sel = wave / PER;
@@ -360,7 +361,7 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_mx_kernel(MxParams p
       (sel == 0 ? (LDS_AS unsigned char*)lds0 : sel == 1 ? (LDS_AS unsigned char*)lds1
                                                          : (LDS_AS unsigned char*)lds2) +
       (wave % PER) * REG;
-  store_tile<MODE, BM, SM, true, CH>(acc, ea, wo, lane, wm, wn, wbuf);
+  store_tile<MODE, BM, SM, true, CH, NCS>(acc, ea, wo, lane, wm, wn, wbuf);
   }  // tiles of this block
 #endif
 }
