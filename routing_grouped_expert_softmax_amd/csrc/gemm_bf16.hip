@@ -516,7 +516,7 @@ hipError_t launch(const Params& p, int blocks, hipStream_t s) {
 #define GEMM_M_CFG 128, 3, 32, 2   // forward gate/up and down
 #endif
 #ifndef GEMM_DU_CFG
-#define GEMM_DU_CFG 128, 2, 32, 2  // gate/up dgrad
+#define GEMM_DU_CFG 128, 3, 32, 2  // gate/up dgrad
 #endif
 #ifndef GEMM_DD_CFG
 #define GEMM_DD_CFG 128, 3, 32, 2  // down dgrad
