@@ -316,6 +316,74 @@ def router_wgrad(x, dlogits_sel, topk_idx, E):
     return dwr
 
 
+# ------------------------------------------------------------------ routing statistics
+# [P2] 2.2 (imbalance grows with the expert pool, so frameworks add a
+# load-balancing auxiliary loss), 4.2 (tokens per expert; twice the mean
+# flags imbalance), 4.3 (aux-loss weight, e.g. 0.001), 5.2 (tokens per
+# expert, mean top-1 probability, expert-gradient L2 norms); [P1] 四 (the
+# router supports load balancing) and the negative-results section (a
+# balance score can improve while the real load worsens, so the real counts
+# are always reported beside it).
+def router_probs(logits):
+    """p_t = softmax of token t's logits over all E experts, in fp64."""
+    lg = logits.astype(np.float64)
+    z = np.exp(lg - lg.max(axis=1, keepdims=True))
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def top1_expert(logits):
+    """Each token's expert with the largest logit, the lower index among
+    equal logits (the first slot of the top-k order)."""
+    lg = logits.astype(np.float32)
+    T = lg.shape[0]
+    out = np.empty(T, dtype=np.int32)
+    for t in range(T):
+        out[t] = int(np.flatnonzero(lg[t] == lg[t].max())[0])
+    return out
+
+
+def route_stats(logits, counts, k, alpha):
+    """Per-expert routing statistics and the switch-style balance loss.
+
+    prob_mean[e] = (1/T) sum_t p_te (the mean router probability);
+    top1_count[e] = tokens whose top-1 expert is e; top1_prob_mean[e] = their
+    mean top-1 probability (0 when there are none); with the load fraction
+    f_e = counts[e] / (T k), aux_loss = alpha * E * sum_e f_e * prob_mean[e]
+    (alpha exactly when load and probability are both uniform)."""
+    T, E = logits.shape
+    p = router_probs(logits)
+    t1 = top1_expert(logits)
+    prob_mean = p.sum(axis=0) / max(T, 1)
+    top1_count = np.bincount(t1, minlength=E).astype(np.int64)
+    top1_sum = np.zeros(E)
+    for t in range(T):
+        top1_sum[t1[t]] += p[t, t1[t]]
+    top1_prob_mean = np.where(top1_count > 0, top1_sum / np.maximum(top1_count, 1), 0.0)
+    f = counts.astype(np.float64) / max(T * k, 1)
+    aux = alpha * E * float((f * prob_mean).sum())
+    return dict(prob_mean=prob_mean, top1_count=top1_count, top1_prob_mean=top1_prob_mean,
+                aux_loss=aux)
+
+
+def aux_loss_bwd(logits, counts, k, alpha, dloss=1.0):
+    """Gradient of dloss * aux_loss with respect to every logit.  The load
+    fractions are counts (piecewise constant in the logits), so only the mean
+    probabilities carry gradient: with a_e = alpha * E * f_e / T,
+    dl[t, e] = dloss * p_te * (a_e - sum_i p_ti a_i)."""
+    T, E = logits.shape
+    p = router_probs(logits)
+    a = alpha * E * (counts.astype(np.float64) / max(T * k, 1)) / max(T, 1)
+    return dloss * p * (a[None, :] - (p * a[None, :]).sum(axis=1, keepdims=True))
+
+
+def expert_grad_norms(dw):
+    """L2 (Frobenius) norm of each expert's weight-gradient matrix dw[e],
+    from the stored values, accumulated in fp64."""
+    E = dw.shape[0]
+    v = dw.reshape(E, -1).astype(np.float64)
+    return np.sqrt((v * v).sum(axis=1))
+
+
 # ------------------------------------------------------------------ MXFP8
 def e4m3_encode(v):
     return lib().oracle_e4m3_encode(float(v))
