@@ -88,8 +88,9 @@ const char* moe_status_string(moe_status s);
 const char* moe_last_error(const moe_ctx* ctx);
 
 /* Device workspace needed by the calls that use it for a layer of this
- * shape: moe_route (per-block expert histograms) and moe_permute_bwd with
- * the router term (a transposed copy of W_r).  The calls run in stream order,
+ * shape: moe_route (per-block expert histograms), moe_permute_bwd with the
+ * router term (a transposed copy of W_r), moe_route_stats and
+ * moe_expert_grad_norms (partial sums).  The calls run in stream order,
  * so they share one region.  *bytes is a host output. */
 moe_status moe_workspace_size(moe_ctx* ctx, int T, int d, int E, int k, moe_dtype dtype,
                               size_t* bytes);
@@ -183,6 +184,48 @@ moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_se
                             const int32_t* src_tk, const int32_t* offsets, int T, int d, int E,
                             int k, moe_dtype dtype, void* dw_router);
 
+/* ------------------------------------------------- routing statistics
+ * [P2] 2.2: a larger expert pool amplifies load imbalance, so frameworks add
+ * a load-balancing auxiliary loss; [P2] 4.2: watch the tokens each expert
+ * receives (twice the mean flags imbalance); [P2] 4.3: the loss weight
+ * starts small (e.g. 0.001); [P2] 5.2: log tokens per expert, mean top-1
+ * probability and expert-gradient L2 norms; [P1] 四: the router supports load
+ * balancing, and [P1]'s negative results warn that a balance score can
+ * improve while the real load worsens, so report counts beside the loss.
+ * Every result is deterministic (fixed summation orders). */
+
+/* Per-expert statistics of one routing step and the switch-style balance
+ * loss.  With p_t = softmax over all E logits of token t and top-1 expert
+ * = the first selected slot (largest logit, lower index on ties):
+ *   prob_mean[e]      = (1/T) sum_t p_te                      fp32 [E]
+ *   top1_count[e]     = tokens whose top-1 expert is e        int32 [E]
+ *   top1_prob_mean[e] = their mean top-1 probability, 0 if none  fp32 [E]
+ *   aux_loss[0]       = alpha * E * sum_e (counts[e] / (T k)) * prob_mean[e]
+ * (alpha exactly at uniform load and probability).  counts are moe_route's
+ * [E] histogram.  Outputs are device arrays (aux_loss one float); T = 0
+ * gives zeros.  Needs the registered workspace (moe_workspace_size). */
+moe_status moe_route_stats(moe_ctx* ctx, const float* logits, const int32_t* counts, int T, int E,
+                           int k, float alpha, float* prob_mean, int32_t* top1_count,
+                           float* top1_prob_mean, float* aux_loss);
+
+/* Gradient of dloss * aux_loss with respect to every logit (dense [T,E]
+ * fp32, overwritten).  The load fractions counts[e]/(T k) are piecewise
+ * constant in the logits, so only the mean probabilities carry gradient:
+ *   dlogits[t,e] = dloss * p_te * (a_e - sum_i p_ti a_i),
+ *   a_e = alpha * E * counts[e] / (T^2 k).
+ * Every row sums to zero.  The selected-slot gradient of the gates
+ * (moe_route_bwd) is separate; the two add. */
+moe_status moe_aux_loss_bwd(moe_ctx* ctx, const float* logits, const int32_t* counts, int T, int E,
+                            int k, float alpha, float dloss, float* dlogits);
+
+/* L2 (Frobenius) norm of each expert's weight-gradient matrix: dw is
+ * [E, rows, cols] in dtype (MOE_BF16 or MOE_F32; cols % 8 == 0 for bf16,
+ * % 4 for fp32), norms[e] = sqrt(sum of squares) with fp32 accumulation in
+ * a fixed order.  Works for dWg, dWu ([E,d,F]) and dWd ([E,F,d]).  Needs
+ * the registered workspace (moe_workspace_size with this E). */
+moe_status moe_expert_grad_norms(moe_ctx* ctx, const void* dw, int E, int rows, int cols,
+                                 moe_dtype dtype, float* norms);
+
 /* ----------------------------------------------------------------- MXFP8
  * MX quantisation of a bf16 [rows, cols] matrix ([P1] 三: MXFP8).  Blocks of
  * 32 elements share the scale byte s + 127 with s = floor(log2(max |v|)) - 8
@@ -226,6 +269,9 @@ typedef enum {
   MOE_K_PERMUTE_BWD,       /* incl. the W_r transpose when the router term is on */
   MOE_K_ROUTER_WGRAD,
   MOE_K_MX_QUANT,          /* MXFP8 quantisation (moe_mx_quantize and the MX FFN) */
+  MOE_K_ROUTE_STATS,       /* routing statistics + balance loss */
+  MOE_K_AUX_BWD,           /* balance-loss logit gradient */
+  MOE_K_GRAD_NORMS,        /* per-expert weight-gradient norms */
   MOE_K_COUNT
 } moe_kernel_id;
 

@@ -29,6 +29,7 @@ class MoeError(RuntimeError):
 _lib = None
 _vp = ctypes.c_void_p
 _int = ctypes.c_int
+_flt = ctypes.c_float
 
 # name -> argument types after the context pointer
 _SIGS = {
@@ -44,6 +45,9 @@ _SIGS = {
     "moe_permute_bwd": [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
     "moe_router_wgrad": [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
     "moe_mx_quantize": [_vp, _int, _int, _int, _vp, _int, _vp, _vp, _int],
+    "moe_route_stats": [_vp, _vp, _int, _int, _int, _flt, _vp, _vp, _vp, _vp],
+    "moe_aux_loss_bwd": [_vp, _vp, _int, _int, _int, _flt, _flt, _vp],
+    "moe_expert_grad_norms": [_vp, _int, _int, _int, _int, _vp],
 }
 EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "moe_last_error",
            "moe_workspace_size", "moe_set_workspace", *_SIGS.keys(), "moe_profile_enable",
@@ -53,7 +57,7 @@ EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "
 KERNELS = ["router_logits", "topk_hist", "expert_scan", "rank", "permute", "gemm_up_swiglu",
            "gemm_down", "combine", "combine_bwd", "route_bwd", "gemm_dgrad_down_swiglu",
            "gemm_wgrad_down", "gemm_dgrad_up", "gemm_wgrad_up", "permute_bwd", "router_wgrad",
-           "mx_quantize"]
+           "mx_quantize", "route_stats", "aux_loss_bwd", "grad_norms"]
 
 
 def lib():
@@ -339,6 +343,47 @@ def moe_mx_quantize(src, axis, group_offsets=None, groups=1):
     context(dev.index).call("moe_mx_quantize", _p(src), rows, cols, axis, _p(group_offsets), groups,
                             _p(codes), _p(scales), kp)
     return codes, scales
+
+
+def moe_route_stats(logits, counts, k, alpha, out=None):
+    """Returns dict(prob_mean [E] fp32, top1_count [E] int32, top1_prob_mean
+    [E] fp32, aux_loss [1] fp32), all on the GPU."""
+    _need_cuda(logits, counts)
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        out = dict(prob_mean=torch.empty(E, dtype=torch.float32, device=dev),
+                   top1_count=torch.empty(E, dtype=torch.int32, device=dev),
+                   top1_prob_mean=torch.empty(E, dtype=torch.float32, device=dev),
+                   aux_loss=torch.empty(1, dtype=torch.float32, device=dev))
+    ctx = context(dev.index)
+    ctx.ensure_workspace(T, 8, E, min(k, E), MOE_F32)
+    ctx.call("moe_route_stats", _p(logits), _p(counts), T, E, k, float(alpha), _p(out["prob_mean"]),
+             _p(out["top1_count"]), _p(out["top1_prob_mean"]), _p(out["aux_loss"]))
+    return out
+
+
+def moe_aux_loss_bwd(logits, counts, k, alpha, dloss=1.0, dlogits=None):
+    """Dense [T,E] fp32 logit gradient of dloss * aux_loss."""
+    _need_cuda(logits, counts)
+    T, E = logits.shape
+    if dlogits is None:
+        dlogits = torch.empty(T, E, dtype=torch.float32, device=logits.device)
+    context(logits.device.index).call("moe_aux_loss_bwd", _p(logits), _p(counts), T, E, k, float(alpha),
+                                      float(dloss), _p(dlogits))
+    return dlogits
+
+
+def moe_expert_grad_norms(dw, norms=None):
+    """Per-expert L2 norms [E] fp32 of a [E, rows, cols] weight gradient."""
+    _need_cuda(dw)
+    E, rows, cols = dw.shape
+    if norms is None:
+        norms = torch.empty(E, dtype=torch.float32, device=dw.device)
+    ctx = context(dw.device.index)
+    ctx.ensure_workspace(1, 8, E, 1, MOE_F32)
+    ctx.call("moe_expert_grad_norms", _p(dw), E, rows, cols, _dt(dw), _p(norms))
+    return norms
 
 
 # ------------------------------------------------------------------ the layer

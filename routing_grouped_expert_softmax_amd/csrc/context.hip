@@ -59,7 +59,7 @@ const char* moe_kernel_name(int id) {
       "router_logits", "topk_hist", "expert_scan", "rank", "permute", "gemm_up_swiglu",
       "gemm_down", "combine", "combine_bwd", "route_bwd", "gemm_dgrad_down_swiglu",
       "gemm_wgrad_down", "gemm_dgrad_up", "gemm_wgrad_up", "permute_bwd", "router_wgrad",
-      "mx_quantize"};
+      "mx_quantize", "route_stats", "aux_loss_bwd", "grad_norms"};
   if (id < 0 || id >= MOE_K_COUNT) return "unknown";
   return names[id];
 }

@@ -456,6 +456,9 @@ size_t moe_internal_wrt_bytes(int d, int E, moe_dtype dt) {
   return ((size_t)d * E * esize(dt) + 255) & ~(size_t)255;
 }
 
+// Defined in stats.hip: workspace of the routing statistics and gradient norms.
+size_t moe_internal_stats_ws_bytes(int E);
+
 // Defined in gemm_bf16.hip: router scores through the MFMA GEMM.
 moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const void* wr, int T_,
                                            int d, int E, float* logits);
@@ -469,8 +472,9 @@ moe_status moe_workspace_size(moe_ctx* ctx, int T_, int d, int E, int k, moe_dty
   MOE_REQUIRE(ctx, bytes != nullptr, "bytes is null");
   MOE_REQUIRE(ctx, T_ >= 0 && d >= 8 && E >= 1 && E <= 1024 && k >= 1 && k <= E && k <= 32,
               "bad shape T=%d d=%d E=%d k=%d", T_, d, E, k);
-  const size_t a = route_ws_bytes(T_, E), b = moe_internal_wrt_bytes(d, E, dtype);
-  *bytes = a > b ? a : b;
+  const size_t a = route_ws_bytes(T_, E), b = moe_internal_wrt_bytes(d, E, dtype),
+               c = moe_internal_stats_ws_bytes(E);
+  *bytes = std::max(a, std::max(b, c));
   return MOE_OK;
 }
 
