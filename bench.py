@@ -15,10 +15,12 @@ HBM bytes per launch from the committed rocprofv3 counter summary when that
 was taken on the current kernel source.  `cpu_baseline` is the CPU oracle
 timed on a bounded sample of the same workload.
 
-Two more legs ride on the default run: `e_scaling` times the same layer at
-E=8 (learned-style routing) for the expert-count scaling loss, and `mxfp8`
-times the MXFP8 grouped experts (quantisation included) on 65536 pre-routed
-rows of a 16-expert, d_model 4096, d_ff 1536 share.
+More legs ride on the default run: `e_scaling` times the same layer at E=8
+(learned-style routing) for the expert-count scaling loss, `mxfp8` times the
+MXFP8 grouped experts (quantisation included) on 65536 pre-routed rows of a
+16-expert, d_model 4096, d_ff 1536 share, and `routing_stats` times the
+routing statistics, balance loss, its logit gradient and the per-expert
+weight-gradient norms on the layer's own buffers (outside the step).
 """
 from __future__ import annotations
 
@@ -163,8 +165,9 @@ def gemm_summary(prof, unit, peak):
     return roof, agg
 
 
-def layer_leg(cfg, steps, warmup, keep_inputs=False):
-    """Time the whole layer forward+backward on one workload."""
+def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False):
+    """Time the whole layer forward+backward on one workload (and, with
+    `with_stats`, the routing statistics on its last step's buffers)."""
     import torch
 
     import moe_inputs as mi
@@ -189,11 +192,61 @@ def layer_leg(cfg, steps, warmup, keep_inputs=False):
                tokens_per_s=cfg.T * steps / (gpu_ms / 1e3), ms_per_step=gpu_ms / steps,
                load={"max": int(counts.max()), "mean": float(counts.float().mean()),
                      "empty": int((counts == 0).sum())})
+    if with_stats:
+        out["routing_stats"] = stats_leg(ctx, cfg, override if override is not None else buf.logits,
+                                         buf, counts)
     if keep_inputs:
         out["inp"] = inp
     del g, buf, override
     torch.cuda.empty_cache()
     return out
+
+
+AUX_ALPHA = 0.001  # balance-loss weight (a small starting value)
+
+
+def stats_leg(ctx, cfg, logits, buf, counts, reps=20):
+    """Time the routing statistics + balance loss, its logit gradient and the
+    per-expert norms of the three expert weight gradients on the layer's own
+    buffers; report the loss beside the real load (a balance score alone can
+    hide a worsening load)."""
+    import torch
+
+    import routing_grouped_expert_softmax_amd as moe
+
+    T, E, k = cfg.T, cfg.E, cfg.k
+    r = buf.route
+    dl = torch.empty(T, E, dtype=torch.float32, device=logits.device)
+    norms = [torch.empty(E, dtype=torch.float32, device=logits.device) for _ in range(3)]
+    st = None
+    for it in range(reps + 2):
+        if it == 2:
+            torch.cuda.synchronize()
+            ctx.profile(True)
+        st = moe.moe_route_stats(logits, r["counts"], k, AUX_ALPHA, st)
+        moe.moe_aux_loss_bwd(logits, r["counts"], k, AUX_ALPHA, 1.0, dl)
+        for i, w in enumerate(("dw_gate", "dw_up", "dw_down")):
+            moe.moe_expert_grad_norms(buf.bwd[w], norms[i])
+    torch.cuda.synchronize()
+    ctx.profile(False)
+    prof = ctx.profile_results()
+    ms = {n: prof[n][1] / prof[n][0] for n in ("route_stats", "aux_loss_bwd", "grad_norms")}
+    esz = buf.bwd["dw_gate"].element_size()
+    nbytes = {"route_stats": T * E * 4, "aux_loss_bwd": T * E * 8, "grad_norms": E * cfg.d * cfg.F * esz}
+    t1 = st["top1_count"].cpu()
+    gn = torch.stack(norms).cpu()
+    return {
+        "alpha": AUX_ALPHA, "aux_loss": float(st["aux_loss"].item()),
+        "load_beside_loss": {"max": int(counts.max()), "mean": float(counts.float().mean()),
+                             "max_over_mean": round(float(counts.max()) / float(counts.float().mean()), 4),
+                             "top1_max": int(t1.max()),
+                             "mean_top1_prob": round(float((st["top1_prob_mean"].cpu() * t1).sum() / T), 6)},
+        "grad_norm_range": [round(float(gn.min()), 6), round(float(gn.max()), 6)],
+        "kernel_ms": {n: round(v, 4) for n, v in ms.items()},
+        "bytes_per_launch": nbytes,
+        "hbm": {n: {"GB/s": round(nbytes[n] / (ms[n] / 1e3) / 1e9, 1),
+                    "frac_hbm": round(nbytes[n] / (ms[n] / 1e3) / 1e9 / PEAK_HBM_GBS, 3)} for n in ms},
+    }
 
 
 def mx_leg(steps, warmup):
@@ -262,6 +315,8 @@ def main():
     ap.add_argument("--no-escaling", action="store_true",
                     help="skip the E=8 leg that gives the expert-count scaling loss")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 grouped-expert leg")
+    ap.add_argument("--no-stats", action="store_true",
+                    help="skip the routing-statistics / balance-loss / gradient-norm leg")
     ap.add_argument("--mx-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
@@ -281,7 +336,8 @@ def main():
         return
 
     cfg = mi.config(args.workload)
-    main_leg = layer_leg(cfg, args.steps, args.warmup, keep_inputs=args.cpu_sample > 0)
+    main_leg = layer_leg(cfg, args.steps, args.warmup, keep_inputs=args.cpu_sample > 0,
+                         with_stats=not args.no_stats)
     prof = main_leg["prof"]
     R = cfg.T * cfg.k
     unit = R * cfg.d * cfg.F
@@ -319,6 +375,8 @@ def main():
         "expert_load": main_leg["load"],
         "wall_s_timed": round(main_leg["wall"], 3),
     }
+    if "routing_stats" in main_leg:
+        result["routing_stats"] = main_leg["routing_stats"]
     if not args.no_escaling and cfg.name == "uniform128":
         base = layer_leg(mi.config("dense8"), args.steps, args.warmup)
         result["e_scaling"] = {

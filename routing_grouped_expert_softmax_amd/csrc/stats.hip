@@ -26,7 +26,9 @@ using namespace moe;
 namespace {
 
 constexpr int kStatBlocks = 256;      // most partial-sum blocks of one pass
-constexpr int kStatRowsInFlight = 4;  // token rows loaded at once per wave
+// token rows loaded at once per wave: 32 logits per lane in flight
+template <int EPL>
+constexpr int rows_in_flight() { return EPL >= 16 ? 2 : 32 / EPL > 16 ? 16 : 32 / EPL; }
 constexpr int kNormChunks = 256;      // most partial sums per expert (norms)
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -81,13 +83,14 @@ __device__ __forceinline__ void load_row(const float* __restrict__ row, int E, i
 // Pass 1 of the statistics: block b covers tokens [b*tpb, (b+1)*tpb), wave w
 // the tokens b*tpb + w, +4, ...  Per expert it sums the probabilities, the
 // top-1 probabilities and the top-1 counts of its tokens, and writes one
-// partial per block: part_p, part_s [nblk][E] fp32, part_c [nblk][E] int32.
+// partial per block, expert-major: part_p, part_s [E][kStatBlocks] fp32,
+// part_c [E][kStatBlocks] int32 (entry e * kStatBlocks + b).
 template <int EPL>
 __global__ void __launch_bounds__(256) stats_partial_kernel(const float* __restrict__ logits, int T_,
                                                             int E, int tpb, float* __restrict__ part_p,
                                                             float* __restrict__ part_s,
                                                             int32_t* __restrict__ part_c) {
-  constexpr int U = kStatRowsInFlight;
+  constexpr int U = rows_in_flight<EPL>();
   __shared__ float sp[4][EPL * 64], ss[4][EPL * 64];
   __shared__ int sc[4][EPL * 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -131,39 +134,55 @@ __global__ void __launch_bounds__(256) stats_partial_kernel(const float* __restr
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += 256) {
-    const size_t o = (size_t)blockIdx.x * E + e;
+    const size_t o = (size_t)e * kStatBlocks + blockIdx.x;
     part_p[o] = ((sp[0][e] + sp[1][e]) + sp[2][e]) + sp[3][e];
     part_s[o] = ((ss[0][e] + ss[1][e]) + ss[2][e]) + ss[3][e];
     part_c[o] = sc[0][e] + sc[1][e] + sc[2][e] + sc[3][e];
   }
 }
 
-// Pass 2: thread e adds expert e's partials in block order; the loss term
-// counts[e] * prob_mean[e] is summed over experts by a fixed tree.
-// scale = alpha * E / (T * k).
-__global__ void __launch_bounds__(1024) stats_final_kernel(
+// Pass 2: one wave per expert adds its nblk partials (lane l takes blocks
+// l, l+64, ... in order, then a butterfly), writes the statistics and the
+// loss term counts[e] * prob_mean[e] into term[e].
+__global__ void __launch_bounds__(256) stats_expert_kernel(
     const float* __restrict__ part_p, const float* __restrict__ part_s,
     const int32_t* __restrict__ part_c, int nblk, const int32_t* __restrict__ counts, int T_, int E,
-    float scale, float* __restrict__ prob_mean, int32_t* __restrict__ top1_count,
-    float* __restrict__ top1_prob_mean, float* __restrict__ aux_loss) {
-  __shared__ float red[1024];
-  const int e = threadIdx.x;
-  float term = 0.f;
-  if (e < E) {
-    float P = 0.f, S = 0.f;
-    int C = 0;
-    for (int b = 0; b < nblk; ++b) {
-      P += part_p[(size_t)b * E + e];
-      S += part_s[(size_t)b * E + e];
-      C += part_c[(size_t)b * E + e];
+    float* __restrict__ prob_mean, int32_t* __restrict__ top1_count,
+    float* __restrict__ top1_prob_mean, float* __restrict__ term) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (e >= E) return;
+  const size_t o = (size_t)e * kStatBlocks;
+  float P = 0.f, S = 0.f;
+  int C = 0;
+#pragma unroll
+  for (int j = 0; j < kStatBlocks / 64; ++j) {
+    const int b = lane + 64 * j;
+    if (b < nblk) {
+      P += part_p[o + b];
+      S += part_s[o + b];
+      C += part_c[o + b];
     }
+  }
+  P = wave_sum(P);
+  S = wave_sum(S);
+#pragma unroll
+  for (int off = 32; off; off >>= 1) C += __shfl_xor(C, off);
+  if (lane == 0) {
     const float pm = T_ > 0 ? P / (float)T_ : 0.f;
     prob_mean[e] = pm;
     top1_count[e] = C;
     top1_prob_mean[e] = C > 0 ? S / (float)C : 0.f;
-    term = (float)counts[e] * pm;
+    term[e] = (float)counts[e] * pm;
   }
-  red[e] = term;
+}
+
+// Pass 3: the loss, scale * sum_e term[e] by a fixed tree over experts
+// (scale = alpha * E / (T * k)).
+__global__ void __launch_bounds__(1024) stats_loss_kernel(const float* __restrict__ term, int E,
+                                                          float scale, float* __restrict__ aux_loss) {
+  __shared__ float red[1024];
+  const int e = threadIdx.x;
+  red[e] = e < E ? term[e] : 0.f;
   __syncthreads();
   for (int h = 512; h > 0; h >>= 1) {
     if (e < h) red[e] += red[e + h];
@@ -179,7 +198,7 @@ template <int EPL>
 __global__ void __launch_bounds__(256) aux_bwd_kernel(const float* __restrict__ logits,
                                                       const int32_t* __restrict__ counts, int T_,
                                                       int E, float coef, float* __restrict__ dl) {
-  constexpr int U = kStatRowsInFlight;
+  constexpr int U = rows_in_flight<EPL>();
   const int lane = threadIdx.x & 63;
   float a[EPL];
 #pragma unroll
@@ -266,10 +285,11 @@ int stat_tpb(int T_) {
 // ---------------------------------------------------------------- C ABI
 using namespace moe_host;
 
-// Workspace of moe_route_stats (three [256][E] partial arrays) and of
-// moe_expert_grad_norms ([E][256] partial sums); both fit in the larger.
+// Workspace of moe_route_stats (three [E][256] partial arrays and the [E]
+// loss terms) and of moe_expert_grad_norms ([E][256] partial sums); both fit
+// in the larger.
 size_t moe_internal_stats_ws_bytes(int E) {
-  const size_t a = (size_t)kStatBlocks * E * 12, b = (size_t)E * kNormChunks * 4;
+  const size_t a = (size_t)kStatBlocks * E * 12 + (size_t)E * 4, b = (size_t)E * kNormChunks * 4;
   return ((a > b ? a : b) + 255) & ~(size_t)255;
 }
 
@@ -314,14 +334,15 @@ moe_status moe_route_stats(moe_ctx* ctx, const float* logits, const int32_t* cou
   float* part_p = (float*)ctx->ws;
   float* part_s = part_p + (size_t)kStatBlocks * E;
   int32_t* part_c = (int32_t*)(part_s + (size_t)kStatBlocks * E);
+  float* term = (float*)(part_c + (size_t)kStatBlocks * E);
   const double scale = (double)alpha * E / ((double)std::max(T_, 1) * k);
   moe_prof_scope ps(ctx, MOE_K_ROUTE_STATS);
   if (nblk > 0)
     STATS_EPL_DISPATCH(E, (stats_partial_kernel<EPL><<<nblk, 256, 0, ctx->stream>>>(
                                logits, T_, E, tpb, part_p, part_s, part_c)));
-  stats_final_kernel<<<1, 1024, 0, ctx->stream>>>(part_p, part_s, part_c, nblk, counts, T_, E,
-                                                  (float)scale, prob_mean, top1_count,
-                                                  top1_prob_mean, aux_loss);
+  stats_expert_kernel<<<(E + 3) / 4, 256, 0, ctx->stream>>>(part_p, part_s, part_c, nblk, counts, T_, E,
+                                                            prob_mean, top1_count, top1_prob_mean, term);
+  stats_loss_kernel<<<1, 1024, 0, ctx->stream>>>(term, E, (float)scale, aux_loss);
   return check_launch(ctx, "moe_route_stats");
 }
 
