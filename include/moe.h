@@ -137,6 +137,24 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
                                int E, int R, int d, int F, moe_dtype dtype, void* g, void* u,
                                void* h, void* yp);
 
+/* Quantise-on-permute for the MXFP8 experts ([P1] 三: MXFP8, with the rows
+ * written straight into the experts' buffers, [P1] 二).  Each token row of x
+ * (bf16 [T,d], d % 32 == 0) is read once and quantised once along d exactly
+ * as moe_mx_quantize axis 0 does, and its codes ([T*k, d] uint8), scale
+ * bytes ([T*k, d/32] uint8) and, when xp is non-NULL, the bf16 row itself
+ * ([T*k, d]) are written into each of its k rows row_of[t,j].  Equal to
+ * moe_permute followed by moe_mx_quantize(axis 0) of xp, byte for byte. */
+moe_status moe_permute_mx(moe_ctx* ctx, const void* x, const int32_t* row_of, int T, int d, int k,
+                          void* xp, uint8_t* xp_codes, uint8_t* xp_scales);
+
+/* moe_grouped_ffn_fwd with MOE_MXFP8 on rows that are already quantised
+ * (moe_permute_mx): the same outputs, bit for bit, without quantising xp
+ * again.  Needs the MXFP8 workspace (moe_mx_workspace_size). */
+moe_status moe_grouped_ffn_fwd_mxq(moe_ctx* ctx, const uint8_t* xp_codes, const uint8_t* xp_scales,
+                                   const void* w_gate, const void* w_up, const void* w_down,
+                                   const int32_t* offsets, int E, int R, int d, int F, void* g,
+                                   void* u, void* h, void* yp);
+
 /* Gate-weighted unpermute-combine: y[t] = sum_j gates[t,j] * yp[row_of[t,j]],
  * summed in slot order in fp32, rounded once.  [P2] 2.1 (return and
  * restore). */

@@ -45,6 +45,8 @@ _SIGS = {
     "moe_permute_bwd": [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
     "moe_router_wgrad": [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
     "moe_mx_quantize": [_vp, _int, _int, _int, _vp, _int, _vp, _vp, _int],
+    "moe_permute_mx": [_vp, _vp, _int, _int, _int, _vp, _vp, _vp],
+    "moe_grouped_ffn_fwd_mxq": [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp, _vp, _vp, _vp],
     "moe_route_stats": [_vp, _vp, _int, _int, _int, _flt, _vp, _vp, _vp, _vp],
     "moe_aux_loss_bwd": [_vp, _vp, _int, _int, _int, _flt, _flt, _vp],
     "moe_expert_grad_norms": [_vp, _int, _int, _int, _int, _vp],
@@ -219,6 +221,42 @@ def moe_permute(x, row_of, xp=None):
         xp = torch.empty(T * k, d, dtype=x.dtype, device=x.device)
     context(x.device.index).call("moe_permute", _p(x), _p(row_of), T, d, k, _dt(x), _p(xp))
     return xp
+
+
+def moe_permute_mx(x, row_of, xp=None, codes=None, scales=None, with_bf16=True):
+    """Quantise-on-permute: returns (xp bf16 [T*k,d] or None, codes [T*k,d]
+    uint8, scales [T*k,d/32] uint8)."""
+    _need_cuda(x, row_of)
+    T, d = x.shape
+    k = row_of.shape[1]
+    dev = x.device
+    if with_bf16 and xp is None:
+        xp = torch.empty(T * k, d, dtype=x.dtype, device=dev)
+    if codes is None:
+        codes = torch.empty(T * k, d, dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(T * k, d // 32, dtype=torch.uint8, device=dev)
+    context(dev.index).call("moe_permute_mx", _p(x), _p(row_of), T, d, k, _p(xp if with_bf16 else None),
+                            _p(codes), _p(scales))
+    return xp if with_bf16 else None, codes, scales
+
+
+def moe_grouped_ffn_fwd_mxq(xp_codes, xp_scales, w_gate, w_up, w_down, offsets, out=None):
+    """MXFP8 grouped FFN forward on pre-quantised rows; returns dict(g, u, h, yp)."""
+    _need_cuda(xp_codes, xp_scales, w_gate, w_up, w_down, offsets)
+    R, d = xp_codes.shape
+    E, _, F = w_gate.shape
+    dev = xp_codes.device
+    context(dev.index).ensure_mx_workspace(E, R, d, F)
+    if out is None:
+        out = dict(g=torch.empty(R, F, dtype=w_gate.dtype, device=dev),
+                   u=torch.empty(R, F, dtype=w_gate.dtype, device=dev),
+                   h=torch.empty(R, F, dtype=w_gate.dtype, device=dev),
+                   yp=torch.empty(R, d, dtype=w_gate.dtype, device=dev))
+    context(dev.index).call("moe_grouped_ffn_fwd_mxq", _p(xp_codes), _p(xp_scales), _p(w_gate), _p(w_up),
+                            _p(w_down), _p(offsets), E, R, d, F, _p(out["g"]), _p(out["u"]), _p(out["h"]),
+                            _p(out["yp"]))
+    return out
 
 
 def moe_grouped_ffn_fwd(xp, w_gate, w_up, w_down, offsets, out=None, mxfp8=False):
@@ -401,9 +439,11 @@ class LayerBuffers:
     bwd: dict
     dx: torch.Tensor
     dw_router: torch.Tensor
+    xq: torch.Tensor | None = None  # MXFP8 codes of xp (quantise-on-permute)
+    xs: torch.Tensor | None = None  # their scale bytes
 
 
-def alloc_layer(T, d, E, k, F, dtype, device):
+def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False):
     dev = torch.device(device)
     R = T * k
     z = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
@@ -413,24 +453,36 @@ def alloc_layer(T, d, E, k, F, dtype, device):
     ffn = dict(g=z(R, F), u=z(R, F), h=z(R, F), yp=z(R, d))
     bwd = dict(dg=z(R, F), du=z(R, F), dxp=z(R, d), dw_gate=z(E, d, F), dw_up=z(E, d, F),
                dw_down=z(E, F, d))
-    return LayerBuffers(logits=z(T, E, dt=torch.float32), route=route, xp=z(R, d), ffn=ffn, y=z(T, d),
-                        dyp=z(R, d), dgates=z(T, k, dt=torch.float32),
-                        dlogits_sel=z(T, k, dt=torch.float32), bwd=bwd, dx=z(T, d), dw_router=z(d, E))
+    buf = LayerBuffers(logits=z(T, E, dt=torch.float32), route=route, xp=z(R, d), ffn=ffn, y=z(T, d),
+                       dyp=z(R, d), dgates=z(T, k, dt=torch.float32),
+                       dlogits_sel=z(T, k, dt=torch.float32), bwd=bwd, dx=z(T, d), dw_router=z(d, E))
+    if mxfp8:
+        buf.xq = z(R, d, dt=torch.uint8)
+        buf.xs = z(R, d // 32, dt=torch.uint8)
+        context(dev.index).ensure_mx_workspace(E, R, d, F)
+    return buf
 
 
-def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logits_override=None):
+def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logits_override=None,
+                  mxfp8=False):
     """Router scores -> route -> permute -> grouped SwiGLU experts -> combine.
     `logits_override` (optional [T,E] fp32 on the GPU) replaces the router
-    scores as the routing input after the router GEMM has run."""
+    scores as the routing input after the router GEMM has run.  mxfp8=True
+    (buffers from alloc_layer(..., mxfp8=True)) quantises on the permute and
+    runs the MXFP8 expert GEMMs."""
     moe_router_logits(x, w_router, buf.logits)
     moe_route(buf.logits if logits_override is None else logits_override, k, buf.route)
-    moe_permute(x, buf.route["row_of"], buf.xp)
-    moe_grouped_ffn_fwd(buf.xp, w_gate, w_up, w_down, buf.route["offsets"], buf.ffn)
+    if mxfp8:
+        moe_permute_mx(x, buf.route["row_of"], buf.xp, buf.xq, buf.xs)
+        moe_grouped_ffn_fwd_mxq(buf.xq, buf.xs, w_gate, w_up, w_down, buf.route["offsets"], buf.ffn)
+    else:
+        moe_permute(x, buf.route["row_of"], buf.xp)
+        moe_grouped_ffn_fwd(buf.xp, w_gate, w_up, w_down, buf.route["offsets"], buf.ffn)
     moe_combine(buf.ffn["yp"], buf.route["gates"], buf.route["row_of"], buf.y)
     return buf.y
 
 
-def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers):
+def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxfp8=False):
     """combine_bwd -> route_bwd -> grouped FFN bwd -> permute_bwd (+router
     dgrad) -> router wgrad.  Returns dx; weight grads are in buf.bwd and
     buf.dw_router."""
@@ -438,7 +490,7 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers):
     moe_combine_bwd(dy, buf.ffn["yp"], r["gates"], r["row_of"], buf.dyp, buf.dgates)
     moe_route_bwd(r["gates"], buf.dgates, buf.dlogits_sel)
     moe_grouped_ffn_bwd(buf.xp, w_gate, w_up, w_down, r["offsets"], buf.ffn["g"], buf.ffn["u"],
-                        buf.ffn["h"], buf.dyp, buf.bwd)
+                        buf.ffn["h"], buf.dyp, buf.bwd, mxfp8=mxfp8)
     moe_permute_bwd(buf.bwd["dxp"], r["row_of"], r["topk_idx"], buf.dlogits_sel, w_router, buf.dx)
     moe_router_wgrad(x, buf.dlogits_sel, r["src_tk"], r["offsets"], w_router.shape[1], buf.dw_router)
     return buf.dx

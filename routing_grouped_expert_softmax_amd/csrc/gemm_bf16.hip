@@ -590,10 +590,10 @@ moe_status moe_internal_ffn_bwd_f32(moe_ctx* ctx, const float* xp, const float* 
 // MXFP8 path (gemm_mx.hip)
 size_t moe_internal_mx_fwd_bytes(int E, int R, int d, int F);
 size_t moe_internal_mx_bwd_bytes(int E, int R, int d, int F);
-moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t* wg,
-                                   const bf16_t* wu, const bf16_t* wd, const int32_t* offsets,
-                                   int E, int R, int d, int F, bf16_t* g, bf16_t* u, bf16_t* h,
-                                   bf16_t* yp);
+moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const uint8_t* xq_in,
+                                   const uint8_t* xs_in, const bf16_t* wg, const bf16_t* wu,
+                                   const bf16_t* wd, const int32_t* offsets, int E, int R, int d,
+                                   int F, bf16_t* g, bf16_t* u, bf16_t* h, bf16_t* yp);
 moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t* wg,
                                    const bf16_t* wu, const bf16_t* wd, const int32_t* offsets,
                                    const bf16_t* g, const bf16_t* u, const bf16_t* h,
@@ -646,7 +646,7 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
   MOE_REQUIRE_PTR(ctx, yp);
   if (R == 0) return MOE_OK;
   if (dtype == MOE_MXFP8)
-    return moe_internal_ffn_fwd_mx(ctx, (const bf16_t*)xp, (const bf16_t*)w_gate,
+    return moe_internal_ffn_fwd_mx(ctx, (const bf16_t*)xp, nullptr, nullptr, (const bf16_t*)w_gate,
                                    (const bf16_t*)w_up, (const bf16_t*)w_down, offsets, E, R, d, F,
                                    (bf16_t*)g, (bf16_t*)u, (bf16_t*)h, (bf16_t*)yp);
   if (dtype == MOE_F32)
@@ -700,6 +700,29 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down GEMM: %s", hipGetErrorString(e));
   }
   return MOE_OK;
+}
+
+moe_status moe_grouped_ffn_fwd_mxq(moe_ctx* ctx, const uint8_t* xp_codes, const uint8_t* xp_scales,
+                                   const void* w_gate, const void* w_up, const void* w_down,
+                                   const int32_t* offsets, int E, int R, int d, int F, void* g,
+                                   void* u, void* h, void* yp) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = ffn_validate(ctx, E, R, d, F, MOE_MXFP8, "moe_grouped_ffn_fwd_mxq");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(ctx, xp_codes);
+  MOE_REQUIRE(ctx, xp_scales != nullptr, "moe_grouped_ffn_fwd_mxq: xp_scales is null");
+  MOE_REQUIRE_PTR(ctx, w_gate);
+  MOE_REQUIRE_PTR(ctx, w_up);
+  MOE_REQUIRE_PTR(ctx, w_down);
+  MOE_REQUIRE_PTR(ctx, offsets);
+  MOE_REQUIRE_PTR(ctx, g);
+  MOE_REQUIRE_PTR(ctx, u);
+  MOE_REQUIRE_PTR(ctx, h);
+  MOE_REQUIRE_PTR(ctx, yp);
+  if (R == 0) return MOE_OK;
+  return moe_internal_ffn_fwd_mx(ctx, nullptr, xp_codes, xp_scales, (const bf16_t*)w_gate,
+                                 (const bf16_t*)w_up, (const bf16_t*)w_down, offsets, E, R, d, F,
+                                 (bf16_t*)g, (bf16_t*)u, (bf16_t*)h, (bf16_t*)yp);
 }
 
 moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,

@@ -425,18 +425,20 @@ size_t moe_internal_mx_bwd_bytes(int E, int R, int d, int F) {
   return L.total;
 }
 
-moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t* wg,
-                                   const bf16_t* wu, const bf16_t* wd, const int32_t* offsets,
-                                   int E, int R, int d, int F, bf16_t* g, bf16_t* u, bf16_t* h,
-                                   bf16_t* yp) {
+// xq_in/xs_in: Xp already quantised rowwise (quantise-on-permute); when
+// null, Xp is quantised here from the bf16 xp.
+moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const uint8_t* xq_in,
+                                   const uint8_t* xs_in, const bf16_t* wg, const bf16_t* wu,
+                                   const bf16_t* wd, const int32_t* offsets, int E, int R, int d,
+                                   int F, bf16_t* g, bf16_t* u, bf16_t* h, bf16_t* yp) {
   const size_t need = moe_internal_mx_fwd_bytes(E, R, d, F);
   if (ctx->ws == nullptr || ctx->ws_bytes < need)
     return fail(ctx, MOE_ERR_WORKSPACE, "MXFP8 forward: workspace %zu bytes < %zu needed",
                 ctx->ws_bytes, need);
   uint8_t* ws = (uint8_t*)ctx->ws;
   MxLayout L;
-  uint8_t* xq = ws + L.put((size_t)R * d);
-  uint8_t* xs = ws + L.put((size_t)R * d / 32);
+  const uint8_t* xq = ws + L.put((size_t)R * d);
+  const uint8_t* xs = ws + L.put((size_t)R * d / 32);
   uint8_t* wgq = ws + L.put((size_t)E * d * F * 2);
   uint8_t* wgs = ws + L.put((size_t)E * d * F * 2 / 32);
   uint8_t* wuq = wgq + (size_t)E * d * F;
@@ -450,7 +452,13 @@ moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
   {
     moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
     // activations along d; weights along d per column, transposed to [F][E*d]
-    e = mx_quantize_rows(xp, R, d, xq, xs, s);
+    if (xq_in) {
+      xq = xq_in;
+      xs = xs_in;
+      e = hipSuccess;
+    } else {
+      e = mx_quantize_rows(xp, R, d, (uint8_t*)xq, (uint8_t*)xs, s);
+    }
     if (e == hipSuccess) e = mx_quantize_cols(wg, E * d, F, nullptr, d, E, wgq, wgs, E * d, s);
     if (e == hipSuccess) e = mx_quantize_cols(wu, E * d, F, nullptr, d, E, wuq, wus, E * d, s);
     if (e == hipSuccess) e = mx_quantize_cols(wd, E * F, d, nullptr, F, E, wdq, wds, E * F, s);

@@ -57,14 +57,9 @@ __device__ __forceinline__ uint32_t e4m3_code(float x) {
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// One thread per 32-element block along a row.
-__global__ void mx_rows_kernel(const uint4* __restrict__ src, long long nblocks, int bpr,
-                               uint4* __restrict__ codes, uint8_t* __restrict__ scales) {
-  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nblocks) return;
-  uint4 v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v[i] = src[b * 4 + i];
+// Quantise one 32-element block held as four 16-byte bf16 chunks: the eight
+// code words (four codes each, element order) and the scale byte.
+__device__ __forceinline__ int quant_block(const uint4 (&v)[4], uint32_t (&out)[8]) {
   float f[32];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -80,7 +75,6 @@ __global__ void mx_rows_kernel(const uint4* __restrict__ src, long long nblocks,
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
   const int sb = mx_scale_byte(amax);
   const int s = sb - 127;
-  uint32_t out[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     uint32_t word = 0;
@@ -88,10 +82,52 @@ __global__ void mx_rows_kernel(const uint4* __restrict__ src, long long nblocks,
     for (int j = 0; j < 4; ++j) word |= e4m3_code(ldexpf(f[q * 4 + j], -s)) << (8 * j);
     out[q] = word;
   }
+  return sb;
+}
+
+// One thread per 32-element block along a row.
+__global__ void mx_rows_kernel(const uint4* __restrict__ src, long long nblocks, int bpr,
+                               uint4* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = src[b * 4 + i];
+  uint32_t out[8];
+  const int sb = quant_block(v, out);
   codes[b * 2] = make_uint4(out[0], out[1], out[2], out[3]);
   codes[b * 2 + 1] = make_uint4(out[4], out[5], out[6], out[7]);
   scales[b] = (uint8_t)sb;
   (void)bpr;
+}
+
+// Quantise-on-permute: thread b takes block b % bpr of token b / bpr, reads
+// it once, quantises it once and writes the codes, the scale byte and
+// (when xp is given) the bf16 block into each of the token's k expert rows.
+__global__ void permute_mx_kernel(const uint4* __restrict__ x, const int32_t* __restrict__ row_of,
+                                  long long nblocks, int bpr, int k, uint4* __restrict__ xp,
+                                  uint4* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const long long t = b / bpr;
+  const int c = (int)(b - t * bpr);
+  uint4 v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[i] = x[b * 4 + i];
+  uint32_t out[8];
+  const int sb = quant_block(v, out);
+  const uint4 c0 = make_uint4(out[0], out[1], out[2], out[3]);
+  const uint4 c1 = make_uint4(out[4], out[5], out[6], out[7]);
+  for (int j = 0; j < k; ++j) {
+    const long long dst = (long long)row_of[t * k + j] * bpr + c;
+    if (xp) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xp[dst * 4 + i] = v[i];
+    }
+    codes[dst * 2] = c0;
+    codes[dst * 2 + 1] = c1;
+    scales[dst] = (uint8_t)sb;
+  }
 }
 
 // Column blocks with groups.  Block (x = 256-column tile, y = 128-deep slice
@@ -238,6 +274,25 @@ hipError_t mx_quantize_cols(const void* src, int rows, int cols, const int32_t* 
   mx_cols_kernel<<<grid, 256, 0, s>>>((const bf16_t*)src, rows, cols, offsets, urows, groups, codes,
                                       scales, kpad_ld);
   return hipGetLastError();
+}
+
+extern "C" moe_status moe_permute_mx(moe_ctx* ctx, const void* x, const int32_t* row_of, int T_,
+                                     int d, int k, void* xp, uint8_t* xp_codes, uint8_t* xp_scales) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, T_ >= 0 && d >= 32 && d % 32 == 0 && k >= 1 && k <= 32 &&
+                       (long long)T_ * k < (1LL << 31),
+              "moe_permute_mx: bad shape T=%d d=%d k=%d (d %% 32 == 0)", T_, d, k);
+  if (T_ == 0) return MOE_OK;
+  MOE_REQUIRE_PTR(ctx, x);
+  MOE_REQUIRE_PTR(ctx, row_of);
+  MOE_REQUIRE_PTR(ctx, xp_codes);
+  MOE_REQUIRE(ctx, xp_scales != nullptr, "moe_permute_mx: xp_scales is null");
+  MOE_REQUIRE(ctx, xp == nullptr || aligned16(xp), "moe_permute_mx: xp not 16-byte aligned");
+  const long long nb = (long long)T_ * (d / 32);
+  moe_prof_scope ps(ctx, MOE_K_PERMUTE);
+  permute_mx_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, ctx->stream>>>(
+      (const uint4*)x, row_of, nb, d / 32, k, (uint4*)xp, (uint4*)xp_codes, xp_scales);
+  return check_launch(ctx, "moe_permute_mx");
 }
 
 extern "C" moe_status moe_mx_quantize(moe_ctx* ctx, const void* src_bf16, int rows, int cols,
