@@ -18,7 +18,9 @@ timed on a bounded sample of the same workload.
 More legs ride on the default run: `e_scaling` times the same layer at E=8
 (learned-style routing) for the expert-count scaling loss, `mxfp8` times the
 MXFP8 grouped experts (quantisation included) on 65536 pre-routed rows of a
-16-expert, d_model 4096, d_ff 1536 share, and `routing_stats` times the
+16-expert, d_model 4096, d_ff 1536 share, `mxfp8_layer` times the main
+workload end to end with quantise-on-permute and MXFP8 expert GEMMs (its
+tokens/s beside the bf16 layer's), and `routing_stats` times the
 routing statistics, balance loss, its logit gradient and the per-expert
 weight-gradient norms on the layer's own buffers (outside the step).
 """
@@ -165,9 +167,10 @@ def gemm_summary(prof, unit, peak):
     return roof, agg
 
 
-def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False):
+def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=False):
     """Time the whole layer forward+backward on one workload (and, with
-    `with_stats`, the routing statistics on its last step's buffers)."""
+    `with_stats`, the routing statistics on its last step's buffers).
+    mxfp8: quantise on the permute and run the MXFP8 expert GEMMs."""
     import torch
 
     import moe_inputs as mi
@@ -178,13 +181,13 @@ def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False):
     g = {k: inp[k].to(dev) for k in ("x", "wr", "wg", "wu", "wd", "dy")}
     override = inp["logits"].to(dev) if "logits" in inp else None
     dtype = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
-    buf = moe.alloc_layer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, dtype, dev)
+    buf = moe.alloc_layer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, dtype, dev, mxfp8=mxfp8)
     ctx = moe.context(0)
     ctx.ensure_workspace(cfg.T, cfg.d, cfg.E, cfg.k, moe._dt(g["x"]))
 
     def step():
-        moe.layer_forward(g["x"], g["wr"], g["wg"], g["wu"], g["wd"], cfg.k, buf, override)
-        moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf)
+        moe.layer_forward(g["x"], g["wr"], g["wg"], g["wu"], g["wd"], cfg.k, buf, override, mxfp8=mxfp8)
+        moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf, mxfp8=mxfp8)
 
     gpu_ms, wall, prof = time_steps(ctx, step, steps, warmup)
     counts = buf.route["counts"].cpu()
@@ -277,13 +280,25 @@ def mx_leg(steps, warmup):
 
     gpu_ms, wall, prof = time_steps(ctx, step, steps, warmup)
     roof, agg = gemm_summary(prof, R * d * F, PEAK_FP8_TFLOPS)
+
+    # the same grouped experts in bf16 on the same rows, for the MXFP8/bf16 ratio
+    def step_bf16():
+        moe.moe_grouped_ffn_fwd(g["xp"], g["wg"], g["wu"], g["wd"], off, fo)
+        moe.moe_grouped_ffn_bwd(g["xp"], g["wg"], g["wu"], g["wd"], off, fo["g"], fo["u"], fo["h"],
+                                g["dyp"], bo)
+
+    bf_ms, _, bf_prof = time_steps(ctx, step_bf16, steps, warmup)
     counts = inp["counts"]
     res = {"workload": f"{cfg.name}: {R} pre-routed rows, d={d}, {E} experts, d_ff={F}, "
                        f"Zipf({cfg.zipf_s}) counts; MXFP8 E4M3 + e8m0 per 32, fp32 accumulate",
            "rows_per_s": round(R * steps / (gpu_ms / 1e3), 1), "ms_per_step": round(gpu_ms / steps, 4),
            "steps": steps, "warmup": warmup, "roofline": roof, "grouped_gemm": agg,
            "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in prof.items()},
-           "expert_load": {"max": int(counts.max()), "mean": float(counts.mean()), "empty": 0}}
+           "expert_load": {"max": int(counts.max()), "mean": float(counts.mean()), "empty": 0},
+           "bf16_same_rows": {"rows_per_s": round(R * steps / (bf_ms / 1e3), 1),
+                              "ms_per_step": round(bf_ms / steps, 4),
+                              "grouped_gemm": gemm_summary(bf_prof, R * d * F, PEAK_BF16_TFLOPS)[1]},
+           "mxfp8_vs_bf16": round(bf_ms / gpu_ms, 4)}
     del g, fo, bo, off
     torch.cuda.empty_cache()
     return res
@@ -387,6 +402,15 @@ def main():
                                                        PEAK_BF16_TFLOPS)[1]["tflops"]}
     if not args.no_mx:
         result["mxfp8"] = mx_leg(args.mx_steps, 3)
+        if cfg.dtype == "bf16":
+            ml = layer_leg(cfg, args.mx_steps, 3, mxfp8=True)
+            mroof, magg = gemm_summary(ml["prof"], unit, PEAK_FP8_TFLOPS)
+            result["mxfp8_layer"] = {
+                "workload": f"{cfg.name} end to end with MXFP8 experts (quantise-on-permute)",
+                "tokens_per_s": round(ml["tokens_per_s"], 1), "ms_per_step": round(ml["ms_per_step"], 4),
+                "vs_bf16_layer": round(ml["tokens_per_s"] / main_leg["tokens_per_s"], 4),
+                "grouped_gemm": magg, "roofline": mroof,
+                "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in ml["prof"].items()}}
     if args.cpu_sample > 0:
         result["cpu_baseline"] = cpu_baseline(cfg, main_leg["inp"], args.cpu_sample)
     print(json.dumps(result), flush=True)
