@@ -200,6 +200,26 @@ def expert_wgrad_elems(xp, dyp, offsets, wg, wu, wd, which, elems):
     return out
 
 
+# ------------------------------------------------------------------ shared expert
+# [P1] 四 lists shared experts among the router options: an expert every
+# token uses besides its k routed ones.  Read as one SwiGLU FFN over all T
+# tokens, ungated, added to the routed output.
+def shared_expert_fwd(x, wg_s, wu_s, wd_s):
+    """The shared expert on every token: the grouped expert with one group
+    holding all T rows (weights [1,d,Fs], [1,d,Fs], [1,Fs,d])."""
+    off = np.array([0, x.shape[0]], dtype=np.int32)
+    return expert_fwd(x, off, wg_s, wu_s, wd_s)
+
+
+def shared_expert_bwd(x, dy, wg_s, wu_s, wd_s):
+    """Its backward for upstream dy (ungated, so dy reaches it unchanged):
+    dx_shared plus the three weight gradients."""
+    off = np.array([0, x.shape[0]], dtype=np.int32)
+    dg = expert_dgrad(x, dy, off, wg_s, wu_s, wd_s)
+    wgr = expert_wgrad(x, dy, off, wg_s, wu_s, wd_s)
+    return dict(dx=dg["dxp"], dg=dg["dg"], du=dg["du"], dwg=wgr["dwg"], dwu=wgr["dwu"], dwd=wgr["dwd"])
+
+
 # ------------------------------------------------------------------ whole layer
 def layer_fwd(x, topk_idx, gates, wg, wu, wd, acc="f64", want_ytj=False):
     """Token-by-token layer forward: y_t = sum_j g_tj * expert_{S_tj}(x_t)
