@@ -161,6 +161,18 @@ moe_status moe_grouped_ffn_fwd_mxq(moe_ctx* ctx, const uint8_t* xp_codes, const 
 moe_status moe_combine(moe_ctx* ctx, const void* yp, const float* gates, const int32_t* row_of,
                        int T, int d, int k, moe_dtype dtype, void* y);
 
+/* Shared expert (an expert every token uses, besides its k routed ones;
+ * [P1] 四 lists shared experts among the framework's router options): one
+ * SwiGLU FFN over all T tokens, ungated, added to the routed output.  Run it
+ * with moe_grouped_ffn_fwd on x itself as one group (offsets {0, T}, E = 1)
+ * and add its output rows here:
+ *   y[t] = sum_j gates[t,j] * yp[row_of[t,j]] + y_shared[t]
+ * (slot order, then the shared row; fp32 sums, one rounding).  y_shared is
+ * [T,d] in dtype. */
+moe_status moe_combine_shared(moe_ctx* ctx, const void* yp, const float* gates,
+                              const int32_t* row_of, const void* y_shared, int T, int d, int k,
+                              moe_dtype dtype, void* y);
+
 /* --------------------------------------------------------------- backward
  * [P2] 1.2: the backward moves every token again. */
 
@@ -194,6 +206,16 @@ moe_status moe_permute_bwd(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
                            const int32_t* topk_idx, const float* dlogits_sel,
                            const void* w_router, int T, int d, int E, int k, moe_dtype dtype,
                            void* dx);
+
+/* moe_permute_bwd plus the shared expert's input gradient dx_shared [T,d]
+ * (from moe_grouped_ffn_bwd over the one all-token group with upstream rows
+ * dy itself, since the shared expert is ungated):
+ *   dx[t] = sum_j dxp[row_of[t,j]] + dx_shared[t] (+ the router term),
+ * in that order, fp32 sums, one rounding. */
+moe_status moe_permute_bwd_shared(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
+                                  const int32_t* topk_idx, const float* dlogits_sel,
+                                  const void* w_router, const void* dx_shared, int T, int d, int E,
+                                  int k, moe_dtype dtype, void* dx);
 
 /* Router weight gradient: dw_router[i,e] = sum over the rows r of expert e
  * (ascending) of dlogits_sel[src_tk[r]] * x[src_tk[r] / k, i]; fp32

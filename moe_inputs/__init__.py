@@ -15,6 +15,8 @@ involved, these synthetic tensors stand in for training activations):
   zipf128  bf16  T=32768 d=2048 E=128 k=4 F=1024  logits = ln Zipf(1.1) + Gumbel
   mx16     MXFP8 65536 pre-routed rows, d=4096, 16 experts, F=1536,
            Zipf(0.8) per-expert counts
+A shared expert's weights (shared_expert_weights) come from streams of
+their own, so adding one leaves every other draw unchanged.
 """
 from __future__ import annotations
 
@@ -122,6 +124,17 @@ def layer_inputs(cfg: LayerConfig, with_weights: bool = True) -> dict:
     elif cfg.routing != "router":
         raise ValueError(cfg.routing)
     return out
+
+
+def shared_expert_weights(cfg: LayerConfig, Fs: int | None = None) -> dict:
+    """Weights of a shared expert of width Fs (default cfg.F): wg_s, wu_s
+    [1,d,Fs] and wd_s [1,Fs,d], N(0, w_std^2) in the workload dtype, drawn
+    from their own seeded streams (the layer's streams are unchanged)."""
+    Fs = cfg.F if Fs is None else Fs
+    rg, ru, rd = _streams(cfg.seed + 1_000_003, 3)
+    return dict(wg_s=to_dtype(_normal(rg, (1, cfg.d, Fs), cfg.w_std), cfg.dtype),
+                wu_s=to_dtype(_normal(ru, (1, cfg.d, Fs), cfg.w_std), cfg.dtype),
+                wd_s=to_dtype(_normal(rd, (1, Fs, cfg.d), cfg.w_std), cfg.dtype))
 
 
 def largest_remainder(total: int, p: np.ndarray) -> np.ndarray:

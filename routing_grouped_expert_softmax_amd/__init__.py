@@ -47,6 +47,8 @@ _SIGS = {
     "moe_mx_quantize": [_vp, _int, _int, _int, _vp, _int, _vp, _vp, _int],
     "moe_permute_mx": [_vp, _vp, _int, _int, _int, _vp, _vp, _vp],
     "moe_grouped_ffn_fwd_mxq": [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp, _vp, _vp, _vp],
+    "moe_combine_shared": [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp],
+    "moe_permute_bwd_shared": [_vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
     "moe_route_stats": [_vp, _vp, _int, _int, _int, _flt, _vp, _vp, _vp, _vp],
     "moe_aux_loss_bwd": [_vp, _vp, _int, _int, _int, _flt, _flt, _vp],
     "moe_expert_grad_norms": [_vp, _int, _int, _int, _int, _vp],
@@ -279,13 +281,18 @@ def moe_grouped_ffn_fwd(xp, w_gate, w_up, w_down, offsets, out=None, mxfp8=False
     return out
 
 
-def moe_combine(yp, gates, row_of, y=None):
-    _need_cuda(yp, gates, row_of)
+def moe_combine(yp, gates, row_of, y=None, y_shared=None):
+    """y = sum_j gates * yp[row_of] (+ y_shared, the shared expert's rows)."""
+    _need_cuda(yp, gates, row_of, y_shared)
     T, k = row_of.shape
     d = yp.shape[1]
     if y is None:
         y = torch.empty(T, d, dtype=yp.dtype, device=yp.device)
-    context(yp.device.index).call("moe_combine", _p(yp), _p(gates), _p(row_of), T, d, k, _dt(yp), _p(y))
+    ctx = context(yp.device.index)
+    if y_shared is None:
+        ctx.call("moe_combine", _p(yp), _p(gates), _p(row_of), T, d, k, _dt(yp), _p(y))
+    else:
+        ctx.call("moe_combine_shared", _p(yp), _p(gates), _p(row_of), _p(y_shared), T, d, k, _dt(yp), _p(y))
     return y
 
 
@@ -332,8 +339,9 @@ def moe_grouped_ffn_bwd(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp, out=Non
     return out
 
 
-def moe_permute_bwd(dxp, row_of, topk_idx=None, dlogits_sel=None, w_router=None, dx=None):
-    _need_cuda(dxp, row_of, topk_idx, dlogits_sel, w_router)
+def moe_permute_bwd(dxp, row_of, topk_idx=None, dlogits_sel=None, w_router=None, dx=None, dx_shared=None):
+    """dx = sum_j dxp[row_of] (+ dx_shared) (+ the router term)."""
+    _need_cuda(dxp, row_of, topk_idx, dlogits_sel, w_router, dx_shared)
     T, k = row_of.shape
     d = dxp.shape[1]
     E = w_router.shape[1] if w_router is not None else 1
@@ -342,8 +350,12 @@ def moe_permute_bwd(dxp, row_of, topk_idx=None, dlogits_sel=None, w_router=None,
     ctx = context(dxp.device.index)
     if w_router is not None:
         ctx.ensure_workspace(T, d, E, min(k, E), _dt(dxp))
-    ctx.call("moe_permute_bwd", _p(dxp), _p(row_of), _p(topk_idx), _p(dlogits_sel), _p(w_router),
-             T, d, E, k, _dt(dxp), _p(dx))
+    if dx_shared is None:
+        ctx.call("moe_permute_bwd", _p(dxp), _p(row_of), _p(topk_idx), _p(dlogits_sel), _p(w_router),
+                 T, d, E, k, _dt(dxp), _p(dx))
+    else:
+        ctx.call("moe_permute_bwd_shared", _p(dxp), _p(row_of), _p(topk_idx), _p(dlogits_sel),
+                 _p(w_router), _p(dx_shared), T, d, E, k, _dt(dxp), _p(dx))
     return dx
 
 
@@ -441,9 +453,12 @@ class LayerBuffers:
     dw_router: torch.Tensor
     xq: torch.Tensor | None = None  # MXFP8 codes of xp (quantise-on-permute)
     xs: torch.Tensor | None = None  # their scale bytes
+    shared: dict | None = None      # shared expert: offsets {0,T}, its forward and backward buffers
 
 
-def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False):
+def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False, shared_F=0):
+    """Every buffer of one forward+backward; shared_F > 0 adds a shared
+    expert of width shared_F (weights [1,d,shared_F] and [1,shared_F,d])."""
     dev = torch.device(device)
     R = T * k
     z = lambda *s, dt=dtype: torch.empty(*s, dtype=dt, device=dev)  # noqa: E731
@@ -456,6 +471,12 @@ def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False):
     buf = LayerBuffers(logits=z(T, E, dt=torch.float32), route=route, xp=z(R, d), ffn=ffn, y=z(T, d),
                        dyp=z(R, d), dgates=z(T, k, dt=torch.float32),
                        dlogits_sel=z(T, k, dt=torch.float32), bwd=bwd, dx=z(T, d), dw_router=z(d, E))
+    if shared_F:
+        Fs = shared_F
+        buf.shared = dict(offsets=torch.tensor([0, T], dtype=torch.int32, device=dev),
+                          ffn=dict(g=z(T, Fs), u=z(T, Fs), h=z(T, Fs), yp=z(T, d)),
+                          bwd=dict(dg=z(T, Fs), du=z(T, Fs), dxp=z(T, d), dw_gate=z(1, d, Fs),
+                                   dw_up=z(1, d, Fs), dw_down=z(1, Fs, d)))
     if mxfp8:
         buf.xq = z(R, d, dt=torch.uint8)
         buf.xs = z(R, d // 32, dt=torch.uint8)
@@ -464,12 +485,14 @@ def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False):
 
 
 def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logits_override=None,
-                  mxfp8=False):
+                  mxfp8=False, shared=None):
     """Router scores -> route -> permute -> grouped SwiGLU experts -> combine.
     `logits_override` (optional [T,E] fp32 on the GPU) replaces the router
     scores as the routing input after the router GEMM has run.  mxfp8=True
     (buffers from alloc_layer(..., mxfp8=True)) quantises on the permute and
-    runs the MXFP8 expert GEMMs."""
+    runs the MXFP8 expert GEMMs.  shared = (w_gate, w_up, w_down) of a shared
+    expert (buffers from alloc_layer(..., shared_F=F_s)) runs it over every
+    token as one group and adds its rows in the combine."""
     moe_router_logits(x, w_router, buf.logits)
     moe_route(buf.logits if logits_override is None else logits_override, k, buf.route)
     if mxfp8:
@@ -478,11 +501,15 @@ def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logit
     else:
         moe_permute(x, buf.route["row_of"], buf.xp)
         moe_grouped_ffn_fwd(buf.xp, w_gate, w_up, w_down, buf.route["offsets"], buf.ffn)
-    moe_combine(buf.ffn["yp"], buf.route["gates"], buf.route["row_of"], buf.y)
+    ys = None
+    if shared is not None:
+        moe_grouped_ffn_fwd(x, *shared, buf.shared["offsets"], buf.shared["ffn"], mxfp8=mxfp8)
+        ys = buf.shared["ffn"]["yp"]
+    moe_combine(buf.ffn["yp"], buf.route["gates"], buf.route["row_of"], buf.y, y_shared=ys)
     return buf.y
 
 
-def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxfp8=False):
+def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxfp8=False, shared=None):
     """combine_bwd -> route_bwd -> grouped FFN bwd -> permute_bwd (+router
     dgrad) -> router wgrad.  Returns dx; weight grads are in buf.bwd and
     buf.dw_router."""
@@ -491,6 +518,13 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxf
     moe_route_bwd(r["gates"], buf.dgates, buf.dlogits_sel)
     moe_grouped_ffn_bwd(buf.xp, w_gate, w_up, w_down, r["offsets"], buf.ffn["g"], buf.ffn["u"],
                         buf.ffn["h"], buf.dyp, buf.bwd, mxfp8=mxfp8)
-    moe_permute_bwd(buf.bwd["dxp"], r["row_of"], r["topk_idx"], buf.dlogits_sel, w_router, buf.dx)
+    dxs = None
+    if shared is not None:
+        sh = buf.shared
+        moe_grouped_ffn_bwd(x, *shared, sh["offsets"], sh["ffn"]["g"], sh["ffn"]["u"], sh["ffn"]["h"], dy,
+                            sh["bwd"], mxfp8=mxfp8)
+        dxs = sh["bwd"]["dxp"]
+    moe_permute_bwd(buf.bwd["dxp"], r["row_of"], r["topk_idx"], buf.dlogits_sel, w_router, buf.dx,
+                    dx_shared=dxs)
     moe_router_wgrad(x, buf.dlogits_sel, r["src_tk"], r["offsets"], w_router.shape[1], buf.dw_router)
     return buf.dx

@@ -84,12 +84,14 @@ __global__ void __launch_bounds__(256) permute_kernel(const uint4* __restrict__ 
   }
 }
 
-// y[t] = sum_j gates[t,j] * yp[row_of[t,j]], slot order, fp32 sums.
+// y[t] = sum_j gates[t,j] * yp[row_of[t,j]] (+ add[t], the shared expert's
+// row, when add is given), slot order then the addend, fp32 sums.
 template <typename T, int KMAX>
 __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ yp,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ row_of, int T_,
-                                                      int nchunk, int k, uint4* __restrict__ y) {
+                                                      int nchunk, int k, const uint4* __restrict__ add,
+                                                      uint4* __restrict__ y) {
   constexpr int V = Vec<T>::N;
   constexpr int CPL = chunks_per_lane<KMAX>();
   const int lane = threadIdx.x & 63;
@@ -125,6 +127,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint4* __restrict__ 
 #pragma unroll
             for (int i = 0; i < V; ++i) acc[i] += g[j] * f[i];
           }
+        }
+        if (add) {
+          float f[V];
+          unpack(add[(size_t)t * nchunk + c], f, T());
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] += f[i];
         }
         y[(size_t)t * nchunk + c] = pack(acc, T());
       }
@@ -202,13 +210,15 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(
   }
 }
 
-// dx[t] = sum_j dxp[row_of[t,j]] + sum_j dl[t,j] * W_r^T[topk[t,j]]  (router
-// term optional; W_r^T is [E,d], made by transpose_kernel).
+// dx[t] = sum_j dxp[row_of[t,j]] (+ add[t], the shared expert's input
+// gradient, when add is given) + sum_j dl[t,j] * W_r^T[topk[t,j]] (router
+// term optional; W_r^T is [E,d], made by transpose_kernel), in that order.
 template <typename T, int KMAX, bool ROUTER>
 __global__ void __launch_bounds__(256) permute_bwd_kernel(
     const uint4* __restrict__ dxp, const int32_t* __restrict__ row_of,
     const int32_t* __restrict__ topk, const float* __restrict__ dls,
-    const uint4* __restrict__ wrt, int T_, int nchunk, int k, uint4* __restrict__ dx) {
+    const uint4* __restrict__ wrt, int T_, int nchunk, int k, const uint4* __restrict__ add,
+    uint4* __restrict__ dx) {
   constexpr int V = Vec<T>::N;
   const int lane = threadIdx.x & 63;
   const int wave = blockIdx.x * kWaves + (threadIdx.x >> 6);
@@ -255,6 +265,12 @@ __global__ void __launch_bounds__(256) permute_bwd_kernel(
 #pragma unroll
             for (int i = 0; i < V; ++i) acc[i] += f[i];
           }
+        }
+        if (add) {
+          float f[V];
+          unpack(add[(size_t)t * nchunk + c], f, T());
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] += f[i];
         }
         if (ROUTER) {
 #pragma unroll
@@ -346,8 +362,11 @@ moe_status moe_permute(moe_ctx* ctx, const void* x, const int32_t* row_of, int T
   return check_launch(ctx, "moe_permute");
 }
 
-moe_status moe_combine(moe_ctx* ctx, const void* yp, const float* gates, const int32_t* row_of,
-                       int T_, int d, int k, moe_dtype dtype, void* y) {
+}  // extern "C"
+
+static moe_status combine_impl(moe_ctx* ctx, const void* yp, const float* gates,
+                               const int32_t* row_of, const void* add, int T_, int d, int k,
+                               moe_dtype dtype, void* y) {
   MOE_CHECK_CTX(ctx);
   moe_status st = rows_common(ctx, T_, d, k, dtype, "moe_combine");
   if (st != MOE_OK) return st;
@@ -360,11 +379,28 @@ moe_status moe_combine(moe_ctx* ctx, const void* yp, const float* gates, const i
   moe_prof_scope ps(ctx, MOE_K_COMBINE);
   if (dtype == MOE_BF16)
     ROWS_DISPATCH_K(k, (combine_kernel<bf16_t, KM><<<grid_for(T_), 256, 0, ctx->stream>>>(
-                           (const uint4*)yp, gates, row_of, T_, nchunk, k, (uint4*)y)));
+                           (const uint4*)yp, gates, row_of, T_, nchunk, k, (const uint4*)add,
+                           (uint4*)y)));
   else
     ROWS_DISPATCH_K(k, (combine_kernel<float, KM><<<grid_for(T_), 256, 0, ctx->stream>>>(
-                           (const uint4*)yp, gates, row_of, T_, nchunk, k, (uint4*)y)));
+                           (const uint4*)yp, gates, row_of, T_, nchunk, k, (const uint4*)add,
+                           (uint4*)y)));
   return check_launch(ctx, "moe_combine");
+}
+
+extern "C" {
+
+moe_status moe_combine(moe_ctx* ctx, const void* yp, const float* gates, const int32_t* row_of,
+                       int T_, int d, int k, moe_dtype dtype, void* y) {
+  return combine_impl(ctx, yp, gates, row_of, nullptr, T_, d, k, dtype, y);
+}
+
+moe_status moe_combine_shared(moe_ctx* ctx, const void* yp, const float* gates,
+                              const int32_t* row_of, const void* y_shared, int T_, int d, int k,
+                              moe_dtype dtype, void* y) {
+  MOE_REQUIRE(ctx, ctx == nullptr || T_ == 0 || (y_shared && aligned16(y_shared)),
+              "moe_combine_shared: y_shared null or not 16-byte aligned");
+  return combine_impl(ctx, yp, gates, row_of, y_shared, T_, d, k, dtype, y);
 }
 
 moe_status moe_combine_bwd(moe_ctx* ctx, const void* dy, const void* yp, const float* gates,
@@ -393,10 +429,12 @@ moe_status moe_combine_bwd(moe_ctx* ctx, const void* dy, const void* yp, const f
   return check_launch(ctx, "moe_combine_bwd");
 }
 
-moe_status moe_permute_bwd(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
-                           const int32_t* topk_idx, const float* dlogits_sel,
-                           const void* w_router, int T_, int d, int E, int k, moe_dtype dtype,
-                           void* dx) {
+}  // extern "C"
+
+static moe_status permute_bwd_impl(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
+                                   const int32_t* topk_idx, const float* dlogits_sel,
+                                   const void* w_router, const void* add, int T_, int d, int E,
+                                   int k, moe_dtype dtype, void* dx) {
   MOE_CHECK_CTX(ctx);
   moe_status st = rows_common(ctx, T_, d, k, dtype, "moe_permute_bwd");
   if (st != MOE_OK) return st;
@@ -432,11 +470,11 @@ moe_status moe_permute_bwd(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
     if (router)                                                                                \
       ROWS_DISPATCH_K(k, (permute_bwd_kernel<TY, KM, true><<<grid_for(T_), 256, 0, ctx->stream>>>( \
                              (const uint4*)dxp, row_of, topk_idx, dlogits_sel, wrt, T_, nchunk, k, \
-                             (uint4*)dx)));                                                    \
+                             (const uint4*)add, (uint4*)dx)));                                 \
     else                                                                                       \
       ROWS_DISPATCH_K(k, (permute_bwd_kernel<TY, KM, false><<<grid_for(T_), 256, 0, ctx->stream>>>( \
                              (const uint4*)dxp, row_of, nullptr, nullptr, nullptr, T_, nchunk, k, \
-                             (uint4*)dx)));                                                    \
+                             (const uint4*)add, (uint4*)dx)));                                 \
   } while (0)
   if (dtype == MOE_BF16)
     PB_LAUNCH(bf16_t);
@@ -444,6 +482,26 @@ moe_status moe_permute_bwd(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
     PB_LAUNCH(float);
 #undef PB_LAUNCH
   return check_launch(ctx, "moe_permute_bwd");
+}
+
+extern "C" {
+
+moe_status moe_permute_bwd(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
+                           const int32_t* topk_idx, const float* dlogits_sel,
+                           const void* w_router, int T_, int d, int E, int k, moe_dtype dtype,
+                           void* dx) {
+  return permute_bwd_impl(ctx, dxp, row_of, topk_idx, dlogits_sel, w_router, nullptr, T_, d, E, k,
+                          dtype, dx);
+}
+
+moe_status moe_permute_bwd_shared(moe_ctx* ctx, const void* dxp, const int32_t* row_of,
+                                  const int32_t* topk_idx, const float* dlogits_sel,
+                                  const void* w_router, const void* dx_shared, int T_, int d, int E,
+                                  int k, moe_dtype dtype, void* dx) {
+  MOE_REQUIRE(ctx, ctx == nullptr || T_ == 0 || (dx_shared && aligned16(dx_shared)),
+              "moe_permute_bwd_shared: dx_shared null or not 16-byte aligned");
+  return permute_bwd_impl(ctx, dxp, row_of, topk_idx, dlogits_sel, w_router, dx_shared, T_, d, E,
+                          k, dtype, dx);
 }
 
 }  // extern "C"
