@@ -20,7 +20,8 @@ More legs ride on the default run: `e_scaling` times the same layer at E=8
 MXFP8 grouped experts (quantisation included) on 65536 pre-routed rows of a
 16-expert, d_model 4096, d_ff 1536 share, `mxfp8_layer` times the main
 workload end to end with quantise-on-permute and MXFP8 expert GEMMs (its
-tokens/s beside the bf16 layer's), and `routing_stats` times the
+tokens/s beside the bf16 layer's), `shared_expert` times the main workload
+with a shared expert of the routed width added, and `routing_stats` times the
 routing statistics, balance loss, its logit gradient and the per-expert
 weight-gradient norms on the layer's own buffers (outside the step).
 """
@@ -167,10 +168,11 @@ def gemm_summary(prof, unit, peak):
     return roof, agg
 
 
-def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=False):
+def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=False, shared_F=0):
     """Time the whole layer forward+backward on one workload (and, with
     `with_stats`, the routing statistics on its last step's buffers).
-    mxfp8: quantise on the permute and run the MXFP8 expert GEMMs."""
+    mxfp8: quantise on the permute and run the MXFP8 expert GEMMs.
+    shared_F > 0: add a shared expert of that width."""
     import torch
 
     import moe_inputs as mi
@@ -181,13 +183,19 @@ def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=Fal
     g = {k: inp[k].to(dev) for k in ("x", "wr", "wg", "wu", "wd", "dy")}
     override = inp["logits"].to(dev) if "logits" in inp else None
     dtype = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
-    buf = moe.alloc_layer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, dtype, dev, mxfp8=mxfp8)
+    buf = moe.alloc_layer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, dtype, dev, mxfp8=mxfp8, shared_F=shared_F)
     ctx = moe.context(0)
     ctx.ensure_workspace(cfg.T, cfg.d, cfg.E, cfg.k, moe._dt(g["x"]))
+    shared = None
+    if shared_F:
+        sw = mi.shared_expert_weights(cfg, shared_F)
+        shared = tuple(sw[k].to(dev) for k in ("wg_s", "wu_s", "wd_s"))
 
     def step():
-        moe.layer_forward(g["x"], g["wr"], g["wg"], g["wu"], g["wd"], cfg.k, buf, override, mxfp8=mxfp8)
-        moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf, mxfp8=mxfp8)
+        moe.layer_forward(g["x"], g["wr"], g["wg"], g["wu"], g["wd"], cfg.k, buf, override, mxfp8=mxfp8,
+                          shared=shared)
+        moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf, mxfp8=mxfp8,
+                           shared=shared)
 
     gpu_ms, wall, prof = time_steps(ctx, step, steps, warmup)
     counts = buf.route["counts"].cpu()
@@ -330,6 +338,7 @@ def main():
     ap.add_argument("--no-escaling", action="store_true",
                     help="skip the E=8 leg that gives the expert-count scaling loss")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 grouped-expert leg")
+    ap.add_argument("--no-shared", action="store_true", help="skip the shared-expert leg")
     ap.add_argument("--no-stats", action="store_true",
                     help="skip the routing-statistics / balance-loss / gradient-norm leg")
     ap.add_argument("--mx-steps", type=int, default=10)
@@ -400,6 +409,15 @@ def main():
             "loss": round(1.0 - main_leg["tokens_per_s"] / base["tokens_per_s"], 4),
             "dense8_grouped_gemm_tflops": gemm_summary(base["prof"], 16384 * 4 * 2048 * 1024,
                                                        PEAK_BF16_TFLOPS)[1]["tflops"]}
+    if not args.no_shared and cfg.dtype == "bf16":
+        sl = layer_leg(cfg, args.mx_steps, 3, shared_F=cfg.F)
+        extra_ms = sl["ms_per_step"] - main_leg["ms_per_step"]
+        sflops = 18.0 * cfg.T * cfg.d * cfg.F
+        result["shared_expert"] = {
+            "workload": f"{cfg.name} + one shared SwiGLU expert of d_ff {cfg.F} over every token",
+            "tokens_per_s": round(sl["tokens_per_s"], 1), "ms_per_step": round(sl["ms_per_step"], 4),
+            "added_ms_per_step": round(extra_ms, 4), "shared_gflop_per_step": round(sflops / 1e9, 1),
+            "shared_tflops_from_added_time": round(sflops / (extra_ms / 1e3) / 1e12, 1) if extra_ms > 0 else None}
     if not args.no_mx:
         result["mxfp8"] = mx_leg(args.mx_steps, 3)
         if cfg.dtype == "bf16":
