@@ -131,7 +131,9 @@ moe_status moe_permute(moe_ctx* ctx, const void* x, const int32_t* row_of, int T
  * device from `offsets` (no host sync): for the rows of expert e,
  * g = xp Wg[e], u = xp Wu[e], h = silu(g) * u, yp = h Wd[e].  g, u, h
  * ([R,F]) are saved for the backward; yp is [R,d].  An expert with no rows
- * does no work.  [P1] 二 (grouped GEMM), [P3] (dropless). */
+ * does no work.  With w_down and yp both NULL only g, u, h are computed:
+ * the recompute step of a backward that did not keep them (bit-identical to
+ * the forward's).  [P1] 二 (grouped GEMM), [P3] (dropless). */
 moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
                                const void* w_up, const void* w_down, const int32_t* offsets,
                                int E, int R, int d, int F, moe_dtype dtype, void* g, void* u,

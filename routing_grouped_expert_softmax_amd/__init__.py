@@ -281,6 +281,24 @@ def moe_grouped_ffn_fwd(xp, w_gate, w_up, w_down, offsets, out=None, mxfp8=False
     return out
 
 
+def moe_grouped_ffn_up(xp, w_gate, w_up, offsets, out=None, mxfp8=False):
+    """The gate/up GEMM + SwiGLU alone (moe_grouped_ffn_fwd with w_down and
+    yp NULL): recomputes g, u, h; returns dict(g, u, h)."""
+    _need_cuda(xp, w_gate, w_up, offsets)
+    R, d = xp.shape
+    E, _, F = w_gate.shape
+    dt = MOE_MXFP8 if mxfp8 else _dt(xp)
+    if mxfp8:
+        context(xp.device.index).ensure_mx_workspace(E, R, d, F)
+    if out is None:
+        out = dict(g=torch.empty(R, F, dtype=xp.dtype, device=xp.device),
+                   u=torch.empty(R, F, dtype=xp.dtype, device=xp.device),
+                   h=torch.empty(R, F, dtype=xp.dtype, device=xp.device))
+    context(xp.device.index).call("moe_grouped_ffn_fwd", _p(xp), _p(w_gate), _p(w_up), None, _p(offsets),
+                                  E, R, d, F, dt, _p(out["g"]), _p(out["u"]), _p(out["h"]), None)
+    return out
+
+
 def moe_combine(yp, gates, row_of, y=None, y_shared=None):
     """y = sum_j gates * yp[row_of] (+ y_shared, the shared expert's rows)."""
     _need_cuda(yp, gates, row_of, y_shared)
@@ -484,6 +502,19 @@ def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False, shared_F=0):
     return buf
 
 
+def saved_activation_bytes(buf: LayerBuffers, recompute=False):
+    """Bytes the forward keeps for the backward (besides x and the weights):
+    routing metadata, gates, the routed yp (for the gate gradient) and,
+    without recompute, xp and g, u, h (and the shared expert's g, u, h)."""
+    r = buf.route
+    keep = [r["topk_idx"], r["gates"], r["counts"], r["offsets"], r["row_of"], r["src_tk"], buf.ffn["yp"]]
+    if not recompute:
+        keep += [buf.xp, buf.ffn["g"], buf.ffn["u"], buf.ffn["h"]]
+        if buf.shared is not None:
+            keep += [buf.shared["ffn"][k] for k in ("g", "u", "h")]
+    return sum(t.numel() * t.element_size() for t in keep)
+
+
 def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logits_override=None,
                   mxfp8=False, shared=None):
     """Router scores -> route -> permute -> grouped SwiGLU experts -> combine.
@@ -509,11 +540,20 @@ def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logit
     return buf.y
 
 
-def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxfp8=False, shared=None):
+def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxfp8=False, shared=None,
+                   recompute=False):
     """combine_bwd -> route_bwd -> grouped FFN bwd -> permute_bwd (+router
     dgrad) -> router wgrad.  Returns dx; weight grads are in buf.bwd and
-    buf.dw_router."""
+    buf.dw_router.  recompute=True reads from the forward only yp, the gates
+    and the routing: xp is permuted again from x and g, u, h (the shared
+    expert's too) are recomputed by the gate/up GEMM before they are used,
+    so the forward need not keep them."""
     r = buf.route
+    if recompute:
+        moe_permute(x, r["row_of"], buf.xp)
+        moe_grouped_ffn_up(buf.xp, w_gate, w_up, r["offsets"], buf.ffn, mxfp8=mxfp8)
+        if shared is not None:
+            moe_grouped_ffn_up(x, shared[0], shared[1], buf.shared["offsets"], buf.shared["ffn"], mxfp8=mxfp8)
     moe_combine_bwd(dy, buf.ffn["yp"], r["gates"], r["row_of"], buf.dyp, buf.dgates)
     moe_route_bwd(r["gates"], buf.dgates, buf.dlogits_sel)
     moe_grouped_ffn_bwd(buf.xp, w_gate, w_up, w_down, r["offsets"], buf.ffn["g"], buf.ffn["u"],

@@ -638,12 +638,16 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
   MOE_REQUIRE_PTR(ctx, xp);
   MOE_REQUIRE_PTR(ctx, w_gate);
   MOE_REQUIRE_PTR(ctx, w_up);
-  MOE_REQUIRE_PTR(ctx, w_down);
   MOE_REQUIRE_PTR(ctx, offsets);
   MOE_REQUIRE_PTR(ctx, g);
   MOE_REQUIRE_PTR(ctx, u);
   MOE_REQUIRE_PTR(ctx, h);
-  MOE_REQUIRE_PTR(ctx, yp);
+  // w_down and yp both NULL: the gate/up GEMM alone (recompute of g, u, h)
+  const bool up_only = w_down == nullptr && yp == nullptr;
+  if (!up_only) {
+    MOE_REQUIRE_PTR(ctx, w_down);
+    MOE_REQUIRE_PTR(ctx, yp);
+  }
   if (R == 0) return MOE_OK;
   if (dtype == MOE_MXFP8)
     return moe_internal_ffn_fwd_mx(ctx, (const bf16_t*)xp, nullptr, nullptr, (const bf16_t*)w_gate,
@@ -678,6 +682,7 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up GEMM: %s", hipGetErrorString(e));
   }
+  if (up_only) return MOE_OK;
   {
     Params p{};
     p.a0 = (const bf16_t*)h;

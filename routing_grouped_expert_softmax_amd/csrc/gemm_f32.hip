@@ -218,6 +218,7 @@ moe_status moe_internal_ffn_fwd_f32(moe_ctx* ctx, const float* xp, const float* 
   p.ntiles = (F + T64 - 1) / T64;
   hipError_t e = run<FWD_UP>(p, (R / T64 + E) * p.ntiles, ctx->stream);
   if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "fp32 gate/up: %s", hipGetErrorString(e));
+  if (wd == nullptr) return MOE_OK;  // gate/up alone (recompute)
   P32 q{};
   q.a0 = h; q.lda = F;
   q.b0 = wd; q.ldb = d; q.b_gstride = (long long)F * d;

@@ -461,7 +461,7 @@ moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const uint8_t
     }
     if (e == hipSuccess) e = mx_quantize_cols(wg, E * d, F, nullptr, d, E, wgq, wgs, E * d, s);
     if (e == hipSuccess) e = mx_quantize_cols(wu, E * d, F, nullptr, d, E, wuq, wus, E * d, s);
-    if (e == hipSuccess) e = mx_quantize_cols(wd, E * F, d, nullptr, F, E, wdq, wds, E * F, s);
+    if (e == hipSuccess && wd) e = mx_quantize_cols(wd, E * F, d, nullptr, F, E, wdq, wds, E * F, s);
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise: %s", hipGetErrorString(e));
   }
   {
@@ -475,6 +475,7 @@ moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const uint8_t
     e = launch_mx<FWD_UP, 256, 2>(p, (R / 256 + E) * p.ntiles, s);
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX gate/up: %s", hipGetErrorString(e));
   }
+  if (wd == nullptr) return MOE_OK;  // gate/up alone (recompute)
   {
     moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
     e = mx_quantize_rows(h, R, F, hq, hs, s);
