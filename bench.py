@@ -21,7 +21,9 @@ MXFP8 grouped experts (quantisation included) on 65536 pre-routed rows of a
 16-expert, d_model 4096, d_ff 1536 share, `mxfp8_layer` times the main
 workload end to end with quantise-on-permute and MXFP8 expert GEMMs (its
 tokens/s beside the bf16 layer's), `shared_expert` times the main workload
-with a shared expert of the routed width added, and `routing_stats` times the
+with a shared expert of the routed width added, `recompute` times it with
+activation recompute (the bytes kept from forward to backward beside the
+throughput), and `routing_stats` times the
 routing statistics, balance loss, its logit gradient and the per-expert
 weight-gradient norms on the layer's own buffers (outside the step).
 """
@@ -168,7 +170,8 @@ def gemm_summary(prof, unit, peak):
     return roof, agg
 
 
-def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=False, shared_F=0):
+def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=False, shared_F=0,
+              recompute=False):
     """Time the whole layer forward+backward on one workload (and, with
     `with_stats`, the routing statistics on its last step's buffers).
     mxfp8: quantise on the permute and run the MXFP8 expert GEMMs.
@@ -195,14 +198,15 @@ def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=Fal
         moe.layer_forward(g["x"], g["wr"], g["wg"], g["wu"], g["wd"], cfg.k, buf, override, mxfp8=mxfp8,
                           shared=shared)
         moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf, mxfp8=mxfp8,
-                           shared=shared)
+                           shared=shared, recompute=recompute)
 
     gpu_ms, wall, prof = time_steps(ctx, step, steps, warmup)
     counts = buf.route["counts"].cpu()
     out = dict(cfg=cfg, gpu_ms=gpu_ms, wall=wall, prof=prof,
                tokens_per_s=cfg.T * steps / (gpu_ms / 1e3), ms_per_step=gpu_ms / steps,
                load={"max": int(counts.max()), "mean": float(counts.float().mean()),
-                     "empty": int((counts == 0).sum())})
+                     "empty": int((counts == 0).sum())},
+               saved_bytes=moe.saved_activation_bytes(buf, recompute=recompute))
     if with_stats:
         out["routing_stats"] = stats_leg(ctx, cfg, override if override is not None else buf.logits,
                                          buf, counts)
@@ -339,6 +343,7 @@ def main():
                     help="skip the E=8 leg that gives the expert-count scaling loss")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 grouped-expert leg")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-expert leg")
+    ap.add_argument("--no-recompute", action="store_true", help="skip the activation-recompute leg")
     ap.add_argument("--no-stats", action="store_true",
                     help="skip the routing-statistics / balance-loss / gradient-norm leg")
     ap.add_argument("--mx-steps", type=int, default=10)
@@ -418,6 +423,15 @@ def main():
             "tokens_per_s": round(sl["tokens_per_s"], 1), "ms_per_step": round(sl["ms_per_step"], 4),
             "added_ms_per_step": round(extra_ms, 4), "shared_gflop_per_step": round(sflops / 1e9, 1),
             "shared_tflops_from_added_time": round(sflops / (extra_ms / 1e3) / 1e12, 1) if extra_ms > 0 else None}
+    if not args.no_recompute:
+        rl = layer_leg(cfg, args.mx_steps, 3, recompute=True)
+        result["recompute"] = {
+            "workload": f"{cfg.name}; backward re-permutes x and recomputes g, u, h (gate/up GEMM)",
+            "tokens_per_s": round(rl["tokens_per_s"], 1), "ms_per_step": round(rl["ms_per_step"], 4),
+            "throughput_vs_saved": round(rl["tokens_per_s"] / main_leg["tokens_per_s"], 4),
+            "saved_activation_bytes": main_leg["saved_bytes"],
+            "recompute_activation_bytes": rl["saved_bytes"],
+            "activation_fraction": round(rl["saved_bytes"] / main_leg["saved_bytes"], 4)}
     if not args.no_mx:
         result["mxfp8"] = mx_leg(args.mx_steps, 3)
         if cfg.dtype == "bf16":
