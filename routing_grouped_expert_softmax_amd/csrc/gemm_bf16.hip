@@ -162,12 +162,13 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
   if (L != L0) lds_barrier();
   Work w;
   if (TR::kKRAGGED) {
-    // expert-major, then n-tile, then m-tile (m fastest)
+    // expert-major, then m-tile, then n-tile (n fastest: the blocks of one
+    // XCD write neighbouring column ranges of the same output rows)
     const int per_e = p.ntiles * p.mtiles;
     w.e = L / per_e;
     const int r = L % per_e;
-    w.nt = r / p.mtiles;
-    w.m0 = (r % p.mtiles) * BM;
+    w.nt = r % p.ntiles;
+    w.m0 = (r / p.ntiles) * BM;
     w.row0 = p.offsets[w.e];
     w.rows = p.offsets[w.e + 1] - w.row0;
   } else if (TR::kSINGLE) {
