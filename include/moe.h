@@ -98,6 +98,15 @@ moe_status moe_workspace_size(moe_ctx* ctx, int T, int d, int E, int k, moe_dtyp
  * MOE_MXFP8: the quantised operands); *bytes is a host output.  Register
  * max(this, moe_workspace_size(...)). */
 moe_status moe_mx_workspace_size(moe_ctx* ctx, int E, int R, int d, int F, size_t* bytes);
+/* Device workspace of moe_grouped_ffn_bwd for this shape; *bytes (host) is 0
+ * when the call needs none.  MOE_MXFP8: the quantised operands (as
+ * moe_mx_workspace_size).  MOE_BF16: the split-K partials of a weight
+ * gradient whose output tiles would leave block slots idle (fewer than two
+ * per compute unit, e.g. a shared expert's single group of T rows): each
+ * group's rows are cut into up to 8 segments whose exact fp32 partial
+ * products are summed in segment order and rounded once.  MOE_F32: 0. */
+moe_status moe_ffn_bwd_workspace_size(moe_ctx* ctx, int E, int R, int d, int F, moe_dtype dtype,
+                                      size_t* bytes);
 /* Register caller-owned device workspace (256-byte aligned). */
 moe_status moe_set_workspace(moe_ctx* ctx, void* ws, size_t bytes);
 

@@ -55,7 +55,7 @@ _SIGS = {
 }
 EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "moe_last_error",
            "moe_workspace_size", "moe_set_workspace", *_SIGS.keys(), "moe_profile_enable",
-           "moe_profile_query", "moe_kernel_name", "moe_mx_workspace_size"]
+           "moe_profile_query", "moe_kernel_name", "moe_mx_workspace_size", "moe_ffn_bwd_workspace_size"]
 
 # kernel ids of the profiling hook (moe_kernel_id in include/moe.h)
 KERNELS = ["router_logits", "topk_hist", "expert_scan", "rank", "permute", "gemm_up_swiglu",
@@ -82,6 +82,8 @@ def lib():
         L.moe_workspace_size.argtypes = [_vp, _int, _int, _int, _int, _int, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_set_workspace.argtypes = [_vp, _vp, ctypes.c_size_t]
         L.moe_mx_workspace_size.argtypes = [_vp, _int, _int, _int, _int, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_ffn_bwd_workspace_size.argtypes = [_vp, _int, _int, _int, _int, _int,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
         for name, sig in _SIGS.items():
             getattr(L, name).argtypes = [_vp, *sig]
         L.moe_profile_enable.argtypes = [_vp, _int]
@@ -124,6 +126,11 @@ class Context:
     def ensure_mx_workspace(self, E, R, d, F):
         n = ctypes.c_size_t()
         self._check(lib().moe_mx_workspace_size(self.handle, E, R, d, F, ctypes.byref(n)))
+        self._grow(n.value)
+
+    def ensure_ffn_bwd_workspace(self, E, R, d, F, dtype):
+        n = ctypes.c_size_t()
+        self._check(lib().moe_ffn_bwd_workspace_size(self.handle, E, R, d, F, dtype, ctypes.byref(n)))
         self._grow(n.value)
 
     def _grow(self, nbytes):
@@ -342,8 +349,7 @@ def moe_grouped_ffn_bwd(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp, out=Non
     R, d = xp.shape
     E, _, F = w_gate.shape
     dt = MOE_MXFP8 if mxfp8 else _dt(xp)
-    if mxfp8:
-        context(xp.device.index).ensure_mx_workspace(E, R, d, F)
+    context(xp.device.index).ensure_ffn_bwd_workspace(E, R, d, F, dt)
     if out is None:
         dev, tdt = xp.device, xp.dtype
         out = dict(dg=torch.empty(R, F, dtype=tdt, device=dev), du=torch.empty(R, F, dtype=tdt, device=dev),

@@ -70,6 +70,7 @@ struct Params {
   int kseg;   // K of segment 0 (DGRAD_UP), else K
   int ntiles;  // tiles along N
   int mtiles;  // tiles along M (K-ragged)
+  int part;    // K-ragged: store exact fp32 split-K partials instead of bf16
 };
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -458,6 +459,12 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
 
   // ---------------------------------------------------------------- epilogue
   EpiArgs ea{p.c0, p.c1, p.c2, p.ldc, p.c_gstride, p.aux0, p.aux1, p.N, p.M};
+  if constexpr (TR::kKRAGGED) {
+    if (p.part) {
+      store_partial_f32<MODE, BM, SM>(acc, ea, w, lane, wm, wn);
+      continue;
+    }
+  }
   if constexpr (epi_staged<MODE>(TL::STAGE, S)) {
     constexpr int CH = epi_chunk<MODE>(TL::STAGE, S);
     constexpr int NCS = epi_ncs<MODE>(TL::STAGE, S);
@@ -602,6 +609,78 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
                                    bf16_t* du, bf16_t* dxp, bf16_t* dwg, bf16_t* dwu,
                                    bf16_t* dwd);
 
+// ---------------------------------------------------------------- split-K
+// A weight-gradient launch has E * mtiles * ntiles output tiles.  When that
+// leaves block slots idle (fewer than two tiles per CU) and the groups are
+// long (a shared expert: one group of every token), each group's K range is
+// cut into S segments of whole 32-row steps, run as S virtual groups that
+// store exact fp32 partial products, then summed in segment order and
+// rounded once.  The choice depends only on the shapes and the chip.
+static int wgrad_splits(int E, int R, int tiles) {
+  const int slots = 2 * device_cus();
+  if (E <= 0 || tiles <= 0 || tiles >= slots) return 1;
+  const long long avg = (long long)R / E;
+  if (avg < 1024) return 1;
+  long long s = (slots + tiles - 1) / tiles;
+  s = std::min<long long>(s, 8);
+  s = std::min<long long>(s, avg / 256);
+  return (int)std::max<long long>(s, 1);
+}
+static int wgrad_up_tiles(int E, int d, int F) { return E * ((d + CfgW::BM - 1) / CfgW::BM) * ((F + 127) / 128); }
+static int wgrad_down_tiles(int E, int d, int F) { return E * ((F + CfgW::BM - 1) / CfgW::BM) * ((d + BN - 1) / BN); }
+// Workspace of the split weight gradients: the partials of the larger one
+// (gate/up: two [E*S, d, F] fp32 arrays) followed by the virtual offsets.
+static size_t wgrad_split_bytes(int E, int R, int d, int F, size_t* part_bytes) {
+  const int su = wgrad_splits(E, R, wgrad_up_tiles(E, d, F));
+  const int sd = wgrad_splits(E, R, wgrad_down_tiles(E, d, F));
+  if (su == 1 && sd == 1) {
+    *part_bytes = 0;
+    return 0;
+  }
+  const size_t up = su > 1 ? 2 * (size_t)E * su * d * F * 4 : 0;
+  const size_t dn = sd > 1 ? (size_t)E * sd * F * d * 4 : 0;
+  *part_bytes = ((up > dn ? up : dn) + 255) & ~(size_t)255;
+  return *part_bytes + (((size_t)E * 8 + 1) * 4 + 255) / 256 * 256;
+}
+
+__global__ void split_offsets_kernel(const int32_t* __restrict__ off, int E, int S,
+                                     int32_t* __restrict__ voff) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i > E * S) return;
+  if (i == E * S) {
+    voff[i] = off[E];
+    return;
+  }
+  const int e = i / S, sgm = i % S;
+  const int lo = off[e], len = off[e + 1] - lo;
+  const int seg = ((len + S - 1) / S + 31) / 32 * 32;
+  voff[i] = lo + min(len, sgm * seg);
+}
+
+// out[e][j] = bf16(sum_s part[e*S + s][j]) in segment order; n4 = float4s per group.
+__global__ void split_reduce_kernel(const float4* __restrict__ part, int S, long long n4,
+                                    long long total4, uint2* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total4) return;
+  const long long e = i / n4, j = i - e * n4;
+  float4 acc = part[(e * S) * n4 + j];
+  for (int sg = 1; sg < S; ++sg) {
+    const float4 v = part[(e * S + sg) * n4 + j];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  out[i] = make_uint2(pack2bf(acc.x, acc.y), pack2bf(acc.z, acc.w));
+}
+
+static hipError_t split_reduce(const float* part, int E, int S, size_t n, bf16_t* out, hipStream_t s) {
+  const long long n4 = (long long)(n / 4), total4 = (long long)E * n4;
+  split_reduce_kernel<<<(unsigned)((total4 + 255) / 256), 256, 0, s>>>((const float4*)part, S, n4,
+                                                                       total4, (uint2*)out);
+  return hipGetLastError();
+}
+
 static moe_status ffn_validate(moe_ctx* ctx, int E, int R, int d, int F, moe_dtype dtype,
                                const char* what) {
   MOE_REQUIRE(ctx, dtype == MOE_F32 || dtype == MOE_BF16 || dtype == MOE_MXFP8,
@@ -626,6 +705,22 @@ moe_status moe_mx_workspace_size(moe_ctx* ctx, int E, int R, int d, int F, size_
   if (st != MOE_OK) return st;
   const size_t a = moe_internal_mx_fwd_bytes(E, R, d, F), b = moe_internal_mx_bwd_bytes(E, R, d, F);
   *bytes = a > b ? a : b;
+  return MOE_OK;
+}
+
+moe_status moe_ffn_bwd_workspace_size(moe_ctx* ctx, int E, int R, int d, int F, moe_dtype dtype,
+                                      size_t* bytes) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, bytes != nullptr, "bytes is null");
+  moe_status st = ffn_validate(ctx, E, R, d, F, dtype, "moe_ffn_bwd_workspace_size");
+  if (st != MOE_OK) return st;
+  size_t part = 0;
+  if (dtype == MOE_MXFP8)
+    *bytes = moe_internal_mx_bwd_bytes(E, R, d, F);
+  else if (dtype == MOE_BF16)
+    *bytes = wgrad_split_bytes(E, R, d, F, &part);
+  else
+    *bytes = 0;
   return MOE_OK;
 }
 
@@ -767,6 +862,13 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
                                     (const float*)g, (const float*)u, (const float*)h,
                                     (const float*)dyp, E, R, d, F, (float*)dg, (float*)du,
                                     (float*)dxp, (float*)dw_gate, (float*)dw_up, (float*)dw_down);
+  size_t part_bytes = 0;
+  const size_t split_need = wgrad_split_bytes(E, R, d, F, &part_bytes);
+  if (split_need > 0 && (ctx->ws == nullptr || ctx->ws_bytes < split_need))
+    return fail(ctx, MOE_ERR_WORKSPACE, "moe_grouped_ffn_bwd: split-K workspace %zu bytes < %zu needed",
+                ctx->ws_bytes, split_need);
+  float* split_part = (float*)ctx->ws;
+  int32_t* split_voff = (int32_t*)((char*)ctx->ws + part_bytes);
   hipError_t e;
   if (R > 0) {
     // down dgrad with the SwiGLU backward in the epilogue
@@ -811,8 +913,21 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.mtiles = (F + CfgW::BM - 1) / CfgW::BM;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
-      e = launch<WGRAD_DOWN, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(p, E * p.ntiles * p.mtiles,
-                                                                    ctx->stream);
+      const int S = wgrad_splits(E, R, E * p.ntiles * p.mtiles);
+      if (S == 1) {
+        e = launch<WGRAD_DOWN, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(p, E * p.ntiles * p.mtiles,
+                                                                      ctx->stream);
+      } else {
+        split_offsets_kernel<<<(E * S + 256) / 256, 256, 0, ctx->stream>>>(offsets, E, S, split_voff);
+        Params q = p;
+        q.offsets = split_voff;
+        q.E = E * S;
+        q.c0 = split_part;
+        q.part = 1;
+        e = launch<WGRAD_DOWN, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(q, q.E * q.ntiles * q.mtiles,
+                                                                      ctx->stream);
+        if (e == hipSuccess) e = split_reduce(split_part, E, S, (size_t)F * d, (bf16_t*)dw_down, ctx->stream);
+      }
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down wgrad: %s", hipGetErrorString(e));
   }
@@ -860,8 +975,25 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.mtiles = (d + CfgW::BM - 1) / CfgW::BM;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
-      e = launch<WGRAD_UP, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(p, E * p.ntiles * p.mtiles,
-                                                                  ctx->stream);
+      const int S = wgrad_splits(E, R, E * p.ntiles * p.mtiles);
+      if (S == 1) {
+        e = launch<WGRAD_UP, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(p, E * p.ntiles * p.mtiles,
+                                                                    ctx->stream);
+      } else {
+        split_offsets_kernel<<<(E * S + 256) / 256, 256, 0, ctx->stream>>>(offsets, E, S, split_voff);
+        Params q = p;
+        q.offsets = split_voff;
+        q.E = E * S;
+        q.c0 = split_part;
+        q.c1 = split_part + (size_t)E * S * d * F;
+        q.part = 1;
+        e = launch<WGRAD_UP, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(q, q.E * q.ntiles * q.mtiles,
+                                                                    ctx->stream);
+        if (e == hipSuccess) e = split_reduce(split_part, E, S, (size_t)d * F, (bf16_t*)dw_gate, ctx->stream);
+        if (e == hipSuccess)
+          e = split_reduce(split_part + (size_t)E * S * d * F, E, S, (size_t)d * F, (bf16_t*)dw_up,
+                           ctx->stream);
+      }
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up wgrad: %s", hipGetErrorString(e));
   }

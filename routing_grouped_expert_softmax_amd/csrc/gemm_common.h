@@ -342,6 +342,7 @@ struct EpiArgs {
 // 32x32 subtile; dual modes hold g (subtiles 0,1) and u (2,3) of the same
 // columns.
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int MODE, int BM, int SM, bool SWIGLU_FROM_BF16>
 __device__ __forceinline__ void store_tile_direct(const f32x16 (&acc)[SM][4], const EpiArgs& a,
                                                   const Work& w, int lane, int wm, int wn) {
@@ -441,6 +442,37 @@ __device__ __forceinline__ void store_tile_direct(const f32x16 (&acc)[SM][4], co
   }
 }
 
+
+// Split-K partials of a K-ragged (wgrad) tile: every lane stores its own
+// 4-column fp32 pieces of group w.e's partial product, exact (no rounding),
+// for a fixed-order reduction into the bf16 weight gradient.  Dual modes
+// write g columns (subtiles 0,1) to c0 and u columns (2,3) to c1.
+template <int MODE, int BM, int SM>
+__device__ __forceinline__ void store_partial_f32(const f32x16 (&acc)[SM][4], const EpiArgs& a,
+                                                  const Work& w, int lane, int wm, int wn) {
+  static_assert(Traits<MODE>::kKRAGGED, "split-K partials are for the K-ragged modes");
+  constexpr int WM = BM / 2;
+  const int ncol4 = 4 * (lane >> 5);
+  const size_t gbase = (size_t)w.e * a.c_gstride;
+#pragma unroll
+  for (int sm = 0; sm < SM; ++sm) {
+    const int m = w.m0 + wm * WM + sm * 32 + (lane & 31);
+    if (m >= a.M) continue;
+#pragma unroll
+    for (int sn = 0; sn < 4; ++sn) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = Traits<MODE>::kDUAL ? w.nt * 128 + wn * 64 + (sn & 1) * 32 + 8 * g4 + ncol4
+                                            : w.nt * BN + wn * 128 + sn * 32 + 8 * g4 + ncol4;
+        if (col >= a.N) continue;
+        float* out = (float*)(Traits<MODE>::kDUAL && sn >= 2 ? a.c1 : a.c0);
+        const f32x4 v = {acc[sm][sn][g4 * 4], acc[sm][sn][g4 * 4 + 1], acc[sm][sn][g4 * 4 + 2],
+                         acc[sm][sn][g4 * 4 + 3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + gbase + (size_t)m * a.ldc + col));
+      }
+    }
+  }
+}
 
 // Epilogue staging region of a wave: inside stage buffer wave / PER at
 // offset (wave % PER) * REG, where PER regions fit in one stage buffer.

@@ -129,6 +129,10 @@ FFN_CASES = [
     ("bf16", 256, 384, [300, 1, 0, 257, 511, 40]),
     ("bf16", 512, 192, [0, 0, 1000, 3]),
     ("bf16", 192, 128, [5] * 40 + [0] * 8 + [300]),
+    # few long groups: the weight gradients split K (fp32 partials, fixed-order sum)
+    ("bf16", 256, 256, [4096]),
+    ("bf16", 256, 384, [3000, 5, 0, 2500]),
+    ("bf16", 128, 256, [2049]),
 ]
 
 
