@@ -264,7 +264,7 @@ def stats_leg(ctx, cfg, logits, buf, counts, reps=20):
     }
 
 
-def mx_leg(steps, warmup):
+def mx_leg(steps, warmup, bf16_ref=True):
     """Time the MXFP8 grouped experts (quantisation included) forward+backward
     on the pre-routed 16-expert workload."""
     import torch
@@ -299,18 +299,21 @@ def mx_leg(steps, warmup):
         moe.moe_grouped_ffn_bwd(g["xp"], g["wg"], g["wu"], g["wd"], off, fo["g"], fo["u"], fo["h"],
                                 g["dyp"], bo)
 
-    bf_ms, _, bf_prof = time_steps(ctx, step_bf16, steps, warmup)
+    bf_ms = bf_prof = None
+    if bf16_ref:
+        bf_ms, _, bf_prof = time_steps(ctx, step_bf16, steps, warmup)
     counts = inp["counts"]
     res = {"workload": f"{cfg.name}: {R} pre-routed rows, d={d}, {E} experts, d_ff={F}, "
                        f"Zipf({cfg.zipf_s}) counts; MXFP8 E4M3 + e8m0 per 32, fp32 accumulate",
            "rows_per_s": round(R * steps / (gpu_ms / 1e3), 1), "ms_per_step": round(gpu_ms / steps, 4),
            "steps": steps, "warmup": warmup, "roofline": roof, "grouped_gemm": agg,
            "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in prof.items()},
-           "expert_load": {"max": int(counts.max()), "mean": float(counts.mean()), "empty": 0},
-           "bf16_same_rows": {"rows_per_s": round(R * steps / (bf_ms / 1e3), 1),
-                              "ms_per_step": round(bf_ms / steps, 4),
-                              "grouped_gemm": gemm_summary(bf_prof, R * d * F, PEAK_BF16_TFLOPS)[1]},
-           "mxfp8_vs_bf16": round(bf_ms / gpu_ms, 4)}
+           "expert_load": {"max": int(counts.max()), "mean": float(counts.mean()), "empty": 0}}
+    if bf16_ref:
+        res["bf16_same_rows"] = {"rows_per_s": round(R * steps / (bf_ms / 1e3), 1),
+                                 "ms_per_step": round(bf_ms / steps, 4),
+                                 "grouped_gemm": gemm_summary(bf_prof, R * d * F, PEAK_BF16_TFLOPS)[1]}
+        res["mxfp8_vs_bf16"] = round(bf_ms / gpu_ms, 4)
     del g, fo, bo, off
     torch.cuda.empty_cache()
     return res
@@ -342,6 +345,10 @@ def main():
     ap.add_argument("--no-escaling", action="store_true",
                     help="skip the E=8 leg that gives the expert-count scaling loss")
     ap.add_argument("--no-mx", action="store_true", help="skip the MXFP8 grouped-expert leg")
+    ap.add_argument("--no-mx-layer", action="store_true",
+                    help="skip the end-to-end MXFP8 layer leg (keeps the MXFP8 grouped-expert leg)")
+    ap.add_argument("--no-mx-bf16-ref", action="store_true",
+                    help="skip timing the bf16 grouped experts on the MXFP8 leg's rows")
     ap.add_argument("--no-shared", action="store_true", help="skip the shared-expert leg")
     ap.add_argument("--no-recompute", action="store_true", help="skip the activation-recompute leg")
     ap.add_argument("--no-stats", action="store_true",
@@ -433,8 +440,8 @@ def main():
             "recompute_activation_bytes": rl["saved_bytes"],
             "activation_fraction": round(rl["saved_bytes"] / main_leg["saved_bytes"], 4)}
     if not args.no_mx:
-        result["mxfp8"] = mx_leg(args.mx_steps, 3)
-        if cfg.dtype == "bf16":
+        result["mxfp8"] = mx_leg(args.mx_steps, 3, bf16_ref=not args.no_mx_bf16_ref)
+        if cfg.dtype == "bf16" and not args.no_mx_layer:
             ml = layer_leg(cfg, args.mx_steps, 3, mxfp8=True)
             mroof, magg = gemm_summary(ml["prof"], unit, PEAK_FP8_TFLOPS)
             result["mxfp8_layer"] = {
