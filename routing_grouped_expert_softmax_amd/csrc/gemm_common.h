@@ -585,6 +585,24 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const Epi
       crow = (size_t)(w.row0 + mloc);
       return mloc < w.rows;
     };
+    // Down dgrad: the saved g, u rows of each (chunk, pass) are loaded one
+    // iteration ahead (coalesced 16-byte loads into registers), so only the
+    // first iteration waits for HBM.
+    constexpr int NGU = MODE == DGRAD_DOWN ? CH / RPI : 1;
+    u32x4 pg[NGU], pu[NGU];
+    auto load_gu = [&](int qq, int hh) {
+      const int mb = wm * WM + qq * CH, c0 = colw + hh * WNO + rw_chunk * 8;
+#pragma unroll
+      for (int it = 0; it < NGU; ++it) {
+        size_t crow;
+        if (row_ok(mb + it * RPI + rw_row, crow) && c0 < a.N) {
+          const size_t off = crow * a.ldc + c0;
+          pg[it] = *reinterpret_cast<const u32x4*>(a.aux0 + off);
+          pu[it] = *reinterpret_cast<const u32x4*>(a.aux1 + off);
+        }
+      }
+    };
+    if (MODE == DGRAD_DOWN) load_gu(0, 0);
 #pragma unroll
     for (int q = 0; q < WM / CH; ++q)
 #pragma unroll
@@ -592,20 +610,20 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const Epi
       const int mbase = wm * WM + q * CH;  // first block-tile row of this chunk
       const int col0 = colw + h * WNO;      // first column of this pass
       if (MODE == DGRAD_DOWN) {
-        // saved g, u rows -> LDS (coalesced 16-byte loads)
+        // this iteration's g, u rows -> LDS, then the next iteration's loads
 #pragma unroll
-        for (int it = 0; it < CH / RPI; ++it) {
+        for (int it = 0; it < NGU; ++it) {
           const int row = it * RPI + rw_row;
           size_t crow;
-          const int col = col0 + rw_chunk * 8;
-          if (row_ok(mbase + row, crow) && col < a.N) {
-            const size_t off = crow * a.ldc + col;
-            const u32x4 gv = *reinterpret_cast<const u32x4*>(a.aux0 + off);
-            const u32x4 uv = *reinterpret_cast<const u32x4*>(a.aux1 + off);
+          if (row_ok(mbase + row, crow) && col0 + rw_chunk * 8 < a.N) {
             const int lo = row * PITCH + ((rw_chunk ^ (row & (CPR - 1))) << 4);
-            *reinterpret_cast<LDS_AS u32x4*>(wbuf + lo) = gv;
-            *reinterpret_cast<LDS_AS u32x4*>(wbuf + MAT + lo) = uv;
+            *reinterpret_cast<LDS_AS u32x4*>(wbuf + lo) = pg[it];
+            *reinterpret_cast<LDS_AS u32x4*>(wbuf + MAT + lo) = pu[it];
           }
+        }
+        if (q * NCS + h + 1 < (WM / CH) * NCS) {
+          asm volatile("" ::: "memory");
+          load_gu(h + 1 < NCS ? q : q + 1, h + 1 < NCS ? h + 1 : 0);
         }
       }
       asm volatile("" ::: "memory");
