@@ -118,6 +118,20 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 inline size_t esize(moe_dtype dt) { return dt == MOE_F32 ? 4 : 2; }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+inline int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 }  // namespace moe_host
 
 #define MOE_CHECK_CTX(ctx) \

@@ -490,25 +490,12 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
 #ifndef GEMM_PERSIST
 #define GEMM_PERSIST 0
 #endif
-// Compute units of the current device (cached per device).
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
 
 // Launch with at most one resident set of blocks (OCC per CU): each block
 // then walks several tiles.  `blocks` is the tile bound of the launch.
 template <int MODE, int BM, int S, int BK, int OCC = 1>
 hipError_t launch(const Params& p, int blocks, hipStream_t s) {
-  if (GEMM_PERSIST) blocks = std::min(blocks, device_cus() / 8 * 8 * OCC);
+  if (GEMM_PERSIST) blocks = std::min(blocks, moe_host::device_cus() / 8 * 8 * OCC);
   blocks = (blocks + 7) / 8 * 8;
   grouped_gemm_kernel<MODE, BM, S, BK, OCC><<<blocks, kThreads, 0, s>>>(p);
   return hipGetLastError();
@@ -617,7 +604,7 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
 // store exact fp32 partial products, then summed in segment order and
 // rounded once.  The choice depends only on the shapes and the chip.
 static int wgrad_splits(int E, int R, int tiles) {
-  const int slots = 2 * device_cus();
+  const int slots = 2 * moe_host::device_cus();
   if (E <= 0 || tiles <= 0 || tiles >= slots) return 1;
   const long long avg = (long long)R / E;
   if (avg < 1024) return 1;

@@ -67,6 +67,7 @@ struct MxParams {
   int kseg;
   int ntiles;
   int mtiles;
+  const int32_t* kbase;  // K-ragged: padded K start of each expert (exclusive scan of roundup(n_e, 128))
 };
 
 constexpr int BK = 128;  // K bytes (= fp8 values) per stage
@@ -123,25 +124,13 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_mx_kernel(MxParams p
   if (TR::kKRAGGED) {
     // the previous tile's epilogue has finished with the LDS stage buffers
     if (L != L0) lds_barrier();
+    // expert-major, then m-tile, then n-tile (n fastest)
     const int per_e = p.ntiles * p.mtiles;
     w.e = L / per_e;
     const int r = L % per_e;
-    w.nt = r / p.mtiles;
-    w.m0 = (r % p.mtiles) * BM;
-    // padded K base: exclusive scan of roundup(n_e, 128) over the experts
-    int local = 0;
-    for (int e = tid; e < w.e; e += kThreads)
-      local += (p.offsets[e + 1] - p.offsets[e] + 127) / 128 * 128;
-    sh[tid] = local;
-    lds_barrier();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const int add = tid >= off ? sh[tid - off] : 0;
-      lds_barrier();
-      sh[tid] += add;
-      lds_barrier();
-    }
-    kbase = __builtin_amdgcn_readfirstlane(sh[kThreads - 1]);
-    lds_barrier();  // sh is rewritten by the next tile's scan
+    w.nt = r % p.ntiles;
+    w.m0 = (r / p.ntiles) * BM;
+    kbase = __builtin_amdgcn_readfirstlane(p.kbase[w.e]);  // padded K start of the expert
     const int n = p.offsets[w.e + 1] - p.offsets[w.e];
     w.row0 = kbase;
     w.rows = (n + 127) / 128 * 128;  // padded K of the expert (padding is zero)
@@ -366,8 +355,30 @@ __global__ void __launch_bounds__(kThreads, 1) grouped_gemm_mx_kernel(MxParams p
 #endif
 }
 
+// Padded K start of every expert for the K-ragged GEMMs: kbase[e] =
+// sum_{e' < e} roundup(n_e', 128), one block, fixed-order scan (E <= 1024).
+__global__ void __launch_bounds__(1024) mx_kbase_kernel(const int32_t* __restrict__ offsets, int E,
+                                                        int32_t* __restrict__ kbase) {
+  __shared__ int sc[1024];
+  const int t = threadIdx.x;
+  const int v = t < E ? (offsets[t + 1] - offsets[t] + 127) / 128 * 128 : 0;
+  sc[t] = v;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = t >= off ? sc[t - off] : 0;
+    __syncthreads();
+    sc[t] += add;
+    __syncthreads();
+  }
+  if (t < E) kbase[t] = sc[t] - v;
+}
+
 template <int MODE, int BM, int S>
 hipError_t launch_mx(const MxParams& p, int blocks, hipStream_t s) {
+  // K-ragged: at most four blocks per CU, each walking its XCD range (the
+  // range set-up is paid once per block; the surplus blocks keep some
+  // dynamic balancing of skewed tile costs)
+  if (Traits<MODE>::kKRAGGED) blocks = std::min(blocks, 4 * moe_host::device_cus());
   blocks = (blocks + 7) / 8 * 8;
   grouped_gemm_mx_kernel<MODE, BM, S><<<blocks, kThreads, 0, s>>>(p);
   return hipGetLastError();
@@ -422,6 +433,7 @@ size_t moe_internal_mx_bwd_bytes(int E, int R, int d, int F) {
   L.put((size_t)F * kp * 3 / 32);
   L.put((size_t)d * kp);           // dyp^T
   L.put((size_t)d * kp / 32);
+  L.put((size_t)(E + 1) * 4);      // padded K start of every expert
   return L.total;
 }
 
@@ -530,6 +542,7 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
   uint8_t* hts = uts + (size_t)F * kp / 32;
   uint8_t* ytq = ws + L.put((size_t)d * kp);
   uint8_t* yts = ws + L.put((size_t)d * kp / 32);
+  int32_t* kbase = (int32_t*)(ws + L.put((size_t)(E + 1) * 4));
   hipStream_t s = ctx->stream;
   hipError_t e;
   {
@@ -543,6 +556,7 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
     if (e == hipSuccess) e = mx_quantize_cols(dyp, R, d, offsets, 0, E, ytq, yts, kp, s);
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise: %s", hipGetErrorString(e));
   }
+  mx_kbase_kernel<<<1, 1024, 0, s>>>(offsets, E, kbase);
   if (R > 0) {
     MxParams p{};
     p.a0 = dyq; p.sa0 = dys; p.lda = d;
@@ -559,7 +573,7 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
     p.a0 = htq; p.sa0 = hts; p.lda = kp;
     p.b0 = ytq; p.sb0 = yts; p.ldb = kp;
     p.c0 = dwd; p.ldc = d; p.c_gstride = (long long)F * d;
-    p.offsets = offsets; p.E = E; p.M = F; p.N = d;
+    p.offsets = offsets; p.E = E; p.M = F; p.N = d; p.kbase = kbase;
     p.ntiles = (d + BN - 1) / BN;
     p.mtiles = (F + 255) / 256;
     moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
@@ -590,7 +604,7 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
     p.a0 = xtq; p.sa0 = xts; p.lda = kp;
     p.b0 = gtq; p.sb0 = gts; p.b1 = utq; p.sb1 = uts; p.ldb = kp;
     p.c0 = dwg; p.c1 = dwu; p.ldc = F; p.c_gstride = (long long)d * F;
-    p.offsets = offsets; p.E = E; p.M = d; p.N = F;
+    p.offsets = offsets; p.E = E; p.M = d; p.N = F; p.kbase = kbase;
     p.ntiles = (F + 127) / 128;
     p.mtiles = (d + 255) / 256;
     moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
