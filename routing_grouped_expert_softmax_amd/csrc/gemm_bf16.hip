@@ -566,7 +566,7 @@ moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const vo
   // runs at (the scores GEMM is bound by reading x once)
   constexpr int kRouterBM = 64;
   const int blocks = ((T_ + kRouterBM - 1) / kRouterBM) * p.ntiles;
-  hipError_t e = launch<ROUTER, kRouterBM, 2, 64, 1>(p, blocks, ctx->stream);
+  hipError_t e = launch<ROUTER, kRouterBM, 4, 32, 1>(p, blocks, ctx->stream);
   if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "router GEMM: %s", hipGetErrorString(e));
   return MOE_OK;
 }
