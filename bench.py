@@ -359,7 +359,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the layer; runs on more than one GPU "
-              "are not part of this build (use --gpus 1).", file=sys.stderr)
+              "are not supported (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
