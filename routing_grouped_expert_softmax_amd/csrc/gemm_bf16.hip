@@ -91,10 +91,10 @@ __device__ __forceinline__ int kc_half(int row, int h) { return h ^ ((row >> 3) 
 __device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 2; }
 
 // Tile geometry of one pipeline stage.
-template <int MODE, int BM, int BK>
+template <int MODE, int BM, int BK, int NW = 4>
 struct Tile {
   using TR = Traits<MODE>;
-  static constexpr int WM = BM / 2;   // wave tile rows (M)
+  static constexpr int WM = BM / (NW / 2);  // wave tile rows (M): NW/2 waves down, 2 across
   static constexpr int SM = WM / 32;  // 32-row subtiles per wave
   static constexpr int GROUP = 16 * BK;     // bytes of one 8-row K-contiguous group
   static constexpr int SLICES = BK / 16;    // 16-deep K slices per stage
@@ -102,18 +102,18 @@ struct Tile {
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = BN * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_INST = A_BYTES / 1024 / 4;  // 1 KiB direct loads per wave
-  static constexpr int B_INST = B_BYTES / 1024 / 4;
+  static constexpr int A_INST = A_BYTES / 1024 / NW;  // 1 KiB direct loads per wave
+  static constexpr int B_INST = B_BYTES / 1024 / NW;
   static constexpr int A_PITCH = TR::kA_KCONTIG ? 128 : BM * 2;  // LDS row pitch (bytes)
   // B: K-contiguous [256][64]; N-contiguous [64][256]; dual: two [64][128]
   static constexpr int B_PITCH = TR::kB_KCONTIG ? 128 : (TR::kDUAL ? 256 : 512);
 };
 
-template <int MODE, int BM, int S, int BK, int OCC>
-__global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
+template <int MODE, int BM, int S, int BK, int OCC, int NW>
+__global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
   using TR = Traits<MODE>;
-  using TL = Tile<MODE, BM, BK>;
+  using TL = Tile<MODE, BM, BK, NW>;
   constexpr int SM = TL::SM;
   // One LDS array per pipeline stage: distinct objects let the compiler see
   // that fragment reads of one stage never alias the loads landing in another.
@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
         soff = kk * (int)esz;
       } else {
         soff = k0 * p.ldb * (int)esz;
-        if (TR::kDUAL && wv >= 2) r = rsb1;  // waves 2,3 load the second matrix
+        if (TR::kDUAL && wv >= NW / 2) r = rsb1;  // the upper half of the waves loads the second matrix
       }
 #pragma unroll
       for (int j = 0; j < TL::B_INST; ++j)
@@ -465,12 +465,12 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
       continue;
     }
   }
-  if constexpr (epi_staged<MODE>(TL::STAGE, S)) {
-    constexpr int CH = epi_chunk<MODE>(TL::STAGE, S);
-    constexpr int NCS = epi_ncs<MODE>(TL::STAGE, S);
+  if constexpr (epi_staged<MODE, NW>(TL::STAGE, S)) {
+    constexpr int CH = epi_chunk<MODE, NW>(TL::STAGE, S);
+    constexpr int NCS = epi_ncs<MODE, NW>(TL::STAGE, S);
     constexpr int REG = epi_region_bytes<MODE>(CH, NCS);
     constexpr int PER = TL::STAGE / REG;
-    static_assert(S * PER >= 4, "epilogue staging regions do not fit the stage buffers");
+    static_assert(S * PER >= NW, "epilogue staging regions do not fit the stage buffers");
     const int sel = wave / PER;
     LDS_AS unsigned char* wbuf =
         (sel == 0 ? (LDS_AS unsigned char*)lds0 : sel == 1 ? (LDS_AS unsigned char*)lds1
@@ -493,40 +493,58 @@ __global__ void __launch_bounds__(kThreads, OCC) grouped_gemm_kernel(Params p) {
 
 // Launch with at most one resident set of blocks (OCC per CU): each block
 // then walks several tiles.  `blocks` is the tile bound of the launch.
-template <int MODE, int BM, int S, int BK, int OCC = 1>
+template <int MODE, int BM, int S, int BK, int OCC = 1, int NW = 4>
 hipError_t launch(const Params& p, int blocks, hipStream_t s) {
   if (GEMM_PERSIST) blocks = std::min(blocks, moe_host::device_cus() / 8 * 8 * OCC);
   blocks = (blocks + 7) / 8 * 8;
-  grouped_gemm_kernel<MODE, BM, S, BK, OCC><<<blocks, kThreads, 0, s>>>(p);
+  grouped_gemm_kernel<MODE, BM, S, BK, OCC, NW><<<blocks, 64 * NW, 0, s>>>(p);
   return hipGetLastError();
 }
 
 // Tile configurations: rows per tile, pipeline stages, K step, blocks per
-// CU.  Two resident blocks per CU (128x256 tiles, 32-deep K steps, 72 KiB of
-// LDS and at most 256 registers per wave) let one block's prologue, barriers
-// and output stores overlap the other block's MFMAs on the same SIMDs.  (The
-// down dgrad's epilogue, which also streams the saved g and u, then stages
-// its columns in two passes to fit.)
+// CU, waves per block.  Two resident blocks per CU (128x256 tiles, 32-deep K
+// steps, 72 KiB of LDS and at most 256 registers per wave) let one block's
+// prologue, barriers and output stores overlap the other block's MFMAs on the
+// same SIMDs.  The two dgrads instead run one 256x256 block per CU with eight
+// waves (64x128 wave tiles, two waves per SIMD): a third less L2->LDS traffic
+// per FLOP and a deeper prefetch, which outweighs the lost overlap there
+// (measured per mode).  (The down dgrad's epilogue, which also streams the
+// saved g and u, stages its columns in two passes to fit.)
 #ifndef GEMM_M_CFG
 #define GEMM_M_CFG 128, 3, 32, 2   // forward gate/up and down
 #endif
+#ifndef GEMM_UP_CFG
+#define GEMM_UP_CFG GEMM_M_CFG     // forward gate/up
+#endif
+#ifndef GEMM_DN_CFG
+#define GEMM_DN_CFG GEMM_M_CFG     // forward down
+#endif
 #ifndef GEMM_DU_CFG
-#define GEMM_DU_CFG 128, 3, 32, 2  // gate/up dgrad
+#define GEMM_DU_CFG 256, 3, 32, 1, 8  // gate/up dgrad
 #endif
 #ifndef GEMM_DD_CFG
-#define GEMM_DD_CFG 128, 3, 32, 2  // down dgrad
+#define GEMM_DD_CFG 256, 3, 32, 1, 8  // down dgrad
 #endif
 #ifndef GEMM_W_CFG
 #define GEMM_W_CFG 128, 3, 32, 2   // both wgrads
 #endif
-template <int BM_, int S_, int BK_, int OCC_>
+#ifndef GEMM_WU_CFG
+#define GEMM_WU_CFG GEMM_W_CFG     // gate/up wgrad
+#endif
+#ifndef GEMM_WD_CFG
+#define GEMM_WD_CFG GEMM_W_CFG     // down wgrad
+#endif
+// rows, stages, K step, blocks per CU, waves per block (NW/2 down, 2 across)
+template <int BM_, int S_, int BK_, int OCC_, int NW_ = 4>
 struct Cfg {
-  static constexpr int BM = BM_, S = S_, BK = BK_, OCC = OCC_;
+  static constexpr int BM = BM_, S = S_, BK = BK_, OCC = OCC_, NW = NW_;
 };
-using CfgM = Cfg<GEMM_M_CFG>;
+using CfgUP = Cfg<GEMM_UP_CFG>;
+using CfgDN = Cfg<GEMM_DN_CFG>;
 using CfgDU = Cfg<GEMM_DU_CFG>;
 using CfgDD = Cfg<GEMM_DD_CFG>;
-using CfgW = Cfg<GEMM_W_CFG>;
+using CfgWU = Cfg<GEMM_WU_CFG>;
+using CfgWD = Cfg<GEMM_WD_CFG>;
 
 // Upper bound of sum_e ceil(n_e / BM) over any split of R rows into E groups.
 int mtile_bound(int R, int E, int BM) { return R / BM + E; }
@@ -540,9 +558,10 @@ using namespace moe_host;
 // bound on sum_e ceil(n_e / BM) tiles, found on the device.
 template <int MODE>
 static hipError_t launch_mragged(Params& p, int R, hipStream_t s) {
-  using C = std::conditional_t<MODE == DGRAD_DOWN, CfgDD,
-                               std::conditional_t<MODE == DGRAD_UP, CfgDU, CfgM>>;
-  return launch<MODE, C::BM, C::S, C::BK, C::OCC>(p, mtile_bound(R, p.E, C::BM) * p.ntiles, s);
+  using C = std::conditional_t<
+      MODE == DGRAD_DOWN, CfgDD,
+      std::conditional_t<MODE == DGRAD_UP, CfgDU, std::conditional_t<MODE == FWD_UP, CfgUP, CfgDN>>>;
+  return launch<MODE, C::BM, C::S, C::BK, C::OCC, C::NW>(p, mtile_bound(R, p.E, C::BM) * p.ntiles, s);
 }
 
 moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const void* wr, int T_,
@@ -613,8 +632,8 @@ static int wgrad_splits(int E, int R, int tiles) {
   s = std::min<long long>(s, avg / 256);
   return (int)std::max<long long>(s, 1);
 }
-static int wgrad_up_tiles(int E, int d, int F) { return E * ((d + CfgW::BM - 1) / CfgW::BM) * ((F + 127) / 128); }
-static int wgrad_down_tiles(int E, int d, int F) { return E * ((F + CfgW::BM - 1) / CfgW::BM) * ((d + BN - 1) / BN); }
+static int wgrad_up_tiles(int E, int d, int F) { return E * ((d + CfgWU::BM - 1) / CfgWU::BM) * ((F + 127) / 128); }
+static int wgrad_down_tiles(int E, int d, int F) { return E * ((F + CfgWD::BM - 1) / CfgWD::BM) * ((d + BN - 1) / BN); }
 // Workspace of the split weight gradients: the partials of the larger one
 // (gate/up: two [E*S, d, F] fp32 arrays) followed by the virtual offsets.
 static size_t wgrad_split_bytes(int E, int R, int d, int F, size_t* part_bytes) {
@@ -897,12 +916,12 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.M = F;
     p.N = d;
     p.ntiles = (d + BN - 1) / BN;
-    p.mtiles = (F + CfgW::BM - 1) / CfgW::BM;
+    p.mtiles = (F + CfgWD::BM - 1) / CfgWD::BM;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
       const int S = wgrad_splits(E, R, E * p.ntiles * p.mtiles);
       if (S == 1) {
-        e = launch<WGRAD_DOWN, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(p, E * p.ntiles * p.mtiles,
+        e = launch<WGRAD_DOWN, CfgWD::BM, CfgWD::S, CfgWD::BK, CfgWD::OCC, CfgWD::NW>(p, E * p.ntiles * p.mtiles,
                                                                       ctx->stream);
       } else {
         split_offsets_kernel<<<(E * S + 256) / 256, 256, 0, ctx->stream>>>(offsets, E, S, split_voff);
@@ -911,7 +930,7 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
         q.E = E * S;
         q.c0 = split_part;
         q.part = 1;
-        e = launch<WGRAD_DOWN, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(q, q.E * q.ntiles * q.mtiles,
+        e = launch<WGRAD_DOWN, CfgWD::BM, CfgWD::S, CfgWD::BK, CfgWD::OCC, CfgWD::NW>(q, q.E * q.ntiles * q.mtiles,
                                                                       ctx->stream);
         if (e == hipSuccess) e = split_reduce(split_part, E, S, (size_t)F * d, (bf16_t*)dw_down, ctx->stream);
       }
@@ -959,12 +978,12 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.M = d;
     p.N = F;
     p.ntiles = (F + 127) / 128;
-    p.mtiles = (d + CfgW::BM - 1) / CfgW::BM;
+    p.mtiles = (d + CfgWU::BM - 1) / CfgWU::BM;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
       const int S = wgrad_splits(E, R, E * p.ntiles * p.mtiles);
       if (S == 1) {
-        e = launch<WGRAD_UP, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(p, E * p.ntiles * p.mtiles,
+        e = launch<WGRAD_UP, CfgWU::BM, CfgWU::S, CfgWU::BK, CfgWU::OCC, CfgWU::NW>(p, E * p.ntiles * p.mtiles,
                                                                     ctx->stream);
       } else {
         split_offsets_kernel<<<(E * S + 256) / 256, 256, 0, ctx->stream>>>(offsets, E, S, split_voff);
@@ -974,7 +993,7 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
         q.c0 = split_part;
         q.c1 = split_part + (size_t)E * S * d * F;
         q.part = 1;
-        e = launch<WGRAD_UP, CfgW::BM, CfgW::S, CfgW::BK, CfgW::OCC>(q, q.E * q.ntiles * q.mtiles,
+        e = launch<WGRAD_UP, CfgWU::BM, CfgWU::S, CfgWU::BK, CfgWU::OCC, CfgWU::NW>(q, q.E * q.ntiles * q.mtiles,
                                                                     ctx->stream);
         if (e == hipSuccess) e = split_reduce(split_part, E, S, (size_t)d * F, (bf16_t*)dw_gate, ctx->stream);
         if (e == hipSuccess)

@@ -56,7 +56,10 @@ struct Work {
 // past the last tile.
 template <int BM>
 __device__ bool find_mtile(int E, const int32_t* offsets, int ntiles, int* sh, Work& w) {
+  // the first kThreads threads hold the experts; any further threads of a
+  // larger block only take part in the barriers
   const int tid = threadIdx.x;
+  const bool act = tid < kThreads;
   const int per = (E + kThreads - 1) / kThreads;  // experts per thread (<= 4)
   int cnt[4], til[4];
   int local = 0;
@@ -72,16 +75,16 @@ __device__ bool find_mtile(int E, const int32_t* offsets, int ntiles, int* sh, W
     local += til[q];
   }
   // exclusive scan of `local` over the block
-  sh[tid] = local;
+  if (act) sh[tid] = local;
   __syncthreads();
   for (int off = 1; off < kThreads; off <<= 1) {
-    const int add = tid >= off ? sh[tid - off] : 0;
+    const int add = act && tid >= off ? sh[tid - off] : 0;
     __syncthreads();
-    sh[tid] += add;
+    if (act) sh[tid] += add;
     __syncthreads();
   }
   const int total = sh[kThreads - 1];
-  int run = sh[tid] - local;
+  int run = act ? sh[tid] - local : total;
   __syncthreads();
   // logical tile of this block: contiguous ranges per XCD
   const int per_xcd = (total + 7) / 8;
@@ -225,7 +228,9 @@ struct MTileSched {
   int per;    // experts per thread
   int total;  // tiles of the launch (block-uniform)
   __device__ void init(int E, const int32_t* offsets, int ntiles, int* sh) {
+    // threads past kThreads (larger blocks) hold no experts
     const int tid = threadIdx.x;
+    const bool act = tid < kThreads;
     per = (E + kThreads - 1) / kThreads;  // <= 4
     int local = 0;
 #pragma unroll
@@ -239,16 +244,16 @@ struct MTileSched {
       }
       local += til[q];
     }
-    sh[tid] = local;
+    if (act) sh[tid] = local;
     lds_barrier();
     for (int off = 1; off < kThreads; off <<= 1) {
-      const int add = tid >= off ? sh[tid - off] : 0;
+      const int add = act && tid >= off ? sh[tid - off] : 0;
       lds_barrier();
-      sh[tid] += add;
+      if (act) sh[tid] += add;
       lds_barrier();
     }
     total = __builtin_amdgcn_readfirstlane(sh[kThreads - 1]);
-    run = sh[tid] - local;
+    run = act ? sh[tid] - local : total;
     lds_barrier();
   }
   // Work of logical tile L < total.  The owning thread publishes it through
@@ -343,10 +348,10 @@ struct EpiArgs {
 // columns.
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-template <int MODE, int BM, int SM, bool SWIGLU_FROM_BF16>
-__device__ __forceinline__ void store_tile_direct(const f32x16 (&acc)[SM][4], const EpiArgs& a,
+template <int MODE, int BM, int SM, bool SWIGLU_FROM_BF16, int SN = 4, int WN = 128>
+__device__ __forceinline__ void store_tile_direct(const f32x16 (&acc)[SM][SN], const EpiArgs& a,
                                                   const Work& w, int lane, int wm, int wn) {
-  constexpr int WM = BM / 2;
+  constexpr int WM = SM * 32;  // wave tile rows
   // Lane holds C[m = mbase + (lane&31)][n = nbase + 8*(r/4) + 4*(lane>>5) + r%4].
   const int ncol4 = 4 * (lane >> 5);
 #pragma unroll
@@ -364,16 +369,16 @@ __device__ __forceinline__ void store_tile_direct(const f32x16 (&acc)[SM][4], co
     if (!mvalid) continue;
     if (Traits<MODE>::kDUAL) {
 #pragma unroll
-      for (int sn = 0; sn < 2; ++sn) {
+      for (int sn = 0; sn < SN / 2; ++sn) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = w.nt * 128 + wn * 64 + sn * 32 + 8 * g4 + ncol4;
+          const int col = w.nt * 128 + wn * (WN / 2) + sn * 32 + 8 * g4 + ncol4;
           if (col >= a.N) continue;
           float gv[4], uv[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             gv[r] = acc[sm][sn][g4 * 4 + r];
-            uv[r] = acc[sm][sn + 2][g4 * 4 + r];
+            uv[r] = acc[sm][sn + SN / 2][g4 * 4 + r];
           }
           if (MODE == FWD_UP) {
             const size_t off = crow * a.ldc + col;
@@ -401,10 +406,10 @@ __device__ __forceinline__ void store_tile_direct(const f32x16 (&acc)[SM][4], co
       }
     } else {
 #pragma unroll
-      for (int sn = 0; sn < 4; ++sn) {
+      for (int sn = 0; sn < SN; ++sn) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int col = w.nt * BN + wn * 128 + sn * 32 + 8 * g4 + ncol4;
+          const int col = w.nt * BN + wn * WN + sn * 32 + 8 * g4 + ncol4;
           if (col >= a.N) continue;
           float v[4];
 #pragma unroll
@@ -447,11 +452,11 @@ __device__ __forceinline__ void store_tile_direct(const f32x16 (&acc)[SM][4], co
 // 4-column fp32 pieces of group w.e's partial product, exact (no rounding),
 // for a fixed-order reduction into the bf16 weight gradient.  Dual modes
 // write g columns (subtiles 0,1) to c0 and u columns (2,3) to c1.
-template <int MODE, int BM, int SM>
-__device__ __forceinline__ void store_partial_f32(const f32x16 (&acc)[SM][4], const EpiArgs& a,
+template <int MODE, int BM, int SM, int SN = 4, int WN = 128>
+__device__ __forceinline__ void store_partial_f32(const f32x16 (&acc)[SM][SN], const EpiArgs& a,
                                                   const Work& w, int lane, int wm, int wn) {
   static_assert(Traits<MODE>::kKRAGGED, "split-K partials are for the K-ragged modes");
-  constexpr int WM = BM / 2;
+  constexpr int WM = SM * 32;  // wave tile rows
   const int ncol4 = 4 * (lane >> 5);
   const size_t gbase = (size_t)w.e * a.c_gstride;
 #pragma unroll
@@ -459,13 +464,14 @@ __device__ __forceinline__ void store_partial_f32(const f32x16 (&acc)[SM][4], co
     const int m = w.m0 + wm * WM + sm * 32 + (lane & 31);
     if (m >= a.M) continue;
 #pragma unroll
-    for (int sn = 0; sn < 4; ++sn) {
+    for (int sn = 0; sn < SN; ++sn) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const int col = Traits<MODE>::kDUAL ? w.nt * 128 + wn * 64 + (sn & 1) * 32 + 8 * g4 + ncol4
-                                            : w.nt * BN + wn * 128 + sn * 32 + 8 * g4 + ncol4;
+        const int col = Traits<MODE>::kDUAL
+                            ? w.nt * 128 + wn * (WN / 2) + (sn % (SN / 2)) * 32 + 8 * g4 + ncol4
+                            : w.nt * BN + wn * WN + sn * 32 + 8 * g4 + ncol4;
         if (col >= a.N) continue;
-        float* out = (float*)(Traits<MODE>::kDUAL && sn >= 2 ? a.c1 : a.c0);
+        float* out = (float*)(Traits<MODE>::kDUAL && sn >= SN / 2 ? a.c1 : a.c0);
         const f32x4 v = {acc[sm][sn][g4 * 4], acc[sm][sn][g4 * 4 + 1], acc[sm][sn][g4 * 4 + 2],
                          acc[sm][sn][g4 * 4 + 3]};
         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(out + gbase + (size_t)m * a.ldc + col));
@@ -507,21 +513,21 @@ template <int MODE>
 constexpr int epi_region_bytes(int ch, int ncs) {
   return epi_nout<MODE>() * ch * epi_wno<MODE>(ncs) * 2;
 }
-// Column passes of the staged epilogue: 1 or 2 (whichever lets four wave
+// Column passes of the staged epilogue: 1 or 2 (whichever lets the NW wave
 // regions of 32 rows fit in the stage buffers), 0 = direct epilogue.
-template <int MODE>
+template <int MODE, int NW = 4>
 constexpr int epi_ncs(int stage_bytes, int stages) {
   if (MODE == ROUTER) return 0;
-  if (stages * (stage_bytes / epi_region_bytes<MODE>(32, 1)) >= 4) return 1;
-  if (!Traits<MODE>::kDUAL && stages * (stage_bytes / epi_region_bytes<MODE>(32, 2)) >= 4) return 2;
+  if (stages * (stage_bytes / epi_region_bytes<MODE>(32, 1)) >= NW) return 1;
+  if (!Traits<MODE>::kDUAL && stages * (stage_bytes / epi_region_bytes<MODE>(32, 2)) >= NW) return 2;
   return 0;
 }
-template <int MODE>
-constexpr bool epi_staged(int stage_bytes, int stages) { return epi_ncs<MODE>(stage_bytes, stages) > 0; }
-// Rows per chunk: 64 when four wave regions fit in the stage buffers, else 32.
-template <int MODE>
+template <int MODE, int NW = 4>
+constexpr bool epi_staged(int stage_bytes, int stages) { return epi_ncs<MODE, NW>(stage_bytes, stages) > 0; }
+// Rows per chunk: 64 when the NW wave regions fit in the stage buffers, else 32.
+template <int MODE, int NW = 4>
 constexpr int epi_chunk(int stage_bytes, int stages) {
-  return stages * (stage_bytes / epi_region_bytes<MODE>(64, epi_ncs<MODE>(stage_bytes, stages))) >= 4
+  return stages * (stage_bytes / epi_region_bytes<MODE>(64, epi_ncs<MODE, NW>(stage_bytes, stages))) >= NW
              ? 64
              : 32;
 }
@@ -536,7 +542,7 @@ template <int MODE, int BM, int SM, bool SWIGLU_FROM_BF16, int CH, int NCS = 1>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const EpiArgs& a,
                                            const Work& w, int lane, int wm, int wn,
                                            LDS_AS unsigned char* wbuf) {
-  constexpr int WM = BM / 2;
+  constexpr int WM = SM * 32;  // wave tile rows
   const int ncol4 = 4 * (lane >> 5);
   if constexpr (MODE == ROUTER) {
     // fp32 scores, E columns: direct stores (small output)
