@@ -7,9 +7,12 @@
 // layer is dropless ([P3]).  The pages' kernel is prior art for another GPU;
 // this one is written for CDNA4:
 //
-//  * Block tile BM x 256 x BK (BM = 256, or 128 for the down dgrad; BK = 64),
-//    four waves in a 2x2 grid, each wave a (BM/2) x 128 sub-tile of 32x32
-//    MFMA tiles with its accumulators in AGPRs.  One block per CU.
+//  * Block tile BM x 256 x BK with BK = 32: NW waves in an (NW/2) x 2 grid,
+//    each wave a 64 x 128 sub-tile of 32x32 MFMA tiles (128 accumulator
+//    registers, at most 256 registers per wave).  Forward GEMMs and wgrads
+//    run 128 x 256 tiles, four waves, two resident blocks per CU; the dgrads
+//    run 256 x 256 tiles, eight waves, one block per CU (see the tile
+//    configurations below).
 //  * Tiles move HBM -> LDS with buffer loads that write LDS directly (16 bytes
 //    per lane), S stages deep, one static LDS array per stage, explicit vmcnt
 //    waits and a fence-free barrier; no VGPR staging, no VALU transposes.
@@ -238,7 +241,7 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
       boff[j] = ((w.nt * BN + n) * p.ldb + (kk * 2 + kc_half(n, hp)) * 8) * (int)esz;
     } else if (TR::kDUAL) {
       // two sub-tiles of [BK k][128 n]: the first BK/4 instructions fill
-      // matrix 0 (waves 0,1), the rest matrix 1 (waves 2,3)
+      // matrix 0 (the lower half of the waves), the rest matrix 1
       const int qq = q % (BK / 4);
       const int k = qq * 4 + (lane >> 4), pc = lane & 15;
       boff[j] = (k * p.ldb + w.nt * 128 + ((pc ^ swz_mn(k)) << 3)) * (int)esz;

@@ -15,7 +15,7 @@ using moe::sigmoid_f;
 using moe::silu_f;
 
 constexpr int BN = 256;        // block tile columns
-constexpr int kThreads = 256;  // four waves
+constexpr int kThreads = 256;  // four waves (the threads that take part in the tile scans)
 
 #define LDS_AS __attribute__((address_space(3)))
 
