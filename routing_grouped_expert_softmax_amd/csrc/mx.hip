@@ -130,19 +130,21 @@ __global__ void permute_mx_kernel(const uint4* __restrict__ x, const int32_t* __
   }
 }
 
-// Column blocks with groups.  Block (x = 256-column tile, y = 128-deep slice
-// of the padded K space).  The slice's 128 x 256 bf16 source tile is staged in
-// LDS with 16-byte row loads (sixteen in flight per thread); then each thread
-// walks one column of it: four 32-row blocks, one full 128-byte line of codes
-// and one 4-byte scale word.  Group g occupies padded K
-// [P_g, P_g + roundup(n_g, 128)), so a slice lies in exactly one group; its
+// Column blocks with groups.  Block (x = 128-column tile, y = 128-deep slice
+// of the padded K space).  The slice's 128 x 128 bf16 source tile is staged in
+// LDS with 16-byte row loads (eight in flight per thread; 32 KiB, so four
+// blocks fit on a CU and one block's loads overlap another's quantisation);
+// then two threads share each column, each quantising two 32-row blocks:
+// half a 128-byte line of codes and two scale bytes.  Group g occupies padded
+// K [P_g, P_g + roundup(n_g, 128)), so a slice lies in exactly one group; its
 // rows past n_g are zeros (code 0, scale byte 0).  The slice's group comes
 // from a block-wide scan of the padded group sizes (groups from `offsets`, or
 // `urows` rows each when offsets is null).
+constexpr int kColTile = 128;
 __global__ void __launch_bounds__(256) mx_cols_kernel(
     const bf16_t* __restrict__ src, int rows, int cols, const int32_t* __restrict__ offsets,
     int urows, int G, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad_ld) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * 256];
+  __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kColTile];
   __shared__ int sh[256 + 4];
   const int tid = threadIdx.x;
   const int per = (G + 255) / 256;
@@ -186,62 +188,66 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(
   const int g = sh[256], sl = sh[257];
   const int gstart = offsets ? offsets[g] : g * urows;
   const int gend = offsets ? offsets[g + 1] : (g + 1) * urows;
-  const int c0 = blockIdx.x * 256;
+  const int c0 = blockIdx.x * kColTile;
   const int r0 = gstart + sl * 128;
   const int nvalid = min(128, gend - r0);  // >= 1
-  // stage: chunk i = (row i / 32, 8 columns (i % 32) * 8), zeros outside
+  // stage: chunk i = (row i / 16, 8 columns (i % 16) * 8), zeros outside
   {
-    uint4 v[16];
+    uint4 v[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < 8; ++j) {
       const int i = tid + 256 * j;
-      const int row = i >> 5, col = c0 + (i & 31) * 8;
+      const int row = i >> 4, col = c0 + (i & 15) * 8;
       v[j] = (row < nvalid && col < cols)
                  ? *reinterpret_cast<const uint4*>(src + (size_t)(r0 + row) * cols + col)
                  : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) reinterpret_cast<uint4*>(tile)[tid + 256 * j] = v[j];
+    for (int j = 0; j < 8; ++j) reinterpret_cast<uint4*>(tile)[tid + 256 * j] = v[j];
   }
   __syncthreads();
-  const int c = c0 + tid;
-  uint32_t code_words[32];
+  // thread -> (column cl, row half h): blocks 2h and 2h+1 of the column
+  const int cl = tid & (kColTile - 1), h = tid >> 7;
+  const int c = c0 + cl;
+  uint32_t code_words[16];
   uint32_t sword = 0;
 #pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
+  for (int bb = 0; bb < 2; ++bb) {
+    const int blk = 2 * h + bb;
     float f[32];
     float amax = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      f[i] = __uint_as_float(((uint32_t)tile[(blk * 32 + i) * 256 + tid]) << 16);
+      f[i] = __uint_as_float(((uint32_t)tile[(blk * 32 + i) * kColTile + cl]) << 16);
       amax = fmaxf(amax, fabsf(f[i]));
     }
     const int sb = mx_scale_byte(amax);
     const int s = sb - 127;
-    sword |= (uint32_t)sb << (8 * blk);
+    sword |= (uint32_t)sb << (8 * bb);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       uint32_t word = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) word |= e4m3_code(ldexpf(f[q * 4 + j], -s)) << (8 * j);
-      code_words[blk * 8 + q] = word;
+      code_words[bb * 8 + q] = word;
     }
   }
   const size_t k = (size_t)y * 128;  // padded K position of the slice
-  if (c < cols) *reinterpret_cast<uint32_t*>(scales + (size_t)c * (kpad_ld / 32) + k / 32) = sword;
+  if (c < cols)
+    *reinterpret_cast<uint16_t*>(scales + (size_t)c * (kpad_ld / 32) + k / 32 + 2 * h) = (uint16_t)sword;
   // codes go back through LDS (144-byte line pitch against bank conflicts) so
   // that each store instruction writes eight whole 128-byte lines
   constexpr int LP = 144;
   __syncthreads();  // every column has been read out of the tile
   unsigned char* lines = reinterpret_cast<unsigned char*>(tile);
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    *reinterpret_cast<uint4*>(lines + tid * LP + 16 * i) =
+  for (int i = 0; i < 4; ++i)
+    *reinterpret_cast<uint4*>(lines + cl * LP + 64 * h + 16 * i) =
         make_uint4(code_words[4 * i], code_words[4 * i + 1], code_words[4 * i + 2],
                    code_words[4 * i + 3]);
   __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < 4; ++j) {
     const int piece = tid + 256 * j, line = piece >> 3, part = piece & 7;
     if (c0 + line < cols)
       *reinterpret_cast<uint4*>(codes + (size_t)(c0 + line) * kpad_ld + k + 16 * part) =
@@ -270,7 +276,7 @@ hipError_t mx_quantize_cols(const void* src, int rows, int cols, const int32_t* 
                             hipStream_t s) {
   // bound on the padded slices: sum_g ceil(n_g / 128) <= rows / 128 + groups
   const int yb = rows / 128 + groups + 1;
-  dim3 grid((cols + 255) / 256, yb);
+  dim3 grid((cols + kColTile - 1) / kColTile, yb);
   mx_cols_kernel<<<grid, 256, 0, s>>>((const bf16_t*)src, rows, cols, offsets, urows, groups, codes,
                                       scales, kpad_ld);
   return hipGetLastError();
