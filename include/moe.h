@@ -46,6 +46,10 @@
  *  - Preconditions: logits are finite (otherwise routing is unspecified but
  *    memory-safe).  A context is not thread-safe: one context per stream.
  *  - Gradients overwrite their outputs (no accumulation into them).
+ *  - Empty batches: T = 0 (R = 0 rows) is valid for every call.  Pointers to
+ *    token- or row-sized arrays may then be NULL; weights, counts, offsets
+ *    and weight gradients may not.  Routing writes zero counts and offsets,
+ *    and every weight gradient (router and experts) is written as zero.
  */
 #ifndef MOE_H
 #define MOE_H

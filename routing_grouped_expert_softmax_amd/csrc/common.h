@@ -147,5 +147,10 @@ inline int device_cus() {
 #define MOE_REQUIRE_PTR(ctx, p) \
   MOE_REQUIRE(ctx, (p) != nullptr && moe_host::aligned16(p), "%s: null or not 16-byte aligned", #p)
 
+// A pointer may be null exactly when the array it points to is empty.
+#define MOE_REQUIRE_PTR_OR_EMPTY(ctx, p, empty)                                    \
+  MOE_REQUIRE(ctx, (empty) || ((p) != nullptr && moe_host::aligned16(p)),         \
+              "%s: null or not 16-byte aligned", #p)
+
 #define MOE_REQUIRE_DTYPE(ctx, dt) \
   MOE_REQUIRE(ctx, (dt) == MOE_F32 || (dt) == MOE_BF16, "unsupported dtype %d", (int)(dt))

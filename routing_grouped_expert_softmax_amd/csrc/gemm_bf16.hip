@@ -740,18 +740,18 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
   MOE_CHECK_CTX(ctx);
   moe_status st = ffn_validate(ctx, E, R, d, F, dtype, "moe_grouped_ffn_fwd");
   if (st != MOE_OK) return st;
-  MOE_REQUIRE_PTR(ctx, xp);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, xp, R == 0);
   MOE_REQUIRE_PTR(ctx, w_gate);
   MOE_REQUIRE_PTR(ctx, w_up);
   MOE_REQUIRE_PTR(ctx, offsets);
-  MOE_REQUIRE_PTR(ctx, g);
-  MOE_REQUIRE_PTR(ctx, u);
-  MOE_REQUIRE_PTR(ctx, h);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, g, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, u, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, h, R == 0);
   // w_down and yp both NULL: the gate/up GEMM alone (recompute of g, u, h)
   const bool up_only = w_down == nullptr && yp == nullptr;
   if (!up_only) {
     MOE_REQUIRE_PTR(ctx, w_down);
-    MOE_REQUIRE_PTR(ctx, yp);
+    MOE_REQUIRE_PTR_OR_EMPTY(ctx, yp, R == 0);
   }
   if (R == 0) return MOE_OK;
   if (dtype == MOE_MXFP8)
@@ -819,16 +819,16 @@ moe_status moe_grouped_ffn_fwd_mxq(moe_ctx* ctx, const uint8_t* xp_codes, const 
   MOE_CHECK_CTX(ctx);
   moe_status st = ffn_validate(ctx, E, R, d, F, MOE_MXFP8, "moe_grouped_ffn_fwd_mxq");
   if (st != MOE_OK) return st;
-  MOE_REQUIRE_PTR(ctx, xp_codes);
-  MOE_REQUIRE(ctx, xp_scales != nullptr, "moe_grouped_ffn_fwd_mxq: xp_scales is null");
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, xp_codes, R == 0);
+  MOE_REQUIRE(ctx, R == 0 || xp_scales != nullptr, "moe_grouped_ffn_fwd_mxq: xp_scales is null");
   MOE_REQUIRE_PTR(ctx, w_gate);
   MOE_REQUIRE_PTR(ctx, w_up);
   MOE_REQUIRE_PTR(ctx, w_down);
   MOE_REQUIRE_PTR(ctx, offsets);
-  MOE_REQUIRE_PTR(ctx, g);
-  MOE_REQUIRE_PTR(ctx, u);
-  MOE_REQUIRE_PTR(ctx, h);
-  MOE_REQUIRE_PTR(ctx, yp);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, g, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, u, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, h, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, yp, R == 0);
   if (R == 0) return MOE_OK;
   return moe_internal_ffn_fwd_mx(ctx, nullptr, xp_codes, xp_scales, (const bf16_t*)w_gate,
                                  (const bf16_t*)w_up, (const bf16_t*)w_down, offsets, E, R, d, F,
@@ -843,18 +843,18 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
   MOE_CHECK_CTX(ctx);
   moe_status st = ffn_validate(ctx, E, R, d, F, dtype, "moe_grouped_ffn_bwd");
   if (st != MOE_OK) return st;
-  MOE_REQUIRE_PTR(ctx, xp);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, xp, R == 0);
   MOE_REQUIRE_PTR(ctx, w_gate);
   MOE_REQUIRE_PTR(ctx, w_up);
   MOE_REQUIRE_PTR(ctx, w_down);
   MOE_REQUIRE_PTR(ctx, offsets);
-  MOE_REQUIRE_PTR(ctx, g);
-  MOE_REQUIRE_PTR(ctx, u);
-  MOE_REQUIRE_PTR(ctx, h);
-  MOE_REQUIRE_PTR(ctx, dyp);
-  MOE_REQUIRE_PTR(ctx, dg);
-  MOE_REQUIRE_PTR(ctx, du);
-  MOE_REQUIRE_PTR(ctx, dxp);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, g, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, u, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, h, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dyp, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dg, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, du, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dxp, R == 0);
   MOE_REQUIRE_PTR(ctx, dw_gate);
   MOE_REQUIRE_PTR(ctx, dw_up);
   MOE_REQUIRE_PTR(ctx, dw_down);

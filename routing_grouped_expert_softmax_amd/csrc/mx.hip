@@ -307,9 +307,9 @@ extern "C" moe_status moe_mx_quantize(moe_ctx* ctx, const void* src_bf16, int ro
   MOE_CHECK_CTX(ctx);
   MOE_REQUIRE(ctx, rows >= 0 && cols >= 32 && cols % 32 == 0, "moe_mx_quantize: bad shape");
   MOE_REQUIRE(ctx, axis == 0 || axis == 1, "moe_mx_quantize: axis must be 0 or 1");
-  MOE_REQUIRE_PTR(ctx, src_bf16);
-  MOE_REQUIRE_PTR(ctx, codes);
-  MOE_REQUIRE(ctx, scales_e8m0 != nullptr, "moe_mx_quantize: scales is null");
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, src_bf16, rows == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, codes, rows == 0);
+  MOE_REQUIRE(ctx, rows == 0 || scales_e8m0 != nullptr, "moe_mx_quantize: scales is null");
   if (rows == 0) return MOE_OK;
   moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
   hipError_t e;

@@ -484,9 +484,9 @@ moe_status moe_router_logits(moe_ctx* ctx, const void* x, const void* w_router, 
   MOE_REQUIRE_DTYPE(ctx, dtype);
   MOE_REQUIRE(ctx, T_ >= 0 && d >= 8 && d % 8 == 0 && E >= 1 && E <= 1024,
               "moe_router_logits: bad shape T=%d d=%d E=%d", T_, d, E);
-  MOE_REQUIRE_PTR(ctx, x);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, x, T_ == 0);
   MOE_REQUIRE_PTR(ctx, w_router);
-  MOE_REQUIRE_PTR(ctx, logits);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, logits, T_ == 0);
   if (T_ == 0) return MOE_OK;
   moe_prof_scope ps(ctx, MOE_K_ROUTER_LOGITS);
   if (dtype == MOE_BF16 && E > 16 && E % 8 == 0)
@@ -524,13 +524,13 @@ moe_status moe_route(moe_ctx* ctx, const float* logits, int T_, int E, int k, in
   MOE_REQUIRE(ctx, T_ >= 0 && E >= 1 && E <= 1024 && k >= 1 && k <= E && k <= 32,
               "moe_route: bad shape T=%d E=%d k=%d", T_, E, k);
   MOE_REQUIRE(ctx, (int64_t)T_ * k < (int64_t)1 << 31, "moe_route: T*k >= 2^31");
-  MOE_REQUIRE_PTR(ctx, logits);
-  MOE_REQUIRE_PTR(ctx, topk_idx);
-  MOE_REQUIRE_PTR(ctx, gates);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, logits, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, topk_idx, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, gates, T_ == 0);
   MOE_REQUIRE_PTR(ctx, counts);
   MOE_REQUIRE_PTR(ctx, offsets);
-  MOE_REQUIRE_PTR(ctx, row_of);
-  MOE_REQUIRE_PTR(ctx, src_tk);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, row_of, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, src_tk, T_ == 0);
   const size_t need = route_ws_bytes(T_, E);
   if (ctx->ws == nullptr || ctx->ws_bytes < need)
     return fail(ctx, MOE_ERR_WORKSPACE, "moe_route: workspace %zu bytes < %zu needed",
@@ -562,9 +562,9 @@ moe_status moe_route_bwd(moe_ctx* ctx, const float* gates, const float* dgates, 
                          float* dlogits_sel) {
   MOE_CHECK_CTX(ctx);
   MOE_REQUIRE(ctx, T_ >= 0 && k >= 1 && k <= 32, "moe_route_bwd: bad shape T=%d k=%d", T_, k);
-  MOE_REQUIRE_PTR(ctx, gates);
-  MOE_REQUIRE_PTR(ctx, dgates);
-  MOE_REQUIRE_PTR(ctx, dlogits_sel);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, gates, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dgates, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dlogits_sel, T_ == 0);
   if (T_ == 0) return MOE_OK;
   moe_prof_scope ps(ctx, MOE_K_ROUTE_BWD);
   route_bwd_kernel<<<(T_ + 255) / 256, 256, 0, ctx->stream>>>(gates, dgates, T_, k, dlogits_sel);
@@ -578,9 +578,9 @@ moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_se
   MOE_REQUIRE_DTYPE(ctx, dtype);
   MOE_REQUIRE(ctx, T_ >= 0 && d >= 8 && d % 8 == 0 && E >= 1 && E <= 1024 && k >= 1 && k <= E,
               "moe_router_wgrad: bad shape");
-  MOE_REQUIRE_PTR(ctx, x);
-  MOE_REQUIRE_PTR(ctx, dlogits_sel);
-  MOE_REQUIRE_PTR(ctx, src_tk);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, x, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dlogits_sel, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, src_tk, T_ == 0);
   MOE_REQUIRE_PTR(ctx, offsets);
   MOE_REQUIRE_PTR(ctx, dw_router);
   const int fc = dtype == MOE_BF16 ? 512 : 256;  // features per block (64 lanes x 16 bytes)

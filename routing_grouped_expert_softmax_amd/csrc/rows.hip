@@ -351,9 +351,9 @@ moe_status moe_permute(moe_ctx* ctx, const void* x, const int32_t* row_of, int T
   MOE_CHECK_CTX(ctx);
   moe_status st = rows_common(ctx, T_, d, k, dtype, "moe_permute");
   if (st != MOE_OK) return st;
-  MOE_REQUIRE_PTR(ctx, x);
-  MOE_REQUIRE_PTR(ctx, row_of);
-  MOE_REQUIRE_PTR(ctx, xp);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, x, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, row_of, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, xp, T_ == 0);
   if (T_ == 0) return MOE_OK;
   const int nchunk = (int)(d * esize(dtype) / 16);
   moe_prof_scope ps(ctx, MOE_K_PERMUTE);
@@ -370,10 +370,10 @@ static moe_status combine_impl(moe_ctx* ctx, const void* yp, const float* gates,
   MOE_CHECK_CTX(ctx);
   moe_status st = rows_common(ctx, T_, d, k, dtype, "moe_combine");
   if (st != MOE_OK) return st;
-  MOE_REQUIRE_PTR(ctx, yp);
-  MOE_REQUIRE_PTR(ctx, gates);
-  MOE_REQUIRE_PTR(ctx, row_of);
-  MOE_REQUIRE_PTR(ctx, y);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, yp, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, gates, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, row_of, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, y, T_ == 0);
   if (T_ == 0) return MOE_OK;
   const int nchunk = (int)(d * esize(dtype) / 16);
   moe_prof_scope ps(ctx, MOE_K_COMBINE);
@@ -409,12 +409,12 @@ moe_status moe_combine_bwd(moe_ctx* ctx, const void* dy, const void* yp, const f
   MOE_CHECK_CTX(ctx);
   moe_status st = rows_common(ctx, T_, d, k, dtype, "moe_combine_bwd");
   if (st != MOE_OK) return st;
-  MOE_REQUIRE_PTR(ctx, dy);
-  MOE_REQUIRE_PTR(ctx, yp);
-  MOE_REQUIRE_PTR(ctx, gates);
-  MOE_REQUIRE_PTR(ctx, row_of);
-  MOE_REQUIRE_PTR(ctx, dyp);
-  MOE_REQUIRE_PTR(ctx, dgates);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dy, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, yp, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, gates, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, row_of, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dyp, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dgates, T_ == 0);
   if (T_ == 0) return MOE_OK;
   const int nchunk = (int)(d * esize(dtype) / 16);
   moe_prof_scope ps(ctx, MOE_K_COMBINE_BWD);
@@ -438,13 +438,13 @@ static moe_status permute_bwd_impl(moe_ctx* ctx, const void* dxp, const int32_t*
   MOE_CHECK_CTX(ctx);
   moe_status st = rows_common(ctx, T_, d, k, dtype, "moe_permute_bwd");
   if (st != MOE_OK) return st;
-  MOE_REQUIRE_PTR(ctx, dxp);
-  MOE_REQUIRE_PTR(ctx, row_of);
-  MOE_REQUIRE_PTR(ctx, dx);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dxp, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, row_of, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dx, T_ == 0);
   const bool router = dlogits_sel != nullptr && w_router != nullptr;
   if (router) {
     MOE_REQUIRE(ctx, E >= 1 && E <= 1024 && k <= E, "moe_permute_bwd: bad E=%d", E);
-    MOE_REQUIRE_PTR(ctx, topk_idx);
+    MOE_REQUIRE_PTR_OR_EMPTY(ctx, topk_idx, T_ == 0);
     MOE_REQUIRE_PTR(ctx, dlogits_sel);
     MOE_REQUIRE_PTR(ctx, w_router);
     const size_t need = moe_internal_wrt_bytes(d, E, dtype);
