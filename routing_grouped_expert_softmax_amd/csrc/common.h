@@ -43,12 +43,12 @@ struct moe_prof_scope {
       }
       s->ev.emplace_back(a, b);
     }
-    hipEventRecord(s->ev[s->used].first, c->stream);
+    // a failed record leaves this launch untimed (the pair is reused)
+    if (hipEventRecord(s->ev[s->used].first, c->stream) != hipSuccess) s = nullptr;
   }
   ~moe_prof_scope() {
     if (!s) return;
-    hipEventRecord(s->ev[s->used].second, c->stream);
-    s->used++;
+    if (hipEventRecord(s->ev[s->used].second, c->stream) == hipSuccess) s->used++;
   }
 };
 

@@ -7,11 +7,11 @@
 // layer is dropless ([P3]).  The pages' kernel is prior art for another GPU;
 // this one is written for CDNA4:
 //
-//  * Block tile BM x 256 x BK with BK = 32: NW waves in an (NW/2) x 2 grid,
-//    each wave a 64 x 128 sub-tile of 32x32 MFMA tiles (128 accumulator
-//    registers, at most 256 registers per wave).  Forward GEMMs and wgrads
-//    run 128 x 256 tiles, four waves, two resident blocks per CU; the dgrads
-//    run 256 x 256 tiles, eight waves, one block per CU (see the tile
+//  * Block tile BM x 256 x BK: NW waves in an (NW/2) x 2 grid, each wave a
+//    64 x 128 sub-tile of 32x32 MFMA tiles (128 accumulator registers, at
+//    most 256 registers per wave).  The forward GEMMs and the wgrads run
+//    128 x 256 x 32 tiles, four waves, two resident blocks per CU; the dgrads
+//    run 256 x 256 x 64 tiles, eight waves, one block per CU (see the tile
 //    configurations below).
 //  * Tiles move HBM -> LDS with buffer loads that write LDS directly (16 bytes
 //    per lane), S stages deep, one static LDS array per stage, explicit vmcnt
@@ -506,13 +506,18 @@ hipError_t launch(const Params& p, int blocks, hipStream_t s) {
 
 // Tile configurations: rows per tile, pipeline stages, K step, blocks per
 // CU, waves per block.  Two resident blocks per CU (128x256 tiles, 32-deep K
-// steps, 72 KiB of LDS and at most 256 registers per wave) let one block's
-// prologue, barriers and output stores overlap the other block's MFMAs on the
-// same SIMDs.  The two dgrads instead run one 256x256 block per CU with eight
-// waves (64x128 wave tiles, two waves per SIMD): a third less L2->LDS traffic
-// per FLOP and a deeper prefetch, which outweighs the lost overlap there
-// (measured per mode).  (The down dgrad's epilogue, which also streams the
-// saved g and u, stages its columns in two passes to fit.)
+// steps in three stages, 72 KiB of LDS, at most 256 registers per wave) let
+// one block's prologue, barriers and output stores overlap the other block's
+// MFMAs on the same SIMDs; the forward GEMMs and the wgrads run so.  The two
+// dgrads instead run one 256x256 block per CU with eight waves (64x128 wave
+// tiles, two waves per SIMD) and 64-deep K steps in two 64 KiB stages: a
+// third less L2->LDS traffic per FLOP and half the barriers, which outweighs
+// the lost overlap there.  In the forward GEMMs, whose epilogues are heavier,
+// 256-row tiles lose: at a few hundred rows per expert an expert's last
+// 256-row tile is often nearly empty yet loads a full weight tile (measured
+// per mode on routed counts).  (The down dgrad's epilogue, which also streams
+// the saved g and u, stages its columns in two 64-column passes of 32 rows
+// to bound its registers.)
 #ifndef GEMM_M_CFG
 #define GEMM_M_CFG 128, 3, 32, 2   // forward gate/up and down
 #endif
@@ -523,10 +528,10 @@ hipError_t launch(const Params& p, int blocks, hipStream_t s) {
 #define GEMM_DN_CFG GEMM_M_CFG     // forward down
 #endif
 #ifndef GEMM_DU_CFG
-#define GEMM_DU_CFG 256, 3, 32, 1, 8  // gate/up dgrad
+#define GEMM_DU_CFG 256, 2, 64, 1, 8  // gate/up dgrad
 #endif
 #ifndef GEMM_DD_CFG
-#define GEMM_DD_CFG 256, 3, 32, 1, 8  // down dgrad
+#define GEMM_DD_CFG 256, 2, 64, 1, 8  // down dgrad
 #endif
 #ifndef GEMM_W_CFG
 #define GEMM_W_CFG 128, 3, 32, 2   // both wgrads

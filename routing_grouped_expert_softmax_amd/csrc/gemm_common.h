@@ -518,6 +518,9 @@ constexpr int epi_region_bytes(int ch, int ncs) {
 template <int MODE, int NW = 4>
 constexpr int epi_ncs(int stage_bytes, int stages) {
   if (MODE == ROUTER) return 0;
+  // the down dgrad prefetches g and u of the next chunk into registers: two
+  // 64-column passes keep that prefetch at 32 VGPRs per lane
+  if (MODE == DGRAD_DOWN && stages * (stage_bytes / epi_region_bytes<MODE>(32, 2)) >= NW) return 2;
   if (stages * (stage_bytes / epi_region_bytes<MODE>(32, 1)) >= NW) return 1;
   if (!Traits<MODE>::kDUAL && stages * (stage_bytes / epi_region_bytes<MODE>(32, 2)) >= NW) return 2;
   return 0;
@@ -527,6 +530,7 @@ constexpr bool epi_staged(int stage_bytes, int stages) { return epi_ncs<MODE, NW
 // Rows per chunk: 64 when the NW wave regions fit in the stage buffers, else 32.
 template <int MODE, int NW = 4>
 constexpr int epi_chunk(int stage_bytes, int stages) {
+  if (MODE == DGRAD_DOWN) return 32;  // register budget of the g, u prefetch
   return stages * (stage_bytes / epi_region_bytes<MODE>(64, epi_ncs<MODE, NW>(stage_bytes, stages))) >= NW
              ? 64
              : 32;
