@@ -203,6 +203,13 @@ moe_status moe_combine_bwd(moe_ctx* ctx, const void* dy, const void* yp, const f
 moe_status moe_route_bwd(moe_ctx* ctx, const float* gates, const float* dgates, int T, int k,
                          float* dlogits_sel);
 
+/* moe_route_bwd that also writes each value in expert-row order,
+ * dl_rows[row_of[t,j]] = dlogits_sel[t,j] (dl_rows [T*k] fp32), the form the
+ * folded router term of moe_grouped_ffn_bwd_router reads. */
+moe_status moe_route_bwd_rows(moe_ctx* ctx, const float* gates, const float* dgates,
+                              const int32_t* row_of, int T, int k, float* dlogits_sel,
+                              float* dl_rows);
+
 /* Backward of moe_grouped_ffn_fwd for upstream rows dyp [R,d]:
  *   dh = dyp Wd[e]^T;  dg = dh * u * silu'(g);  du = dh * silu(g)
  *   dxp = dg Wg[e]^T + du Wu[e]^T
@@ -214,6 +221,24 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
                                const void* g, const void* u, const void* h, const void* dyp,
                                int E, int R, int d, int F, moe_dtype dtype, void* dg, void* du,
                                void* dxp, void* dw_gate, void* dw_up, void* dw_down);
+
+/* moe_grouped_ffn_bwd with the router's share of the input gradient folded
+ * into the gate/up dgrad (MOE_BF16 only).  Row r of expert e holds token t's
+ * slot j; dl_rows[r] = dlogits_sel[t,j] (from moe_route_bwd_rows).  Its fp32
+ * sum gets dl_rows[r] * w_router[:,e] before the one rounding:
+ *   dxp[r] = dg Wg[e]^T + du Wu[e]^T + dlogits_sel[t,j] * W_r[:,e]
+ * so moe_permute_bwd without the router term (dlogits_sel, w_router NULL)
+ * then gives the whole input gradient of the layer, the router's included
+ * (the router scores are x W_r, W_r [d,E] bf16).  Every other output as in
+ * moe_grouped_ffn_bwd.  dl_rows [R] fp32 may be NULL only when R == 0;
+ * another dtype returns MOE_ERR_INVALID_ARGUMENT. */
+moe_status moe_grouped_ffn_bwd_router(moe_ctx* ctx, const void* xp, const void* w_gate,
+                                      const void* w_up, const void* w_down,
+                                      const int32_t* offsets, const void* g, const void* u,
+                                      const void* h, const void* dyp, const float* dl_rows,
+                                      const void* w_router, int E, int R, int d, int F,
+                                      moe_dtype dtype, void* dg, void* du, void* dxp,
+                                      void* dw_gate, void* dw_up, void* dw_down);
 
 /* dx[t] = sum_j dxp[row_of[t,j]]  (+ sum_j dlogits_sel[t,j] * w_router[:, topk_idx[t,j]]
  * when dlogits_sel and w_router are both non-NULL), fp32 accumulation. */

@@ -42,6 +42,9 @@ _SIGS = {
     "moe_route_bwd": [_vp, _vp, _int, _int, _vp],
     "moe_grouped_ffn_bwd": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int,
                             _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_grouped_ffn_bwd_router": [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _int,
+                                   _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_route_bwd_rows": [_vp, _vp, _vp, _int, _int, _vp, _vp],
     "moe_permute_bwd": [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
     "moe_router_wgrad": [_vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp],
     "moe_mx_quantize": [_vp, _int, _int, _int, _vp, _int, _vp, _vp, _int],
@@ -334,17 +337,28 @@ def moe_combine_bwd(dy, yp, gates, row_of, dyp=None, dgates=None):
     return dyp, dgates
 
 
-def moe_route_bwd(gates, dgates, dlogits_sel=None):
-    _need_cuda(gates, dgates)
+def moe_route_bwd(gates, dgates, dlogits_sel=None, row_of=None, dl_rows=None):
+    """Logit gradient at the selected slots [T,k]; with row_of also returns
+    dl_rows [T*k], the same values in expert-row order."""
+    _need_cuda(gates, dgates, row_of, dl_rows)
     T, k = gates.shape
     if dlogits_sel is None:
         dlogits_sel = torch.empty(T, k, dtype=torch.float32, device=gates.device)
-    context(gates.device.index).call("moe_route_bwd", _p(gates), _p(dgates), T, k, _p(dlogits_sel))
-    return dlogits_sel
+    ctx = context(gates.device.index)
+    if row_of is None:
+        ctx.call("moe_route_bwd", _p(gates), _p(dgates), T, k, _p(dlogits_sel))
+        return dlogits_sel
+    if dl_rows is None:
+        dl_rows = torch.empty(T * k, dtype=torch.float32, device=gates.device)
+    ctx.call("moe_route_bwd_rows", _p(gates), _p(dgates), _p(row_of), T, k, _p(dlogits_sel), _p(dl_rows))
+    return dlogits_sel, dl_rows
 
 
-def moe_grouped_ffn_bwd(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp, out=None, mxfp8=False):
-    """Returns dict(dg, du, dxp, dw_gate, dw_up, dw_down)."""
+def moe_grouped_ffn_bwd(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp, out=None, mxfp8=False, router=None):
+    """Returns dict(dg, du, dxp, dw_gate, dw_up, dw_down).  router =
+    (dl_rows [R] fp32, w_router [d,E]) folds the router's input-gradient
+    term into dxp (bf16 only): row r of expert e then also holds
+    dl_rows[r] * w_router[:, e] (dl_rows from moe_route_bwd(..., row_of))."""
     _need_cuda(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp)
     R, d = xp.shape
     E, _, F = w_gate.shape
@@ -356,10 +370,21 @@ def moe_grouped_ffn_bwd(xp, w_gate, w_up, w_down, offsets, g, u, h, dyp, out=Non
                    dxp=torch.empty(R, d, dtype=tdt, device=dev),
                    dw_gate=torch.empty_like(w_gate), dw_up=torch.empty_like(w_up),
                    dw_down=torch.empty_like(w_down))
-    context(xp.device.index).call("moe_grouped_ffn_bwd", _p(xp), _p(w_gate), _p(w_up), _p(w_down),
-                                  _p(offsets), _p(g), _p(u), _p(h), _p(dyp), E, R, d, F, dt,
-                                  _p(out["dg"]), _p(out["du"]), _p(out["dxp"]), _p(out["dw_gate"]),
-                                  _p(out["dw_up"]), _p(out["dw_down"]))
+    outs = (_p(out["dg"]), _p(out["du"]), _p(out["dxp"]), _p(out["dw_gate"]), _p(out["dw_up"]),
+            _p(out["dw_down"]))
+    if router is None:
+        context(xp.device.index).call("moe_grouped_ffn_bwd", _p(xp), _p(w_gate), _p(w_up), _p(w_down),
+                                      _p(offsets), _p(g), _p(u), _p(h), _p(dyp), E, R, d, F, dt, *outs)
+    else:
+        dl_rows, w_router = router
+        _need_cuda(dl_rows, w_router)
+        if w_router.shape != (d, E):
+            raise MoeError(f"w_router must be [{d}, {E}], got {tuple(w_router.shape)}")
+        if dl_rows.numel() < R or dl_rows.dtype != torch.float32:
+            raise MoeError("dl_rows must be fp32 with R entries")
+        context(xp.device.index).call("moe_grouped_ffn_bwd_router", _p(xp), _p(w_gate), _p(w_up), _p(w_down),
+                                      _p(offsets), _p(g), _p(u), _p(h), _p(dyp), _p(dl_rows),
+                                      _p(w_router), E, R, d, F, dt, *outs)
     return out
 
 
@@ -478,6 +503,7 @@ class LayerBuffers:
     xq: torch.Tensor | None = None  # MXFP8 codes of xp (quantise-on-permute)
     xs: torch.Tensor | None = None  # their scale bytes
     shared: dict | None = None      # shared expert: offsets {0,T}, its forward and backward buffers
+    dl_rows: torch.Tensor | None = None  # logit gradients in expert-row order (bf16 router fold)
 
 
 def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False, shared_F=0):
@@ -494,7 +520,8 @@ def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False, shared_F=0):
                dw_down=z(E, F, d))
     buf = LayerBuffers(logits=z(T, E, dt=torch.float32), route=route, xp=z(R, d), ffn=ffn, y=z(T, d),
                        dyp=z(R, d), dgates=z(T, k, dt=torch.float32),
-                       dlogits_sel=z(T, k, dt=torch.float32), bwd=bwd, dx=z(T, d), dw_router=z(d, E))
+                       dlogits_sel=z(T, k, dt=torch.float32), bwd=bwd, dx=z(T, d), dw_router=z(d, E),
+                       dl_rows=z(R, dt=torch.float32))
     if shared_F:
         Fs = shared_F
         buf.shared = dict(offsets=torch.tensor([0, T], dtype=torch.int32, device=dev),
@@ -549,7 +576,10 @@ def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logit
 def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxfp8=False, shared=None,
                    recompute=False):
     """combine_bwd -> route_bwd -> grouped FFN bwd -> permute_bwd (+router
-    dgrad) -> router wgrad.  Returns dx; weight grads are in buf.bwd and
+    dgrad) -> router wgrad.  In bf16 the router's input-gradient term is
+    folded into the gate/up dgrad (moe_grouped_ffn_bwd_router) and the
+    permute backward only sums rows; fp32 and MXFP8 add it in the permute
+    backward.  Returns dx; weight grads are in buf.bwd and
     buf.dw_router.  recompute=True reads from the forward only yp, the gates
     and the routing: xp is permuted again from x and g, u, h (the shared
     expert's too) are recomputed by the gate/up GEMM before they are used,
@@ -561,16 +591,24 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxf
         if shared is not None:
             moe_grouped_ffn_up(x, shared[0], shared[1], buf.shared["offsets"], buf.shared["ffn"], mxfp8=mxfp8)
     moe_combine_bwd(dy, buf.ffn["yp"], r["gates"], r["row_of"], buf.dyp, buf.dgates)
-    moe_route_bwd(r["gates"], buf.dgates, buf.dlogits_sel)
+    fold = not mxfp8 and buf.xp.dtype == torch.bfloat16
+    if fold:
+        moe_route_bwd(r["gates"], buf.dgates, buf.dlogits_sel, row_of=r["row_of"], dl_rows=buf.dl_rows)
+    else:
+        moe_route_bwd(r["gates"], buf.dgates, buf.dlogits_sel)
     moe_grouped_ffn_bwd(buf.xp, w_gate, w_up, w_down, r["offsets"], buf.ffn["g"], buf.ffn["u"],
-                        buf.ffn["h"], buf.dyp, buf.bwd, mxfp8=mxfp8)
+                        buf.ffn["h"], buf.dyp, buf.bwd, mxfp8=mxfp8,
+                        router=(buf.dl_rows, w_router) if fold else None)
     dxs = None
     if shared is not None:
         sh = buf.shared
         moe_grouped_ffn_bwd(x, *shared, sh["offsets"], sh["ffn"]["g"], sh["ffn"]["u"], sh["ffn"]["h"], dy,
                             sh["bwd"], mxfp8=mxfp8)
         dxs = sh["bwd"]["dxp"]
-    moe_permute_bwd(buf.bwd["dxp"], r["row_of"], r["topk_idx"], buf.dlogits_sel, w_router, buf.dx,
-                    dx_shared=dxs)
+    if fold:
+        moe_permute_bwd(buf.bwd["dxp"], r["row_of"], dx=buf.dx, dx_shared=dxs)
+    else:
+        moe_permute_bwd(buf.bwd["dxp"], r["row_of"], r["topk_idx"], buf.dlogits_sel, w_router, buf.dx,
+                        dx_shared=dxs)
     moe_router_wgrad(x, buf.dlogits_sel, r["src_tk"], r["offsets"], w_router.shape[1], buf.dw_router)
     return buf.dx

@@ -74,6 +74,10 @@ struct Params {
   int ntiles;  // tiles along N
   int mtiles;  // tiles along M (K-ragged)
   int part;    // K-ragged: store exact fp32 split-K partials instead of bf16
+  // DGRAD_UP, optional router term: row r of expert e gets
+  // rdl[r] * rw[:, e] (rw is the [N, E] router weight matrix)
+  const float* rdl;
+  const bf16_t* rw;
 };
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -125,6 +129,9 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) unsigned char lds2[S > 2 ? TL::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char lds3[S > 3 ? TL::STAGE : 16];
   __shared__ int sh[kThreads + 4];
+  // router term (DGRAD_UP): the tile's W_r column and its rows' logit gradients
+  __shared__ float rcol[MODE == DGRAD_UP ? BN : 1];
+  __shared__ float rrow[MODE == DGRAD_UP ? BM : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -406,9 +413,29 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
+  // Router term (DGRAD_UP): its two small loads go out before the first
+  // stage's and land in LDS before the first K step's barrier (the wait the
+  // compiler puts before the LDS writes ends with the first stage's loads,
+  // which the first step waits for anyway at two stages).  The previous
+  // tile's epilogue read these arrays before this tile's first barrier.
+  float rwv = 0.f, rdv = 0.f;
+  const bool rterm = MODE == DGRAD_UP && p.rdl != nullptr;
+  if (rterm) {
+    if (tid < BN) {
+      const int col = w.nt * BN + tid;
+      rwv = col < p.N ? bf2f(p.rw[(size_t)col * p.E + w.e]) : 0.f;
+    }
+    if (tid < BM) rdv = tid < w.rows ? p.rdl[w.row0 + tid] : 0.f;
+  }
   if (0 < nk) issue(0, I0{});
   if (S > 2 && 1 < nk) issue(1, I1{});
   if (S > 3 && 2 < nk) issue(2, I2{});
+  if constexpr (MODE == DGRAD_UP) {
+    if (rterm) {
+      if (tid < BN) rcol[tid] = rwv;
+      if (tid < BM) rrow[tid] = rdv;
+    }
+  }
   // One K step on stage CUR, loading step kt+S-1 into stage NXT.  The wait
   // covers only this wave's loads of step kt (later steps stay in flight);
   // the barrier has no memory fence (a fence would drain every load).
@@ -459,6 +486,26 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
     main_loop(std::false_type{});
   // all waves are done with the stage buffers before the block exits
   asm volatile("s_barrier" ::: "memory");
+
+  if constexpr (MODE == DGRAD_UP) {
+    if (p.rdl != nullptr) {
+      // Router term of the input gradient, a rank-1 update of the fp32 tile:
+      // acc[m][n] += dl(row m) * W_r[n][e], both factors staged in LDS at the
+      // start of the tile.
+      float dlv[SM];
+#pragma unroll
+      for (int sm = 0; sm < SM; ++sm) dlv[sm] = rrow[wm * TL::WM + sm * 32 + (lane & 31)];
+      const int ncol4 = 4 * (lane >> 5);
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float wv = rcol[wn * 128 + sn * 32 + 8 * (r >> 2) + ncol4 + (r & 3)];
+#pragma unroll
+          for (int sm = 0; sm < SM; ++sm) acc[sm][sn][r] += dlv[sm] * wv;
+        }
+    }
+  }
 
   // ---------------------------------------------------------------- epilogue
   EpiArgs ea{p.c0, p.c1, p.c2, p.ldc, p.c_gstride, p.aux0, p.aux1, p.N, p.M};
@@ -840,11 +887,12 @@ moe_status moe_grouped_ffn_fwd_mxq(moe_ctx* ctx, const uint8_t* xp_codes, const 
                                  (bf16_t*)g, (bf16_t*)u, (bf16_t*)h, (bf16_t*)yp);
 }
 
-moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
+static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
                                const void* w_up, const void* w_down, const int32_t* offsets,
                                const void* g, const void* u, const void* h, const void* dyp,
                                int E, int R, int d, int F, moe_dtype dtype, void* dg, void* du,
-                               void* dxp, void* dw_gate, void* dw_up, void* dw_down) {
+                               void* dxp, void* dw_gate, void* dw_up, void* dw_down,
+                               const float* dl_rows, const void* rw) {
   MOE_CHECK_CTX(ctx);
   moe_status st = ffn_validate(ctx, E, R, d, F, dtype, "moe_grouped_ffn_bwd");
   if (st != MOE_OK) return st;
@@ -962,6 +1010,8 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.N = d;
     p.K = 2 * F;
     p.kseg = F;
+    p.rdl = dl_rows;
+    p.rw = (const bf16_t*)rw;
     p.ntiles = (d + BN - 1) / BN;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_DGRAD_UP);
@@ -1012,6 +1062,30 @@ moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up wgrad: %s", hipGetErrorString(e));
   }
   return MOE_OK;
+}
+
+moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,
+                               const void* w_up, const void* w_down, const int32_t* offsets,
+                               const void* g, const void* u, const void* h, const void* dyp,
+                               int E, int R, int d, int F, moe_dtype dtype, void* dg, void* du,
+                               void* dxp, void* dw_gate, void* dw_up, void* dw_down) {
+  return ffn_bwd_impl(ctx, xp, w_gate, w_up, w_down, offsets, g, u, h, dyp, E, R, d, F, dtype, dg,
+                      du, dxp, dw_gate, dw_up, dw_down, nullptr, nullptr);
+}
+
+moe_status moe_grouped_ffn_bwd_router(moe_ctx* ctx, const void* xp, const void* w_gate,
+                                      const void* w_up, const void* w_down,
+                                      const int32_t* offsets, const void* g, const void* u,
+                                      const void* h, const void* dyp,
+                                      const float* dl_rows, const void* w_router, int E, int R,
+                                      int d, int F, moe_dtype dtype, void* dg, void* du,
+                                      void* dxp, void* dw_gate, void* dw_up, void* dw_down) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, dtype == MOE_BF16, "moe_grouped_ffn_bwd_router: bf16 only");
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dl_rows, R == 0);
+  MOE_REQUIRE_PTR(ctx, w_router);
+  return ffn_bwd_impl(ctx, xp, w_gate, w_up, w_down, offsets, g, u, h, dyp, E, R, d, F, dtype, dg,
+                      du, dxp, dw_gate, dw_up, dw_down, dl_rows, w_router);
 }
 
 }  // extern "C"

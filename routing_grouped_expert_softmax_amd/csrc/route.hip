@@ -373,14 +373,19 @@ __global__ void fill_i32_kernel(int32_t* p, int n, int v) {
 
 // ---------------------------------------------------------------- backward
 __global__ void route_bwd_kernel(const float* __restrict__ gates, const float* __restrict__ dgates,
-                                 int T_, int k, float* __restrict__ dls) {
+                                 int T_, int k, float* __restrict__ dls,
+                                 const int32_t* __restrict__ row_of, float* __restrict__ dl_rows) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= T_) return;
   const float* g = gates + (size_t)t * k;
   const float* dg = dgates + (size_t)t * k;
   float s = 0.f;
   for (int j = 0; j < k; ++j) s += g[j] * dg[j];
-  for (int j = 0; j < k; ++j) dls[(size_t)t * k + j] = g[j] * (dg[j] - s);
+  for (int j = 0; j < k; ++j) {
+    const float v = g[j] * (dg[j] - s);
+    dls[(size_t)t * k + j] = v;
+    if (dl_rows) dl_rows[row_of[(size_t)t * k + j]] = v;  // expert-row order
+  }
 }
 
 // Router weight gradient.  One block per (expert, 64*V-feature chunk), V
@@ -567,8 +572,26 @@ moe_status moe_route_bwd(moe_ctx* ctx, const float* gates, const float* dgates, 
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, dlogits_sel, T_ == 0);
   if (T_ == 0) return MOE_OK;
   moe_prof_scope ps(ctx, MOE_K_ROUTE_BWD);
-  route_bwd_kernel<<<(T_ + 255) / 256, 256, 0, ctx->stream>>>(gates, dgates, T_, k, dlogits_sel);
+  route_bwd_kernel<<<(T_ + 255) / 256, 256, 0, ctx->stream>>>(gates, dgates, T_, k, dlogits_sel,
+                                                                nullptr, nullptr);
   return check_launch(ctx, "moe_route_bwd");
+}
+
+moe_status moe_route_bwd_rows(moe_ctx* ctx, const float* gates, const float* dgates,
+                              const int32_t* row_of, int T_, int k, float* dlogits_sel,
+                              float* dl_rows) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, T_ >= 0 && k >= 1 && k <= 32, "moe_route_bwd_rows: bad shape T=%d k=%d", T_, k);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, gates, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dgates, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, row_of, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dlogits_sel, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dl_rows, T_ == 0);
+  if (T_ == 0) return MOE_OK;
+  moe_prof_scope ps(ctx, MOE_K_ROUTE_BWD);
+  route_bwd_kernel<<<(T_ + 255) / 256, 256, 0, ctx->stream>>>(gates, dgates, T_, k, dlogits_sel,
+                                                                row_of, dl_rows);
+  return check_launch(ctx, "moe_route_bwd_rows");
 }
 
 moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_sel,

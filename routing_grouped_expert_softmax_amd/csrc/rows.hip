@@ -10,6 +10,16 @@
 // and moves its rows in 16-byte lane chunks (1 KiB per wave instruction), so
 // every global access is a fully coalesced 16-byte vector access.  The k row
 // indices of the token are wave-uniform scalar loads.
+//
+// Cache policy (measured on the whole layer): every row the combine backward
+// and the permute backward read or write goes nontemporal.  The dyp rows the
+// down dgrad reads next then reach HBM during the row kernel instead of
+// sitting dirty in L2 while the GEMM streams its operands (down dgrad about
+// 2 % faster, the combine backward itself 6 % faster), and rows read once do
+// not evict GEMM operands.  The combine keeps cached loads (the combine
+// backward re-reads the same expert outputs).  The permute keeps cached
+// stores: nontemporal ones speed the gate/up GEMM after it by about as much
+// as they slow the permute.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -17,6 +27,17 @@
 using namespace moe;
 
 namespace {
+
+// 16-byte nontemporal load and store.
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+__device__ __forceinline__ uint4 ntld(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void ntst(uint4 v, uint4* p) {
+  const u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, (u32x4_t*)p);
+}
 
 template <typename T>
 struct Vec {
@@ -168,10 +189,10 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(
       for (int u = 0; u < CPL; ++u) {
         const int c = cb + 64 * u;
         if (c < nchunk) {
-          draw[u] = dy[(size_t)t * nchunk + c];
+          draw[u] = ntld(&dy[(size_t)t * nchunk + c]);
 #pragma unroll
           for (int j = 0; j < KMAX; ++j)
-            if (j < k) raw[u][j] = yp[(size_t)rows[j] * nchunk + c];
+            if (j < k) raw[u][j] = ntld(&yp[(size_t)rows[j] * nchunk + c]);
         }
       }
 #pragma unroll
@@ -190,7 +211,7 @@ __global__ void __launch_bounds__(256) combine_bwd_kernel(
               dot[j] += d[i] * f[i];
               o[i] = g[j] * d[i];
             }
-            dyp[(size_t)rows[j] * nchunk + c] = pack(o, T());
+            ntst(pack(o, T()), &dyp[(size_t)rows[j] * nchunk + c]);
           }
         }
       }
@@ -244,7 +265,7 @@ __global__ void __launch_bounds__(256) permute_bwd_kernel(
 #pragma unroll
           for (int j = 0; j < KMAX; ++j) {
             if (j < k) {
-              raw[u][j] = dxp[(size_t)rows[j] * nchunk + c];
+              raw[u][j] = ntld(&dxp[(size_t)rows[j] * nchunk + c]);
               if (ROUTER) wraw[u][ROUTER ? j : 0] = wrt[(size_t)ex[j] * nchunk + c];
             }
           }
@@ -283,7 +304,7 @@ __global__ void __launch_bounds__(256) permute_bwd_kernel(
             }
           }
         }
-        dx[(size_t)t * nchunk + c] = pack(acc, T());
+        ntst(pack(acc, T()), &dx[(size_t)t * nchunk + c]);
       }
     }
   }
