@@ -61,7 +61,9 @@ def row_bytes(name, T, d, k, F, E, esz=2):
         "permute": T * d * esz + R * d * esz + idx,
         "combine": R * d * esz + T * d * esz + idx + T * k * 4,
         "combine_bwd": T * d * esz + R * d * esz + R * d * esz + idx + 2 * T * k * 4,
-        "permute_bwd": R * d * esz + T * d * esz + idx * 2 + T * k * 4,
+        # bf16: the router term is folded into the gate/up dgrad, so the
+        # permute backward reads only the k rows and their indices
+        "permute_bwd": R * d * esz + T * d * esz + idx,
     }.get(name)
 
 
