@@ -20,12 +20,12 @@
 // (2kk + half) of its row.
 //
 // Scheduling, stages and the epilogue are the bf16 kernel's (gemm_common.h).
-// Tiles are 256 x 256 x 128 in two stages, one block per CU, in one of two
-// wave layouts per mode: four waves (128 x 128 wave tiles, 256 accumulator
-// registers, one wave per SIMD) or eight (64 x 128 wave tiles, two waves per
-// SIMD, one scale-row load per wave).  Eight waves measured 10-20 % faster
-// for the gate/up forward and both wgrads; the down GEMM and the two dgrads
-// keep four, because at eight their loops spill accumulators.
+// Tiles are 256 x 256 x 128 in two stages, one block per CU, eight waves
+// (64 x 128 wave tiles, 128 accumulator registers, two waves per SIMD, one
+// scale-row load per wave): 6-15 % faster per mode than four waves of
+// 128 x 128 (one wave per SIMD, nothing to hide the LDS and barrier latency).
+// The register budget of 256 per wave holds with the code-load offsets kept
+// as two per-lane values plus uniform row steps.
 // Wgrad operands are the column-quantised per-expert token blocks: expert e's
 // K range starts at the exclusive scan of roundup(n_e, 128).
 #include <hip/hip_runtime.h>
@@ -192,9 +192,12 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_mx_kernel(MxParams p)
   // chunk is the physical one XOR bit 3 of the row.  Scale tiles: 64 rows per
   // instruction, one 32-bit word (4 scale blocks) per lane.
   const int lda_s = p.lda / 32, ldb_s = p.ldb / 32;
-  int aoff[TL::A_INST], boff[TL::B_INST], asoff[TL::AS_INST + 1], bsoff[TL::BS_INST + 1];
+  static_assert(TL::A_INST % 2 == 0 && TL::B_INST % 2 == 0, "code loads come in even/odd pairs");
+  // Code loads j and j + 2 of a wave are 16 rows apart with the same swizzle:
+  // two per-lane offsets (j even, odd) plus a uniform 16-row step each.
+  int aoff[2], boff[2], asoff[TL::AS_INST + 1], bsoff[TL::BS_INST + 1];
 #pragma unroll
-  for (int j = 0; j < TL::A_INST; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int q = wv * TL::A_INST + j;
     const int row = q * 8 + (lane & 7), c = (lane >> 3) ^ ((row >> 3) & 1);
     aoff[j] = (TR::kKRAGGED ? (w.m0 + row) : row) * p.lda + c * 16;
@@ -205,7 +208,7 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_mx_kernel(MxParams p)
     asoff[j] = (TR::kKRAGGED ? (w.m0 + row) : row) * lda_s;
   }
 #pragma unroll
-  for (int j = 0; j < TL::B_INST; ++j) {
+  for (int j = 0; j < 2; ++j) {
     const int q = wv * TL::B_INST + j;
     const int row = q * 8 + (lane & 7), c = (lane >> 3) ^ ((row >> 3) & 1);
     // dual: rows 0..127 of the tile from matrix 0, 128..255 from matrix 1
@@ -252,10 +255,12 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_mx_kernel(MxParams p)
     }
 #pragma unroll
     for (int j = 0; j < TL::A_INST; ++j)
-      dma16(ra, (LDS_AS void*)(base + (wv * TL::A_INST + j) * 1024), aoff[j], kk);
+      dma16(ra, (LDS_AS void*)(base + (wv * TL::A_INST + j) * 1024), aoff[j & 1],
+            kk + (j >> 1) * 16 * p.lda);
 #pragma unroll
     for (int j = 0; j < TL::B_INST; ++j)
-      dma16(rb, (LDS_AS void*)(base + TL::A_BYTES + (wv * TL::B_INST + j) * 1024), boff[j], kk);
+      dma16(rb, (LDS_AS void*)(base + TL::A_BYTES + (wv * TL::B_INST + j) * 1024), boff[j & 1],
+            kk + (j >> 1) * 16 * p.ldb);
     // dual scale rows: waves 0,1 rows 0..127 (matrix 0), 2,3 rows 128..255
 #pragma unroll
     for (int j = 0; j < TL::AS_INST; ++j)
@@ -412,13 +417,10 @@ __global__ void __launch_bounds__(1024) mx_kbase_kernel(const int32_t* __restric
 
 // Tile configurations per mode: rows per tile, stages, waves per block.
 #ifndef MX_CFG
-#define MX_CFG 256, 2, 4
-#endif
-#ifndef MX8_CFG
-#define MX8_CFG 256, 2, 8
+#define MX_CFG 256, 2, 8
 #endif
 #ifndef MX_UP_CFG
-#define MX_UP_CFG MX8_CFG
+#define MX_UP_CFG MX_CFG
 #endif
 #ifndef MX_DN_CFG
 #define MX_DN_CFG MX_CFG
@@ -430,10 +432,10 @@ __global__ void __launch_bounds__(1024) mx_kbase_kernel(const int32_t* __restric
 #define MX_DU_CFG MX_CFG
 #endif
 #ifndef MX_WD_CFG
-#define MX_WD_CFG MX8_CFG
+#define MX_WD_CFG MX_CFG
 #endif
 #ifndef MX_WU_CFG
-#define MX_WU_CFG MX8_CFG
+#define MX_WU_CFG MX_CFG
 #endif
 template <int BM_, int S_, int NW_>
 struct MxCfg {
