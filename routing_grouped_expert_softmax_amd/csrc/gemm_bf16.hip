@@ -223,10 +223,22 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   // Per-lane byte offsets of this wave's direct loads (fixed over the K loop;
   // the K advance goes in the scalar offset).  Each load moves 16 bytes per
   // lane into LDS at (instruction base + 16 * lane), so the global side picks
-  // the source chunk that belongs at that (swizzled) LDS position.
-  int aoff[TL::A_INST], boff[TL::B_INST];
+  // the source chunk that belongs at that (swizzled) LDS position.  The
+  // swizzle repeats every P instructions of a wave, so load j uses the
+  // per-lane offset of load j % P plus a uniform (j / P) * R rows (in the
+  // scalar offset): P per-lane values per operand instead of one per load.
+  constexpr int A_RPI = 64 / (BM / 8);  // k rows per load, M-contiguous A
+  constexpr int PA = TR::kA_KCONTIG ? (TL::GPI == 1 ? 2 : 1) : (A_RPI >= 4 ? 1 : 4 / A_RPI);
+  constexpr int RA = TR::kA_KCONTIG ? PA * TL::GPI * 8 : PA * A_RPI;
+  constexpr int PB = TR::kB_KCONTIG ? (TL::GPI == 1 ? 2 : 1) : (TR::kDUAL ? 1 : 2);
+  constexpr int RB = TR::kB_KCONTIG ? PB * TL::GPI * 8 : 4;
+  static_assert(TL::A_INST % PA == 0 && TL::B_INST % PB == 0, "loads per wave come in whole periods");
+  static_assert(!TR::kDUAL || TR::kB_KCONTIG || (BK / 4) % TL::B_INST == 0,
+                "a wave's loads stay inside one matrix of the pair");
+  const int astep = RA * p.lda * (int)esz, bstep = RB * p.ldb * (int)esz;
+  int aoff[PA], boff[PB];
 #pragma unroll
-  for (int j = 0; j < TL::A_INST; ++j) {
+  for (int j = 0; j < PA; ++j) {
     const int q = wv * TL::A_INST + j;  // 1 KiB instruction index inside the A tile
     if (TR::kA_KCONTIG) {
       // instruction q fills groups q*GPI..; lane = (group, slice, row % 8, half)
@@ -240,7 +252,7 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
     }
   }
 #pragma unroll
-  for (int j = 0; j < TL::B_INST; ++j) {
+  for (int j = 0; j < PB; ++j) {
     const int q = wv * TL::B_INST + j;
     if (TR::kB_KCONTIG) {
       const int kk = (lane >> 4) % TL::SLICES, gi = (lane >> 4) / TL::SLICES;
@@ -285,7 +297,8 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
       }
 #pragma unroll
       for (int j = 0; j < TL::A_INST; ++j)
-        dma16(r, (LDS_AS void*)(base + (wv * TL::A_INST + j) * 1024), aoff[j], soff);
+        dma16(r, (LDS_AS void*)(base + (wv * TL::A_INST + j) * 1024), aoff[j % PA],
+              soff + (j / PA) * astep);
     }
     // B
     {
@@ -305,7 +318,8 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
       }
 #pragma unroll
       for (int j = 0; j < TL::B_INST; ++j)
-        dma16(r, (LDS_AS void*)(bbase + (wv * TL::B_INST + j) * 1024), boff[j], soff);
+        dma16(r, (LDS_AS void*)(bbase + (wv * TL::B_INST + j) * 1024), boff[j % PB],
+              soff + (j / PB) * bstep);
     }
   };
 
