@@ -20,7 +20,8 @@ More legs ride on the default run: `e_scaling` times the same layer at E=8
 MXFP8 grouped experts (quantisation included) on 65536 pre-routed rows of a
 16-expert, d_model 4096, d_ff 1536 share, `mxfp8_layer` times the main
 workload end to end with quantise-on-permute and MXFP8 expert GEMMs (its
-tokens/s beside the bf16 layer's), `shared_expert` times the main workload
+tokens/s beside the bf16 layer's; for uniform128 also dense8 and zipf128,
+each beside its own bf16 layer), `shared_expert` times the main workload
 with a shared expert of the routed width added, `recompute` times it with
 activation recompute (the bytes kept from forward to backward beside the
 throughput), and `routing_stats` times the
@@ -415,6 +416,7 @@ def main():
     }
     if "routing_stats" in main_leg:
         result["routing_stats"] = main_leg["routing_stats"]
+    base = None
     if not args.no_escaling and cfg.name == "uniform128":
         base = layer_leg(mi.config("dense8"), args.steps, args.warmup)
         result["e_scaling"] = {
@@ -452,6 +454,18 @@ def main():
                 "vs_bf16_layer": round(ml["tokens_per_s"] / main_leg["tokens_per_s"], 4),
                 "grouped_gemm": magg, "roofline": mroof,
                 "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in ml["prof"].items()}}
+            if cfg.name == "uniform128":
+                # the other two routed workloads end to end in MXFP8 beside bf16
+                others = {}
+                for name in ("dense8", "zipf128"):
+                    oc = mi.config(name)
+                    ob = base if (name == "dense8" and base is not None) else layer_leg(oc, args.mx_steps, 3)
+                    om = layer_leg(oc, args.mx_steps, 3, mxfp8=True)
+                    others[name] = {"bf16_tokens_per_s": round(ob["tokens_per_s"], 1),
+                                    "mxfp8_tokens_per_s": round(om["tokens_per_s"], 1),
+                                    "mxfp8_vs_bf16": round(om["tokens_per_s"] / ob["tokens_per_s"], 4),
+                                    "mxfp8_expert_load": om["load"]}
+                result["mxfp8_layer"]["other_workloads"] = others
     if args.cpu_sample > 0:
         result["cpu_baseline"] = cpu_baseline(cfg, main_leg["inp"], args.cpu_sample)
     print(json.dumps(result), flush=True)
