@@ -145,47 +145,52 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(
     const bf16_t* __restrict__ src, int rows, int cols, const int32_t* __restrict__ offsets,
     int urows, int G, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad_ld) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kColTile];
-  __shared__ int sh[256 + 4];
+  __shared__ int sh[4];
   const int tid = threadIdx.x;
-  const int per = (G + 255) / 256;
-  int ps[4];  // 128-row slices per group
-  int plocal = 0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int g = tid * per + q;
-    ps[q] = 0;
-    if (q < per && g < G) {
-      const int n = offsets ? offsets[g + 1] - offsets[g] : urows;
-      ps[q] = (n + 127) / 128;
-    }
-    plocal += ps[q];
-  }
-  sh[tid] = plocal;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
-  }
-  int prun = sh[tid] - plocal;
-  const int total = sh[255];
-  __syncthreads();
   const int y = blockIdx.y;
-  if (tid == 0) sh[256] = -1;
-  __syncthreads();
+  // The block's (group, 128-row slice): closed form for equal groups; else
+  // wave 0 scans the per-group slice counts with shuffles (16 groups per
+  // lane) and publishes the result through one barrier.
+  int g, sl;
+  if (offsets == nullptr) {
+    const int pg = (urows + 127) / 128;  // slices per group
+    if (pg == 0 || y >= G * pg) return;
+    g = y / pg;
+    sl = y - g * pg;
+  } else {
+    if (tid < 64) {
+      const int lane = tid;
+      const int per = (G + 63) / 64;  // <= 16 (G <= 1024)
+      int cnt[16];
+      int local = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int g = tid * per + q;
-    if (q < per && g < G && y >= prun && y < prun + ps[q]) {
-      sh[256] = g;
-      sh[257] = y - prun;  // slice within the group
+      for (int q = 0; q < 16; ++q) {
+        const int gg = lane * per + q;
+        cnt[q] = (q < per && gg < G) ? (offsets[gg + 1] - offsets[gg] + 127) / 128 : 0;
+        local += cnt[q];
+      }
+      int incl = local;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+      }
+      if (lane == 0) sh[0] = -1;
+      int prun = incl - local;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (cnt[q] > 0 && y >= prun && y < prun + cnt[q]) {
+          sh[0] = lane * per + q;
+          sh[1] = y - prun;  // slice within the group
+        }
+        prun += cnt[q];
+      }
     }
-    prun += ps[q];
+    __syncthreads();
+    if (sh[0] < 0) return;
+    g = sh[0];
+    sl = sh[1];
   }
-  __syncthreads();
-  if (y >= total || sh[256] < 0) return;
-  const int g = sh[256], sl = sh[257];
   const int gstart = offsets ? offsets[g] : g * urows;
   const int gend = offsets ? offsets[g + 1] : (g + 1) * urows;
   const int c0 = blockIdx.x * kColTile;
