@@ -32,27 +32,30 @@ __device__ __forceinline__ int mx_scale_byte(float amax) {
   return c < 0 ? 0 : (c > 254 ? 254 : c);
 }
 
-// E4M3 code of x (already divided by the block scale): round to the grid of
-// the value's binade with rintf (ties to even), computed in float.
-__device__ __forceinline__ uint32_t e4m3_code(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (!(a == a)) return 0x7fu;
-  if (a >= 448.0f) return sign | 0x7eu;
-  // binade exponent e (>= -6: below 2^-6 the grid step stays 2^-9)
-  int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;
-  if (e < -6) e = -6;
-  const float m = rintf(ldexpf(a, 3 - e));  // grid units of 2^(e-3)
-  int mi = (int)m;                          // 0..16
-  if (mi < 8) return sign | (uint32_t)mi;   // subnormal (e == -6)
-  if (mi == 16) {                           // rounded up into the next binade
-    mi = 8;
-    e += 1;
-  }
-  uint32_t code = ((uint32_t)(e + 7) << 3) | (uint32_t)(mi - 8);
-  if (code > 0x7eu) code = 0x7eu;
-  return sign | code;
+// E4M3 codes of four values already divided by the block scale, packed in
+// element order: the hardware conversion (v_cvt_pk_fp8_f32, OCP E4M3, round
+// to nearest even) of the values clamped to +-448, which is the saturating
+// encoding; a NaN element becomes 0x7f (the clamp alone would turn it into a
+// bound).  Checked on every bf16 bit pattern against a plain encoder that
+// rounds each value to its binade's grid: equal for all non-NaN inputs,
+// signed zeros and subnormals included.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  const float lo = -448.0f, hi = 448.0f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi),
+                                          __builtin_amdgcn_fmed3f(b, lo, hi), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, lo, hi),
+                                      __builtin_amdgcn_fmed3f(d, lo, hi), w, true);
+  uint32_t r = (uint32_t)w;
+  if (a != a) r = (r & 0xffffff00u) | 0x0000007fu;
+  if (b != b) r = (r & 0xffff00ffu) | 0x00007f00u;
+  if (c != c) r = (r & 0xff00ffffu) | 0x007f0000u;
+  if (d != d) r = (r & 0x00ffffffu) | 0x7f000000u;
+  return r;
 }
+
+// 2^-s as a float for a block scale exponent s in [-127, 127] (a normal
+// number for every s the scale byte can give a bf16 block: s <= 119).
+__device__ __forceinline__ float pow2_neg(int s) { return __uint_as_float((uint32_t)(127 - s) << 23); }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -74,14 +77,10 @@ __device__ __forceinline__ int quant_block(const uint4 (&v)[4], uint32_t (&out)[
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
   const int sb = mx_scale_byte(amax);
-  const int s = sb - 127;
+  const float inv = pow2_neg(sb - 127);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) word |= e4m3_code(ldexpf(f[q * 4 + j], -s)) << (8 * j);
-    out[q] = word;
-  }
+  for (int q = 0; q < 8; ++q)
+    out[q] = e4m3x4(f[q * 4] * inv, f[q * 4 + 1] * inv, f[q * 4 + 2] * inv, f[q * 4 + 3] * inv);
   return sb;
 }
 
@@ -227,15 +226,12 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(
       amax = fmaxf(amax, fabsf(f[i]));
     }
     const int sb = mx_scale_byte(amax);
-    const int s = sb - 127;
+    const float inv = pow2_neg(sb - 127);
     sword |= (uint32_t)sb << (8 * bb);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) word |= e4m3_code(ldexpf(f[q * 4 + j], -s)) << (8 * j);
-      code_words[bb * 8 + q] = word;
-    }
+    for (int q = 0; q < 8; ++q)
+      code_words[bb * 8 + q] =
+          e4m3x4(f[q * 4] * inv, f[q * 4 + 1] * inv, f[q * 4 + 2] * inv, f[q * 4 + 3] * inv);
   }
   const size_t k = (size_t)y * 128;  // padded K position of the slice
   if (c < cols)

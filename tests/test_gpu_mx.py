@@ -35,11 +35,12 @@ def _bf16_tensor(a):
 def _special_matrix(rows, cols, seed):
     """bf16 values that reach every branch of the codec: ordinary normals,
     blocks scaled to tiny (subnormal bf16) and huge magnitudes, all-zero
-    blocks, signed zeros, exact E4M3 rounding ties and saturating values."""
+    blocks, signed zeros, exact E4M3 rounding ties, saturating values and NaN
+    elements (code 0x7f; the block scale comes from the other elements)."""
     rng = np.random.default_rng(seed)
     a = rng.standard_normal((rows, cols)).astype(np.float32)
     nblk = cols // 32
-    kinds = rng.integers(0, 7, size=(rows, nblk))
+    kinds = rng.integers(0, 8, size=(rows, nblk))
     for r in range(rows):
         for b in range(nblk):
             blk = a[r, 32 * b:32 * b + 32]
@@ -57,6 +58,9 @@ def _special_matrix(rows, cols, seed):
                 blk[0] = 1.0
             elif k == 5:
                 blk[:] = rng.integers(-1000, 1001, size=32) * np.float32(2.0 ** -20)
+            elif k == 6:
+                blk[rng.integers(0, 32, size=2)] = np.nan
+                blk[rng.integers(0, 32)] = np.copysign(np.float32(np.nan), np.float32(-1.0))
     return mi.f32(_bf16_tensor(a))
 
 
