@@ -93,8 +93,9 @@ const char* moe_last_error(const moe_ctx* ctx);
 
 /* Device workspace needed by the calls that use it for a layer of this
  * shape: moe_route (per-block expert histograms), moe_permute_bwd with the
- * router term (a transposed copy of W_r), moe_route_stats and
- * moe_expert_grad_norms (partial sums).  The calls run in stream order,
+ * router term (a transposed copy of W_r), moe_router_wgrad (fp32 partials
+ * per 256-row chunk), moe_route_stats and moe_expert_grad_norms (partial
+ * sums).  The calls run in stream order,
  * so they share one region.  *bytes is a host output. */
 moe_status moe_workspace_size(moe_ctx* ctx, int T, int d, int E, int k, moe_dtype dtype,
                               size_t* bytes);
@@ -259,7 +260,10 @@ moe_status moe_permute_bwd_shared(moe_ctx* ctx, const void* dxp, const int32_t* 
 
 /* Router weight gradient: dw_router[i,e] = sum over the rows r of expert e
  * (ascending) of dlogits_sel[src_tk[r]] * x[src_tk[r] / k, i]; fp32
- * accumulation in a fixed order, stored in dtype. */
+ * accumulation in a fixed order (rows summed in 256-row chunks, the chunk
+ * sums added in order, so a hot expert's rows spread over the chip),
+ * stored in dtype.  Needs the registered workspace (moe_workspace_size with
+ * this T, d, E, k) when T > 0. */
 moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_sel,
                             const int32_t* src_tk, const int32_t* offsets, int T, int d, int E,
                             int k, moe_dtype dtype, void* dw_router);

@@ -414,6 +414,7 @@ def moe_router_wgrad(x, dlogits_sel, src_tk, offsets, E, dw_router=None):
     k = dlogits_sel.shape[1]
     if dw_router is None:
         dw_router = torch.empty(d, E, dtype=x.dtype, device=x.device)
+    context(x.device.index).ensure_workspace(T, d, E, min(k, E), _dt(x))
     context(x.device.index).call("moe_router_wgrad", _p(x), _p(dlogits_sel), _p(src_tk), _p(offsets),
                                  T, d, E, k, _dt(x), _p(dw_router))
     return dw_router

@@ -388,24 +388,68 @@ __global__ void route_bwd_kernel(const float* __restrict__ gates, const float* _
   }
 }
 
-// Router weight gradient.  One block per (expert, 64*V-feature chunk), V
-// features (16 bytes) per lane: wave w walks the expert's rows r0+w, r0+w+4,
-// ... with eight independent row gathers in flight per step, accumulating in
-// fp32 in row order; the four waves are then summed in a fixed order, so the
-// result is deterministic.
+// Router weight gradient, two passes so that a hot expert's rows spread over
+// the whole chip (with skewed routing one expert can own a fifth of all
+// rows).  Pass 1: the rows of every expert are cut into chunks of kRwChunk;
+// one block per (64*V-feature range, chunk), V features (16 bytes) per lane,
+// wave w walking the chunk's rows w, w+4, ... with eight row gathers in
+// flight, fp32 sums in row order, the four waves summed in a fixed order into
+// an fp32 partial per chunk.  Pass 2: dW_r[:, e] is the sum of expert e's
+// chunk partials in chunk order.  Deterministic for given routing.
+constexpr int kRwChunk = 256;
+__host__ __device__ inline int rw_chunk_bound(int R, int E) { return R / kRwChunk + E; }
+
 template <typename T>
-__global__ void __launch_bounds__(256) router_wgrad_kernel(
+__global__ void __launch_bounds__(256) router_wgrad_part_kernel(
     const T* __restrict__ x, const float* __restrict__ dls, const int32_t* __restrict__ src_tk,
-    const int32_t* __restrict__ offsets, int d, int E, int k, T* __restrict__ dwr) {
+    const int32_t* __restrict__ offsets, int d, int E, int k, float* __restrict__ part,
+    int32_t* __restrict__ cstart) {
   constexpr int V = 16 / sizeof(T);  // features per lane
   constexpr int FC = 64 * V;         // features per block
   constexpr int U = 8;               // rows in flight per wave
-  __shared__ float part[4][FC];
-  const int e = blockIdx.y;
-  const int f0 = blockIdx.x * FC;
+  __shared__ float red[4][FC];
+  __shared__ int sh[2];
+  const int y = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int r0 = offsets[e], r1 = offsets[e + 1];
+  // expert and first row of chunk y: wave 0 scans the chunk counts
+  if (w == 0) {
+    const int per = (E + 63) / 64;  // <= 16 experts per lane
+    int cnt[16];
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = lane * per + q;
+      cnt[q] = (q < per && e < E) ? (offsets[e + 1] - offsets[e] + kRwChunk - 1) / kRwChunk : 0;
+      local += cnt[q];
+    }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 0) sh[0] = -1;
+    int run = incl - local;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int e = lane * per + q;
+      if (y == 0 && blockIdx.x == 0 && q < per && e < E) {
+        cstart[e] = run;  // first chunk of each expert, for pass 2
+        if (e == E - 1) cstart[E] = run + cnt[q];
+      }
+      if (cnt[q] > 0 && y >= run && y < run + cnt[q]) {
+        sh[0] = e;
+        sh[1] = offsets[e] + (y - run) * kRwChunk;
+      }
+      run += cnt[q];
+    }
+  }
+  __syncthreads();
+  if (sh[0] < 0) return;
+  const int e = sh[0], c0 = sh[1];
+  const int c1 = min(c0 + kRwChunk, offsets[e + 1]);
+  const int f0 = blockIdx.x * FC;
   float acc[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) acc[v] = 0.f;
@@ -416,8 +460,8 @@ __global__ void __launch_bounds__(256) router_wgrad_kernel(
 #pragma unroll
       for (int v = 0; v < V; ++v) acc[v] += wt * Elem<T>::ld(xv, v);
     };
-    int r = r0 + w;
-    for (; r + 4 * (U - 1) < r1; r += 4 * U) {
+    int r = c0 + w;
+    for (; r + 4 * (U - 1) < c1; r += 4 * U) {
       int flat[U];
       float wt[U];
       uint4 raw[U];
@@ -431,18 +475,33 @@ __global__ void __launch_bounds__(256) router_wgrad_kernel(
 #pragma unroll
       for (int j = 0; j < U; ++j) add(wt[j], raw[j]);
     }
-    for (; r < r1; r += 4) {
+    for (; r < c1; r += 4) {
       const int flat = src_tk[r];
       add(dls[flat], *reinterpret_cast<const uint4*>(x + (size_t)(flat / k) * d + fi));
     }
   }
 #pragma unroll
-  for (int v = 0; v < V; ++v) part[w][lane * V + v] = acc[v];
+  for (int v = 0; v < V; ++v) red[w][lane * V + v] = acc[v];
   __syncthreads();
-  for (int f = threadIdx.x; f < FC; f += 256) {
-    const float s = ((part[0][f] + part[1][f]) + part[2][f]) + part[3][f];
-    if (f0 + f < d) Elem<T>::st(dwr, (size_t)(f0 + f) * E + e, s);
+  for (int f = threadIdx.x; f < FC; f += 256)
+    if (f0 + f < d) part[(size_t)y * d + f0 + f] = ((red[0][f] + red[1][f]) + red[2][f]) + red[3][f];
+}
+
+// Pass 2: one thread per (feature, expert); no chunks (an expert without
+// rows, or cstart == nullptr for an empty batch) gives exact zeros.
+template <typename T>
+__global__ void router_wgrad_sum_kernel(const float* __restrict__ part,
+                                        const int32_t* __restrict__ cstart, int d, int E,
+                                        T* __restrict__ dwr) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long long)d * E) return;
+  const int f = (int)(i / E), e = (int)(i % E);
+  float s = 0.f;
+  if (cstart) {
+    const int cb = cstart[e], ce = cstart[e + 1];
+    for (int c = cb; c < ce; ++c) s += part[(size_t)c * d + f];
   }
+  Elem<T>::st(dwr, (size_t)f * E + e, s);
 }
 
 
@@ -454,6 +513,13 @@ using namespace moe_host;
 static size_t route_ws_bytes(int T_, int E) {
   const size_t nblk = (size_t)(T_ + kTokBlock - 1) / kTokBlock;
   return ((size_t)E * nblk * sizeof(int32_t) + 255) & ~(size_t)255;
+}
+
+// Router weight-gradient partials: one fp32 row of d per row chunk, then the
+// first-chunk index of every expert.
+static size_t router_wgrad_ws_bytes(int T_, int d, int E, int k) {
+  const size_t parts = (size_t)rw_chunk_bound(T_ * k, E) * d * sizeof(float);
+  return ((parts + 255) & ~(size_t)255) + (((size_t)(E + 1) * sizeof(int32_t) + 255) & ~(size_t)255);
 }
 
 // Router-transpose scratch used by moe_permute_bwd (W_r^T, [E,d]).
@@ -478,8 +544,8 @@ moe_status moe_workspace_size(moe_ctx* ctx, int T_, int d, int E, int k, moe_dty
   MOE_REQUIRE(ctx, T_ >= 0 && d >= 8 && E >= 1 && E <= 1024 && k >= 1 && k <= E && k <= 32,
               "bad shape T=%d d=%d E=%d k=%d", T_, d, E, k);
   const size_t a = route_ws_bytes(T_, E), b = moe_internal_wrt_bytes(d, E, dtype),
-               c = moe_internal_stats_ws_bytes(E);
-  *bytes = std::max(a, std::max(b, c));
+               c = moe_internal_stats_ws_bytes(E), r = router_wgrad_ws_bytes(T_, d, E, k);
+  *bytes = std::max(std::max(a, r), std::max(b, c));
   return MOE_OK;
 }
 
@@ -606,15 +672,33 @@ moe_status moe_router_wgrad(moe_ctx* ctx, const void* x, const float* dlogits_se
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, src_tk, T_ == 0);
   MOE_REQUIRE_PTR(ctx, offsets);
   MOE_REQUIRE_PTR(ctx, dw_router);
+  const size_t need = router_wgrad_ws_bytes(T_, d, E, k);
+  if (T_ > 0 && (ctx->ws == nullptr || ctx->ws_bytes < need))
+    return fail(ctx, MOE_ERR_WORKSPACE, "moe_router_wgrad: workspace %zu bytes < %zu needed",
+                ctx->ws_bytes, need);
   const int fc = dtype == MOE_BF16 ? 512 : 256;  // features per block (64 lanes x 16 bytes)
-  dim3 grid((d + fc - 1) / fc, E);
+  float* part = reinterpret_cast<float*>(ctx->ws);
+  int32_t* cstart = T_ > 0 ? reinterpret_cast<int32_t*>(
+                                 reinterpret_cast<char*>(ctx->ws) +
+                                 (((size_t)rw_chunk_bound(T_ * k, E) * d * sizeof(float) + 255) & ~(size_t)255))
+                           : nullptr;
+  const long long n2 = (long long)d * E;
   moe_prof_scope ps(ctx, MOE_K_ROUTER_WGRAD);
+  if (T_ > 0) {
+    dim3 grid((d + fc - 1) / fc, rw_chunk_bound(T_ * k, E));
+    if (dtype == MOE_BF16)
+      router_wgrad_part_kernel<bf16_t><<<grid, 256, 0, ctx->stream>>>(
+          (const bf16_t*)x, dlogits_sel, src_tk, offsets, d, E, k, part, cstart);
+    else
+      router_wgrad_part_kernel<float><<<grid, 256, 0, ctx->stream>>>(
+          (const float*)x, dlogits_sel, src_tk, offsets, d, E, k, part, cstart);
+  }
   if (dtype == MOE_BF16)
-    router_wgrad_kernel<bf16_t><<<grid, 256, 0, ctx->stream>>>(
-        (const bf16_t*)x, dlogits_sel, src_tk, offsets, d, E, k, (bf16_t*)dw_router);
+    router_wgrad_sum_kernel<bf16_t><<<(unsigned)((n2 + 255) / 256), 256, 0, ctx->stream>>>(
+        part, cstart, d, E, (bf16_t*)dw_router);
   else
-    router_wgrad_kernel<float><<<grid, 256, 0, ctx->stream>>>(
-        (const float*)x, dlogits_sel, src_tk, offsets, d, E, k, (float*)dw_router);
+    router_wgrad_sum_kernel<float><<<(unsigned)((n2 + 255) / 256), 256, 0, ctx->stream>>>(
+        part, cstart, d, E, (float*)dw_router);
   return check_launch(ctx, "moe_router_wgrad");
 }
 

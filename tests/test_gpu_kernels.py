@@ -121,6 +121,30 @@ def test_permute_combine_and_backward(moe, dtype, T, d, E, k):
     assert_close(mi.f32(dwr.cpu()), ref, tol_for(dtype), "dW_r")
 
 
+@pytest.mark.parametrize("dtype,T,d,E,k", [("bf16", 3000, 512, 16, 2), ("fp32", 1500, 256, 8, 4)])
+def test_router_wgrad_skewed(moe, dtype, T, d, E, k):
+    """One hot expert whose rows span many 256-row chunks, two empty experts,
+    ragged chunk tails: against the oracle, and bit-identical on a repeat."""
+    rng = np.random.default_rng(T + d)
+    c = mi.layer_inputs(mi.config("tiny", T=T, d=d, E=E, k=k, dtype=dtype, x_std=1.0), with_weights=False)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, 3] += 6.0  # nearly every token picks expert 3
+    logits[:, [1, E - 1]] = -1e4  # never picked
+    r = moe.moe_route(torch.from_numpy(logits).to(DEV), k)
+    counts = r["counts"].cpu().numpy()
+    assert counts[3] > 4 * 256 and counts[1] == 0 and counts[E - 1] == 0
+    x = c["x"].to(DEV)
+    dls = torch.from_numpy(rng.standard_normal((T, k)).astype(np.float32)).to(DEV)
+    dwr = moe.moe_router_wgrad(x, dls, r["src_tk"], r["offsets"], E)
+    again = moe.moe_router_wgrad(x, dls, r["src_tk"], r["offsets"], E)
+    torch.cuda.synchronize()
+    assert torch.equal(dwr, again)
+    ref = oracle.router_wgrad(mi.f32(c["x"]), dls.cpu().numpy(), r["topk_idx"].cpu().numpy(), E)
+    got = mi.f32(dwr.cpu())
+    assert not got[:, 1].any() and not got[:, E - 1].any()
+    assert_close(got, ref, tol_for(dtype), "dW_r (skewed)")
+
+
 # ------------------------------------------------------------------ grouped FFN
 FFN_CASES = [
     # dtype, d, F, counts
