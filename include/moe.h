@@ -105,11 +105,14 @@ moe_status moe_workspace_size(moe_ctx* ctx, int T, int d, int E, int k, moe_dtyp
 moe_status moe_mx_workspace_size(moe_ctx* ctx, int E, int R, int d, int F, size_t* bytes);
 /* Device workspace of moe_grouped_ffn_bwd for this shape; *bytes (host) is 0
  * when the call needs none.  MOE_MXFP8: the quantised operands (as
- * moe_mx_workspace_size).  MOE_BF16: the split-K partials of a weight
- * gradient whose output tiles would leave block slots idle (fewer than two
- * per compute unit, e.g. a shared expert's single group of T rows): each
- * group's rows are cut into up to 8 segments whose exact fp32 partial
- * products are summed in segment order and rounded once.  MOE_F32: 0. */
+ * moe_mx_workspace_size).  MOE_BF16: 256 bytes of per-XCD tile ranges for
+ * the two weight gradients (planned by the down dgrad from the routed
+ * counts, cost-balanced when skewed routing would overload one XCD), then
+ * the split-K partials of a weight gradient whose output tiles would leave
+ * block slots idle (fewer than two per compute unit, e.g. a shared expert's
+ * single group of T rows): each group's rows are cut into up to 8 segments
+ * whose exact fp32 partial products are summed in segment order and rounded
+ * once.  MOE_F32: 0. */
 moe_status moe_ffn_bwd_workspace_size(moe_ctx* ctx, int E, int R, int d, int F, moe_dtype dtype,
                                       size_t* bytes);
 /* Register caller-owned device workspace (256-byte aligned). */

@@ -78,7 +78,18 @@ struct Params {
   // rdl[r] * rw[:, e] (rw is the [N, E] router weight matrix)
   const float* rdl;
   const bf16_t* rw;
+  // K-ragged: per-XCD tile ranges [first, end) as 8 pairs; nullptr = equal
+  // tile counts per XCD
+  const int32_t* xr;
+  // DGRAD_DOWN: block 0 also writes the ranges of the two weight gradients
+  // that follow (xr_pe0 / xr_pe1 tiles per group)
+  int32_t* xr_out0;
+  int32_t* xr_out1;
+  int xr_pe0, xr_pe1;
 };
+
+// K step of the weight gradients, for their XCD range plans
+constexpr int kWgradBK = 32;
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
@@ -138,6 +149,34 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // Tile blocks are numbered from 0; with a plan (DGRAD_DOWN, xr_out0 set)
+  // the first eight blocks of the grid plan instead: block x < 8 writes the
+  // tile ranges of XCD x for the two weight gradients launched after this
+  // kernel (they read them in stream order) and exits.  Plan blocks are short
+  // and first in the grid, so their compute units take tiles right after.
+  int bid = blockIdx.x, nblk = gridDim.x;
+  if constexpr (MODE == DGRAD_DOWN) {
+    if (p.xr_out0 != nullptr) {
+      if (bid < 8) {
+        if (wv == 0) {
+          int f0, f1;
+          kragged_xcd_range<kWgradBK>(p.offsets, p.E, p.xr_pe0, bid, f0, f1);
+          if (lane == 0) {
+            p.xr_out0[2 * bid] = f0;
+            p.xr_out0[2 * bid + 1] = f1;
+          }
+          kragged_xcd_range<kWgradBK>(p.offsets, p.E, p.xr_pe1, bid, f0, f1);
+          if (lane == 0) {
+            p.xr_out1[2 * bid] = f0;
+            p.xr_out1[2 * bid + 1] = f1;
+          }
+        }
+        return;
+      }
+      bid -= 8;  // keeps bid % 8 == blockIdx.x % 8, the XCD
+      nblk -= 8;
+    }
+  }
 
   // ---------------------------------------------------------------- work
   // Logical tiles are split into eight contiguous ranges of equal tile count,
@@ -147,13 +186,21 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   MTileSched<BM> ms;
   int first, end;  // this XCD's range of logical tiles
   if (TR::kKRAGGED) {
-    // equal tile counts per XCD: at the short K of a uniformly loaded layer
-    // (a few hundred rows per expert) computing cost-balanced ranges in every
-    // block costs more than the imbalance they remove
-    const int total = p.E * p.ntiles * p.mtiles;
-    const int per_xcd = (total + 7) / 8;
-    first = min((int)(blockIdx.x & 7) * per_xcd, total);
-    end = min(first + per_xcd, total);
+    // A tile costs as many K steps as its expert has rows: with skewed
+    // routing one expert's tiles would pile onto one XCD.  The ranges come
+    // precomputed (cost-balanced unless equal tile counts are within 10 % of
+    // balanced); blocks of an XCD whose range is longer than its share of
+    // the grid walk several tiles.
+    const int x = bid & 7;
+    if (p.xr != nullptr) {
+      first = p.xr[2 * x];
+      end = p.xr[2 * x + 1];
+    } else {
+      const int total = p.E * p.ntiles * p.mtiles;
+      const int per_xcd = (total + 7) / 8;
+      first = min(x * per_xcd, total);
+      end = min(first + per_xcd, total);
+    }
   } else {
     int total;
     if (TR::kSINGLE) {
@@ -163,11 +210,11 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
       total = ms.total;
     }
     const int per_xcd = (total + 7) / 8;
-    first = (blockIdx.x & 7) * per_xcd;
+    first = (bid & 7) * per_xcd;
     end = min(first + per_xcd, total);
   }
-  const int nslot = gridDim.x >> 3;
-  const int L0 = first + (int)(blockIdx.x >> 3);
+  const int nslot = nblk >> 3;
+  const int L0 = first + (bid >> 3);
   for (int L = L0; L < end; L += nslot) {
   // the previous tile's epilogue has finished with the LDS stage buffers
   if (L != L0) lds_barrier();
@@ -630,7 +677,10 @@ static hipError_t launch_mragged(Params& p, int R, hipStream_t s) {
   using C = std::conditional_t<
       MODE == DGRAD_DOWN, CfgDD,
       std::conditional_t<MODE == DGRAD_UP, CfgDU, std::conditional_t<MODE == FWD_UP, CfgUP, CfgDN>>>;
-  return launch<MODE, C::BM, C::S, C::BK, C::OCC, C::NW>(p, mtile_bound(R, p.E, C::BM) * p.ntiles, s);
+  // (+8 plan blocks when the down dgrad plans the weight gradients' ranges;
+  // the tile count is already a multiple of 8 after launch() rounds it)
+  const int tiles = (mtile_bound(R, p.E, C::BM) * p.ntiles + 7) / 8 * 8;
+  return launch<MODE, C::BM, C::S, C::BK, C::OCC, C::NW>(p, tiles + (p.xr_out0 != nullptr ? 8 : 0), s);
 }
 
 moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const void* wr, int T_,
@@ -705,6 +755,9 @@ static int wgrad_up_tiles(int E, int d, int F) { return E * ((d + CfgWU::BM - 1)
 static int wgrad_down_tiles(int E, int d, int F) { return E * ((F + CfgWD::BM - 1) / CfgWD::BM) * ((d + BN - 1) / BN); }
 // Workspace of the split weight gradients: the partials of the larger one
 // (gate/up: two [E*S, d, F] fp32 arrays) followed by the virtual offsets.
+// The bf16 backward's workspace: the XCD range tables of the two weight
+// gradients (kPlanBytes), then the split-K partials and virtual offsets.
+constexpr size_t kPlanBytes = 256;
 static size_t wgrad_split_bytes(int E, int R, int d, int F, size_t* part_bytes) {
   const int su = wgrad_splits(E, R, wgrad_up_tiles(E, d, F));
   const int sd = wgrad_splits(E, R, wgrad_down_tiles(E, d, F));
@@ -716,6 +769,19 @@ static size_t wgrad_split_bytes(int E, int R, int d, int F, size_t* part_bytes) 
   const size_t dn = sd > 1 ? (size_t)E * sd * F * d * 4 : 0;
   *part_bytes = ((up > dn ? up : dn) + 255) & ~(size_t)255;
   return *part_bytes + (((size_t)E * 8 + 1) * 4 + 255) / 256 * 256;
+}
+
+// Per-XCD tile ranges of a split-K weight gradient over its virtual groups:
+// one wave per XCD, xr[2x], xr[2x+1] = [first, end) of XCD x.
+__global__ void __launch_bounds__(512) xcd_plan_kernel(const int32_t* __restrict__ off, int E,
+                                                       int per_e, int32_t* __restrict__ xr) {
+  const int x = threadIdx.x >> 6;
+  int first, end;
+  kragged_xcd_range<kWgradBK>(off, E, per_e, x, first, end);
+  if ((threadIdx.x & 63) == 0) {
+    xr[2 * x] = first;
+    xr[2 * x + 1] = end;
+  }
 }
 
 __global__ void split_offsets_kernel(const int32_t* __restrict__ off, int E, int S,
@@ -793,7 +859,7 @@ moe_status moe_ffn_bwd_workspace_size(moe_ctx* ctx, int E, int R, int d, int F, 
   if (dtype == MOE_MXFP8)
     *bytes = moe_internal_mx_bwd_bytes(E, R, d, F);
   else if (dtype == MOE_BF16)
-    *bytes = wgrad_split_bytes(E, R, d, F, &part);
+    *bytes = kPlanBytes + wgrad_split_bytes(E, R, d, F, &part);
   else
     *bytes = 0;
   return MOE_OK;
@@ -939,12 +1005,20 @@ static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
                                     (const float*)dyp, E, R, d, F, (float*)dg, (float*)du,
                                     (float*)dxp, (float*)dw_gate, (float*)dw_up, (float*)dw_down);
   size_t part_bytes = 0;
-  const size_t split_need = wgrad_split_bytes(E, R, d, F, &part_bytes);
-  if (split_need > 0 && (ctx->ws == nullptr || ctx->ws_bytes < split_need))
-    return fail(ctx, MOE_ERR_WORKSPACE, "moe_grouped_ffn_bwd: split-K workspace %zu bytes < %zu needed",
-                ctx->ws_bytes, split_need);
-  float* split_part = (float*)ctx->ws;
-  int32_t* split_voff = (int32_t*)((char*)ctx->ws + part_bytes);
+  const size_t need = kPlanBytes + wgrad_split_bytes(E, R, d, F, &part_bytes);
+  if (ctx->ws == nullptr || ctx->ws_bytes < need)
+    return fail(ctx, MOE_ERR_WORKSPACE, "moe_grouped_ffn_bwd: workspace %zu bytes < %zu needed",
+                ctx->ws_bytes, need);
+  int32_t* plan_dn = (int32_t*)ctx->ws;  // XCD ranges of the down wgrad
+  int32_t* plan_up = plan_dn + 16;       // and of the gate/up wgrad
+  float* split_part = (float*)((char*)ctx->ws + kPlanBytes);
+  int32_t* split_voff = (int32_t*)((char*)ctx->ws + kPlanBytes + part_bytes);
+  const int dn_per_e = ((d + BN - 1) / BN) * ((F + CfgWD::BM - 1) / CfgWD::BM);
+  const int up_per_e = ((F + 127) / 128) * ((d + CfgWU::BM - 1) / CfgWU::BM);
+  static_assert(CfgWD::BK == kWgradBK && CfgWU::BK == kWgradBK, "weight-gradient plans use kWgradBK");
+  // the down dgrad (R > 0) plans both weight gradients' XCD ranges; with no
+  // rows every tile costs the same and equal counts are exact
+  const bool planned = R > 0;
   hipError_t e;
   if (R > 0) {
     // down dgrad with the SwiGLU backward in the epilogue
@@ -965,6 +1039,10 @@ static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
     p.K = d;
     p.kseg = d;
     p.ntiles = (F + BN - 1) / BN;
+    p.xr_out0 = plan_dn;
+    p.xr_out1 = plan_up;
+    p.xr_pe0 = dn_per_e;
+    p.xr_pe1 = up_per_e;
     {
       moe_prof_scope ps(ctx, MOE_K_GEMM_DGRAD_DOWN);
       e = launch_mragged<DGRAD_DOWN>(p, R, ctx->stream);
@@ -991,13 +1069,16 @@ static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
       const int S = wgrad_splits(E, R, E * p.ntiles * p.mtiles);
       if (S == 1) {
+        p.xr = planned ? plan_dn : nullptr;
         e = launch<WGRAD_DOWN, CfgWD::BM, CfgWD::S, CfgWD::BK, CfgWD::OCC, CfgWD::NW>(p, E * p.ntiles * p.mtiles,
                                                                       ctx->stream);
       } else {
         split_offsets_kernel<<<(E * S + 256) / 256, 256, 0, ctx->stream>>>(offsets, E, S, split_voff);
+        xcd_plan_kernel<<<1, 512, 0, ctx->stream>>>(split_voff, E * S, dn_per_e, plan_dn);
         Params q = p;
         q.offsets = split_voff;
         q.E = E * S;
+        q.xr = plan_dn;
         q.c0 = split_part;
         q.part = 1;
         e = launch<WGRAD_DOWN, CfgWD::BM, CfgWD::S, CfgWD::BK, CfgWD::OCC, CfgWD::NW>(q, q.E * q.ntiles * q.mtiles,
@@ -1055,13 +1136,16 @@ static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
       moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
       const int S = wgrad_splits(E, R, E * p.ntiles * p.mtiles);
       if (S == 1) {
+        p.xr = planned ? plan_up : nullptr;
         e = launch<WGRAD_UP, CfgWU::BM, CfgWU::S, CfgWU::BK, CfgWU::OCC, CfgWU::NW>(p, E * p.ntiles * p.mtiles,
                                                                     ctx->stream);
       } else {
         split_offsets_kernel<<<(E * S + 256) / 256, 256, 0, ctx->stream>>>(offsets, E, S, split_voff);
+        xcd_plan_kernel<<<1, 512, 0, ctx->stream>>>(split_voff, E * S, up_per_e, plan_up);
         Params q = p;
         q.offsets = split_voff;
         q.E = E * S;
+        q.xr = plan_up;
         q.c0 = split_part;
         q.c1 = split_part + (size_t)E * S * d * F;
         q.part = 1;
