@@ -149,15 +149,18 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // Tile blocks are numbered from 0; with a plan (DGRAD_DOWN, xr_out0 set)
-  // the first eight blocks of the grid plan instead: block x < 8 writes the
-  // tile ranges of XCD x for the two weight gradients launched after this
-  // kernel (they read them in stream order) and exits.  Plan blocks are short
-  // and first in the grid, so their compute units take tiles right after.
+  // With a plan (DGRAD_DOWN, xr_out0 set) the last eight blocks of the grid
+  // plan instead of computing: the one on XCD x writes that XCD's tile ranges
+  // for the two weight gradients launched after this kernel (they read them
+  // in stream order) and exits.  Dispatched last, the plan blocks run while
+  // the final tiles finish (at the front of the grid they delayed eight
+  // compute units' first tiles).
   int bid = blockIdx.x, nblk = gridDim.x;
   if constexpr (MODE == DGRAD_DOWN) {
     if (p.xr_out0 != nullptr) {
-      if (bid < 8) {
+      nblk -= 8;
+      if (bid >= nblk) {
+        bid &= 7;
         if (wv == 0) {
           int f0, f1;
           kragged_xcd_range<kWgradBK>(p.offsets, p.E, p.xr_pe0, bid, f0, f1);
@@ -173,8 +176,6 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
         }
         return;
       }
-      bid -= 8;  // keeps bid % 8 == blockIdx.x % 8, the XCD
-      nblk -= 8;
     }
   }
 
@@ -677,8 +678,8 @@ static hipError_t launch_mragged(Params& p, int R, hipStream_t s) {
   using C = std::conditional_t<
       MODE == DGRAD_DOWN, CfgDD,
       std::conditional_t<MODE == DGRAD_UP, CfgDU, std::conditional_t<MODE == FWD_UP, CfgUP, CfgDN>>>;
-  // (+8 plan blocks when the down dgrad plans the weight gradients' ranges;
-  // the tile count is already a multiple of 8 after launch() rounds it)
+  // (+8 plan blocks at the end of the grid when the down dgrad plans the
+  // weight gradients' ranges; the tile count is rounded to a multiple of 8)
   const int tiles = (mtile_bound(R, p.E, C::BM) * p.ntiles + 7) / 8 * 8;
   return launch<MODE, C::BM, C::S, C::BK, C::OCC, C::NW>(p, tiles + (p.xr_out0 != nullptr ? 8 : 0), s);
 }
