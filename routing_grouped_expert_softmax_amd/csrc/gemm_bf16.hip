@@ -33,7 +33,9 @@
 //    expert the m-tiles sharing one weight tile are consecutive, so they meet
 //    in the same L2.  K-ragged launches (wgrad) have a fixed tile grid per
 //    expert and loop over that expert's own rows; an expert with no rows
-//    writes zeros.
+//    writes zeros.  Their XCD ranges balance K steps, not tile counts (with
+//    skewed routing a hot expert's tiles would pile onto one XCD): the down
+//    dgrad plans them for both weight gradients in eight extra blocks.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -180,10 +182,11 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   }
 
   // ---------------------------------------------------------------- work
-  // Logical tiles are split into eight contiguous ranges of equal tile count,
-  // one per XCD (block b runs on XCD b % 8), so the blocks of one XCD share
-  // operands in its L2.  Block b takes tiles first + b / 8, + nslot, ... of
-  // its XCD's range.
+  // Logical tiles are split into eight contiguous ranges, one per XCD (block
+  // b runs on XCD b % 8), so the blocks of one XCD share operands in its L2:
+  // equal tile counts for row-ragged launches, cost-balanced ranges for
+  // K-ragged ones.  Block b takes tiles first + b / 8, + nslot, ... of its
+  // XCD's range.
   MTileSched<BM> ms;
   int first, end;  // this XCD's range of logical tiles
   if (TR::kKRAGGED) {
