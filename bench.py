@@ -68,12 +68,32 @@ def row_bytes(name, T, d, k, F, E, esz=2):
     }.get(name)
 
 
+def _code_only(text):
+    """Source text without // comments (outside string literals), trailing
+    blanks and empty lines: what the kernel is built from."""
+    out = []
+    for line in text.splitlines():
+        cut = None
+        i = line.find("//")
+        while i >= 0:
+            if line.count('"', 0, i) % 2 == 0:
+                cut = i
+                break
+            i = line.find("//", i + 2)
+        code = (line if cut is None else line[:cut]).rstrip()
+        if code:
+            out.append(code)
+    return "\n".join(out)
+
+
 def source_hash(paths=None):
-    """First 16 hex digits of the SHA-256 of the bf16 grouped-GEMM sources."""
+    """First 16 hex digits of the SHA-256 of the bf16 grouped-GEMM sources'
+    code (comments and blank lines do not count: they cannot change the
+    kernels the counters were taken on)."""
     h = hashlib.sha256()
     for path in paths or GEMM_SOURCES:
-        with open(path, "rb") as fh:
-            h.update(fh.read())
+        with open(path, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
