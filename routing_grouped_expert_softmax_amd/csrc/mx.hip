@@ -137,8 +137,8 @@ __global__ void permute_mx_kernel(const uint4* __restrict__ x, const int32_t* __
 // half a 128-byte line of codes and two scale bytes.  Group g occupies padded
 // K [P_g, P_g + roundup(n_g, 128)), so a slice lies in exactly one group; its
 // rows past n_g are zeros (code 0, scale byte 0).  The slice's group comes
-// from a block-wide scan of the padded group sizes (groups from `offsets`, or
-// `urows` rows each when offsets is null).
+// from the padded group sizes: a closed form when every group has `urows`
+// rows (offsets null), else a shuffle scan by wave 0.
 constexpr int kColTile = 128;
 __global__ void __launch_bounds__(256) mx_cols_kernel(
     const bf16_t* __restrict__ src, int rows, int cols, const int32_t* __restrict__ offsets,
