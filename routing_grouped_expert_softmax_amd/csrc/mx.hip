@@ -35,22 +35,45 @@ __device__ __forceinline__ int mx_scale_byte(float amax) {
 // E4M3 codes of four values already divided by the block scale, packed in
 // element order: the hardware conversion (v_cvt_pk_fp8_f32, OCP E4M3, round
 // to nearest even) of the values clamped to +-448, which is the saturating
-// encoding; a NaN element becomes 0x7f (the clamp alone would turn it into a
-// bound).  Checked on every bf16 bit pattern against a plain encoder that
-// rounds each value to its binade's grid: equal for all non-NaN inputs,
-// signed zeros and subnormals included.
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+// encoding of every value but NaN (the clamp turns a NaN into a bound).
+// Checked on every bf16 bit pattern against a plain encoder that rounds each
+// value to its binade's grid: equal for all non-NaN inputs, signed zeros and
+// subnormals included.
+__device__ __forceinline__ uint32_t e4m3x4_finite(float a, float b, float c, float d) {
   const float lo = -448.0f, hi = 448.0f;
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi),
                                           __builtin_amdgcn_fmed3f(b, lo, hi), 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, lo, hi),
                                       __builtin_amdgcn_fmed3f(d, lo, hi), w, true);
-  uint32_t r = (uint32_t)w;
+  return (uint32_t)w;
+}
+
+// The same with NaN kept: a NaN element becomes 0x7f.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  uint32_t r = e4m3x4_finite(a, b, c, d);
   if (a != a) r = (r & 0xffffff00u) | 0x0000007fu;
   if (b != b) r = (r & 0xffff00ffu) | 0x00007f00u;
   if (c != c) r = (r & 0xff00ffffu) | 0x007f0000u;
   if (d != d) r = (r & 0x00ffffffu) | 0x7f000000u;
   return r;
+}
+
+// Codes of one 32-element block f scaled by inv = 2^-s, as eight words.  A
+// NaN is rare, so the block is encoded without the per-element NaN fix-ups
+// and encoded again with them only when one of its elements is NaN (one
+// unordered compare per pair of elements finds that).
+__device__ __forceinline__ void e4m3_block(const float (&f)[32], float inv, uint32_t* out) {
+  bool nan = false;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) nan |= __builtin_isunordered(f[2 * i], f[2 * i + 1]);
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    out[q] = e4m3x4_finite(f[q * 4] * inv, f[q * 4 + 1] * inv, f[q * 4 + 2] * inv, f[q * 4 + 3] * inv);
+  if (nan) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      out[q] = e4m3x4(f[q * 4] * inv, f[q * 4 + 1] * inv, f[q * 4 + 2] * inv, f[q * 4 + 3] * inv);
+  }
 }
 
 // 2^-s as a float for a block scale exponent s in [-127, 127] (a normal
@@ -78,9 +101,7 @@ __device__ __forceinline__ int quant_block(const uint4 (&v)[4], uint32_t (&out)[
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(f[i]));
   const int sb = mx_scale_byte(amax);
   const float inv = pow2_neg(sb - 127);
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-    out[q] = e4m3x4(f[q * 4] * inv, f[q * 4 + 1] * inv, f[q * 4 + 2] * inv, f[q * 4 + 3] * inv);
+  e4m3_block(f, inv, out);
   return sb;
 }
 
@@ -228,10 +249,7 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(
     const int sb = mx_scale_byte(amax);
     const float inv = pow2_neg(sb - 127);
     sword |= (uint32_t)sb << (8 * bb);
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      code_words[bb * 8 + q] =
-          e4m3x4(f[q * 4] * inv, f[q * 4 + 1] * inv, f[q * 4 + 2] * inv, f[q * 4 + 3] * inv);
+    e4m3_block(f, inv, code_words + bb * 8);
   }
   const size_t k = (size_t)y * 128;  // padded K position of the slice
   if (c < cols)
