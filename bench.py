@@ -7,7 +7,14 @@ grouped SwiGLU experts, gate-weighted combine, then combine backward, routing
 backward, grouped dgrad/wgrad, permute backward with the router term, and the
 router weight gradient.  Inputs are resident in HBM before timing starts.
 
-Prints ONE JSON line.  `value` is tokens/s over the timed steps.  `roofline`
+Prints ONE JSON line.  `value` is tokens/s over the timed steps: W warm-up
+then K replays of the whole step captured once in a HIP graph, between two
+synchronisations (the replays' outputs are checked equal to the eager step's;
+if capture fails the eager steps are timed instead, and `timing` says which).
+`eager` is the same K steps launched kernel by kernel; `graph` adds the
+median, p10 and p90 of single replays, warm and with the caches flushed by a
+1 GiB write before each replay; `smi` holds rocm-smi's clocks before and
+after.  `roofline`
 describes the dominant kernel (largest total time): its algorithmic FLOPs per
 launch over its average launch time, measured with HIP events recorded on the
 library's stream around every launch in the timed region; `traffic` is its
@@ -174,6 +181,76 @@ def time_steps(ctx, step, steps, warmup):
     return e0.elapsed_time(e1), wall, ctx.profile_results()
 
 
+def graph_timing(step, check, steps, warmup, replays=50, warm=10):
+    """The step captured once in a HIP graph and replayed. First `warmup`
+    replays, then exactly `steps` replays back to back between two
+    synchronisations (the bench's timed steps); then each replay timed by its
+    own pair of events: median, p10 and p90 per replay, "warm" (replays back
+    to back) and "cold" (a 1 GiB buffer written before every replay, which
+    evicts the 256 MB Infinity Cache and the L2s). `check()` compares the
+    layer's outputs after all replays with the eager step's."""
+    import torch
+
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    out = {"steps_ms": e0.elapsed_time(e1), "steps_wall_s": time.perf_counter() - w0,
+           "replays": replays, "warmup_replays": warm}
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    for mode in ("warm", "cold"):
+        for _ in range(warm):
+            graph.replay()
+        ev = []
+        for i in range(replays):
+            if mode == "cold":
+                scratch.fill_(i & 0xff)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]  # noqa: E731
+        out[mode] = {"median_ms": round(q(0.5), 4), "p10_ms": round(q(0.1), 4),
+                     "p90_ms": round(q(0.9), 4)}
+    out["replay_matches_eager"] = bool(check())
+    del graph, scratch
+    return out
+
+
+def smi_snapshot():
+    """Clocks and power of the GPU from rocm-smi (a child process), or the
+    reason they could not be read."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        data = json.loads(r.stdout)
+        card = next(iter(v for k, v in sorted(data.items()) if k.startswith("card")))
+        return {k: v for k, v in card.items() if "clk" in k.lower() or "power" in k.lower()}
+    except Exception as exc:  # reported, never fatal: the timing does not depend on it
+        return {"error": f"{type(exc).__name__}: {exc}"[:200]}
+
+
 def gemm_summary(prof, unit, peak):
     """Dominant grouped-GEMM kernel (largest total time) and the six GEMMs
     together: algorithmic FLOPs over the HIP-event kernel times."""
@@ -194,7 +271,7 @@ def gemm_summary(prof, unit, peak):
 
 
 def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=False, shared_F=0,
-              recompute=False):
+              recompute=False, graph=False):
     """Time the whole layer forward+backward on one workload (and, with
     `with_stats`, the routing statistics on its last step's buffers).
     mxfp8: quantise on the permute and run the MXFP8 expert GEMMs.
@@ -230,6 +307,21 @@ def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=Fal
                load={"max": int(counts.max()), "mean": float(counts.float().mean()),
                      "empty": int((counts == 0).sum())},
                saved_bytes=moe.saved_activation_bytes(buf, recompute=recompute))
+    if graph:
+        ref = {"y": buf.y.clone(), "dx": buf.dx.clone(), "dw_up": buf.bwd["dw_up"].clone(),
+               "dw_router": buf.dw_router.clone()}
+        for t in (buf.y, buf.dx, buf.bwd["dw_up"], buf.dw_router):
+            t.zero_()
+        try:
+            gr = graph_timing(step, steps=steps, warmup=warmup, check=lambda: all(
+                torch.equal(ref[n], t) for n, t in (("y", buf.y), ("dx", buf.dx),
+                                                    ("dw_up", buf.bwd["dw_up"]),
+                                                    ("dw_router", buf.dw_router))))
+            gr["tokens_per_s_warm_median"] = round(cfg.T / (gr["warm"]["median_ms"] / 1e3), 1)
+            gr["tokens_per_s_cold_median"] = round(cfg.T / (gr["cold"]["median_ms"] / 1e3), 1)
+        except Exception as exc:  # the eager timing above still stands
+            gr = {"error": f"{type(exc).__name__}: {exc}"[:300]}
+        out["graph"] = gr
     if with_stats:
         out["routing_stats"] = stats_leg(ctx, cfg, override if override is not None else buf.logits,
                                          buf, counts)
@@ -376,6 +468,9 @@ def main():
     ap.add_argument("--no-recompute", action="store_true", help="skip the activation-recompute leg")
     ap.add_argument("--no-stats", action="store_true",
                     help="skip the routing-statistics / balance-loss / gradient-norm leg")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing (median / p10 / p90, warm and cold)")
+    ap.add_argument("--no-smi", action="store_true", help="skip reading clocks and power with rocm-smi")
     ap.add_argument("--mx-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
@@ -395,8 +490,10 @@ def main():
         return
 
     cfg = mi.config(args.workload)
+    smi_before = smi_snapshot() if not args.no_smi else None
     main_leg = layer_leg(cfg, args.steps, args.warmup, keep_inputs=args.cpu_sample > 0,
-                         with_stats=not args.no_stats)
+                         with_stats=not args.no_stats, graph=not args.no_graph)
+    smi_after = smi_snapshot() if not args.no_smi else None
     prof = main_leg["prof"]
     R = cfg.T * cfg.k
     unit = R * cfg.d * cfg.F
@@ -410,14 +507,21 @@ def main():
             gbs = row_bytes(name, cfg.T, cfg.d, cfg.k, cfg.F, cfg.E) / (ms / n / 1e3) / 1e9
             rows[name] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
 
+    # The timed steps: K replays of the whole step captured in one HIP graph
+    # (outputs checked against the eager step), else K eager steps.
+    gr = main_leg.get("graph") or {}
+    if gr.get("replay_matches_eager"):
+        timed_ms, wall, timing = gr["steps_ms"], gr["steps_wall_s"], "hip_graph_replay"
+    else:
+        timed_ms, wall, timing = main_leg["gpu_ms"], main_leg["wall"], "eager"
     result = {
         "metric": METRIC,
-        "value": round(main_leg["tokens_per_s"], 1),
+        "value": round(cfg.T * args.steps / (timed_ms / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(main_leg["ms_per_step"], 4),
+        "ms_per_step": round(timed_ms / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -432,8 +536,16 @@ def main():
         "row_movers": rows,
         "kernel_ms": {name: round(ms / n, 4) for name, (n, ms) in prof.items()},
         "expert_load": main_leg["load"],
-        "wall_s_timed": round(main_leg["wall"], 3),
+        "timing": timing,
+        "wall_s_timed": round(wall, 3),
+        "eager": {"tokens_per_s": round(main_leg["tokens_per_s"], 1),
+                  "ms_per_step": round(main_leg["ms_per_step"], 4),
+                  "note": "K steps launched one kernel at a time; kernel_ms and roofline come from this run"},
     }
+    if "graph" in main_leg:
+        result["graph"] = main_leg["graph"]
+    if smi_before is not None:
+        result["smi"] = {"before": smi_before, "after": smi_after}
     if "routing_stats" in main_leg:
         result["routing_stats"] = main_leg["routing_stats"]
     base = None
