@@ -236,6 +236,60 @@ def graph_timing(step, check, steps, warmup, replays=50, warm=10):
     return out
 
 
+def copy_peak(mib=1024, reps=10):
+    """Measured HBM ceiling for the row movers: `mib` MiB copied by the
+    runtime's device-to-device copy and by an elementwise fp32 kernel
+    (x * 1, four floats = 16 bytes per vector access); bytes read + written
+    per second of the faster, best of `reps` launches each, timed with
+    events."""
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    ways = {"memcpy": lambda: dst.copy_(src), "elementwise": lambda: torch.mul(src, 1.0, out=dst)}
+    best = {}
+    for name, f in ways.items():
+        f()
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            best[name] = min(best.get(name, ms), ms)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {name: round(2 * n / (ms / 1e3) / 1e9, 1) for name, ms in best.items()}
+
+
+def mfma_probe(iters=50000):
+    """Sustained bf16 MFMA rate: the library's register-only probe on three
+    blocks of four waves per CU (one round, no tail), timed with events;
+    best of three launches."""
+    import torch
+
+    import routing_grouped_expert_softmax_amd as moe
+
+    blocks = 3 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = moe.moe_mfma_peak_probe(blocks, 1000)
+    best = None
+    for _ in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moe.moe_mfma_peak_probe(blocks, iters, sink=sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    flops = blocks * 4 * iters * 4 * 32768
+    return {"tflops": round(flops / (best / 1e3) / 1e12, 1), "ms": round(best, 3), "blocks": blocks,
+            "iters": iters}
+
+
 def smi_snapshot():
     """Clocks and power of the GPU from rocm-smi (a child process), or the
     reason they could not be read."""
@@ -500,12 +554,21 @@ def main():
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
     roof, agg = gemm_summary(prof, unit, peak)
     roof["traffic"] = read_traffic(roof["kernel"], cfg.name)
+    probe = None
+    if cfg.dtype == "bf16":
+        probe = mfma_probe()
+        probe["frac_of_published_peak"] = round(probe["tflops"] / PEAK_BF16_TFLOPS, 4)
+        agg["frac_of_measured_peak"] = round(agg["tflops"] / probe["tflops"], 4)
     rows = {}
+    copies = copy_peak()
+    copy_gbs = max(copies.values())
     for name in ("permute", "combine", "combine_bwd", "permute_bwd"):
         if name in prof and cfg.dtype == "bf16":
             n, ms = prof[name]
             gbs = row_bytes(name, cfg.T, cfg.d, cfg.k, cfg.F, cfg.E) / (ms / n / 1e3) / 1e9
-            rows[name] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
+            rows[name] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 3),
+                          "frac_copy": round(gbs / copy_gbs, 3)}
+    rows["copy_peak_GB/s"] = copies
 
     # The timed steps: K replays of the whole step captured in one HIP graph
     # (outputs checked against the eager step), else K eager steps.
@@ -533,6 +596,7 @@ def main():
                    "parallelism": "single GPU (one GPU's share; no collectives)"},
         "roofline": roof,
         "grouped_gemm": agg,
+        "mfma_probe": probe,
         "row_movers": rows,
         "kernel_ms": {name: round(ms / n, 4) for name, (n, ms) in prof.items()},
         "expert_load": main_leg["load"],

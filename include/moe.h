@@ -372,6 +372,18 @@ moe_status moe_profile_query(moe_ctx* ctx, int kernel_id, int* launches, double*
 /* Static name of a kernel id. */
 const char* moe_kernel_name(int kernel_id);
 
+/* Measurement probe (not a step of the layer): the sustained bf16
+ * matrix-core rate at the clock the chip holds under pure MFMA load, for
+ * quoting the grouped GEMMs beside a measured ceiling as well as the
+ * published peak.  Launches `blocks` blocks of 256 threads; every wave runs
+ * `iters` rounds of four independent v_mfma_f32_32x32x16_bf16 (32768 FLOPs
+ * each) on register operands whose elements are a and b rounded to bf16,
+ * then writes one float per thread to the device buffer sink (blocks*256
+ * floats, caller-owned): 1024*a*b*iters, exact while below 2^24.  FLOPs per
+ * launch = blocks * 4 * iters * 4 * 32768.  MOE_ERR_INVALID_ARGUMENT for blocks
+ * outside [1, 2^20], iters < 1 or a null sink. */
+moe_status moe_mfma_peak_probe(moe_ctx* ctx, int blocks, int iters, float a, float b, float* sink);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,6 +55,7 @@ _SIGS = {
     "moe_route_stats": [_vp, _vp, _int, _int, _int, _flt, _vp, _vp, _vp, _vp],
     "moe_aux_loss_bwd": [_vp, _vp, _int, _int, _int, _flt, _flt, _vp],
     "moe_expert_grad_norms": [_vp, _int, _int, _int, _int, _vp],
+    "moe_mfma_peak_probe": [_int, _int, _flt, _flt, _vp],
 }
 EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "moe_last_error",
            "moe_workspace_size", "moe_set_workspace", *_SIGS.keys(), "moe_profile_enable",
@@ -613,3 +614,17 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxf
                         dx_shared=dxs)
     moe_router_wgrad(x, buf.dlogits_sel, r["src_tk"], r["offsets"], w_router.shape[1], buf.dw_router)
     return buf.dx
+
+
+def moe_mfma_peak_probe(blocks, iters, a=1.0, b=1.0, sink=None):
+    """Launch the matrix-core rate probe: `blocks` blocks of four waves, each
+    wave `iters` rounds of four v_mfma_f32_32x32x16_bf16 on register operands
+    (32768 FLOPs each).  Returns the sink, one float per thread, equal to
+    1024·a·b·iters (a and b as bf16) while that is exact in fp32."""
+    if sink is None:
+        sink = torch.empty(blocks * 256, dtype=torch.float32, device=f"cuda:{torch.cuda.current_device()}")
+    _need_cuda(sink)
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 256:
+        raise MoeError("sink must be float32 with at least blocks*256 elements")
+    context().call("moe_mfma_peak_probe", blocks, iters, a, b, _p(sink))
+    return sink

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["context.hip", "route.hip", "rows.hip", "gemm_bf16.hip", "gemm_f32.hip", "mx.hip",
-           "gemm_mx.hip", "stats.hip"]
+           "gemm_mx.hip", "stats.hip", "peak.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
