@@ -525,6 +525,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the HIP-graph replay timing (median / p10 / p90, warm and cold)")
     ap.add_argument("--no-smi", action="store_true", help="skip reading clocks and power with rocm-smi")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured MFMA-rate and device-copy ceilings")
     ap.add_argument("--mx-steps", type=int, default=10)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration) and exit")
@@ -555,20 +557,22 @@ def main():
     roof, agg = gemm_summary(prof, unit, peak)
     roof["traffic"] = read_traffic(roof["kernel"], cfg.name)
     probe = None
-    if cfg.dtype == "bf16":
+    if cfg.dtype == "bf16" and not args.no_ceilings:
         probe = mfma_probe()
         probe["frac_of_published_peak"] = round(probe["tflops"] / PEAK_BF16_TFLOPS, 4)
         agg["frac_of_measured_peak"] = round(agg["tflops"] / probe["tflops"], 4)
     rows = {}
-    copies = copy_peak()
-    copy_gbs = max(copies.values())
+    copies = copy_peak() if not args.no_ceilings else None
+    copy_gbs = max(copies.values()) if copies else None
     for name in ("permute", "combine", "combine_bwd", "permute_bwd"):
         if name in prof and cfg.dtype == "bf16":
             n, ms = prof[name]
             gbs = row_bytes(name, cfg.T, cfg.d, cfg.k, cfg.F, cfg.E) / (ms / n / 1e3) / 1e9
-            rows[name] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 3),
-                          "frac_copy": round(gbs / copy_gbs, 3)}
-    rows["copy_peak_GB/s"] = copies
+            rows[name] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
+            if copy_gbs:
+                rows[name]["frac_copy"] = round(gbs / copy_gbs, 3)
+    if copies:
+        rows["copy_peak_GB/s"] = copies
 
     # The timed steps: K replays of the whole step captured in one HIP graph
     # (outputs checked against the eager step), else K eager steps.
