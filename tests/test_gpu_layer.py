@@ -148,26 +148,21 @@ def test_full_size_sampled(moe, name):
     rng = np.random.default_rng(123)
     x, wr, dy = mi.f32(inp["x"]), mi.f32(inp["wr"]), mi.f32(inp["dy"])
     wg, wu, wd = mi.f32(inp["wg"]), mi.f32(inp["wu"]), mi.f32(inp["wd"])
-    # routing on every token
+    # routing on every token, bit-exact: the oracle routes the same fp32
+    # scores the GPU routed (generated ones, or the GPU's own router output,
+    # which is checked against the oracle's scores separately)
     if "logits" in inp:
-        r = oracle.route(inp["logits"].numpy(), cfg.k, "f32")
-        for key in ("topk_idx", "counts", "offsets", "row_of"):
-            assert np.array_equal(buf.route[key].cpu().numpy(), r[key]), key
-        assert np.array_equal(buf.route["src_tk"].cpu().numpy(), r["src_tk"])
+        src = inp["logits"].numpy()
     else:
         logits = oracle.router_logits(x, wr, "f32")
-        assert_close(buf.logits.cpu().numpy(), logits, 1e-5, "logits")
-        r = oracle.route(logits, cfg.k, "f32")
-        gt = buf.route["topk_idx"].cpu().numpy()
-        differ = np.any(gt != r["topk_idx"], axis=1)
-        near = topk_margin(logits, cfg.k) < 1e-4
-        assert not np.any(differ & ~near), "routing differs away from near ties"
-        if not differ.any():
-            for key in ("counts", "offsets", "row_of"):
-                assert np.array_equal(buf.route[key].cpu().numpy(), r[key]), key
+        src = buf.logits.cpu().numpy()
+        assert_close(src, logits, 1e-5, "logits")
+    r = oracle.route(src, cfg.k, "f32")
+    for key in ("topk_idx", "counts", "offsets", "row_of", "src_tk"):
+        assert np.array_equal(buf.route[key].cpu().numpy(), r[key]), key
+    np.testing.assert_allclose(buf.route["gates"].cpu().numpy(), r["gates"], rtol=0, atol=1e-5)
     gates = r["gates"]
     tok = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 48, replace=False)]))
-    tok = tok[np.all(buf.route["topk_idx"].cpu().numpy()[tok] == r["topk_idx"][tok], axis=1)]
     # forward output and input gradient at the sampled tokens
     y = oracle.layer_fwd(x[tok], r["topk_idx"][tok], gates[tok], wg, wu, wd)
     assert_close(buf.y.float().cpu().numpy()[tok], y, 2e-2, "y (sampled tokens)")

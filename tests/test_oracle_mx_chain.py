@@ -123,3 +123,119 @@ def test_sampled_rows_and_elements_match_full_chain():
     el2 = np.array([[0, 3, 5], [2, 127, 63], [3, 10, 0], [1, 4, 4]])
     got = oracle.mx_expert_wgrad_elems(xp, dyp, offsets, wg, wu, wd, 2, el2)
     np.testing.assert_allclose(got, b["dwd"][el2[:, 0], el2[:, 1], el2[:, 2]], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------ exact backward pins
+# Operands for which every backward product of the chain is lossless along the
+# axis the chain must quantise it on, and lossy along any other: powers of two
+# (closed under products, so dh, dg, du stay on E4M3's grid) with scale
+# structure the MX block axis must respect.
+#   * Wg, Wu: row i of an expert's [d, F] matrix carries 2^(18 (i mod 3)), so
+#     blocks along F (the dgrad's reduction axis) share one binade range,
+#     while blocks along d would span 2^36 and flush their small entries.
+#   * xp, h: expert e's rows carry 2^(18 e) and column j another
+#     2^(18 (j mod 3)): blocks down a column that restart at each expert are
+#     lossless; blocks that straddle two experts, or run along the row, flush.
+#   * g = 64 everywhere: sigmoid(64) is exactly 1 in fp64, so dg = dh u and
+#     du = 64 dh exactly (the SwiGLU backward's own formula is pinned above).
+#   * dyp has one nonzero per row, so dh = dyp Wd^T is a single product.
+_AXIS_D, _AXIS_F = 64, 96
+_AXIS_COUNTS = [40, 0, 64, 37]
+
+
+def _axis_operands(seed=21):
+    rng = np.random.default_rng(seed)
+    d, F, counts = _AXIS_D, _AXIS_F, _AXIS_COUNTS
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    pw = lambda *s: rng.choice([-2.0, -1.0, -0.5, 0.5, 1.0, 2.0], size=s)  # noqa: E731
+    expert = np.repeat(np.arange(E), counts)
+    rowscale = np.ldexp(1.0, 18 * expert)[:, None]
+    xp = pw(R, d) * rowscale * np.ldexp(1.0, 18 * (np.arange(d) % 3))[None, :]
+    h = pw(R, F) * rowscale * np.ldexp(1.0, 18 * (np.arange(F) % 3))[None, :]
+    wscale = np.ldexp(1.0, 18 * (np.arange(d) % 3))[None, :, None]
+    wg, wu = pw(E, d, F) * wscale, pw(E, d, F) * wscale
+    wd = pw(E, F, d) * (rng.random((E, F, d)) < 0.8)
+    dyp = np.zeros((R, d))
+    dyp[np.arange(R), rng.integers(0, d, R)] = pw(R)
+    g = np.full((R, F), 64.0)
+    u = pw(R, F)
+    f32 = lambda a: a.astype(np.float32)  # noqa: E731 — exact: every value is a float32
+    return offsets, f32(xp), f32(dyp), f32(wg), f32(wu), f32(wd), g, u, f32(h)
+
+
+def _exact_bwd(offsets, xp, dyp, wg, wu, wd, u):
+    """fp64 products of the unquantised operands (exact here: every sum is of
+    powers of two within a few dozen binades)."""
+    E = wg.shape[0]
+    R, F = u.shape
+    dh = np.zeros((R, F))
+    for e in range(E):
+        lo, hi = offsets[e], offsets[e + 1]
+        dh[lo:hi] = dyp[lo:hi].astype(np.float64) @ wd[e].astype(np.float64).T
+    dg, du = dh * u, 64.0 * dh
+    dxp = np.zeros((R, xp.shape[1]))
+    dwg, dwu = np.zeros(wg.shape), np.zeros(wu.shape)
+    dwd = np.zeros(wd.shape)
+    return dh, dg, du, dxp, dwg, dwu, dwd
+
+
+def _axis_pin(b, offsets, xp, dyp, wg, wu, wd, u, h):
+    """Which outputs of the chain's backward equal the exact products."""
+    _, dg, du, dxp, dwg, dwu, dwd = _exact_bwd(offsets, xp, dyp, wg, wu, wd, u)
+    x64, h64, y64 = xp.astype(np.float64), h.astype(np.float64), dyp.astype(np.float64)
+    for e in range(wg.shape[0]):
+        lo, hi = offsets[e], offsets[e + 1]
+        dxp[lo:hi] = dg[lo:hi] @ wg[e].astype(np.float64).T + du[lo:hi] @ wu[e].astype(np.float64).T
+        dwg[e] = x64[lo:hi].T @ dg[lo:hi]
+        dwu[e] = x64[lo:hi].T @ du[lo:hi]
+        dwd[e] = h64[lo:hi].T @ y64[lo:hi]
+    want = dict(dg=dg, du=du, dxp=dxp, dwg=dwg, dwu=dwu, dwd=dwd)
+    return {k: bool(np.array_equal(b[k], want[k])) for k in want}
+
+
+def test_axis_operands_are_lossless_only_on_the_chain_axes():
+    offsets, xp, dyp, wg, wu, wd, g, u, h = _axis_operands()
+    for w in (wg[0], wu[2]):
+        assert np.array_equal(oracle.mx_rows(w), w)              # blocks along F
+        assert not np.array_equal(oracle.mx_cols(w, None), w)    # blocks along d
+    for a in (xp, h):
+        assert np.array_equal(oracle.mx_cols(a, offsets), a)     # restart per expert
+        assert not np.array_equal(oracle.mx_cols(a, None), a)    # straddling experts
+        assert not np.array_equal(oracle.mx_rows(a), a)          # along the row
+
+
+def test_mx_bwd_exact_on_axis_structured_operands():
+    offsets, xp, dyp, wg, wu, wd, g, u, h = _axis_operands()
+    b = oracle.mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, g, u, h)
+    ok = _axis_pin(b, offsets, xp, dyp, wg, wu, wd, u, h)
+    assert all(ok.values()), ok
+    assert np.any(b["dxp"]) and np.any(b["dwg"]) and np.any(b["dwd"])
+    assert not np.any(b["dwg"][1]) and not np.any(b["dwd"][1])  # the empty expert
+
+
+def test_mx_bwd_pin_detects_planted_wrong_axes(monkeypatch):
+    """Each planted mistake in the chain's quantisation axes breaks the exact
+    pin on the outputs it feeds."""
+    offsets, xp, dyp, wg, wu, wd, g, u, h = _axis_operands()
+    rows, cols = oracle.mx_rows, oracle.mx_cols
+    d, F = _AXIS_D, _AXIS_F
+
+    def run():
+        b = oracle.mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, g, u, h)
+        return _axis_pin(b, offsets, xp, dyp, wg, wu, wd, u, h)
+
+    # Wg^T / Wu^T of the dgrad quantised along d instead of F
+    monkeypatch.setattr(oracle, "mx_rows", lambda a: cols(a, None) if a.shape == (d, F) else rows(a))
+    ok = run()
+    assert not ok["dxp"] and ok["dwg"] and ok["dwd"], ok
+    monkeypatch.setattr(oracle, "mx_rows", rows)
+    # weight-gradient column blocks that do not restart at expert boundaries
+    monkeypatch.setattr(oracle, "mx_cols", lambda a, off: cols(a, None))
+    ok = run()
+    assert not ok["dwg"] and not ok["dwu"] and not ok["dwd"] and ok["dxp"], ok
+    # weight-gradient operands blocked along their rows instead of down columns
+    monkeypatch.setattr(oracle, "mx_cols", lambda a, off: rows(a) if off is not None else cols(a, off))
+    ok = run()
+    assert not ok["dwg"] and not ok["dwu"] and not ok["dwd"] and ok["dxp"], ok
