@@ -37,8 +37,8 @@
  *    the context's stream, so the whole layer can be captured in a HIP graph.
  *    counts/offsets are never read by the host.
  *  - Errors: host-side validation returns MOE_ERR_INVALID_ARGUMENT (null or
- *    misaligned pointers, sizes out of range) or MOE_ERR_UNSUPPORTED, and
- *    never aborts; launch failures return MOE_ERR_HIP.  moe_last_error gives
+ *    misaligned pointers, sizes out of range, two outputs of one call whose
+ *    byte ranges overlap) or MOE_ERR_UNSUPPORTED, and never aborts; launch failures return MOE_ERR_HIP.  moe_last_error gives
  *    the text.  Device faults surface asynchronously, as in HIP.
  *  - Limits: 1 <= k <= min(E, 32); E <= 1024; T*k < 2^31; d % 8 == 0 and
  *    F % 8 == 0 (16-byte bf16 rows); data pointers 16-byte aligned.  The bf16
@@ -121,7 +121,9 @@ moe_status moe_set_workspace(moe_ctx* ctx, void* ws, size_t bytes);
 /* ---------------------------------------------------------------- forward */
 
 /* Router scores: logits[t,e] = sum_i x[t,i] * w_router[i,e], fp32
- * accumulation, fp32 output.  [P2] 1.1, 2.1. */
+ * accumulation, fp32 output, any E up to 1024 in either dtype (bf16 with
+ * E > 16, E % 8 == 0 and d % 64 == 0 runs on the matrix cores; every other
+ * shape on the vector ALUs, 64 experts per pass over x).  [P2] 1.1, 2.1. */
 moe_status moe_router_logits(moe_ctx* ctx, const void* x, const void* w_router, int T, int d,
                              int E, moe_dtype dtype, float* logits);
 

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <cstdarg>
+#include <initializer_list>
 #include <cstdio>
 #include <string>
 #include <utility>
@@ -132,7 +133,38 @@ inline int device_cus() {
   return cus[dev];
 }
 
+// One output array of a call: its device address range.  NULL or empty
+// arrays take part in no overlap.
+struct OutSpan {
+  const void* p;
+  size_t bytes;
+  const char* name;
+};
+
+// Every pair of a call's outputs must be disjoint (a kernel may write them
+// in any order, so overlapping outputs would race).
+inline moe_status check_disjoint(moe_ctx* ctx, const char* fn, std::initializer_list<OutSpan> outs) {
+  for (const OutSpan* a = outs.begin(); a != outs.end(); ++a) {
+    if (a->p == nullptr || a->bytes == 0) continue;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a->p), a1 = a0 + a->bytes;
+    for (const OutSpan* b = a + 1; b != outs.end(); ++b) {
+      if (b->p == nullptr || b->bytes == 0) continue;
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(b->p), b1 = b0 + b->bytes;
+      if (a0 < b1 && b0 < a1)
+        return fail(ctx, MOE_ERR_INVALID_ARGUMENT, "%s: outputs %s and %s overlap", fn, a->name, b->name);
+    }
+  }
+  return MOE_OK;
+}
+
 }  // namespace moe_host
+
+// Rejects the call when two of its outputs overlap.
+#define MOE_REQUIRE_DISJOINT(ctx, fn, ...)                                        \
+  do {                                                                            \
+    const moe_status st_dj_ = moe_host::check_disjoint((ctx), (fn), {__VA_ARGS__}); \
+    if (st_dj_ != MOE_OK) return st_dj_;                                          \
+  } while (0)
 
 #define MOE_CHECK_CTX(ctx) \
   do {                     \

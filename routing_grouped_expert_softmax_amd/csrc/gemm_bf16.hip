@@ -889,6 +889,11 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
     MOE_REQUIRE_PTR(ctx, w_down);
     MOE_REQUIRE_PTR_OR_EMPTY(ctx, yp, R == 0);
   }
+  {
+    const size_t es = dtype == MOE_F32 ? 4 : 2, rf = (size_t)R * F * es;
+    MOE_REQUIRE_DISJOINT(ctx, "moe_grouped_ffn_fwd", {g, rf, "g"}, {u, rf, "u"}, {h, rf, "h"},
+                         {yp, (size_t)R * d * es, "yp"});
+  }
   if (R == 0) return MOE_OK;
   if (dtype == MOE_MXFP8)
     return moe_internal_ffn_fwd_mx(ctx, (const bf16_t*)xp, nullptr, nullptr, (const bf16_t*)w_gate,
@@ -965,6 +970,11 @@ moe_status moe_grouped_ffn_fwd_mxq(moe_ctx* ctx, const uint8_t* xp_codes, const 
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, u, R == 0);
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, h, R == 0);
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, yp, R == 0);
+  {
+    const size_t rf = (size_t)R * F * 2;
+    MOE_REQUIRE_DISJOINT(ctx, "moe_grouped_ffn_fwd_mxq", {g, rf, "g"}, {u, rf, "u"}, {h, rf, "h"},
+                         {yp, (size_t)R * d * 2, "yp"});
+  }
   if (R == 0) return MOE_OK;
   return moe_internal_ffn_fwd_mx(ctx, nullptr, xp_codes, xp_scales, (const bf16_t*)w_gate,
                                  (const bf16_t*)w_up, (const bf16_t*)w_down, offsets, E, R, d, F,
@@ -995,6 +1005,12 @@ static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
   MOE_REQUIRE_PTR(ctx, dw_gate);
   MOE_REQUIRE_PTR(ctx, dw_up);
   MOE_REQUIRE_PTR(ctx, dw_down);
+  {
+    const size_t es = dtype == MOE_F32 ? 4 : 2, rf = (size_t)R * F * es, w = (size_t)E * d * F * es;
+    MOE_REQUIRE_DISJOINT(ctx, "moe_grouped_ffn_bwd", {dg, rf, "dg"}, {du, rf, "du"},
+                         {dxp, (size_t)R * d * es, "dxp"}, {dw_gate, w, "dw_gate"}, {dw_up, w, "dw_up"},
+                         {dw_down, w, "dw_down"});
+  }
   if (dtype == MOE_MXFP8)
     return moe_internal_ffn_bwd_mx(ctx, (const bf16_t*)xp, (const bf16_t*)w_gate,
                                    (const bf16_t*)w_up, (const bf16_t*)w_down, offsets,

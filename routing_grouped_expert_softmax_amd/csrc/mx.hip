@@ -313,6 +313,11 @@ extern "C" moe_status moe_permute_mx(moe_ctx* ctx, const void* x, const int32_t*
   MOE_REQUIRE_PTR(ctx, xp_codes);
   MOE_REQUIRE(ctx, xp_scales != nullptr, "moe_permute_mx: xp_scales is null");
   MOE_REQUIRE(ctx, xp == nullptr || aligned16(xp), "moe_permute_mx: xp not 16-byte aligned");
+  {
+    const size_t n = (size_t)T_ * k * d;
+    MOE_REQUIRE_DISJOINT(ctx, "moe_permute_mx", {xp, n * 2, "xp"}, {xp_codes, n, "xp_codes"},
+                         {xp_scales, n / 32, "xp_scales"});
+  }
   const long long nb = (long long)T_ * (d / 32);
   moe_prof_scope ps(ctx, MOE_K_PERMUTE);
   permute_mx_kernel<<<(unsigned)((nb + 255) / 256), 256, 0, ctx->stream>>>(
@@ -330,6 +335,13 @@ extern "C" moe_status moe_mx_quantize(moe_ctx* ctx, const void* src_bf16, int ro
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, codes, rows == 0);
   MOE_REQUIRE(ctx, rows == 0 || scales_e8m0 != nullptr, "moe_mx_quantize: scales is null");
   if (rows == 0) return MOE_OK;
+  if (axis == 0) {
+    MOE_REQUIRE_DISJOINT(ctx, "moe_mx_quantize", {codes, (size_t)rows * cols, "codes"},
+                         {scales_e8m0, (size_t)rows * cols / 32, "scales"});
+  } else if (kpad_ld > 0) {
+    MOE_REQUIRE_DISJOINT(ctx, "moe_mx_quantize", {codes, (size_t)cols * kpad_ld, "codes"},
+                         {scales_e8m0, (size_t)cols * (kpad_ld / 32), "scales"});
+  }
   moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
   hipError_t e;
   if (axis == 0) {

@@ -6,7 +6,7 @@
 // stays resident on the GPU ([P1] 核心特点 二, GPU-resident routing).
 //
 // Device layout of the routing workspace: block_counts[E][nblk] int32 with
-// nblk = ceil(T / 256): expert-major, so the scan kernel reads each expert's
+// nblk = ceil(T / 64) (one block of 64 tokens each): expert-major, so the scan kernel reads each expert's
 // per-block counts contiguously.
 #include <hip/hip_runtime.h>
 
@@ -23,11 +23,14 @@ constexpr int kTokBlock = 64;  // tokens per routing block (one wave, one token 
 // lane takes 16-byte chunks of the token's row and the matching rows of W_r
 // (E contiguous values per feature), accumulating all E dot products in
 // registers; the E partial sums are reduced across the wave in a fixed order.
-// (Large E uses the MFMA grouped GEMM with a single group; see gemm_bf16.hip.)
+// One launch covers the experts [e0, e0 + Ec) with Ec <= EMAX; E is the row
+// length of W_r and of the logits.  (bf16 with E > 16 and E % 8 == 0 uses the
+// MFMA grouped GEMM with a single group, see gemm_bf16.hip; any other E above
+// 64 runs here as several 64-expert launches, each reading x again.)
 template <typename T, int EMAX, bool EXACT>
 __global__ void __launch_bounds__(256) router_logits_small_kernel(const T* __restrict__ x,
                                                                   const T* __restrict__ wr, int T_,
-                                                                  int d, int E,
+                                                                  int d, int E, int e0, int Ec,
                                                                   float* __restrict__ logits) {
   constexpr int V = 16 / sizeof(T);
   const int lane = threadIdx.x & 63;
@@ -45,7 +48,7 @@ __global__ void __launch_bounds__(256) router_logits_small_kernel(const T* __res
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const float xf = Elem<T>::ld(xv, v);
-        const T* wrow = wr + (size_t)(c * V + v) * E;
+        const T* wrow = wr + (size_t)(c * V + v) * E + e0;
         if constexpr (EXACT) {
           constexpr int NV = EMAX * sizeof(T) / 16;
 #pragma unroll
@@ -58,7 +61,7 @@ __global__ void __launch_bounds__(256) router_logits_small_kernel(const T* __res
         } else {
 #pragma unroll
           for (int e = 0; e < EMAX; ++e)
-            if (e < E) acc[e] += xf * Elem<T>::ld(wrow, e);
+            if (e < Ec) acc[e] += xf * Elem<T>::ld(wrow, e);
         }
       }
     }
@@ -72,7 +75,7 @@ __global__ void __launch_bounds__(256) router_logits_small_kernel(const T* __res
     if (lane == 0) {
 #pragma unroll
       for (int e = 0; e < EMAX; ++e)
-        if (e < E) logits[(size_t)t * E + e] = acc[e];
+        if (e < Ec) logits[(size_t)t * E + e0 + e] = acc[e];
     }
   }
 }
@@ -515,6 +518,7 @@ static size_t route_ws_bytes(int T_, int E) {
   return ((size_t)E * nblk * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
+
 // Router weight-gradient partials: one fp32 row of d per row chunk, then the
 // first-chunk index of every expert.
 static size_t router_wgrad_ws_bytes(int T_, int d, int E, int k) {
@@ -560,12 +564,12 @@ moe_status moe_router_logits(moe_ctx* ctx, const void* x, const void* w_router, 
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, logits, T_ == 0);
   if (T_ == 0) return MOE_OK;
   moe_prof_scope ps(ctx, MOE_K_ROUTER_LOGITS);
-  if (dtype == MOE_BF16 && E > 16 && E % 8 == 0)
+  if (dtype == MOE_BF16 && E > 16 && E % 8 == 0 && d % 64 == 0)
     return moe_internal_router_logits_mfma(ctx, x, w_router, T_, d, E, logits);
   const int blocks = std::min(1024, (T_ + 3) / 4);
 #define RL_LAUNCH(TY, EM, EX)                                                                   \
   router_logits_small_kernel<TY, EM, EX><<<blocks, 256, 0, ctx->stream>>>(                      \
-      (const TY*)x, (const TY*)w_router, T_, d, E, logits)
+      (const TY*)x, (const TY*)w_router, T_, d, E, 0, E, logits)
 #define RL_CASE(EM)                                                                             \
   if (E <= EM) {                                                                                \
     if (dtype == MOE_BF16) {                                                                    \
@@ -584,13 +588,26 @@ moe_status moe_router_logits(moe_ctx* ctx, const void* x, const void* w_router, 
   RL_CASE(64)
 #undef RL_CASE
 #undef RL_LAUNCH
-  return fail(ctx, MOE_ERR_UNSUPPORTED,
-              "moe_router_logits: E=%d needs bf16 with E %% 8 == 0 (MFMA path)", E);
+  // E > 64 without the MFMA path (fp32, or bf16 with E % 8 != 0): 64
+  // experts per launch
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int ec = std::min(64, E - e0);
+    if (dtype == MOE_BF16)
+      router_logits_small_kernel<bf16_t, 64, false><<<blocks, 256, 0, ctx->stream>>>(
+          (const bf16_t*)x, (const bf16_t*)w_router, T_, d, E, e0, ec, logits);
+    else
+      router_logits_small_kernel<float, 64, false><<<blocks, 256, 0, ctx->stream>>>(
+          (const float*)x, (const float*)w_router, T_, d, E, e0, ec, logits);
+  }
+  return check_launch(ctx, "moe_router_logits");
 }
 
-moe_status moe_route(moe_ctx* ctx, const float* logits, int T_, int E, int k, int32_t* topk_idx,
-                     float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
-                     int32_t* src_tk) {
+}  // extern "C"
+
+// Host-side checks of moe_route.
+static moe_status route_validate(moe_ctx* ctx, const float* logits, int T_, int E, int k,
+                                 int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets,
+                                 int32_t* row_of, int32_t* src_tk) {
   MOE_CHECK_CTX(ctx);
   MOE_REQUIRE(ctx, T_ >= 0 && E >= 1 && E <= 1024 && k >= 1 && k <= E && k <= 32,
               "moe_route: bad shape T=%d E=%d k=%d", T_, E, k);
@@ -602,12 +619,21 @@ moe_status moe_route(moe_ctx* ctx, const float* logits, int T_, int E, int k, in
   MOE_REQUIRE_PTR(ctx, offsets);
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, row_of, T_ == 0);
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, src_tk, T_ == 0);
-  const size_t need = route_ws_bytes(T_, E);
-  if (ctx->ws == nullptr || ctx->ws_bytes < need)
-    return fail(ctx, MOE_ERR_WORKSPACE, "moe_route: workspace %zu bytes < %zu needed",
-                ctx->ws_bytes, need);
+  {
+    const size_t tk = (size_t)T_ * k * 4;
+    MOE_REQUIRE_DISJOINT(ctx, "moe_route", {topk_idx, tk, "topk_idx"}, {gates, tk, "gates"},
+                         {counts, (size_t)E * 4, "counts"}, {offsets, (size_t)(E + 1) * 4, "offsets"},
+                         {row_of, tk, "row_of"}, {src_tk, tk, "src_tk"});
+  }
+  return MOE_OK;
+}
+
+// Routing with block_counts in `bc` (E * ceil(T / 64) int32, fully written by
+// the top-k kernel before it is read).
+static moe_status route_launch(moe_ctx* ctx, const float* logits, int T_, int E, int k,
+                               int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets,
+                               int32_t* row_of, int32_t* src_tk, int32_t* bc) {
   const int nblk = (T_ + kTokBlock - 1) / kTokBlock;
-  int32_t* bc = reinterpret_cast<int32_t*>(ctx->ws);
   if (T_ == 0) {
     // no tokens: every count and offset is zero
     fill_i32_kernel<<<(E + 256) / 256, 256, 0, ctx->stream>>>(counts, E, 0);
@@ -628,6 +654,22 @@ moe_status moe_route(moe_ctx* ctx, const float* logits, int T_, int E, int k, in
                      ctx);
   return check_launch(ctx, "moe_route");
 }
+
+extern "C" {
+
+moe_status moe_route(moe_ctx* ctx, const float* logits, int T_, int E, int k, int32_t* topk_idx,
+                     float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
+                     int32_t* src_tk) {
+  moe_status st = route_validate(ctx, logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk);
+  if (st != MOE_OK) return st;
+  const size_t need = route_ws_bytes(T_, E);
+  if (ctx->ws == nullptr || ctx->ws_bytes < need)
+    return fail(ctx, MOE_ERR_WORKSPACE, "moe_route: workspace %zu bytes < %zu needed",
+                ctx->ws_bytes, need);
+  return route_launch(ctx, logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk,
+                      reinterpret_cast<int32_t*>(ctx->ws));
+}
+
 
 moe_status moe_route_bwd(moe_ctx* ctx, const float* gates, const float* dgates, int T_, int k,
                          float* dlogits_sel) {
@@ -653,6 +695,8 @@ moe_status moe_route_bwd_rows(moe_ctx* ctx, const float* gates, const float* dga
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, row_of, T_ == 0);
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, dlogits_sel, T_ == 0);
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, dl_rows, T_ == 0);
+  MOE_REQUIRE_DISJOINT(ctx, "moe_route_bwd_rows", {dlogits_sel, (size_t)T_ * k * 4, "dlogits_sel"},
+                       {dl_rows, (size_t)T_ * k * 4, "dl_rows"});
   if (T_ == 0) return MOE_OK;
   moe_prof_scope ps(ctx, MOE_K_ROUTE_BWD);
   route_bwd_kernel<<<(T_ + 255) / 256, 256, 0, ctx->stream>>>(gates, dgates, T_, k, dlogits_sel,

@@ -436,6 +436,8 @@ moe_status moe_combine_bwd(moe_ctx* ctx, const void* dy, const void* yp, const f
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, row_of, T_ == 0);
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, dyp, T_ == 0);
   MOE_REQUIRE_PTR_OR_EMPTY(ctx, dgates, T_ == 0);
+  MOE_REQUIRE_DISJOINT(ctx, "moe_combine_bwd", {dyp, (size_t)T_ * k * d * esize(dtype), "dyp"},
+                       {dgates, (size_t)T_ * k * 4, "dgates"});
   if (T_ == 0) return MOE_OK;
   const int nchunk = (int)(d * esize(dtype) / 16);
   moe_prof_scope ps(ctx, MOE_K_COMBINE_BWD);

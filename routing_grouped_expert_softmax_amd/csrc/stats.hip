@@ -325,6 +325,9 @@ moe_status moe_route_stats(moe_ctx* ctx, const float* logits, const int32_t* cou
   MOE_REQUIRE(ctx, counts && prob_mean && top1_count && top1_prob_mean && aux_loss,
               "moe_route_stats: null output or counts");
   MOE_REQUIRE(ctx, T_ == 0 || logits, "moe_route_stats: logits is null");
+  MOE_REQUIRE_DISJOINT(ctx, "moe_route_stats", {prob_mean, (size_t)E * 4, "prob_mean"},
+                       {top1_count, (size_t)E * 4, "top1_count"},
+                       {top1_prob_mean, (size_t)E * 4, "top1_prob_mean"}, {aux_loss, 4, "aux_loss"});
   const size_t need = moe_internal_stats_ws_bytes(E);
   if (ctx->ws == nullptr || ctx->ws_bytes < need)
     return fail(ctx, MOE_ERR_WORKSPACE, "moe_route_stats: workspace %zu bytes < %zu needed",

@@ -65,7 +65,12 @@ def test_route_adversarial(moe):
 
 
 @pytest.mark.parametrize("dtype,T,d,E", [("fp32", 256, 128, 8), ("bf16", 300, 256, 8),
-                                         ("bf16", 520, 512, 128), ("bf16", 64, 2048, 16)])
+                                         ("bf16", 520, 512, 128), ("bf16", 64, 2048, 16),
+                                         # E > 64 on the VALU kernel in 64-expert passes:
+                                         # fp32, bf16 with E % 8 != 0 or d % 64 != 0
+                                         ("fp32", 300, 128, 128), ("fp32", 70, 64, 1000),
+                                         ("fp32", 33, 2048, 77), ("bf16", 130, 128, 100),
+                                         ("bf16", 200, 96, 128)])
 def test_router_logits(moe, dtype, T, d, E):
     c = mi.layer_inputs(mi.config("tiny", T=T, d=d, E=E, dtype=dtype, x_std=1.0), with_weights=False)
     got = moe.moe_router_logits(c["x"].to(DEV), c["wr"].to(DEV)).cpu().numpy()
