@@ -141,6 +141,21 @@ moe_status moe_route(moe_ctx* ctx, const float* logits, int T, int E, int k, int
                      float* gates, int32_t* counts, int32_t* offsets, int32_t* row_of,
                      int32_t* src_tk);
 
+/* moe_route for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, results (bit for bit) and errors, but no registered
+ * workspace is used and nothing is allocated.  Its per-block expert counts
+ * live in one static device array of 2^20 int32 (4 MiB), which every GPU the
+ * library runs on holds until the process ends; shapes with
+ * E * ceil(T / 64) > 2^20 (e.g. T > 524288 at E = 128, T > 65536 at
+ * E = 1024) return MOE_ERR_UNSUPPORTED.  All calls on one GPU share that
+ * array: calls in one stream are ordered, but calls that overlap in time on
+ * one GPU (other streams, other threads) race.  The first call on a device
+ * looks up the array's device address (hipGetSymbolAddress). */
+moe_status moe_route_noalloc(moe_ctx* ctx, const float* logits, int T, int E, int k,
+                             int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets,
+                             int32_t* row_of, int32_t* src_tk);
+
 /* Rowwise permute: xp[row_of[t,j]] = x[t] for every (t,j); xp is [T*k, d].
  * [P1] 二 (rows written straight into the experts' input buffers). */
 moe_status moe_permute(moe_ctx* ctx, const void* x, const int32_t* row_of, int T, int d, int k,

@@ -35,6 +35,7 @@ _flt = ctypes.c_float
 _SIGS = {
     "moe_router_logits": [_vp, _vp, _int, _int, _int, _int, _vp],
     "moe_route": [_vp, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_route_noalloc": [_vp, _int, _int, _int, _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_permute": [_vp, _vp, _int, _int, _int, _int, _vp],
     "moe_grouped_ffn_fwd": [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _vp, _vp, _vp, _vp],
     "moe_combine": [_vp, _vp, _vp, _int, _int, _int, _int, _vp],
@@ -223,6 +224,17 @@ def moe_route(logits, k, out=None):
     ctx.ensure_workspace(T, 8, E, k, MOE_F32)
     ctx.call("moe_route", _p(logits), T, E, k, _p(out["topk_idx"]), _p(out["gates"]), _p(out["counts"]),
              _p(out["offsets"]), _p(out["row_of"]), _p(out["src_tk"]))
+    return out
+
+
+def moe_route_noalloc(out, logits, k):
+    """moe_route into caller-provided outputs (the dict moe_route returns),
+    without the library workspace: the call allocates nothing."""
+    _need_cuda(logits)
+    T, E = logits.shape
+    context(logits.device.index).call(
+        "moe_route_noalloc", _p(logits), T, E, k, _p(out["topk_idx"]), _p(out["gates"]),
+        _p(out["counts"]), _p(out["offsets"]), _p(out["row_of"]), _p(out["src_tk"]))
     return out
 
 

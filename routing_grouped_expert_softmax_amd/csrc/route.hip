@@ -10,6 +10,8 @@
 // per-block counts contiguously.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "common.h"
 
 using namespace moe;
@@ -518,6 +520,36 @@ static size_t route_ws_bytes(int T_, int E) {
   return ((size_t)E * nblk * sizeof(int32_t) + 255) & ~(size_t)255;
 }
 
+// Routing scratch of moe_route_noalloc: block_counts of up to kScratchInts
+// entries (E * ceil(T / 64) <= 2^20, 4 MiB), one copy per GPU for the life of
+// the process.  Host code never uses this name as an address: it is resolved
+// per device with hipGetSymbolAddress and kept in scratch_ptr.
+constexpr size_t kScratchInts = (size_t)1 << 20;
+static __device__ __align__(256) int32_t scratch[kScratchInts];
+
+// Device address of `scratch` on `device`, looked up once per device with that
+// device current (each GPU holds its own copy at its own address).
+static moe_status scratch_address(moe_ctx* ctx, int32_t** out) {
+  static std::mutex mu;
+  static int32_t* scratch_ptr[64] = {nullptr};
+  const int dev = ctx->device;
+  if (dev < 0 || dev >= 64) return fail(ctx, MOE_ERR_UNSUPPORTED, "moe_route_noalloc: device %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(ctx, MOE_ERR_HIP, "moe_route_noalloc: scratch address on device %d: %s", dev,
+                  hipGetErrorString(e));
+    scratch_ptr[dev] = static_cast<int32_t*>(ptr);
+  }
+  *out = scratch_ptr[dev];
+  return MOE_OK;
+}
 
 // Router weight-gradient partials: one fp32 row of d per row chunk, then the
 // first-chunk index of every expert.
@@ -604,7 +636,7 @@ moe_status moe_router_logits(moe_ctx* ctx, const void* x, const void* w_router, 
 
 }  // extern "C"
 
-// Host-side checks of moe_route.
+// Checks shared by moe_route and moe_route_noalloc.
 static moe_status route_validate(moe_ctx* ctx, const float* logits, int T_, int E, int k,
                                  int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets,
                                  int32_t* row_of, int32_t* src_tk) {
@@ -670,6 +702,21 @@ moe_status moe_route(moe_ctx* ctx, const float* logits, int T_, int E, int k, in
                       reinterpret_cast<int32_t*>(ctx->ws));
 }
 
+moe_status moe_route_noalloc(moe_ctx* ctx, const float* logits, int T_, int E, int k,
+                             int32_t* topk_idx, float* gates, int32_t* counts, int32_t* offsets,
+                             int32_t* row_of, int32_t* src_tk) {
+  moe_status st = route_validate(ctx, logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk);
+  if (st != MOE_OK) return st;
+  const size_t nblk = (size_t)(T_ + kTokBlock - 1) / kTokBlock;
+  if ((size_t)E * nblk > kScratchInts)
+    return fail(ctx, MOE_ERR_UNSUPPORTED,
+                "moe_route_noalloc: E * ceil(T/64) = %zu exceeds the %zu-entry scratch (T=%d E=%d)",
+                (size_t)E * nblk, kScratchInts, T_, E);
+  int32_t* bc = nullptr;
+  st = scratch_address(ctx, &bc);
+  if (st != MOE_OK) return st;
+  return route_launch(ctx, logits, T_, E, k, topk_idx, gates, counts, offsets, row_of, src_tk, bc);
+}
 
 moe_status moe_route_bwd(moe_ctx* ctx, const float* gates, const float* dgates, int T_, int k,
                          float* dlogits_sel) {
