@@ -396,6 +396,17 @@ def aux_loss_bwd(logits, counts, k, alpha, dloss=1.0):
     return dloss * p * (a[None, :] - (p * a[None, :]).sum(axis=1, keepdims=True))
 
 
+def router_dense_bwd(x, wr, dlogits):
+    """The router's share of a gradient that reaches every logit (the balance
+    loss's dense dl from aux_loss_bwd; [P1] 四: the router balances load, so
+    that loss trains the router): with logits = x W_r,
+    dx[t, i] = sum_e dl[t, e] * W_r[i, e] and dW_r[i, e] = sum_t x[t, i] * dl[t, e],
+    both as fp64 products.  The result adds to the layer's own dx and dW_r."""
+    dl = np.asarray(dlogits, dtype=np.float64)
+    return dict(dx=dl @ np.asarray(wr, dtype=np.float64).T,
+                dwr=np.asarray(x, dtype=np.float64).T @ dl)
+
+
 def expert_grad_norms(dw):
     """L2 (Frobenius) norm of each expert's weight-gradient matrix dw[e],
     from the stored values, accumulated in fp64."""

@@ -598,19 +598,10 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
 #endif
 }
 
-// GEMM_PERSIST=1 caps the grid at one resident set of blocks so each block
-// walks several tiles.  Measured neutral: the first K step of a block's next
-// tile waits on the vector-memory counter, which also counts the previous
-// tile's output stores, so they are not hidden.  Off by default.
-#ifndef GEMM_PERSIST
-#define GEMM_PERSIST 0
-#endif
-
-// Launch with at most one resident set of blocks (OCC per CU): each block
-// then walks several tiles.  `blocks` is the tile bound of the launch.
+// Launch over `blocks` (the tile bound of the launch, rounded up to whole
+// XCD rounds); blocks past the real tile count exit.
 template <int MODE, int BM, int S, int BK, int OCC = 1, int NW = 4>
 hipError_t launch(const Params& p, int blocks, hipStream_t s) {
-  if (GEMM_PERSIST) blocks = std::min(blocks, moe_host::device_cus() / 8 * 8 * OCC);
   blocks = (blocks + 7) / 8 * 8;
   grouped_gemm_kernel<MODE, BM, S, BK, OCC, NW><<<blocks, 64 * NW, 0, s>>>(p);
   return hipGetLastError();

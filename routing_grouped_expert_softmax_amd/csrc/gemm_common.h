@@ -308,14 +308,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, unsigned long long
 // it as an LDS write that every later LDS read must wait for: the kernel
 // waits for these loads itself (s_waitcnt vmcnt) before the barrier that
 // publishes a stage.  The instruction has no register outputs.  M0 carries
-// the LDS address (one wait state between writing M0 and the load).
+// the LDS address (one wait state between writing M0 and the load) and is
+// declared clobbered, so the compiler keeps nothing of its own in M0 across
+// the statement.
 __device__ __forceinline__ void dma16(rsrc_t r, LDS_AS void* lds, int voff,
                                       int soff) {
   const unsigned lds_addr = (unsigned)(uintptr_t)lds;
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
                : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
+               : "memory", "m0");
 }
 
 // 4-byte-per-lane variant (lane l writes lds + 4*l), for block-scale rows.
@@ -324,7 +326,7 @@ __device__ __forceinline__ void dma4(rsrc_t r, LDS_AS void* lds, int voff, int s
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
                : "s"(lds_addr), "v"(voff), "s"(r), "s"(soff)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Output description for the epilogue.

@@ -91,3 +91,58 @@ def test_expert_grad_norms():
     assert n[3] == 0.0
     for e in range(4):
         assert n[e] == pytest.approx(np.linalg.norm(dw[e].astype(np.float64)), rel=1e-13)
+
+
+# ---------------------------------------------------------------- balance loss -> router
+def _aux_of(x, wr, counts, k, alpha):
+    return oracle.route_stats(x @ wr, counts, k, alpha)["aux_loss"]
+
+
+def test_router_dense_bwd_matches_finite_differences():
+    # The balance loss as a function of the router's inputs, loss(x W_r) with
+    # the counts held at their routed values (piecewise constant): central
+    # differences in x and in W_r against router_dense_bwd of the loss's
+    # dense logit gradient.
+    rng = np.random.default_rng(11)
+    T, d, E, k, alpha, dloss = 9, 5, 6, 2, 0.07, 1.3
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((d, E)) * 0.5
+    counts = oracle.route((x @ wr).astype(np.float32), k)["counts"]
+    g = oracle.router_dense_bwd(x, wr, oracle.aux_loss_bwd(x @ wr, counts, k, alpha, dloss))
+    assert g["dx"].shape == (T, d) and g["dwr"].shape == (d, E)
+    h = 1e-6
+    for (t, i) in [(0, 0), (3, 4), (8, 2), (5, 1)]:
+        up, dn = x.copy(), x.copy()
+        up[t, i] += h
+        dn[t, i] -= h
+        fd = (_aux_of(up, wr, counts, k, alpha) - _aux_of(dn, wr, counts, k, alpha)) / (2 * h)
+        assert dloss * fd == pytest.approx(g["dx"][t, i], rel=1e-6, abs=1e-12), (t, i)
+    for i in range(d):
+        for e in range(E):
+            up, dn = wr.copy(), wr.copy()
+            up[i, e] += h
+            dn[i, e] -= h
+            fd = (_aux_of(x, up, counts, k, alpha) - _aux_of(x, dn, counts, k, alpha)) / (2 * h)
+            assert dloss * fd == pytest.approx(g["dwr"][i, e], rel=1e-6, abs=1e-12), (i, e)
+
+
+def test_router_dense_bwd_pin_sees_planted_mistakes():
+    # the finite-difference reference differs clearly from plausible slips:
+    # a dropped transpose in dx (square case) or dl summed without x
+    rng = np.random.default_rng(12)
+    T, d, E, k, alpha = 7, 6, 6, 2, 0.05
+    x = rng.standard_normal((T, d))
+    wr = rng.standard_normal((d, E))
+    counts = oracle.route((x @ wr).astype(np.float32), k)["counts"]
+    dl = oracle.aux_loss_bwd(x @ wr, counts, k, alpha)
+    h = 1e-6
+    fd_dx = np.zeros((T, d))
+    for t in range(T):
+        for i in range(d):
+            up, dn = x.copy(), x.copy()
+            up[t, i] += h
+            dn[t, i] -= h
+            fd_dx[t, i] = (_aux_of(up, wr, counts, k, alpha) - _aux_of(dn, wr, counts, k, alpha)) / (2 * h)
+    good = oracle.router_dense_bwd(x, wr, dl)["dx"]
+    assert np.abs(good - fd_dx).max() < 1e-8 * np.abs(fd_dx).max() + 1e-14
+    assert np.abs(dl @ wr - fd_dx).max() > 0.1 * np.abs(fd_dx).max()   # W_r not transposed
