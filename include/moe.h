@@ -322,6 +322,22 @@ moe_status moe_route_stats(moe_ctx* ctx, const float* logits, const int32_t* cou
 moe_status moe_aux_loss_bwd(moe_ctx* ctx, const float* logits, const int32_t* counts, int T, int E,
                             int k, float alpha, float dloss, float* dlogits);
 
+/* The balance loss trains the router ([P1] 四: the router balances load;
+ * [P2] 2.2, 4.3): its logit gradient (moe_aux_loss_bwd, dense [T,E]) flows
+ * through logits = x W_r into the layer's input and router gradients.  This
+ * call ADDS that share in place:
+ *   dx[t,i]        += sum_e dlogits[t,e] * w_router[i,e]    (e ascending)
+ *   dw_router[i,e] += sum_t x[t,i] * dlogits[t,e]           (t ascending in
+ *                     512-token chunks, the chunk sums added in order)
+ * fp32 sums, each element rounded once to dtype (MOE_F32 or MOE_BF16; x, dx
+ * [T,d], w_router, dw_router [d,E] in dtype).  Deterministic.  Call it after
+ * moe_permute_bwd and moe_router_wgrad have written dx and dw_router.  Needs
+ * the registered workspace (moe_workspace_size with this T, d, E) when
+ * T > 0; T <= 2097120. */
+moe_status moe_router_dense_bwd(moe_ctx* ctx, const void* x, const void* w_router,
+                                const float* dlogits, int T, int d, int E, moe_dtype dtype,
+                                void* dx, void* dw_router);
+
 /* L2 (Frobenius) norm of each expert's weight-gradient matrix: dw is
  * [E, rows, cols] in dtype (MOE_BF16 or MOE_F32; cols % 8 == 0 for bf16,
  * % 4 for fp32), norms[e] = sqrt(sum of squares) with fp32 accumulation in
@@ -376,6 +392,7 @@ typedef enum {
   MOE_K_ROUTE_STATS,       /* routing statistics + balance loss */
   MOE_K_AUX_BWD,           /* balance-loss logit gradient */
   MOE_K_GRAD_NORMS,        /* per-expert weight-gradient norms */
+  MOE_K_ROUTER_DENSE_BWD,  /* balance-loss gradient through the router */
   MOE_K_COUNT
 } moe_kernel_id;
 

@@ -56,6 +56,7 @@ _SIGS = {
     "moe_route_stats": [_vp, _vp, _int, _int, _int, _flt, _vp, _vp, _vp, _vp],
     "moe_aux_loss_bwd": [_vp, _vp, _int, _int, _int, _flt, _flt, _vp],
     "moe_expert_grad_norms": [_vp, _int, _int, _int, _int, _vp],
+    "moe_router_dense_bwd": [_vp, _vp, _vp, _int, _int, _int, _int, _vp, _vp],
     "moe_mfma_peak_probe": [_int, _int, _flt, _flt, _vp],
 }
 EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "moe_last_error",
@@ -66,7 +67,7 @@ EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "
 KERNELS = ["router_logits", "topk_hist", "expert_scan", "rank", "permute", "gemm_up_swiglu",
            "gemm_down", "combine", "combine_bwd", "route_bwd", "gemm_dgrad_down_swiglu",
            "gemm_wgrad_down", "gemm_dgrad_up", "gemm_wgrad_up", "permute_bwd", "router_wgrad",
-           "mx_quantize", "route_stats", "aux_loss_bwd", "grad_norms"]
+           "mx_quantize", "route_stats", "aux_loss_bwd", "grad_norms", "router_dense_bwd"]
 
 
 def lib():
@@ -487,6 +488,19 @@ def moe_aux_loss_bwd(logits, counts, k, alpha, dloss=1.0, dlogits=None):
     return dlogits
 
 
+def moe_router_dense_bwd(x, w_router, dlogits, dx, dw_router):
+    """Add the router's share of a dense [T,E] logit gradient in place:
+    dx += dlogits @ w_router^T, dw_router += x^T @ dlogits."""
+    _need_cuda(x, w_router, dlogits, dx, dw_router)
+    T, d = x.shape
+    E = w_router.shape[1]
+    ctx = context(x.device.index)
+    ctx.ensure_workspace(T, d, E, 1, _dt(x))
+    ctx.call("moe_router_dense_bwd", _p(x), _p(w_router), _p(dlogits), T, d, E, _dt(x), _p(dx),
+             _p(dw_router))
+    return dx, dw_router
+
+
 def moe_expert_grad_norms(dw, norms=None):
     """Per-expert L2 norms [E] fp32 of a [E, rows, cols] weight gradient."""
     _need_cuda(dw)
@@ -518,6 +532,7 @@ class LayerBuffers:
     xs: torch.Tensor | None = None  # their scale bytes
     shared: dict | None = None      # shared expert: offsets {0,T}, its forward and backward buffers
     dl_rows: torch.Tensor | None = None  # logit gradients in expert-row order (bf16 router fold)
+    aux_dl: torch.Tensor | None = None   # dense [T,E] balance-loss logit gradient (aux_alpha)
 
 
 def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False, shared_F=0):
@@ -588,7 +603,7 @@ def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logit
 
 
 def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxfp8=False, shared=None,
-                   recompute=False):
+                   recompute=False, aux_alpha=None):
     """combine_bwd -> route_bwd -> grouped FFN bwd -> permute_bwd (+router
     dgrad) -> router wgrad.  In bf16 the router's input-gradient term is
     folded into the gate/up dgrad (moe_grouped_ffn_bwd_router) and the
@@ -597,7 +612,9 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxf
     buf.dw_router.  recompute=True reads from the forward only yp, the gates
     and the routing: xp is permuted again from x and g, u, h (the shared
     expert's too) are recomputed by the gate/up GEMM before they are used,
-    so the forward need not keep them."""
+    so the forward need not keep them.  aux_alpha (the balance-loss weight)
+    adds the gradient of that loss, taken at the router's scores with this
+    step's counts, to dx and dW_r (moe_aux_loss_bwd, moe_router_dense_bwd)."""
     r = buf.route
     if recompute:
         moe_permute(x, r["row_of"], buf.xp)
@@ -625,6 +642,12 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxf
         moe_permute_bwd(buf.bwd["dxp"], r["row_of"], r["topk_idx"], buf.dlogits_sel, w_router, buf.dx,
                         dx_shared=dxs)
     moe_router_wgrad(x, buf.dlogits_sel, r["src_tk"], r["offsets"], w_router.shape[1], buf.dw_router)
+    if aux_alpha is not None:
+        T, E = buf.logits.shape
+        if buf.aux_dl is None:
+            buf.aux_dl = torch.empty(T, E, dtype=torch.float32, device=buf.logits.device)
+        moe_aux_loss_bwd(buf.logits, r["counts"], r["topk_idx"].shape[1], aux_alpha, 1.0, buf.aux_dl)
+        moe_router_dense_bwd(x, w_router, buf.aux_dl, buf.dx, buf.dw_router)
     return buf.dx
 
 

@@ -515,6 +515,7 @@ __global__ void router_wgrad_sum_kernel(const float* __restrict__ part,
 // ---------------------------------------------------------------- C ABI
 using namespace moe_host;
 
+size_t moe_internal_router_dense_ws_bytes(int T_, int d, int E);  // stats.hip
 static size_t route_ws_bytes(int T_, int E) {
   const size_t nblk = (size_t)(T_ + kTokBlock - 1) / kTokBlock;
   return ((size_t)E * nblk * sizeof(int32_t) + 255) & ~(size_t)255;
@@ -580,8 +581,9 @@ moe_status moe_workspace_size(moe_ctx* ctx, int T_, int d, int E, int k, moe_dty
   MOE_REQUIRE(ctx, T_ >= 0 && d >= 8 && E >= 1 && E <= 1024 && k >= 1 && k <= E && k <= 32,
               "bad shape T=%d d=%d E=%d k=%d", T_, d, E, k);
   const size_t a = route_ws_bytes(T_, E), b = moe_internal_wrt_bytes(d, E, dtype),
-               c = moe_internal_stats_ws_bytes(E), r = router_wgrad_ws_bytes(T_, d, E, k);
-  *bytes = std::max(std::max(a, r), std::max(b, c));
+               c = moe_internal_stats_ws_bytes(E), r = router_wgrad_ws_bytes(T_, d, E, k),
+               dn = moe_internal_router_dense_ws_bytes(T_, d, E);
+  *bytes = std::max(std::max(std::max(a, r), std::max(b, c)), dn);
   return MOE_OK;
 }
 

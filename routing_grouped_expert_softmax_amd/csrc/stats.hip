@@ -280,6 +280,153 @@ int stat_tpb(int T_) {
   return std::max(4, (tpb + 3) / 4 * 4);
 }
 
+// ------------------------------------------------- balance loss -> router
+// C[M, N] += A[M, K] B[K, N] with fp32 products summed in ascending k, for the
+// router's share of a dense logit gradient dl [T, E] (logits = x W_r):
+//   dx      = dl W_r^T : M = T, N = d, K = E; A = dl rows, B[k][n] = W_r[n][k];
+//   dW_r^T  = dl^T x   : M = E, N = d, K = T; A[m][k] = dl[k][m], B = x rows.
+// A block owns a 32 x 256 tile of C and walks K in 32-deep chunks staged in
+// LDS as fp32 (the next chunk's global loads are in flight while the current
+// one is summed); each thread keeps a 4 x 8 register tile.  DX: add the tile
+// to dx in place (one rounding).  Otherwise (dW_r^T): the K range is split in
+// blocks of kDenseChunk tokens (grid.z) whose fp32 partials go to part[z] and
+// are summed in order by router_dense_wsum_kernel.
+constexpr int kDenseChunk = 512;  // tokens per dW_r partial
+template <typename T, bool DX>
+__global__ void __launch_bounds__(256) router_dense_kernel(const float* __restrict__ dl,
+                                                           const T* __restrict__ b, int T_, int d,
+                                                           int E, T* __restrict__ dx,
+                                                           float* __restrict__ part) {
+  __shared__ float As[32][36];   // [k][m] (16-byte aligned rows)
+  __shared__ float Bs[32][260];  // [k][n]
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte vector
+  constexpr int NQ = 32 / V;         // B vectors per thread per chunk
+  const int tid = threadIdx.x;
+  const int M = DX ? T_ : E;
+  const int K = DX ? E : T_;
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 256;
+  const int kbeg = DX ? 0 : blockIdx.z * kDenseChunk;
+  const int kend = DX ? K : min(K, kbeg + kDenseChunk);
+  const int mg = tid >> 5, ng = tid & 31;  // 8 x 32 threads: C rows 4 mg.., columns 8 ng..
+  const int ar = tid >> 3, ac = (tid & 7) * 4;  // A staging: row, first of 4 columns
+  float acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+  float areg[4], breg[NQ][V];
+  // global -> registers of the K chunk at k0 (zeros past the edges)
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      // DX: A row m = ar, k = ac + q (dl rows); else A[m][k] = dl[k][m]: row k = ar
+      const int m = DX ? m0 + ar : m0 + ac + q, k = DX ? k0 + ac + q : k0 + ar;
+      areg[q] = (m < M && k < kend) ? dl[DX ? (size_t)m * E + k : (size_t)k * E + m] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) breg[q][v] = 0.f;
+      if (DX) {
+        // B[k][n] = W_r[n][k]: V consecutive k of W_r row n = n0 + tid
+        const int n = n0 + tid, kk = k0 + q * V;
+        if (n < d) {
+          const T* src = b + (size_t)n * E + kk;
+          if (E % V == 0 && kk + V <= kend) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(src);
+            const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+            for (int v = 0; v < V; ++v) breg[q][v] = Elem<T>::ld(e, v);
+          } else {
+#pragma unroll
+            for (int v = 0; v < V; ++v)
+              if (kk + v < kend) breg[q][v] = Elem<T>::ld(src, v);
+          }
+        }
+      } else {
+        // B = x rows: V consecutive n of row k
+        const int idx = q * 256 + tid;
+        const int r = idx / (256 / V), c = (idx % (256 / V)) * V;
+        const int k = k0 + r, n = n0 + c;
+        if (k < kend && n < d) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(b + (size_t)k * d + n);
+          const T* e = reinterpret_cast<const T*>(&raw);
+#pragma unroll
+          for (int v = 0; v < V; ++v) breg[q][v] = Elem<T>::ld(e, v);
+        }
+      }
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (DX) As[ac + q][ar] = areg[q];
+      else As[ar][ac + q] = areg[q];
+    }
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      if (DX) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) Bs[q * V + v][tid] = breg[q][v];
+      } else {
+        const int idx = q * 256 + tid;
+        const int r = idx / (256 / V), c = (idx % (256 / V)) * V;
+#pragma unroll
+        for (int v = 0; v < V; ++v) Bs[r][c + v] = breg[q][v];
+      }
+    }
+  };
+  if (kbeg < kend) load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += 32) {
+    __syncthreads();  // the previous chunk's sums are done with the tiles
+    stash();
+    __syncthreads();
+    if (k0 + 32 < kend) load(k0 + 32);  // in flight while this chunk is summed
+#pragma unroll 4
+    for (int kk = 0; kk < 32; ++kk) {
+      float a[4], bv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][mg * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bv[j] = Bs[kk][ng * 8 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], bv[j], acc[i][j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + mg * 4 + i;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int n = n0 + ng * 8 + j;
+      if (n >= d) continue;
+      if (DX) {
+        const size_t o = (size_t)m * d + n;
+        Elem<T>::st(dx, o, Elem<T>::ld(dx, o) + acc[i][j]);
+      } else {
+        part[((size_t)blockIdx.z * E + m) * d + n] = acc[i][j];
+      }
+    }
+  }
+}
+
+// dW_r[n][e] += sum over chunks z (in order) of part[z][e][n], one rounding.
+template <typename T>
+__global__ void __launch_bounds__(256) router_dense_wsum_kernel(const float* __restrict__ part,
+                                                                int nz, int d, int E,
+                                                                T* __restrict__ dwr) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // e * d + n
+  if (i >= (long long)E * d) return;
+  const int e = (int)(i / d), n = (int)(i % d);
+  float s = 0.f;
+  for (int z = 0; z < nz; ++z) s += part[(size_t)z * E * d + i];
+  const size_t o = (size_t)n * E + e;
+  Elem<T>::st(dwr, o, Elem<T>::ld(dwr, o) + s);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI
@@ -288,6 +435,13 @@ using namespace moe_host;
 // Workspace of moe_route_stats (three [E][256] partial arrays and the [E]
 // loss terms) and of moe_expert_grad_norms ([E][256] partial sums); both fit
 // in the larger.
+// Workspace of moe_router_dense_bwd: fp32 dW_r^T partials, one [E, d] block
+// per kDenseChunk tokens.
+size_t moe_internal_router_dense_ws_bytes(int T_, int d, int E) {
+  const size_t nz = (size_t)(T_ + kDenseChunk - 1) / kDenseChunk;
+  return (nz * E * d * sizeof(float) + 255) & ~(size_t)255;
+}
+
 size_t moe_internal_stats_ws_bytes(int E) {
   const size_t a = (size_t)kStatBlocks * E * 12 + (size_t)E * 4, b = (size_t)E * kNormChunks * 4;
   return ((a > b ? a : b) + 255) & ~(size_t)255;
@@ -363,6 +517,46 @@ moe_status moe_aux_loss_bwd(moe_ctx* ctx, const float* logits, const int32_t* co
   STATS_EPL_DISPATCH(E, (aux_bwd_kernel<EPL><<<blocks, 256, 0, ctx->stream>>>(logits, counts, T_, E,
                                                                                (float)coef, dlogits)));
   return check_launch(ctx, "moe_aux_loss_bwd");
+}
+
+moe_status moe_router_dense_bwd(moe_ctx* ctx, const void* x, const void* w_router,
+                                const float* dlogits, int T_, int d, int E, moe_dtype dtype,
+                                void* dx, void* dw_router) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE_DTYPE(ctx, dtype);
+  MOE_REQUIRE(ctx, T_ >= 0 && T_ <= 65535 * 32 && d >= 8 && d % 8 == 0 && E >= 1 && E <= 1024,
+              "moe_router_dense_bwd: bad shape T=%d d=%d E=%d", T_, d, E);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, x, T_ == 0);
+  MOE_REQUIRE_PTR(ctx, w_router);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dlogits, T_ == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dx, T_ == 0);
+  MOE_REQUIRE_PTR(ctx, dw_router);
+  MOE_REQUIRE_DISJOINT(ctx, "moe_router_dense_bwd", {dx, (size_t)T_ * d * esize(dtype), "dx"},
+                       {dw_router, (size_t)d * E * esize(dtype), "dw_router"});
+  if (T_ == 0) return MOE_OK;  // nothing to add
+  const size_t need = moe_internal_router_dense_ws_bytes(T_, d, E);
+  if (ctx->ws == nullptr || ctx->ws_bytes < need)
+    return fail(ctx, MOE_ERR_WORKSPACE, "moe_router_dense_bwd: workspace %zu bytes < %zu needed",
+                ctx->ws_bytes, need);
+  float* part = (float*)ctx->ws;
+  const int nz = (T_ + kDenseChunk - 1) / kDenseChunk;
+  const dim3 gdx((d + 255) / 256, (T_ + 31) / 32), gdw((d + 255) / 256, (E + 31) / 32, nz);
+  const unsigned gsum = (unsigned)(((long long)E * d + 255) / 256);
+  moe_prof_scope ps(ctx, MOE_K_ROUTER_DENSE_BWD);
+  if (dtype == MOE_BF16) {
+    router_dense_kernel<bf16_t, true><<<gdx, 256, 0, ctx->stream>>>(
+        dlogits, (const bf16_t*)w_router, T_, d, E, (bf16_t*)dx, nullptr);
+    router_dense_kernel<bf16_t, false><<<gdw, 256, 0, ctx->stream>>>(
+        dlogits, (const bf16_t*)x, T_, d, E, nullptr, part);
+    router_dense_wsum_kernel<bf16_t><<<gsum, 256, 0, ctx->stream>>>(part, nz, d, E, (bf16_t*)dw_router);
+  } else {
+    router_dense_kernel<float, true><<<gdx, 256, 0, ctx->stream>>>(
+        dlogits, (const float*)w_router, T_, d, E, (float*)dx, nullptr);
+    router_dense_kernel<float, false><<<gdw, 256, 0, ctx->stream>>>(
+        dlogits, (const float*)x, T_, d, E, nullptr, part);
+    router_dense_wsum_kernel<float><<<gsum, 256, 0, ctx->stream>>>(part, nz, d, E, (float*)dw_router);
+  }
+  return check_launch(ctx, "moe_router_dense_bwd");
 }
 
 moe_status moe_expert_grad_norms(moe_ctx* ctx, const void* dw, int E, int rows, int cols,
