@@ -59,6 +59,8 @@ GEMM_KERNELS = {  # algorithmic FLOPs per launch in units of R*d*F
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 GEMM_SOURCES = [os.path.join(ROOT, "routing_grouped_expert_softmax_amd", "csrc", f)
                 for f in ("gemm_bf16.hip", "gemm_common.h")]
+MX_GEMM_SOURCES = [os.path.join(ROOT, "routing_grouped_expert_softmax_amd", "csrc", f)
+                   for f in ("gemm_mx.hip", "gemm_common.h")]
 
 
 def row_bytes(name, T, d, k, F, E, esz=2):
@@ -123,6 +125,29 @@ def read_traffic(kernel, workload):
         return None
 
 
+def read_mfma_busy(workload, paths=None):
+    """Per-GEMM matrix-core utilisation from the committed rocprofv3 counter
+    summary profiles/mfma_gemm_<workload>.txt: {kernel: {"mfma_busy": ...,
+    "clock_ghz": ..., "executed_over_algorithmic": ...}}, or None when it is
+    absent or was taken on a different version of the kernel source."""
+    path = os.path.join(PROFILE_DIR, f"mfma_gemm_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    out, src = {}, None
+    for line in open(path):
+        if line.startswith("#") or ":" not in line:
+            continue
+        key, val = (s.strip() for s in line.split(":", 1))
+        if key == "source_sha256_16":
+            src = val
+        elif key.startswith("kernel "):
+            name = key.split(" ", 1)[1]
+            out[name] = {k: float(v) for k, v in (kv.split("=") for kv in val.split())}
+    if src != source_hash(paths) or not out:
+        return None
+    return out
+
+
 def cpu_baseline(cfg, inp, sample_tokens):
     """Time the CPU oracle (fp32 accumulation, all host cores) on the first
     `sample_tokens` tokens of the same workload: routing, token-by-token
@@ -151,9 +176,21 @@ def cpu_baseline(cfg, inp, sample_tokens):
     oracle.expert_wgrad(xp, dyp, r["offsets"], wg, wu, wd, acc="f32")
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
-    return {"value": S / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": S / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {S} of {cfg.T} tokens of {cfg.name}, all {cfg.E} experts, full "
                       f"weights; fp32-accumulating oracle, fwd+bwd, {dt:.1f} s"}
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def time_steps(ctx, step, steps, warmup):
@@ -324,8 +361,40 @@ def gemm_summary(prof, unit, peak):
     return roof, agg
 
 
+def cold_row_movers(ctx, g, buf, reps=10):
+    """Each row mover of the layer launched alone on the layer's own buffers,
+    with a 1 GiB buffer read before every launch, so its rows come from HBM:
+    the read replaces every line of the 256 MB Infinity Cache and the L2s with
+    clean ones (a write would leave dirty lines whose write-back the measured
+    kernel would pay for).  Mean launch time per kernel from the library's
+    HIP events."""
+    import torch
+
+    import routing_grouped_expert_softmax_amd as moe
+
+    r = buf.route
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
+    calls = {"permute": lambda: moe.moe_permute(g["x"], r["row_of"], buf.xp),
+             "combine": lambda: moe.moe_combine(buf.ffn["yp"], r["gates"], r["row_of"], buf.y),
+             "combine_bwd": lambda: moe.moe_combine_bwd(g["dy"], buf.ffn["yp"], r["gates"], r["row_of"],
+                                                        buf.dyp, buf.dgates),
+             "permute_bwd": lambda: moe.moe_permute_bwd(buf.bwd["dxp"], r["row_of"], dx=buf.dx)}
+    torch.cuda.synchronize()
+    ctx.profile(True)
+    for i in range(reps):
+        for f in calls.values():
+            scratch.sum()
+            f()
+    torch.cuda.synchronize()
+    ctx.profile(False)
+    prof = ctx.profile_results()
+    del scratch
+    torch.cuda.empty_cache()
+    return {n: prof[n][1] / prof[n][0] for n in calls if n in prof}
+
+
 def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=False, shared_F=0,
-              recompute=False, graph=False):
+              recompute=False, graph=False, cold_rows=False):
     """Time the whole layer forward+backward on one workload (and, with
     `with_stats`, the routing statistics on its last step's buffers).
     mxfp8: quantise on the permute and run the MXFP8 expert GEMMs.
@@ -378,7 +447,9 @@ def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=Fal
         out["graph"] = gr
     if with_stats:
         out["routing_stats"] = stats_leg(ctx, cfg, override if override is not None else buf.logits,
-                                         buf, counts)
+                                         buf, counts, g)
+    if cold_rows:
+        out["cold_rows_ms"] = cold_row_movers(ctx, g, buf)
     if keep_inputs:
         out["inp"] = inp
     del g, buf, override
@@ -389,7 +460,7 @@ def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=Fal
 AUX_ALPHA = 0.001  # balance-loss weight (a small starting value)
 
 
-def stats_leg(ctx, cfg, logits, buf, counts, reps=20):
+def stats_leg(ctx, cfg, logits, buf, counts, g, reps=20):
     """Time the routing statistics + balance loss, its logit gradient and the
     per-expert norms of the three expert weight gradients on the layer's own
     buffers; report the loss beside the real load (a balance score alone can
@@ -403,20 +474,28 @@ def stats_leg(ctx, cfg, logits, buf, counts, reps=20):
     dl = torch.empty(T, E, dtype=torch.float32, device=logits.device)
     norms = [torch.empty(E, dtype=torch.float32, device=logits.device) for _ in range(3)]
     st = None
+    # the balance loss's share of dx and dW_r, added into copies of the
+    # layer's gradients (the buffers themselves stay as the step left them)
+    dx_acc, dwr_acc = buf.dx.clone(), buf.dw_router.clone()
     for it in range(reps + 2):
         if it == 2:
             torch.cuda.synchronize()
             ctx.profile(True)
         st = moe.moe_route_stats(logits, r["counts"], k, AUX_ALPHA, st)
         moe.moe_aux_loss_bwd(logits, r["counts"], k, AUX_ALPHA, 1.0, dl)
+        moe.moe_router_dense_bwd(g["x"], g["wr"], dl, dx_acc, dwr_acc)
         for i, w in enumerate(("dw_gate", "dw_up", "dw_down")):
             moe.moe_expert_grad_norms(buf.bwd[w], norms[i])
     torch.cuda.synchronize()
     ctx.profile(False)
     prof = ctx.profile_results()
-    ms = {n: prof[n][1] / prof[n][0] for n in ("route_stats", "aux_loss_bwd", "grad_norms")}
+    ms = {n: prof[n][1] / prof[n][0] for n in ("route_stats", "aux_loss_bwd", "grad_norms",
+                                                "router_dense_bwd")}
+    del dx_acc, dwr_acc
+    dense_flops = 4.0 * T * cfg.d * E  # dx and dW_r, one multiply-add per (t, i, e) each
     esz = buf.bwd["dw_gate"].element_size()
     nbytes = {"route_stats": T * E * 4, "aux_loss_bwd": T * E * 8, "grad_norms": E * cfg.d * cfg.F * esz}
+    ms_hbm = {n: v for n, v in ms.items() if n in nbytes}
     t1 = st["top1_count"].cpu()
     gn = torch.stack(norms).cpu()
     return {
@@ -429,7 +508,13 @@ def stats_leg(ctx, cfg, logits, buf, counts, reps=20):
         "kernel_ms": {n: round(v, 4) for n, v in ms.items()},
         "bytes_per_launch": nbytes,
         "hbm": {n: {"GB/s": round(nbytes[n] / (ms[n] / 1e3) / 1e9, 1),
-                    "frac_hbm": round(nbytes[n] / (ms[n] / 1e3) / 1e9 / PEAK_HBM_GBS, 3)} for n in ms},
+                    "frac_hbm": round(nbytes[n] / (ms[n] / 1e3) / 1e9 / PEAK_HBM_GBS, 3)} for n in ms_hbm},
+        # the balance loss's gradient through the router (moe_router_dense_bwd): fp32
+        # multiply-adds on the vector ALUs, against the fp32 vector peak
+        "router_dense_bwd": {"alpha": AUX_ALPHA, "gflop": round(dense_flops / 1e9, 2),
+                             "tflops": round(dense_flops / (ms["router_dense_bwd"] / 1e3) / 1e12, 2),
+                             "frac_fp32_valu": round(dense_flops / (ms["router_dense_bwd"] / 1e3) / 1e12
+                                                     / PEAK_FP32_TFLOPS, 4)},
     }
 
 
@@ -478,6 +563,10 @@ def mx_leg(steps, warmup, bf16_ref=True):
            "steps": steps, "warmup": warmup, "roofline": roof, "grouped_gemm": agg,
            "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in prof.items()},
            "expert_load": {"max": int(counts.max()), "mean": float(counts.mean()), "empty": 0}}
+    busy = read_mfma_busy(cfg.name, MX_GEMM_SOURCES)
+    if busy:
+        agg["mfma_busy"] = {n: busy[n]["mfma_busy"] for n in GEMM_KERNELS if n in busy}
+        agg["clock_ghz"] = {n: busy[n]["clock_ghz"] for n in GEMM_KERNELS if n in busy}
     if bf16_ref:
         res["bf16_same_rows"] = {"rows_per_s": round(R * steps / (bf_ms / 1e3), 1),
                                  "ms_per_step": round(bf_ms / steps, 4),
@@ -548,7 +637,8 @@ def main():
     cfg = mi.config(args.workload)
     smi_before = smi_snapshot() if not args.no_smi else None
     main_leg = layer_leg(cfg, args.steps, args.warmup, keep_inputs=args.cpu_sample > 0,
-                         with_stats=not args.no_stats, graph=not args.no_graph)
+                         with_stats=not args.no_stats, graph=not args.no_graph,
+                         cold_rows=cfg.dtype == "bf16" and not args.no_ceilings)
     smi_after = smi_snapshot() if not args.no_smi else None
     prof = main_leg["prof"]
     R = cfg.T * cfg.k
@@ -556,6 +646,18 @@ def main():
     peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
     roof, agg = gemm_summary(prof, unit, peak)
     roof["traffic"] = read_traffic(roof["kernel"], cfg.name)
+    roof["traffic_source"] = ("rocprofv3 FETCH_SIZE + WRITE_SIZE per launch, calibrated on a plain copy: "
+                              "bytes between the L2s and the memory fabric, Infinity Cache hits "
+                              "included, so an upper bound of the HBM bytes")
+    busy = read_mfma_busy(cfg.name)
+    if busy:
+        agg["mfma_busy"] = {n: busy[n]["mfma_busy"] for n in GEMM_KERNELS if n in busy}
+        agg["clock_ghz"] = {n: busy[n]["clock_ghz"] for n in GEMM_KERNELS if n in busy}
+        if roof["kernel"] in busy:
+            roof["mfma_busy"] = busy[roof["kernel"]]["mfma_busy"]
+    agg["mfma_busy_source"] = (f"profiles/mfma_gemm_{cfg.name}.txt (rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES over "
+                               "1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs)" if busy else
+                               "absent or taken on another version of the GEMM source")
     probe = None
     if cfg.dtype == "bf16" and not args.no_ceilings:
         probe = mfma_probe()
@@ -564,13 +666,22 @@ def main():
     rows = {}
     copies = copy_peak() if not args.no_ceilings else None
     copy_gbs = max(copies.values()) if copies else None
+    cold = main_leg.get("cold_rows_ms") or {}
     for name in ("permute", "combine", "combine_bwd", "permute_bwd"):
         if name in prof and cfg.dtype == "bf16":
             n, ms = prof[name]
-            gbs = row_bytes(name, cfg.T, cfg.d, cfg.k, cfg.F, cfg.E) / (ms / n / 1e3) / 1e9
-            rows[name] = {"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
-            if copy_gbs:
-                rows[name]["frac_copy"] = round(gbs / copy_gbs, 3)
+            nbytes = row_bytes(name, cfg.T, cfg.d, cfg.k, cfg.F, cfg.E)
+            warm = nbytes / (ms / n / 1e3) / 1e9
+            # "in_layer": inside the step, where a row mover may find its rows in the
+            # 256 MB Infinity Cache (the kernel before it just touched them);
+            # "GB/s" / "frac_hbm": the same launch with the caches flushed first
+            rows[name] = {"in_layer_GB/s": round(warm, 1)}
+            if name in cold:
+                gbs = nbytes / (cold[name] / 1e3) / 1e9
+                rows[name].update({"GB/s": round(gbs, 1), "frac_hbm": round(gbs / PEAK_HBM_GBS, 3),
+                                   "cold_ms": round(cold[name], 4)})
+                if copy_gbs:
+                    rows[name]["frac_copy"] = round(gbs / copy_gbs, 3)
     if copies:
         rows["copy_peak_GB/s"] = copies
 
