@@ -704,6 +704,62 @@ moe_status moe_internal_router_logits_mfma(moe_ctx* ctx, const void* x, const vo
   return MOE_OK;
 }
 
+// The router's share of a dense logit gradient on the matrix cores (bf16
+// operands, fp32 sums; dlb is the gradient rounded to bf16, wrt = W_r^T
+// [E,d]):
+//   dx[T,d] += dlb[T,E] wrt[E,d]: the one-group score GEMM (MODE 6) whose
+//     epilogue adds each fp32 tile into dx and rounds once;
+//   part[g][d][E] = x_g^T dlb_g for the token chunks g of voff (nz chunks):
+//     the K-ragged down-wgrad GEMM (MODE 5) over the chunks as groups,
+//     storing exact fp32 partials that the caller sums in chunk order.
+// Needs d % 64 == 0 and E % 64 == 0.
+moe_status moe_internal_router_dense_mfma(moe_ctx* ctx, const bf16_t* x, const bf16_t* dlb,
+                                          const bf16_t* wrt, const int32_t* voff, int nz, int T_,
+                                          int d, int E, bf16_t* dx, float* part) {
+  hipError_t e;
+  {
+    Params p{};
+    p.a0 = dlb;
+    p.lda = E;
+    p.b0 = wrt;
+    p.ldb = d;
+    p.c0 = dx;
+    p.aux0 = dx;
+    p.ldc = d;
+    p.M = T_;
+    p.N = d;
+    p.K = E;
+    p.kseg = E;
+    p.ntiles = (d + BN - 1) / BN;
+    p.E = 1;
+    constexpr int kBM = 64;
+    const int blocks = ((T_ + kBM - 1) / kBM) * p.ntiles;
+    e = launch<ROUTER, kBM, 4, 32, 1>(p, blocks, ctx->stream);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "router dense dx GEMM: %s", hipGetErrorString(e));
+  }
+  {
+    Params p{};
+    p.a0 = x;
+    p.lda = d;
+    p.b0 = dlb;
+    p.ldb = E;
+    p.c0 = part;
+    p.ldc = E;
+    p.c_gstride = (long long)d * E;
+    p.offsets = voff;
+    p.E = nz;
+    p.M = d;
+    p.N = E;
+    p.ntiles = (E + BN - 1) / BN;
+    p.mtiles = (d + CfgWD::BM - 1) / CfgWD::BM;
+    p.part = 1;
+    e = launch<WGRAD_DOWN, CfgWD::BM, CfgWD::S, CfgWD::BK, CfgWD::OCC, CfgWD::NW>(p, nz * p.ntiles * p.mtiles,
+                                                                              ctx->stream);
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "router dense dW GEMM: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
 // fp32 path (gemm_f32.hip)
 moe_status moe_internal_ffn_fwd_f32(moe_ctx* ctx, const float* xp, const float* wg,
                                     const float* wu, const float* wd, const int32_t* offsets,

@@ -417,8 +417,20 @@ __device__ __forceinline__ void store_tile_direct(const f32x16 (&acc)[SM][SN], c
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = acc[sm][sn][g4 * 4 + r];
           if (MODE == ROUTER) {
-            float* c = (float*)a.c0 + crow * a.ldc + col;
-            *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
+            if (a.aux0 != nullptr) {
+              // add into a bf16 matrix: c0 = aux0 + tile, one rounding (c0 may be aux0)
+              const size_t off = crow * a.ldc + col;
+              const uint2 raw = *reinterpret_cast<const uint2*>(a.aux0 + off);
+              const uint32_t w[2] = {raw.x, raw.y};
+              float s[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                s[r] = __uint_as_float((r & 1) ? (w[r >> 1] & 0xffff0000u) : (w[r >> 1] << 16)) + v[r];
+              *reinterpret_cast<uint2*>((bf16_t*)a.c0 + off) = make_uint2(pack2bf(s[0], s[1]), pack2bf(s[2], s[3]));
+            } else {
+              float* c = (float*)a.c0 + crow * a.ldc + col;
+              *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
+            }
           } else if (MODE == DGRAD_DOWN) {
             const size_t off = crow * a.ldc + col;
             const uint2 graw = *reinterpret_cast<const uint2*>(a.aux0 + off);

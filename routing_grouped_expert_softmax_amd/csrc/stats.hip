@@ -413,6 +413,34 @@ __global__ void __launch_bounds__(256) router_dense_kernel(const float* __restri
   }
 }
 
+// Inputs of the matrix-core path: dl rounded to bf16 (nearest even), W_r^T
+// [E,d] from W_r [d,E], and the token-chunk offsets {0, 512, ..., T}.
+__global__ void dense_prep_kernel(const float* __restrict__ dl, long long n_dl,
+                                  const bf16_t* __restrict__ wr, int d, int E, int T_, int nz,
+                                  bf16_t* __restrict__ dlb, bf16_t* __restrict__ wrt,
+                                  int32_t* __restrict__ voff) {
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n_dl; i += stride)
+    dlb[i] = f2bf(dl[i]);
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < (long long)d * E; i += stride) {
+    const int e = (int)(i / d), n = (int)(i % d);  // wrt[e][n] = wr[n][e]
+    wrt[i] = wr[(size_t)n * E + e];
+  }
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i <= nz; i += stride)
+    voff[i] = (int32_t)min((long long)T_, i * kDenseChunk);
+}
+
+// dW_r[i][e] += sum over chunks z (in order) of part[z][i][e] (the matrix-core
+// path's [d][E] partials), one rounding.
+__global__ void __launch_bounds__(256) router_dense_sum_de_kernel(const float* __restrict__ part, int nz,
+                                                                  long long n, bf16_t* __restrict__ dwr) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int z = 0; z < nz; ++z) s += part[(size_t)z * n + i];
+  dwr[i] = f2bf(bf2f(dwr[i]) + s);
+}
+
 // dW_r[n][e] += sum over chunks z (in order) of part[z][e][n], one rounding.
 template <typename T>
 __global__ void __launch_bounds__(256) router_dense_wsum_kernel(const float* __restrict__ part,
@@ -435,12 +463,19 @@ using namespace moe_host;
 // Workspace of moe_route_stats (three [E][256] partial arrays and the [E]
 // loss terms) and of moe_expert_grad_norms ([E][256] partial sums); both fit
 // in the larger.
-// Workspace of moe_router_dense_bwd: fp32 dW_r^T partials, one [E, d] block
-// per kDenseChunk tokens.
+// Workspace of moe_router_dense_bwd: fp32 dW_r partials, one [E, d] block per
+// kDenseChunk tokens; the matrix-core path (bf16) also keeps dl in bf16, W_r^T
+// and the chunk offsets in front of them.
+static size_t a256(size_t b) { return (b + 255) & ~(size_t)255; }
 size_t moe_internal_router_dense_ws_bytes(int T_, int d, int E) {
   const size_t nz = (size_t)(T_ + kDenseChunk - 1) / kDenseChunk;
-  return (nz * E * d * sizeof(float) + 255) & ~(size_t)255;
+  return a256((size_t)T_ * E * 2) + a256((size_t)E * d * 2) + a256((nz + 1) * 4) +
+         a256(nz * E * d * sizeof(float));
 }
+
+moe_status moe_internal_router_dense_mfma(moe_ctx* ctx, const bf16_t* x, const bf16_t* dlb,
+                                          const bf16_t* wrt, const int32_t* voff, int nz, int T_,
+                                          int d, int E, bf16_t* dx, float* part);  // gemm_bf16.hip
 
 size_t moe_internal_stats_ws_bytes(int E) {
   const size_t a = (size_t)kStatBlocks * E * 12 + (size_t)E * 4, b = (size_t)E * kNormChunks * 4;
@@ -543,7 +578,23 @@ moe_status moe_router_dense_bwd(moe_ctx* ctx, const void* x, const void* w_route
   const dim3 gdx((d + 255) / 256, (T_ + 31) / 32), gdw((d + 255) / 256, (E + 31) / 32, nz);
   const unsigned gsum = (unsigned)(((long long)E * d + 255) / 256);
   moe_prof_scope ps(ctx, MOE_K_ROUTER_DENSE_BWD);
-  if (dtype == MOE_BF16) {
+  if (dtype == MOE_BF16 && d % 64 == 0 && E % 64 == 0) {
+    // matrix cores: dl rounded to bf16 as the GEMM operand, fp32 sums
+    char* w = (char*)ctx->ws;
+    bf16_t* dlb = (bf16_t*)w;
+    w += a256((size_t)T_ * E * 2);
+    bf16_t* wrt = (bf16_t*)w;
+    w += a256((size_t)E * d * 2);
+    int32_t* voff = (int32_t*)w;
+    w += a256((size_t)(nz + 1) * 4);
+    float* pde = (float*)w;
+    dense_prep_kernel<<<1024, 256, 0, ctx->stream>>>(dlogits, (long long)T_ * E, (const bf16_t*)w_router,
+                                                     d, E, T_, nz, dlb, wrt, voff);
+    moe_status st = moe_internal_router_dense_mfma(ctx, (const bf16_t*)x, dlb, wrt, voff, nz, T_, d, E,
+                                                   (bf16_t*)dx, pde);
+    if (st != MOE_OK) return st;
+    router_dense_sum_de_kernel<<<gsum, 256, 0, ctx->stream>>>(pde, nz, (long long)d * E, (bf16_t*)dw_router);
+  } else if (dtype == MOE_BF16) {
     router_dense_kernel<bf16_t, true><<<gdx, 256, 0, ctx->stream>>>(
         dlogits, (const bf16_t*)w_router, T_, d, E, (bf16_t*)dx, nullptr);
     router_dense_kernel<bf16_t, false><<<gdw, 256, 0, ctx->stream>>>(

@@ -1,6 +1,7 @@
 """The balance loss's gradient carried into the router ([P1] 四: the router
 balances load; [P2] 2.2, 4.3): moe_router_dense_bwd adds dl W_r^T to dx and
-x^T dl to dW_r in place.  Checked against the oracle's router_dense_bwd on
+x^T dl to dW_r in place (bf16 with E, d multiples of 64 on the matrix cores,
+the rest on the vector ALUs).  Checked against the oracle's router_dense_bwd on
 its own (zero and nonzero starting gradients, ragged E and d, the benchmark's
 full shape) and inside the layer (layer_backward with aux_alpha) against the
 oracle's layer gradients plus the balance loss's share."""
@@ -73,7 +74,9 @@ ALPHA = 1000.0  # large, so the balance loss's share is a visible part of dx and
 
 @pytest.mark.parametrize("name,over", [("tiny", {}),
                                        ("tiny", dict(dtype="bf16", T=700, E=16, k=4, x_std=1.0)),
-                                       ("tiny", dict(dtype="bf16", T=1000, d=256, E=8, k=2, F=320, x_std=1.0))])
+                                       ("tiny", dict(dtype="bf16", T=1000, d=256, E=8, k=2, F=320, x_std=1.0)),
+                                       # E and d multiples of 64: the matrix-core path
+                                       ("tiny", dict(dtype="bf16", T=600, d=256, E=64, k=4, F=256, x_std=1.0))])
 def test_layer_with_balance_loss(moe, name, over):
     cfg = mi.config(name, **over)
     inp = mi.layer_inputs(cfg)
