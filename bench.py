@@ -509,13 +509,26 @@ def stats_leg(ctx, cfg, logits, buf, counts, g, reps=20):
         "bytes_per_launch": nbytes,
         "hbm": {n: {"GB/s": round(nbytes[n] / (ms[n] / 1e3) / 1e9, 1),
                     "frac_hbm": round(nbytes[n] / (ms[n] / 1e3) / 1e9 / PEAK_HBM_GBS, 3)} for n in ms_hbm},
-        # the balance loss's gradient through the router (moe_router_dense_bwd): fp32
-        # multiply-adds on the vector ALUs, against the fp32 vector peak
-        "router_dense_bwd": {"alpha": AUX_ALPHA, "gflop": round(dense_flops / 1e9, 2),
-                             "tflops": round(dense_flops / (ms["router_dense_bwd"] / 1e3) / 1e12, 2),
-                             "frac_fp32_valu": round(dense_flops / (ms["router_dense_bwd"] / 1e3) / 1e12
-                                                     / PEAK_FP32_TFLOPS, 4)},
+        # the balance loss's gradient through the router (moe_router_dense_bwd): bf16
+        # with E, d multiples of 64 runs on the matrix cores (against the bf16 peak),
+        # otherwise fp32 multiply-adds on the vector ALUs (against the fp32 vector peak)
+        "router_dense_bwd": dense_summary(cfg, esz, dense_flops, ms["router_dense_bwd"]),
     }
+
+
+def dense_summary(cfg, esz, flops, ms):
+    """Roofline line of moe_router_dense_bwd on the layer's shape."""
+    T, d, E = cfg.T, cfg.d, cfg.E
+    mfma = esz == 2 and d % 64 == 0 and E % 64 == 0
+    peak = PEAK_BF16_TFLOPS if mfma else PEAK_FP32_TFLOPS
+    # dx read and written, x and dl read (W_r is L2-resident)
+    nbytes = 2 * T * d * esz + T * d * esz + T * E * 4
+    tf = flops / (ms / 1e3) / 1e12
+    return {"alpha": AUX_ALPHA, "path": "mfma bf16" if mfma else "valu fp32", "ms": round(ms, 4),
+            "gflop": round(flops / 1e9, 2), "tflops": round(tf, 2), "peak": peak,
+            "frac_peak": round(tf / peak, 4), "algorithmic_bytes": nbytes,
+            "GB/s": round(nbytes / (ms / 1e3) / 1e9, 1),
+            "frac_hbm": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 3)}
 
 
 def mx_leg(steps, warmup, bf16_ref=True):
