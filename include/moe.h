@@ -326,11 +326,14 @@ moe_status moe_aux_loss_bwd(moe_ctx* ctx, const float* logits, const int32_t* co
  * [P2] 2.2, 4.3): its logit gradient (moe_aux_loss_bwd, dense [T,E]) flows
  * through logits = x W_r into the layer's input and router gradients.  This
  * call ADDS that share in place:
- *   dx[t,i]        += sum_e dlogits[t,e] * w_router[i,e]    (e ascending)
- *   dw_router[i,e] += sum_t x[t,i] * dlogits[t,e]           (t ascending in
- *                     512-token chunks, the chunk sums added in order)
- * fp32 sums, each element rounded once to dtype (MOE_F32 or MOE_BF16; x, dx
- * [T,d], w_router, dw_router [d,E] in dtype).  Deterministic.  Call it after
+ *   dx[t,i]        += sum_e dlogits[t,e] * w_router[i,e]
+ *   dw_router[i,e] += sum_t x[t,i] * dlogits[t,e]   (tokens in 512-token
+ *                     chunks, the chunk sums added in chunk order)
+ * fp32 sums in a fixed order, each element rounded once to dtype (MOE_F32
+ * or MOE_BF16; x, dx [T,d], w_router, dw_router [d,E] in dtype).  MOE_BF16
+ * with d and E multiples of 64 runs on the matrix cores with dlogits rounded
+ * to bf16 as the operand; every other case uses fp32 multiply-adds.
+ * Deterministic.  Call it after
  * moe_permute_bwd and moe_router_wgrad have written dx and dw_router.  Needs
  * the registered workspace (moe_workspace_size with this T, d, E) when
  * T > 0; T <= 2097120. */
