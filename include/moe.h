@@ -191,6 +191,44 @@ moe_status moe_grouped_ffn_fwd_mxq(moe_ctx* ctx, const uint8_t* xp_codes, const 
                                    const int32_t* offsets, int E, int R, int d, int F, void* g,
                                    void* u, void* h, void* yp);
 
+/* MXFP8 weight pack ([P1] 三: MXFP8; one quantisation of the expert
+ * weights serves the forward and the backward of a step).  Bytes of the pack
+ * for E experts of model width d and expert width F (d, F % 128 == 0);
+ * *bytes is a host output. */
+moe_status moe_mx_weight_pack_size(moe_ctx* ctx, int E, int d, int F, size_t* bytes);
+
+/* Quantise w_gate, w_up ([E,d,F] bf16) and w_down ([E,F,d] bf16) into
+ * `pack` (caller-owned device memory, 256-byte aligned, pack_bytes >=
+ * moe_mx_weight_pack_size).  Each weight is read once and written in both
+ * MX layouts the grouped FFN reads: blocks of 32 along each expert matrix's
+ * rows (the forward GEMMs' K; as moe_mx_quantize axis 1 with one group per
+ * expert) and along its columns (the data-gradient GEMMs' K; as axis 0).
+ * The layout inside the pack is the library's own.  Quantise again after
+ * every change of the weights: a pack is not tied to the weights it was
+ * made from. */
+moe_status moe_mx_quantize_weights(moe_ctx* ctx, const void* w_gate, const void* w_up,
+                                   const void* w_down, int E, int d, int F, void* pack,
+                                   size_t pack_bytes);
+
+/* moe_grouped_ffn_fwd with MOE_MXFP8, the weights taken from a pack: the
+ * same outputs bit for bit, without quantising the weights.  The rows come
+ * either as bf16 xp (quantised in the call) or already quantised
+ * (xp_codes, xp_scales from moe_permute_mx): give exactly one of xp and
+ * xp_codes.  yp NULL: the gate/up GEMM alone (recompute of g, u, h).
+ * Needs the MXFP8 workspace (moe_mx_workspace_size). */
+moe_status moe_grouped_ffn_fwd_mxp(moe_ctx* ctx, const void* xp, const uint8_t* xp_codes,
+                                   const uint8_t* xp_scales, const void* pack, size_t pack_bytes,
+                                   const int32_t* offsets, int E, int R, int d, int F, void* g,
+                                   void* u, void* h, void* yp);
+
+/* moe_grouped_ffn_bwd with MOE_MXFP8, the weights taken from a pack: the
+ * same outputs bit for bit.  Needs the MXFP8 workspace. */
+moe_status moe_grouped_ffn_bwd_mxp(moe_ctx* ctx, const void* xp, const void* pack,
+                                   size_t pack_bytes, const int32_t* offsets, const void* g,
+                                   const void* u, const void* h, const void* dyp, int E, int R,
+                                   int d, int F, void* dg, void* du, void* dxp, void* dw_gate,
+                                   void* dw_up, void* dw_down);
+
 /* Gate-weighted unpermute-combine: y[t] = sum_j gates[t,j] * yp[row_of[t,j]],
  * summed in slot order in fp32, rounded once.  [P2] 2.1 (return and
  * restore). */
@@ -369,6 +407,18 @@ moe_status moe_expert_grad_norms(moe_ctx* ctx, const void* dw, int E, int rows, 
 moe_status moe_mx_quantize(moe_ctx* ctx, const void* src_bf16, int rows, int cols, int axis,
                            const int32_t* group_offsets, int groups, uint8_t* codes,
                            uint8_t* scales_e8m0, int kpad_ld);
+
+/* Both layouts of moe_mx_quantize from one read of src: codes_cols and
+ * scales_cols exactly as axis 1 writes them (same group_offsets, groups,
+ * kpad_ld rules), codes_rows and scales_rows exactly as axis 0 writes them
+ * for the rows the groups cover (group_offsets[0] .. group_offsets[groups],
+ * all rows when group_offsets is NULL).  ([P1] 三: an operand that both a
+ * data-gradient GEMM and a weight-gradient GEMM read is quantised along
+ * each one's K.) */
+moe_status moe_mx_quantize_both(moe_ctx* ctx, const void* src_bf16, int rows, int cols,
+                                const int32_t* group_offsets, int groups, uint8_t* codes_cols,
+                                uint8_t* scales_cols, int kpad_ld, uint8_t* codes_rows,
+                                uint8_t* scales_rows);
 
 /* -------------------------------------------------------------- profiling
  * Per-kernel timing with HIP events recorded on the context's stream around

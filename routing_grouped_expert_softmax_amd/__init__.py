@@ -58,10 +58,17 @@ _SIGS = {
     "moe_expert_grad_norms": [_vp, _int, _int, _int, _int, _vp],
     "moe_router_dense_bwd": [_vp, _vp, _vp, _int, _int, _int, _int, _vp, _vp],
     "moe_mfma_peak_probe": [_int, _int, _flt, _flt, _vp],
+    "moe_mx_quantize_both": [_vp, _int, _int, _vp, _int, _vp, _vp, _int, _vp, _vp],
+    "moe_mx_quantize_weights": [_vp, _vp, _vp, _int, _int, _int, _vp, ctypes.c_size_t],
+    "moe_grouped_ffn_fwd_mxp": [_vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _int, _int, _int, _int, _vp, _vp,
+                                _vp, _vp],
+    "moe_grouped_ffn_bwd_mxp": [_vp, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
+                                _vp, _vp, _vp, _vp, _vp, _vp],
 }
 EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "moe_last_error",
            "moe_workspace_size", "moe_set_workspace", *_SIGS.keys(), "moe_profile_enable",
-           "moe_profile_query", "moe_kernel_name", "moe_mx_workspace_size", "moe_ffn_bwd_workspace_size"]
+           "moe_profile_query", "moe_kernel_name", "moe_mx_workspace_size", "moe_ffn_bwd_workspace_size",
+           "moe_mx_weight_pack_size"]
 
 # kernel ids of the profiling hook (moe_kernel_id in include/moe.h)
 KERNELS = ["router_logits", "topk_hist", "expert_scan", "rank", "permute", "gemm_up_swiglu",
@@ -90,6 +97,7 @@ def lib():
         L.moe_mx_workspace_size.argtypes = [_vp, _int, _int, _int, _int, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_ffn_bwd_workspace_size.argtypes = [_vp, _int, _int, _int, _int, _int,
                                                  ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_mx_weight_pack_size.argtypes = [_vp, _int, _int, _int, ctypes.POINTER(ctypes.c_size_t)]
         for name, sig in _SIGS.items():
             getattr(L, name).argtypes = [_vp, *sig]
         L.moe_profile_enable.argtypes = [_vp, _int]
@@ -247,6 +255,100 @@ def moe_permute(x, row_of, xp=None):
         xp = torch.empty(T * k, d, dtype=x.dtype, device=x.device)
     context(x.device.index).call("moe_permute", _p(x), _p(row_of), T, d, k, _dt(x), _p(xp))
     return xp
+
+
+@dataclass
+class MxWeightPack:
+    """The expert weights quantised once in both MXFP8 layouts
+    (moe_mx_quantize_weights): a uint8 device buffer and its shape."""
+    data: torch.Tensor
+    E: int
+    d: int
+    F: int
+
+
+def moe_mx_weight_pack_size(E, d, F, device=0):
+    n = ctypes.c_size_t()
+    ctx = context(device)
+    ctx._check(lib().moe_mx_weight_pack_size(ctx.handle, E, d, F, ctypes.byref(n)))
+    return n.value
+
+
+def moe_mx_quantize_weights(w_gate, w_up, w_down, pack: MxWeightPack | None = None):
+    """Quantise the bf16 expert weights (w_gate, w_up [E,d,F], w_down
+    [E,F,d]) into a pack read by moe_grouped_ffn_fwd_mxp/bwd_mxp; returns it."""
+    _need_cuda(w_gate, w_up, w_down)
+    E, d, F = w_gate.shape
+    dev = w_gate.device
+    if pack is None:
+        n = moe_mx_weight_pack_size(E, d, F, dev.index)
+        pack = MxWeightPack(torch.empty(n, dtype=torch.uint8, device=dev), E, d, F)
+    if (pack.E, pack.d, pack.F) != (E, d, F):
+        raise MoeError(f"pack is for E={pack.E} d={pack.d} F={pack.F}, weights are {E}x{d}x{F}")
+    context(dev.index).call("moe_mx_quantize_weights", _p(w_gate), _p(w_up), _p(w_down), E, d, F,
+                            _p(pack.data), pack.data.numel())
+    return pack
+
+
+def moe_mx_quantize_both(src, group_offsets=None, groups=1):
+    """Both MX layouts of a bf16 [rows, cols] tensor from one read: returns
+    (codes_cols [cols, kpad], scales_cols [cols, kpad/32], codes_rows
+    [rows, cols], scales_rows [rows, cols/32]) as moe_mx_quantize axis 1 and
+    axis 0 give them."""
+    _need_cuda(src, group_offsets)
+    rows, cols = src.shape
+    dev = src.device
+    kp = mx_kpad(rows, groups)
+    cc = torch.empty(cols, kp, dtype=torch.uint8, device=dev)
+    cs = torch.empty(cols, kp // 32, dtype=torch.uint8, device=dev)
+    rc = torch.empty(rows, cols, dtype=torch.uint8, device=dev)
+    rs = torch.empty(rows, cols // 32, dtype=torch.uint8, device=dev)
+    context(dev.index).call("moe_mx_quantize_both", _p(src), rows, cols, _p(group_offsets), groups, _p(cc),
+                            _p(cs), kp, _p(rc), _p(rs))
+    return cc, cs, rc, rs
+
+
+def moe_grouped_ffn_fwd_mxp(pack: MxWeightPack, offsets, xp=None, xp_codes=None, xp_scales=None, out=None,
+                            up_only=False):
+    """MXFP8 grouped FFN forward with the weights from a pack, on bf16 rows xp
+    or on rows already quantised (xp_codes, xp_scales); returns dict(g, u, h,
+    yp), without yp when up_only (the gate/up GEMM alone)."""
+    rows = xp if xp is not None else xp_codes
+    _need_cuda(rows, xp_scales, offsets, pack.data)
+    R = rows.shape[0]
+    E, d, F = pack.E, pack.d, pack.F
+    dev = rows.device
+    context(dev.index).ensure_mx_workspace(E, R, d, F)
+    if out is None:
+        out = dict(g=torch.empty(R, F, dtype=torch.bfloat16, device=dev),
+                   u=torch.empty(R, F, dtype=torch.bfloat16, device=dev),
+                   h=torch.empty(R, F, dtype=torch.bfloat16, device=dev))
+        if not up_only:
+            out["yp"] = torch.empty(R, d, dtype=torch.bfloat16, device=dev)
+    context(dev.index).call("moe_grouped_ffn_fwd_mxp", _p(xp), _p(xp_codes), _p(xp_scales), _p(pack.data),
+                            pack.data.numel(), _p(offsets), E, R, d, F, _p(out["g"]), _p(out["u"]),
+                            _p(out["h"]), None if up_only else _p(out["yp"]))
+    return out
+
+
+def moe_grouped_ffn_bwd_mxp(xp, pack: MxWeightPack, offsets, g, u, h, dyp, out=None):
+    """MXFP8 grouped FFN backward with the weights from a pack; returns
+    dict(dg, du, dxp, dw_gate, dw_up, dw_down)."""
+    _need_cuda(xp, offsets, g, u, h, dyp, pack.data)
+    R = xp.shape[0]
+    E, d, F = pack.E, pack.d, pack.F
+    dev = xp.device
+    context(dev.index).ensure_ffn_bwd_workspace(E, R, d, F, MOE_MXFP8)
+    if out is None:
+        bf = torch.bfloat16
+        out = dict(dg=torch.empty(R, F, dtype=bf, device=dev), du=torch.empty(R, F, dtype=bf, device=dev),
+                   dxp=torch.empty(R, d, dtype=bf, device=dev), dw_gate=torch.empty(E, d, F, dtype=bf, device=dev),
+                   dw_up=torch.empty(E, d, F, dtype=bf, device=dev),
+                   dw_down=torch.empty(E, F, d, dtype=bf, device=dev))
+    context(dev.index).call("moe_grouped_ffn_bwd_mxp", _p(xp), _p(pack.data), pack.data.numel(), _p(offsets),
+                            _p(g), _p(u), _p(h), _p(dyp), E, R, d, F, _p(out["dg"]), _p(out["du"]),
+                            _p(out["dxp"]), _p(out["dw_gate"]), _p(out["dw_up"]), _p(out["dw_down"]))
+    return out
 
 
 def moe_permute_mx(x, row_of, xp=None, codes=None, scales=None, with_bf16=True):
@@ -533,6 +635,7 @@ class LayerBuffers:
     shared: dict | None = None      # shared expert: offsets {0,T}, its forward and backward buffers
     dl_rows: torch.Tensor | None = None  # logit gradients in expert-row order (bf16 router fold)
     aux_dl: torch.Tensor | None = None   # dense [T,E] balance-loss logit gradient (aux_alpha)
+    wpack: MxWeightPack | None = None    # MXFP8: the expert weights quantised once per step
 
 
 def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False, shared_F=0):
@@ -560,7 +663,12 @@ def alloc_layer(T, d, E, k, F, dtype, device, mxfp8=False, shared_F=0):
     if mxfp8:
         buf.xq = z(R, d, dt=torch.uint8)
         buf.xs = z(R, d // 32, dt=torch.uint8)
+        buf.wpack = MxWeightPack(z(moe_mx_weight_pack_size(E, d, F, dev.index), dt=torch.uint8), E, d, F)
         context(dev.index).ensure_mx_workspace(E, R, d, F)
+        if shared_F:
+            n = moe_mx_weight_pack_size(1, d, shared_F, dev.index)
+            buf.shared["wpack"] = MxWeightPack(z(n, dt=torch.uint8), 1, d, shared_F)
+            context(dev.index).ensure_mx_workspace(1, T, d, shared_F)
     return buf
 
 
@@ -582,21 +690,29 @@ def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logit
     """Router scores -> route -> permute -> grouped SwiGLU experts -> combine.
     `logits_override` (optional [T,E] fp32 on the GPU) replaces the router
     scores as the routing input after the router GEMM has run.  mxfp8=True
-    (buffers from alloc_layer(..., mxfp8=True)) quantises on the permute and
-    runs the MXFP8 expert GEMMs.  shared = (w_gate, w_up, w_down) of a shared
+    (buffers from alloc_layer(..., mxfp8=True)) quantises the expert weights
+    once into buf.wpack (both layouts, for this forward and the backward of
+    the step), quantises on the permute and runs the MXFP8 expert GEMMs.  shared = (w_gate, w_up, w_down) of a shared
     expert (buffers from alloc_layer(..., shared_F=F_s)) runs it over every
     token as one group and adds its rows in the combine."""
     moe_router_logits(x, w_router, buf.logits)
     moe_route(buf.logits if logits_override is None else logits_override, k, buf.route)
     if mxfp8:
+        # the weights are quantised once here, in both layouts; the backward
+        # of this step reads the same pack
+        moe_mx_quantize_weights(w_gate, w_up, w_down, buf.wpack)
         moe_permute_mx(x, buf.route["row_of"], buf.xp, buf.xq, buf.xs)
-        moe_grouped_ffn_fwd_mxq(buf.xq, buf.xs, w_gate, w_up, w_down, buf.route["offsets"], buf.ffn)
+        moe_grouped_ffn_fwd_mxp(buf.wpack, buf.route["offsets"], xp_codes=buf.xq, xp_scales=buf.xs, out=buf.ffn)
     else:
         moe_permute(x, buf.route["row_of"], buf.xp)
         moe_grouped_ffn_fwd(buf.xp, w_gate, w_up, w_down, buf.route["offsets"], buf.ffn)
     ys = None
     if shared is not None:
-        moe_grouped_ffn_fwd(x, *shared, buf.shared["offsets"], buf.shared["ffn"], mxfp8=mxfp8)
+        if mxfp8:
+            moe_mx_quantize_weights(*shared, buf.shared["wpack"])
+            moe_grouped_ffn_fwd_mxp(buf.shared["wpack"], buf.shared["offsets"], xp=x, out=buf.shared["ffn"])
+        else:
+            moe_grouped_ffn_fwd(x, *shared, buf.shared["offsets"], buf.shared["ffn"])
         ys = buf.shared["ffn"]["yp"]
     moe_combine(buf.ffn["yp"], buf.route["gates"], buf.route["row_of"], buf.y, y_shared=ys)
     return buf.y
@@ -609,7 +725,8 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxf
     folded into the gate/up dgrad (moe_grouped_ffn_bwd_router) and the
     permute backward only sums rows; fp32 and MXFP8 add it in the permute
     backward.  Returns dx; weight grads are in buf.bwd and
-    buf.dw_router.  recompute=True reads from the forward only yp, the gates
+    buf.dw_router.  mxfp8: the weights are read from buf.wpack, which
+    layer_forward of this step filled (run it after every weight change).  recompute=True reads from the forward only yp, the gates
     and the routing: xp is permuted again from x and g, u, h (the shared
     expert's too) are recomputed by the gate/up GEMM before they are used,
     so the forward need not keep them.  aux_alpha (the balance-loss weight)
@@ -618,23 +735,37 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxf
     r = buf.route
     if recompute:
         moe_permute(x, r["row_of"], buf.xp)
-        moe_grouped_ffn_up(buf.xp, w_gate, w_up, r["offsets"], buf.ffn, mxfp8=mxfp8)
+        if mxfp8:
+            moe_grouped_ffn_fwd_mxp(buf.wpack, r["offsets"], xp=buf.xp, out=buf.ffn, up_only=True)
+        else:
+            moe_grouped_ffn_up(buf.xp, w_gate, w_up, r["offsets"], buf.ffn)
         if shared is not None:
-            moe_grouped_ffn_up(x, shared[0], shared[1], buf.shared["offsets"], buf.shared["ffn"], mxfp8=mxfp8)
+            if mxfp8:
+                moe_grouped_ffn_fwd_mxp(buf.shared["wpack"], buf.shared["offsets"], xp=x, out=buf.shared["ffn"],
+                                        up_only=True)
+            else:
+                moe_grouped_ffn_up(x, shared[0], shared[1], buf.shared["offsets"], buf.shared["ffn"])
     moe_combine_bwd(dy, buf.ffn["yp"], r["gates"], r["row_of"], buf.dyp, buf.dgates)
     fold = not mxfp8 and buf.xp.dtype == torch.bfloat16
     if fold:
         moe_route_bwd(r["gates"], buf.dgates, buf.dlogits_sel, row_of=r["row_of"], dl_rows=buf.dl_rows)
     else:
         moe_route_bwd(r["gates"], buf.dgates, buf.dlogits_sel)
-    moe_grouped_ffn_bwd(buf.xp, w_gate, w_up, w_down, r["offsets"], buf.ffn["g"], buf.ffn["u"],
-                        buf.ffn["h"], buf.dyp, buf.bwd, mxfp8=mxfp8,
-                        router=(buf.dl_rows, w_router) if fold else None)
+    if mxfp8:
+        moe_grouped_ffn_bwd_mxp(buf.xp, buf.wpack, r["offsets"], buf.ffn["g"], buf.ffn["u"], buf.ffn["h"],
+                                buf.dyp, buf.bwd)
+    else:
+        moe_grouped_ffn_bwd(buf.xp, w_gate, w_up, w_down, r["offsets"], buf.ffn["g"], buf.ffn["u"],
+                            buf.ffn["h"], buf.dyp, buf.bwd, router=(buf.dl_rows, w_router) if fold else None)
     dxs = None
     if shared is not None:
         sh = buf.shared
-        moe_grouped_ffn_bwd(x, *shared, sh["offsets"], sh["ffn"]["g"], sh["ffn"]["u"], sh["ffn"]["h"], dy,
-                            sh["bwd"], mxfp8=mxfp8)
+        if mxfp8:
+            moe_grouped_ffn_bwd_mxp(x, sh["wpack"], sh["offsets"], sh["ffn"]["g"], sh["ffn"]["u"], sh["ffn"]["h"],
+                                    dy, sh["bwd"])
+        else:
+            moe_grouped_ffn_bwd(x, *shared, sh["offsets"], sh["ffn"]["g"], sh["ffn"]["u"], sh["ffn"]["h"], dy,
+                                sh["bwd"])
         dxs = sh["bwd"]["dxp"]
     if fold:
         moe_permute_bwd(buf.bwd["dxp"], r["row_of"], dx=buf.dx, dx_shared=dxs)

@@ -44,6 +44,7 @@
 
 #include "common.h"
 #include "gemm_common.h"
+#include "mx.h"
 
 using namespace moe;
 using namespace moe_gemm;
@@ -776,14 +777,18 @@ size_t moe_internal_mx_fwd_bytes(int E, int R, int d, int F);
 size_t moe_internal_mx_bwd_bytes(int E, int R, int d, int F);
 moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const uint8_t* xq_in,
                                    const uint8_t* xs_in, const bf16_t* wg, const bf16_t* wu,
-                                   const bf16_t* wd, const int32_t* offsets, int E, int R, int d,
-                                   int F, bf16_t* g, bf16_t* u, bf16_t* h, bf16_t* yp);
+                                   const bf16_t* wd, const MxWeights* pw, const int32_t* offsets,
+                                   int E, int R, int d, int F, bf16_t* g, bf16_t* u, bf16_t* h,
+                                   bf16_t* yp);
 moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t* wg,
-                                   const bf16_t* wu, const bf16_t* wd, const int32_t* offsets,
-                                   const bf16_t* g, const bf16_t* u, const bf16_t* h,
-                                   const bf16_t* dyp, int E, int R, int d, int F, bf16_t* dg,
-                                   bf16_t* du, bf16_t* dxp, bf16_t* dwg, bf16_t* dwu,
+                                   const bf16_t* wu, const bf16_t* wd, const MxWeights* pw,
+                                   const int32_t* offsets, const bf16_t* g, const bf16_t* u,
+                                   const bf16_t* h, const bf16_t* dyp, int E, int R, int d, int F,
+                                   bf16_t* dg, bf16_t* du, bf16_t* dxp, bf16_t* dwg, bf16_t* dwu,
                                    bf16_t* dwd);
+size_t moe_internal_mx_pack_layout(int E, int d, int F, uint8_t* base, MxWeights* w);
+moe_status moe_internal_mx_quantize_weights(moe_ctx* ctx, const bf16_t* wg, const bf16_t* wu,
+                                            const bf16_t* wd, int E, int d, int F, uint8_t* pack);
 
 // ---------------------------------------------------------------- split-K
 // A weight-gradient launch has E * mtiles * ntiles output tiles.  When that
@@ -944,7 +949,7 @@ moe_status moe_grouped_ffn_fwd(moe_ctx* ctx, const void* xp, const void* w_gate,
   if (R == 0) return MOE_OK;
   if (dtype == MOE_MXFP8)
     return moe_internal_ffn_fwd_mx(ctx, (const bf16_t*)xp, nullptr, nullptr, (const bf16_t*)w_gate,
-                                   (const bf16_t*)w_up, (const bf16_t*)w_down, offsets, E, R, d, F,
+                                   (const bf16_t*)w_up, (const bf16_t*)w_down, nullptr, offsets, E, R, d, F,
                                    (bf16_t*)g, (bf16_t*)u, (bf16_t*)h, (bf16_t*)yp);
   if (dtype == MOE_F32)
     return moe_internal_ffn_fwd_f32(ctx, (const float*)xp, (const float*)w_gate,
@@ -1024,8 +1029,114 @@ moe_status moe_grouped_ffn_fwd_mxq(moe_ctx* ctx, const uint8_t* xp_codes, const 
   }
   if (R == 0) return MOE_OK;
   return moe_internal_ffn_fwd_mx(ctx, nullptr, xp_codes, xp_scales, (const bf16_t*)w_gate,
-                                 (const bf16_t*)w_up, (const bf16_t*)w_down, offsets, E, R, d, F,
+                                 (const bf16_t*)w_up, (const bf16_t*)w_down, nullptr, offsets, E, R, d, F,
                                  (bf16_t*)g, (bf16_t*)u, (bf16_t*)h, (bf16_t*)yp);
+}
+
+moe_status moe_mx_weight_pack_size(moe_ctx* ctx, int E, int d, int F, size_t* bytes) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, bytes != nullptr, "bytes is null");
+  moe_status st = ffn_validate(ctx, E, 0, d, F, MOE_MXFP8, "moe_mx_weight_pack_size");
+  if (st != MOE_OK) return st;
+  *bytes = moe_internal_mx_pack_layout(E, d, F, nullptr, nullptr);
+  return MOE_OK;
+}
+
+// The pack a call was given, checked against its shape.
+static moe_status pack_regions(moe_ctx* ctx, const void* pack, size_t pack_bytes, int E, int d, int F,
+                               const char* what, MxWeights* w) {
+  MOE_REQUIRE(ctx, pack != nullptr && (reinterpret_cast<uintptr_t>(pack) & 255u) == 0,
+              "%s: pack null or not 256-byte aligned", what);
+  const size_t need = moe_internal_mx_pack_layout(E, d, F, nullptr, nullptr);
+  MOE_REQUIRE(ctx, pack_bytes >= need, "%s: pack of %zu bytes < %zu for E=%d d=%d F=%d", what,
+              pack_bytes, need, E, d, F);
+  moe_internal_mx_pack_layout(E, d, F, (uint8_t*)pack, w);
+  return MOE_OK;
+}
+
+moe_status moe_mx_quantize_weights(moe_ctx* ctx, const void* w_gate, const void* w_up,
+                                   const void* w_down, int E, int d, int F, void* pack,
+                                   size_t pack_bytes) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = ffn_validate(ctx, E, 0, d, F, MOE_MXFP8, "moe_mx_quantize_weights");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR(ctx, w_gate);
+  MOE_REQUIRE_PTR(ctx, w_up);
+  MOE_REQUIRE_PTR(ctx, w_down);
+  MxWeights w;
+  st = pack_regions(ctx, pack, pack_bytes, E, d, F, "moe_mx_quantize_weights", &w);
+  if (st != MOE_OK) return st;
+  return moe_internal_mx_quantize_weights(ctx, (const bf16_t*)w_gate, (const bf16_t*)w_up,
+                                          (const bf16_t*)w_down, E, d, F, (uint8_t*)pack);
+}
+
+moe_status moe_grouped_ffn_fwd_mxp(moe_ctx* ctx, const void* xp, const uint8_t* xp_codes,
+                                   const uint8_t* xp_scales, const void* pack, size_t pack_bytes,
+                                   const int32_t* offsets, int E, int R, int d, int F, void* g,
+                                   void* u, void* h, void* yp) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = ffn_validate(ctx, E, R, d, F, MOE_MXFP8, "moe_grouped_ffn_fwd_mxp");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE(ctx, R == 0 || (xp != nullptr) != (xp_codes != nullptr),
+              "moe_grouped_ffn_fwd_mxp: give exactly one of xp and xp_codes");
+  if (xp_codes) {
+    MOE_REQUIRE_PTR(ctx, xp_codes);
+    MOE_REQUIRE(ctx, xp_scales != nullptr, "moe_grouped_ffn_fwd_mxp: xp_scales is null");
+  } else {
+    MOE_REQUIRE_PTR_OR_EMPTY(ctx, xp, R == 0);
+  }
+  MOE_REQUIRE_PTR(ctx, offsets);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, g, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, u, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, h, R == 0);
+  if (yp) MOE_REQUIRE_PTR(ctx, yp);
+  {
+    const size_t rf = (size_t)R * F * 2;
+    MOE_REQUIRE_DISJOINT(ctx, "moe_grouped_ffn_fwd_mxp", {g, rf, "g"}, {u, rf, "u"}, {h, rf, "h"},
+                         {yp, (size_t)R * d * 2, "yp"});
+  }
+  MxWeights w;
+  st = pack_regions(ctx, pack, pack_bytes, E, d, F, "moe_grouped_ffn_fwd_mxp", &w);
+  if (st != MOE_OK) return st;
+  if (R == 0) return MOE_OK;
+  return moe_internal_ffn_fwd_mx(ctx, (const bf16_t*)xp, xp_codes, xp_scales, nullptr, nullptr, nullptr,
+                                 &w, offsets, E, R, d, F, (bf16_t*)g, (bf16_t*)u, (bf16_t*)h,
+                                 (bf16_t*)yp);
+}
+
+moe_status moe_grouped_ffn_bwd_mxp(moe_ctx* ctx, const void* xp, const void* pack,
+                                   size_t pack_bytes, const int32_t* offsets, const void* g,
+                                   const void* u, const void* h, const void* dyp, int E, int R,
+                                   int d, int F, void* dg, void* du, void* dxp, void* dw_gate,
+                                   void* dw_up, void* dw_down) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = ffn_validate(ctx, E, R, d, F, MOE_MXFP8, "moe_grouped_ffn_bwd_mxp");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, xp, R == 0);
+  MOE_REQUIRE_PTR(ctx, offsets);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, g, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, u, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, h, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dyp, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dg, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, du, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dxp, R == 0);
+  MOE_REQUIRE_PTR(ctx, dw_gate);
+  MOE_REQUIRE_PTR(ctx, dw_up);
+  MOE_REQUIRE_PTR(ctx, dw_down);
+  {
+    const size_t rf = (size_t)R * F * 2, w = (size_t)E * d * F * 2;
+    MOE_REQUIRE_DISJOINT(ctx, "moe_grouped_ffn_bwd_mxp", {dg, rf, "dg"}, {du, rf, "du"},
+                         {dxp, (size_t)R * d * 2, "dxp"}, {dw_gate, w, "dw_gate"}, {dw_up, w, "dw_up"},
+                         {dw_down, w, "dw_down"});
+  }
+  MxWeights w;
+  st = pack_regions(ctx, pack, pack_bytes, E, d, F, "moe_grouped_ffn_bwd_mxp", &w);
+  if (st != MOE_OK) return st;
+  return moe_internal_ffn_bwd_mx(ctx, (const bf16_t*)xp, nullptr, nullptr, nullptr, &w, offsets,
+                                 (const bf16_t*)g, (const bf16_t*)u, (const bf16_t*)h,
+                                 (const bf16_t*)dyp, E, R, d, F, (bf16_t*)dg, (bf16_t*)du,
+                                 (bf16_t*)dxp, (bf16_t*)dw_gate, (bf16_t*)dw_up, (bf16_t*)dw_down);
 }
 
 static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
@@ -1060,7 +1171,7 @@ static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
   }
   if (dtype == MOE_MXFP8)
     return moe_internal_ffn_bwd_mx(ctx, (const bf16_t*)xp, (const bf16_t*)w_gate,
-                                   (const bf16_t*)w_up, (const bf16_t*)w_down, offsets,
+                                   (const bf16_t*)w_up, (const bf16_t*)w_down, nullptr, offsets,
                                    (const bf16_t*)g, (const bf16_t*)u, (const bf16_t*)h,
                                    (const bf16_t*)dyp, E, R, d, F, (bf16_t*)dg, (bf16_t*)du,
                                    (bf16_t*)dxp, (bf16_t*)dw_gate, (bf16_t*)dw_up,

@@ -512,12 +512,56 @@ size_t moe_internal_mx_bwd_bytes(int E, int R, int d, int F) {
   return L.total;
 }
 
+// Weight pack: the three expert weights in the two layouts the MXFP8 GEMMs
+// read, each region 256-byte aligned.  Forward (blocks along each expert
+// matrix's rows, the forward GEMMs' K; transposed): Wg, Wu codes [F][E*d],
+// Wd codes [d][E*F].  Backward (blocks along the columns, the data-gradient
+// GEMMs' K): Wg, Wu codes [E*d][F], Wd codes [E*F][d].  Scales follow their
+// codes ([..][../32]).  base null: sizes only.
+size_t moe_internal_mx_pack_layout(int E, int d, int F, uint8_t* base, MxWeights* w) {
+  MxLayout L;
+  const size_t wgu = (size_t)E * d * F;
+  const size_t o[12] = {L.put(wgu), L.put(wgu / 32), L.put(wgu), L.put(wgu / 32), L.put(wgu), L.put(wgu / 32),
+                        L.put(wgu), L.put(wgu / 32), L.put(wgu), L.put(wgu / 32), L.put(wgu), L.put(wgu / 32)};
+  if (base && w) {
+    w->fgq = base + o[0]; w->fgs = base + o[1];
+    w->fuq = base + o[2]; w->fus = base + o[3];
+    w->fdq = base + o[4]; w->fds = base + o[5];
+    w->bgq = base + o[6]; w->bgs = base + o[7];
+    w->buq = base + o[8]; w->bus = base + o[9];
+    w->bdq = base + o[10]; w->bds = base + o[11];
+  }
+  return L.total;
+}
+
+// Each weight read once, both layouts written (mx_quantize_both, one group of
+// rows per expert matrix).
+moe_status moe_internal_mx_quantize_weights(moe_ctx* ctx, const bf16_t* wg, const bf16_t* wu,
+                                            const bf16_t* wd, int E, int d, int F, uint8_t* pack) {
+  MxWeights w;
+  moe_internal_mx_pack_layout(E, d, F, pack, &w);
+  hipStream_t s = ctx->stream;
+  moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
+  hipError_t e = mx_quantize_both(wg, E * d, F, nullptr, d, E, (uint8_t*)w.fgq, (uint8_t*)w.fgs, E * d,
+                                  (uint8_t*)w.bgq, (uint8_t*)w.bgs, s);
+  if (e == hipSuccess)
+    e = mx_quantize_both(wu, E * d, F, nullptr, d, E, (uint8_t*)w.fuq, (uint8_t*)w.fus, E * d,
+                         (uint8_t*)w.buq, (uint8_t*)w.bus, s);
+  if (e == hipSuccess)
+    e = mx_quantize_both(wd, E * F, d, nullptr, F, E, (uint8_t*)w.fdq, (uint8_t*)w.fds, E * F,
+                         (uint8_t*)w.bdq, (uint8_t*)w.bds, s);
+  if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise weights: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
 // xq_in/xs_in: Xp already quantised rowwise (quantise-on-permute); when
-// null, Xp is quantised here from the bf16 xp.
+// null, Xp is quantised here from the bf16 xp.  pw: the weights already
+// quantised (a weight pack); when null, they are quantised here.
 moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const uint8_t* xq_in,
                                    const uint8_t* xs_in, const bf16_t* wg, const bf16_t* wu,
-                                   const bf16_t* wd, const int32_t* offsets, int E, int R, int d,
-                                   int F, bf16_t* g, bf16_t* u, bf16_t* h, bf16_t* yp) {
+                                   const bf16_t* wd, const MxWeights* pw, const int32_t* offsets,
+                                   int E, int R, int d, int F, bf16_t* g, bf16_t* u, bf16_t* h,
+                                   bf16_t* yp) {
   const size_t need = moe_internal_mx_fwd_bytes(E, R, d, F);
   if (ctx->ws == nullptr || ctx->ws_bytes < need)
     return fail(ctx, MOE_ERR_WORKSPACE, "MXFP8 forward: workspace %zu bytes < %zu needed",
@@ -546,9 +590,15 @@ moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const uint8_t
     } else {
       e = mx_quantize_rows(xp, R, d, (uint8_t*)xq, (uint8_t*)xs, s);
     }
-    if (e == hipSuccess) e = mx_quantize_cols(wg, E * d, F, nullptr, d, E, wgq, wgs, E * d, s);
-    if (e == hipSuccess) e = mx_quantize_cols(wu, E * d, F, nullptr, d, E, wuq, wus, E * d, s);
-    if (e == hipSuccess && wd) e = mx_quantize_cols(wd, E * F, d, nullptr, F, E, wdq, wds, E * F, s);
+    if (pw) {
+      wgq = (uint8_t*)pw->fgq; wgs = (uint8_t*)pw->fgs;
+      wuq = (uint8_t*)pw->fuq; wus = (uint8_t*)pw->fus;
+      wdq = (uint8_t*)pw->fdq; wds = (uint8_t*)pw->fds;
+    } else {
+      if (e == hipSuccess) e = mx_quantize_cols(wg, E * d, F, nullptr, d, E, wgq, wgs, E * d, s);
+      if (e == hipSuccess) e = mx_quantize_cols(wu, E * d, F, nullptr, d, E, wuq, wus, E * d, s);
+      if (e == hipSuccess && wd) e = mx_quantize_cols(wd, E * F, d, nullptr, F, E, wdq, wds, E * F, s);
+    }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise: %s", hipGetErrorString(e));
   }
   {
@@ -562,7 +612,7 @@ moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const uint8_t
     e = launch_mx<FWD_UP, MxUP::BM, MxUP::S, MxUP::NW>(p, (R / MxUP::BM + E) * p.ntiles, s);
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX gate/up: %s", hipGetErrorString(e));
   }
-  if (wd == nullptr) return MOE_OK;  // gate/up alone (recompute)
+  if (yp == nullptr) return MOE_OK;  // gate/up alone (recompute)
   {
     moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
     e = mx_quantize_rows(h, R, F, hq, hs, s);
@@ -583,10 +633,10 @@ moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const uint8_t
 }
 
 moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t* wg,
-                                   const bf16_t* wu, const bf16_t* wd, const int32_t* offsets,
-                                   const bf16_t* g, const bf16_t* u, const bf16_t* h,
-                                   const bf16_t* dyp, int E, int R, int d, int F, bf16_t* dg,
-                                   bf16_t* du, bf16_t* dxp, bf16_t* dwg, bf16_t* dwu,
+                                   const bf16_t* wu, const bf16_t* wd, const MxWeights* pw,
+                                   const int32_t* offsets, const bf16_t* g, const bf16_t* u,
+                                   const bf16_t* h, const bf16_t* dyp, int E, int R, int d, int F,
+                                   bf16_t* dg, bf16_t* du, bf16_t* dxp, bf16_t* dwg, bf16_t* dwu,
                                    bf16_t* dwd) {
   const size_t need = moe_internal_mx_bwd_bytes(E, R, d, F);
   if (ctx->ws == nullptr || ctx->ws_bytes < need)
@@ -622,13 +672,20 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
   hipError_t e;
   {
     moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
-    e = mx_quantize_rows(dyp, R, d, dyq, dys, s);
-    if (e == hipSuccess) e = mx_quantize_rows(wd, E * F, d, wdq, wds, s);
-    if (e == hipSuccess) e = mx_quantize_rows(wg, E * d, F, wgq, wgs, s);
-    if (e == hipSuccess) e = mx_quantize_rows(wu, E * d, F, wuq, wus, s);
+    // dyp in both layouts from one read (rows for the down dgrad, expert
+    // column blocks for the down wgrad)
+    e = mx_quantize_both(dyp, R, d, offsets, 0, E, ytq, yts, kp, dyq, dys, s);
+    if (pw) {
+      wdq = (uint8_t*)pw->bdq; wds = (uint8_t*)pw->bds;
+      wgq = (uint8_t*)pw->bgq; wgs = (uint8_t*)pw->bgs;
+      wuq = (uint8_t*)pw->buq; wus = (uint8_t*)pw->bus;
+    } else {
+      if (e == hipSuccess) e = mx_quantize_rows(wd, E * F, d, wdq, wds, s);
+      if (e == hipSuccess) e = mx_quantize_rows(wg, E * d, F, wgq, wgs, s);
+      if (e == hipSuccess) e = mx_quantize_rows(wu, E * d, F, wuq, wus, s);
+    }
     if (e == hipSuccess) e = mx_quantize_cols(xp, R, d, offsets, 0, E, xtq, xts, kp, s);
     if (e == hipSuccess) e = mx_quantize_cols(h, R, F, offsets, 0, E, htq, hts, kp, s);
-    if (e == hipSuccess) e = mx_quantize_cols(dyp, R, d, offsets, 0, E, ytq, yts, kp, s);
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise: %s", hipGetErrorString(e));
   }
   mx_kbase_kernel<<<1, 1024, 0, s>>>(offsets, E, kbase);
@@ -657,10 +714,8 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
   }
   {
     moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
-    e = mx_quantize_rows(dg, R, F, dgq, dgs, s);
-    if (e == hipSuccess) e = mx_quantize_rows(du, R, F, duq, dus, s);
-    if (e == hipSuccess) e = mx_quantize_cols(dg, R, F, offsets, 0, E, gtq, gts, kp, s);
-    if (e == hipSuccess) e = mx_quantize_cols(du, R, F, offsets, 0, E, utq, uts, kp, s);
+    e = mx_quantize_both(dg, R, F, offsets, 0, E, gtq, gts, kp, dgq, dgs, s);
+    if (e == hipSuccess) e = mx_quantize_both(du, R, F, offsets, 0, E, utq, uts, kp, duq, dus, s);
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise dg/du: %s", hipGetErrorString(e));
   }
   if (R > 0) {

@@ -160,10 +160,17 @@ __global__ void permute_mx_kernel(const uint4* __restrict__ x, const int32_t* __
 // rows past n_g are zeros (code 0, scale byte 0).  The slice's group comes
 // from the padded group sizes: a closed form when every group has `urows`
 // rows (offsets null), else a shuffle scan by wave 0.
+// ROWS: the same read also yields the rowwise layout (rcodes [rows, cols],
+// rscales [rows, cols/32], as mx_rows_kernel writes them).  A 32-column
+// block of a row is the 16-byte chunks of four consecutive lanes in the
+// staging loads, so its amax is two shuffles away; each lane encodes and
+// stores its own eight codes.
 constexpr int kColTile = 128;
+template <bool ROWS>
 __global__ void __launch_bounds__(256) mx_cols_kernel(
     const bf16_t* __restrict__ src, int rows, int cols, const int32_t* __restrict__ offsets,
-    int urows, int G, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad_ld) {
+    int urows, int G, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, int kpad_ld,
+    uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[128 * kColTile];
   __shared__ int sh[4];
   const int tid = threadIdx.x;
@@ -229,6 +236,40 @@ __global__ void __launch_bounds__(256) mx_cols_kernel(
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) reinterpret_cast<uint4*>(tile)[tid + 256 * j] = v[j];
+    if (ROWS) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = tid + 256 * j;
+        const int row = i >> 4, col = c0 + (i & 15) * 8;
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        float f[8];
+        float amax = 0.f;
+        bool nan = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f[2 * q] = bf_lo(w[q]);
+          f[2 * q + 1] = bf_hi(w[q]);
+          amax = fmaxf(amax, fmaxf(fabsf(f[2 * q]), fabsf(f[2 * q + 1])));
+          nan |= __builtin_isunordered(f[2 * q], f[2 * q + 1]);
+        }
+        // lanes 4m .. 4m+3 hold the block's four chunks (every lane takes part)
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        const int sb = mx_scale_byte(amax);
+        const float inv = pow2_neg(sb - 127);
+        uint32_t c0w = e4m3x4_finite(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+        uint32_t c1w = e4m3x4_finite(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+        if (nan) {
+          c0w = e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+          c1w = e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+        }
+        if (row < nvalid && col < cols) {
+          const size_t r = (size_t)(r0 + row);
+          *reinterpret_cast<uint2*>(rcodes + r * cols + col) = make_uint2(c0w, c1w);
+          if ((i & 3) == 0) rscales[r * (cols / 32) + col / 32] = (uint8_t)sb;
+        }
+      }
+    }
   }
   __syncthreads();
   // thread -> (column cl, row half h): blocks 2h and 2h+1 of the column
@@ -296,8 +337,18 @@ hipError_t mx_quantize_cols(const void* src, int rows, int cols, const int32_t* 
   // bound on the padded slices: sum_g ceil(n_g / 128) <= rows / 128 + groups
   const int yb = rows / 128 + groups + 1;
   dim3 grid((cols + kColTile - 1) / kColTile, yb);
-  mx_cols_kernel<<<grid, 256, 0, s>>>((const bf16_t*)src, rows, cols, offsets, urows, groups, codes,
-                                      scales, kpad_ld);
+  mx_cols_kernel<false><<<grid, 256, 0, s>>>((const bf16_t*)src, rows, cols, offsets, urows, groups,
+                                             codes, scales, kpad_ld, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t mx_quantize_both(const void* src, int rows, int cols, const int32_t* offsets, int urows,
+                            int groups, uint8_t* codes, uint8_t* scales, int kpad_ld,
+                            uint8_t* rcodes, uint8_t* rscales, hipStream_t s) {
+  const int yb = rows / 128 + groups + 1;
+  dim3 grid((cols + kColTile - 1) / kColTile, yb);
+  mx_cols_kernel<true><<<grid, 256, 0, s>>>((const bf16_t*)src, rows, cols, offsets, urows, groups,
+                                            codes, scales, kpad_ld, rcodes, rscales);
   return hipGetLastError();
 }
 
@@ -356,5 +407,34 @@ extern "C" moe_status moe_mx_quantize(moe_ctx* ctx, const void* src_bf16, int ro
                          codes, scales_e8m0, kpad_ld, ctx->stream);
   }
   if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "moe_mx_quantize: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_mx_quantize_both(moe_ctx* ctx, const void* src_bf16, int rows, int cols,
+                                           const int32_t* group_offsets, int groups,
+                                           uint8_t* codes_cols, uint8_t* scales_cols, int kpad_ld,
+                                           uint8_t* codes_rows, uint8_t* scales_rows) {
+  MOE_CHECK_CTX(ctx);
+  MOE_REQUIRE(ctx, rows >= 0 && cols >= 32 && cols % 32 == 0, "moe_mx_quantize_both: bad shape");
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, src_bf16, rows == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, codes_cols, rows == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, codes_rows, rows == 0);
+  MOE_REQUIRE(ctx, rows == 0 || (scales_cols != nullptr && scales_rows != nullptr),
+              "moe_mx_quantize_both: scales are null");
+  if (rows == 0) return MOE_OK;
+  MOE_REQUIRE(ctx, groups >= 1 && groups <= 1024, "moe_mx_quantize_both: 1 <= groups <= 1024");
+  MOE_REQUIRE(ctx, group_offsets != nullptr || groups == 1,
+              "moe_mx_quantize_both: group_offsets is null with groups > 1");
+  MOE_REQUIRE(ctx, kpad_ld % 128 == 0 && kpad_ld >= mx_kpad_bound(rows, groups) - 127,
+              "moe_mx_quantize_both: kpad_ld %d too small or not a multiple of 128", kpad_ld);
+  MOE_REQUIRE_DISJOINT(ctx, "moe_mx_quantize_both", {codes_cols, (size_t)cols * kpad_ld, "codes_cols"},
+                       {scales_cols, (size_t)cols * (kpad_ld / 32), "scales_cols"},
+                       {codes_rows, (size_t)rows * cols, "codes_rows"},
+                       {scales_rows, (size_t)rows * cols / 32, "scales_rows"});
+  moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
+  const hipError_t e = mx_quantize_both(src_bf16, rows, cols, group_offsets, group_offsets ? 0 : rows,
+                                        groups, codes_cols, scales_cols, kpad_ld, codes_rows,
+                                        scales_rows, ctx->stream);
+  if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "moe_mx_quantize_both: %s", hipGetErrorString(e));
   return MOE_OK;
 }
