@@ -533,7 +533,9 @@ def dense_summary(cfg, esz, flops, ms):
 
 def mx_leg(steps, warmup, bf16_ref=True):
     """Time the MXFP8 grouped experts (quantisation included) forward+backward
-    on the pre-routed 16-expert workload."""
+    on the pre-routed 16-expert workload: each step quantises the weights
+    once into a pack (both layouts) and runs the forward and the backward
+    on it, as the layer does."""
     import torch
 
     import moe_inputs as mi
@@ -551,11 +553,13 @@ def mx_leg(steps, warmup, bf16_ref=True):
               dw_down=z(E, F, d))
     ctx = moe.context(0)
     ctx.ensure_mx_workspace(E, R, d, F)
+    pack = moe.MxWeightPack(torch.empty(moe.moe_mx_weight_pack_size(E, d, F), dtype=torch.uint8, device=dev),
+                            E, d, F)
 
     def step():
-        moe.moe_grouped_ffn_fwd(g["xp"], g["wg"], g["wu"], g["wd"], off, fo, mxfp8=True)
-        moe.moe_grouped_ffn_bwd(g["xp"], g["wg"], g["wu"], g["wd"], off, fo["g"], fo["u"], fo["h"],
-                                g["dyp"], bo, mxfp8=True)
+        moe.moe_mx_quantize_weights(g["wg"], g["wu"], g["wd"], pack)
+        moe.moe_grouped_ffn_fwd_mxp(pack, off, xp=g["xp"], out=fo)
+        moe.moe_grouped_ffn_bwd_mxp(g["xp"], pack, off, fo["g"], fo["u"], fo["h"], g["dyp"], bo)
 
     gpu_ms, wall, prof = time_steps(ctx, step, steps, warmup)
     roof, agg = gemm_summary(prof, R * d * F, PEAK_FP8_TFLOPS)
