@@ -332,14 +332,38 @@ def smi_snapshot():
     reason they could not be read."""
     import subprocess
 
+    out = {}
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True,
                            text=True, timeout=30)
         data = json.loads(r.stdout)
         card = next(iter(v for k, v in sorted(data.items()) if k.startswith("card")))
-        return {k: v for k, v in card.items() if "clk" in k.lower() or "power" in k.lower()}
+        out = {k: v for k, v in card.items() if "clk" in k.lower() or "power" in k.lower()}
     except Exception as exc:  # reported, never fatal: the timing does not depend on it
-        return {"error": f"{type(exc).__name__}: {exc}"[:200]}
+        out["error"] = f"{type(exc).__name__}: {exc}"[:200]
+    if not any("power" in k.lower() for k in out):
+        # rocm-smi reports no package power on some systems: ask amd-smi
+        try:
+            r = subprocess.run(["amd-smi", "metric", "--power", "--json"], capture_output=True, text=True,
+                               timeout=30)
+            data = json.loads(r.stdout)
+            gpu = data[0] if isinstance(data, list) else data
+            if isinstance(gpu, dict) and isinstance(gpu.get("gpu_data"), list):
+                gpu = gpu["gpu_data"][0]
+
+            def flat(d, pre=""):
+                for k, v in d.items():
+                    if isinstance(v, dict) and set(v) >= {"value", "unit"}:
+                        yield pre + k, f"{v['value']} {v['unit']}"
+                    elif isinstance(v, dict):
+                        yield from flat(v, pre + k + ".")
+                    elif k != "gpu":
+                        yield pre + k, v
+            pw = {k: v for k, v in flat(gpu.get("power", gpu))}
+            out.update({"amd-smi " + k: v for k, v in pw.items()} or {"power": "not reported by amd-smi"})
+        except Exception as exc:
+            out["power_error"] = f"{type(exc).__name__}: {exc}"[:200]
+    return out
 
 
 def gemm_summary(prof, unit, peak):
