@@ -79,8 +79,13 @@ def test_router_logits(moe, dtype, T, d, E):
 
 
 # ------------------------------------------------------------------ rows
+# The row kernels have a guard-free form for k equal to the dispatch width
+# (2, 4, 8, 32) with rows of whole lane passes: bf16 top-4 d=2048, fp32 top-2
+# d=2048 (also the permute's), bf16 top-8 d=1024 and top-32 d=512 take it;
+# the ragged widths (d=264, fp32 d=128) take the guarded form.
 @pytest.mark.parametrize("dtype,T,d,E,k", [("fp32", 256, 128, 8, 2), ("bf16", 333, 264, 16, 4),
-                                           ("bf16", 1000, 2048, 8, 4)])
+                                           ("bf16", 1000, 2048, 8, 4), ("fp32", 300, 2048, 8, 2),
+                                           ("bf16", 200, 1024, 16, 8), ("bf16", 100, 512, 32, 32)])
 def test_permute_combine_and_backward(moe, dtype, T, d, E, k):
     rng = np.random.default_rng(T)
     c = mi.layer_inputs(mi.config("tiny", T=T, d=d, E=E, k=k, dtype=dtype, x_std=1.0), with_weights=False)
