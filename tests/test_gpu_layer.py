@@ -47,7 +47,14 @@ def topk_margin(logits, k):
 @pytest.mark.parametrize("name,over", [("tiny", {}),
                                        ("tiny", dict(dtype="bf16", T=700, E=16, k=4, x_std=1.0)),
                                        ("tiny", dict(dtype="bf16", T=1000, d=256, E=8, k=2, F=320,
-                                                     x_std=1.0, routing="zipf", n_dead=2))])
+                                                     x_std=1.0, routing="zipf", n_dead=2)),
+                                       # degenerate cases: one token; one expert, top-1 (a dense
+                                       # SwiGLU FFN, gate 1, no router gradient); every expert
+                                       # selected (k = E, the gates are the full softmax)
+                                       ("tiny", dict(T=1)),
+                                       ("tiny", dict(dtype="bf16", T=1, E=16, k=4, x_std=1.0)),
+                                       ("tiny", dict(T=130, E=1, k=1)),
+                                       ("tiny", dict(dtype="bf16", T=200, E=4, k=4, x_std=1.0))])
 def test_layer_end_to_end(moe, name, over):
     cfg = mi.config(name, **over)
     inp = mi.layer_inputs(cfg)
