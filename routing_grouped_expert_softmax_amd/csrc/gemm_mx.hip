@@ -437,9 +437,6 @@ __global__ void __launch_bounds__(1024) mx_kbase_kernel(const int32_t* __restric
 #ifndef MX_WU_CFG
 #define MX_WU_CFG MX_CFG
 #endif
-#ifndef MX_KRAGGED_BLOCKS_PER_CU
-#define MX_KRAGGED_BLOCKS_PER_CU 1
-#endif
 template <int BM_, int S_, int NW_>
 struct MxCfg {
   static constexpr int BM = BM_, S = S_, NW = NW_;
@@ -453,11 +450,16 @@ using MxWU = MxCfg<MX_WU_CFG>;
 
 template <int MODE, int BM, int S, int NW>
 hipError_t launch_mx(const MxParams& p, int blocks, hipStream_t s) {
-  // K-ragged: one block per CU, each walking its part of its XCD's
-  // cost-balanced range (the range set-up is paid once per CU; four blocks
-  // per CU, for some dynamic balancing of skewed tile costs, were 4-7 %
-  // slower with 128 experts of 2048 x 1024, both uniformly and Zipf-routed)
-  if (Traits<MODE>::kKRAGGED) blocks = std::min(blocks, MX_KRAGGED_BLOCKS_PER_CU * moe_host::device_cus());
+  // K-ragged: blocks walk their XCD's cost-balanced tile range.  With at
+  // least 16 tiles per CU, one block per CU (the range set-up paid once per
+  // CU: 4-7 % faster with 128 experts of 2048 x 1024, uniformly or
+  // Zipf-routed); with fewer, four blocks per CU, whose dynamic dispatch
+  // evens out skewed tile costs that fixed strides over a few tiles would
+  // not (16 Zipf-routed experts of 4096 x 1536: 14 % faster down wgrad).
+  if (Traits<MODE>::kKRAGGED) {
+    const int cus = moe_host::device_cus();
+    blocks = std::min(blocks, (blocks >= 16 * cus ? 1 : 4) * cus);
+  }
   blocks = (blocks + 7) / 8 * 8;
   grouped_gemm_mx_kernel<MODE, BM, S, NW><<<blocks, 64 * NW, 0, s>>>(p);
   return hipGetLastError();
