@@ -48,6 +48,34 @@ struct Work {
   int nt;        // n-tile
 };
 
+// Exclusive block scan of one count per thread over the first kThreads
+// threads (the others pass 0 and get the total): an inclusive scan within
+// each wave by shuffles, then the kThreads / 64 wave totals through LDS
+// (sh[0 .. kThreads/64)), two barriers.  Every thread of the block calls it.
+__device__ __forceinline__ void block_excl_scan(int local, int* sh, int& excl, int& total) {
+  const int tid = threadIdx.x;
+  const bool act = tid < kThreads;
+  const int lane = tid & 63, wid = tid >> 6;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  if (act && lane == 63) sh[wid] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int wv = 0; wv < kThreads / 64; ++wv) {
+    const int v = sh[wv];
+    tot += v;
+    if (wv < wid) before += v;
+  }
+  total = __builtin_amdgcn_readfirstlane(tot);
+  excl = act ? before + incl - local : total;
+  __syncthreads();
+}
+
 // Block-wide search of (expert, tile) for logical tile L in an M-ragged launch.
 // Returns false when L is past the real total.
 // Tile of a one-tile-per-block row-ragged launch: expert e owns
@@ -59,7 +87,6 @@ __device__ bool find_mtile(int E, const int32_t* offsets, int ntiles, int* sh, W
   // the first kThreads threads hold the experts; any further threads of a
   // larger block only take part in the barriers
   const int tid = threadIdx.x;
-  const bool act = tid < kThreads;
   const int per = (E + kThreads - 1) / kThreads;  // experts per thread (<= 4)
   int cnt[4], til[4];
   int local = 0;
@@ -75,17 +102,8 @@ __device__ bool find_mtile(int E, const int32_t* offsets, int ntiles, int* sh, W
     local += til[q];
   }
   // exclusive scan of `local` over the block
-  if (act) sh[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int add = act && tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    if (act) sh[tid] += add;
-    __syncthreads();
-  }
-  const int total = sh[kThreads - 1];
-  int run = act ? sh[tid] - local : total;
-  __syncthreads();
+  int run, total;
+  block_excl_scan(local, sh, run, total);
   // logical tile of this block: contiguous ranges per XCD
   const int per_xcd = (total + 7) / 8;
   const int slot = blockIdx.x >> 3;
@@ -230,7 +248,6 @@ struct MTileSched {
   __device__ void init(int E, const int32_t* offsets, int ntiles, int* sh) {
     // threads past kThreads (larger blocks) hold no experts
     const int tid = threadIdx.x;
-    const bool act = tid < kThreads;
     per = (E + kThreads - 1) / kThreads;  // <= 4
     int local = 0;
 #pragma unroll
@@ -244,17 +261,7 @@ struct MTileSched {
       }
       local += til[q];
     }
-    if (act) sh[tid] = local;
-    lds_barrier();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const int add = act && tid >= off ? sh[tid - off] : 0;
-      lds_barrier();
-      if (act) sh[tid] += add;
-      lds_barrier();
-    }
-    total = __builtin_amdgcn_readfirstlane(sh[kThreads - 1]);
-    run = act ? sh[tid] - local : total;
-    lds_barrier();
+    block_excl_scan(local, sh, run, total);
   }
   // Work of logical tile L < total.  The owning thread publishes it through
   // sh[kThreads..+2]; the caller keeps a barrier between one call's reads and
