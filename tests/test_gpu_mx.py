@@ -128,7 +128,8 @@ def _ffn_mx(moe, inp):
 
 
 @pytest.mark.parametrize("d,F,counts", [(256, 384, [300, 0, 129, 517]), (128, 128, [31, 1, 128, 256, 0]),
-                                        (512, 256, [1000])])
+                                        (512, 256, [1000]),
+                                        (128, 128, [(i * 37) % 23 for i in range(300)])])
 def test_mx_grouped_ffn(moe, d, F, counts):
     counts = np.array(counts)
     E, R = len(counts), int(counts.sum())
