@@ -529,12 +529,19 @@ def mx_expert_fwd(xp, offsets, wg, wu, wd):
     return dict(g=g, u=u, h=h, yp=yp)
 
 
-def mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, g, u, h):
+def mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, g, u, h, wgrad="mx"):
     """MXFP8 backward for upstream rows dyp, given the forward's bf16 g, u and
     h: dh = Q(dyp) Q(Wd^T) (blocks along d), dg/du from bf16 g, u in fp64
     then rounded to bf16, dxp = Q(dg) Q(Wg^T) + Q(du) Q(Wu^T) (blocks along F),
     and per expert dWd = Qc(h)^T Qc(dyp), dWg = Qc(xp)^T Qc(dg),
-    dWu = Qc(xp)^T Qc(du) with blocks along that expert's rows."""
+    dWu = Qc(xp)^T Qc(du) with blocks along that expert's rows.
+
+    wgrad="bf16": MXFP8 on the data-gradient products only (the fourth page
+    names MXFP8 for selected operations); the weight gradients are the fp64
+    products of the unquantised bf16 operands, dWd = h^T dyp, dWg = xp^T dg,
+    dWu = xp^T du per expert, the data gradients unchanged."""
+    if wgrad not in ("mx", "bf16"):
+        raise ValueError("wgrad must be 'mx' or 'bf16'")
     R, d = xp.shape
     E, _, F = wg.shape
     dyq = mx_rows(dyp)
@@ -553,8 +560,12 @@ def mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, g, u, h):
         if hi > lo:
             dxp[lo:hi] = dgq[lo:hi] @ mx_rows(wg[e]).T + duq[lo:hi] @ mx_rows(wu[e]).T
     off = np.asarray(offsets, dtype=np.int32)
-    xc, hc, yc = mx_cols(xp, off), mx_cols(h, off), mx_cols(dyp, off)
-    gc, uc = mx_cols(dg, off), mx_cols(du, off)
+    if wgrad == "mx":
+        xc, hc, yc = mx_cols(xp, off), mx_cols(h, off), mx_cols(dyp, off)
+        gc, uc = mx_cols(dg, off), mx_cols(du, off)
+    else:
+        f64 = lambda a: np.asarray(a, dtype=np.float64)  # noqa: E731
+        xc, hc, yc, gc, uc = f64(xp), f64(h), f64(dyp), dg, du
     dwg = np.zeros((E, d, F))
     dwu = np.zeros((E, d, F))
     dwd = np.zeros((E, F, d))

@@ -239,3 +239,73 @@ def test_mx_bwd_pin_detects_planted_wrong_axes(monkeypatch):
     monkeypatch.setattr(oracle, "mx_cols", lambda a, off: rows(a) if off is not None else cols(a, off))
     ok = run()
     assert not ok["dwg"] and not ok["dwu"] and not ok["dwd"] and ok["dxp"], ok
+
+
+def _brute_wgrads(offsets, xp, dyp, dg, du, h):
+    """Weight gradients by triple loops over the bf16 operands (fp64 sums)."""
+    E = len(offsets) - 1
+    R, d = xp.shape
+    F = dg.shape[1]
+    dwg = np.zeros((E, d, F))
+    dwu = np.zeros((E, d, F))
+    dwd = np.zeros((E, F, d))
+    for e in range(E):
+        for r in range(int(offsets[e]), int(offsets[e + 1])):
+            for a in range(d):
+                for b in range(F):
+                    dwg[e, a, b] += float(xp[r, a]) * float(dg[r, b])
+                    dwu[e, a, b] += float(xp[r, a]) * float(du[r, b])
+            for a in range(F):
+                for b in range(d):
+                    dwd[e, a, b] += float(h[r, a]) * float(dyp[r, b])
+    return dwg, dwu, dwd
+
+
+def _bf16_wgrad_case():
+    counts = [5, 0, 9, 3]
+    offsets, xp, wg, wu, wd, dyp = _ragged(23, 4, counts, 32, 32)
+    fw = oracle.mx_expert_fwd(xp, offsets, wg, wu, wd)
+    return offsets, xp, dyp, wg, wu, wd, fw
+
+
+def test_mx_bwd_bf16_wgrad_brute_force():
+    """wgrad='bf16': the data gradients are the all-MXFP8 chain's, bit for
+    bit; the weight gradients are the exact products of the bf16 operands
+    (checked by loops), and differ from the MX weight gradients."""
+    offsets, xp, dyp, wg, wu, wd, fw = _bf16_wgrad_case()
+    mx = oracle.mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, fw["g"], fw["u"], fw["h"])
+    bb = oracle.mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, fw["g"], fw["u"], fw["h"], wgrad="bf16")
+    for k in ("dg", "du", "dxp"):
+        assert np.array_equal(bb[k], mx[k]), k
+    dwg, dwu, dwd = _brute_wgrads(offsets, xp, dyp, bb["dg"], bb["du"], fw["h"])
+    for k, want in (("dwg", dwg), ("dwu", dwu), ("dwd", dwd)):
+        np.testing.assert_allclose(bb[k], want, rtol=1e-12, atol=1e-12, err_msg=k)
+        assert not np.array_equal(bb[k], mx[k]), k
+    assert not np.any(bb["dwg"][1]) and not np.any(bb["dwd"][1])  # the empty expert
+
+
+def test_mx_bwd_bf16_wgrad_pin_detects_planted_swap(monkeypatch):
+    """A planted mistake (dg and du swapped in the gate/up weight gradients)
+    fails the brute-force pin."""
+    offsets, xp, dyp, wg, wu, wd, fw = _bf16_wgrad_case()
+    ref = oracle.mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, fw["g"], fw["u"], fw["h"])
+    real = oracle.mx_expert_bwd
+
+    def planted(*a, **kw):
+        out = real(*a, **kw)
+        out["dwg"], out["dwu"] = out["dwu"], out["dwg"]
+        return out
+
+    monkeypatch.setattr(oracle, "mx_expert_bwd", planted)
+    bb = oracle.mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, fw["g"], fw["u"], fw["h"], wgrad="bf16")
+    dwg, _, _ = _brute_wgrads(offsets, xp, dyp, ref["dg"], ref["du"], fw["h"])
+    assert not np.allclose(bb["dwg"], dwg, rtol=1e-12, atol=1e-12)
+
+
+def test_mx_bwd_rejects_unknown_wgrad():
+    offsets, xp, dyp, wg, wu, wd, fw = _bf16_wgrad_case()
+    try:
+        oracle.mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, fw["g"], fw["u"], fw["h"], wgrad="fp8")
+    except ValueError:
+        return
+    raise AssertionError("unknown wgrad accepted")
