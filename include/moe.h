@@ -17,7 +17,9 @@
  *  - MXFP8 is supported for the expert GEMMs ([P1] 三).
  * Pages: [P1] "认识 Olmo-core 3" (meetcoding.cn/olmo-core/introduction.html);
  * [P2] the practitioner article at discosf.com/news/6174547; [P3] vibecoding.ru
- * news "Обучение MoE ускорилось: Olmo-core 3 дал прирост в 2,7 раза".
+ * news "Обучение MoE ускорилось: Olmo-core 3 дал прирост в 2,7 раза"; [P5] the
+ * bigchange.ai article on the Olmo-core 3 MoE training stack (its overview
+ * names MXFP8 for selected operations).
  *
  * Shapes: T tokens, d = d_model, E experts, k = top-k, F = d_ff, R = T*k rows.
  * Expert i/o is SwiGLU without biases:  y = (silu(x Wg) * (x Wu)) Wd.
@@ -228,6 +230,22 @@ moe_status moe_grouped_ffn_bwd_mxp(moe_ctx* ctx, const void* xp, const void* pac
                                    const void* u, const void* h, const void* dyp, int E, int R,
                                    int d, int F, void* dg, void* du, void* dxp, void* dw_gate,
                                    void* dw_up, void* dw_down);
+
+/* moe_grouped_ffn_bwd_mxp with MXFP8 on the data-gradient GEMMs only (MXFP8
+ * for selected operations, [P5] overview; [P1] 三): dh and dxp run
+ * on MXFP8 operands exactly as in moe_grouped_ffn_bwd_mxp (dg, du, dxp are
+ * the same bytes), while the three weight gradients run on the unquantised
+ * bf16 operands (xp, dg, du, h, dyp) with fp32 sums and one bf16 rounding, as
+ * MOE_BF16 computes them:
+ *   dWd[e] = h_e^T dyp_e;  dWg[e] = xp_e^T dg_e;  dWu[e] = xp_e^T du_e.
+ * Only the rowwise layouts of dyp, dg and du are quantised.  Arguments,
+ * layouts and errors as moe_grouped_ffn_bwd_mxp; the workspace is
+ * moe_mx_workspace_size's (which covers both backward forms). */
+moe_status moe_grouped_ffn_bwd_mxp_bf16w(moe_ctx* ctx, const void* xp, const void* pack,
+                                         size_t pack_bytes, const int32_t* offsets, const void* g,
+                                         const void* u, const void* h, const void* dyp, int E,
+                                         int R, int d, int F, void* dg, void* du, void* dxp,
+                                         void* dw_gate, void* dw_up, void* dw_down);
 
 /* Gate-weighted unpermute-combine: y[t] = sum_j gates[t,j] * yp[row_of[t,j]],
  * summed in slot order in fp32, rounded once.  [P2] 2.1 (return and

@@ -536,10 +536,11 @@ def mx_expert_bwd(xp, dyp, offsets, wg, wu, wd, g, u, h, wgrad="mx"):
     and per expert dWd = Qc(h)^T Qc(dyp), dWg = Qc(xp)^T Qc(dg),
     dWu = Qc(xp)^T Qc(du) with blocks along that expert's rows.
 
-    wgrad="bf16": MXFP8 on the data-gradient products only (the fourth page
-    names MXFP8 for selected operations); the weight gradients are the fp64
-    products of the unquantised bf16 operands, dWd = h^T dyp, dWg = xp^T dg,
-    dWu = xp^T du per expert, the data gradients unchanged."""
+    wgrad="bf16": MXFP8 on the data-gradient products only (the bigchange.ai
+    page's overview names MXFP8 for selected operations); the weight
+    gradients are the fp64 products of the unquantised bf16 operands,
+    dWd = h^T dyp, dWg = xp^T dg, dWu = xp^T du per expert, the data
+    gradients unchanged."""
     if wgrad not in ("mx", "bf16"):
         raise ValueError("wgrad must be 'mx' or 'bf16'")
     R, d = xp.shape

@@ -64,6 +64,8 @@ _SIGS = {
                                 _vp, _vp],
     "moe_grouped_ffn_bwd_mxp": [_vp, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int,
                                 _vp, _vp, _vp, _vp, _vp, _vp],
+    "moe_grouped_ffn_bwd_mxp_bf16w": [_vp, _vp, ctypes.c_size_t, _vp, _vp, _vp, _vp, _vp, _int, _int, _int,
+                                      _int, _vp, _vp, _vp, _vp, _vp, _vp],
 }
 EXPORTS = ["moe_create", "moe_destroy", "moe_set_stream", "moe_status_string", "moe_last_error",
            "moe_workspace_size", "moe_set_workspace", *_SIGS.keys(), "moe_profile_enable",
@@ -334,18 +336,28 @@ def moe_grouped_ffn_fwd_mxp(pack: MxWeightPack, offsets, xp=None, xp_codes=None,
 def moe_grouped_ffn_bwd_mxp(xp, pack: MxWeightPack, offsets, g, u, h, dyp, out=None):
     """MXFP8 grouped FFN backward with the weights from a pack; returns
     dict(dg, du, dxp, dw_gate, dw_up, dw_down)."""
+    return _ffn_bwd_pack("moe_grouped_ffn_bwd_mxp", xp, pack, offsets, g, u, h, dyp, out)
+
+
+def moe_grouped_ffn_bwd_mxp_bf16w(xp, pack: MxWeightPack, offsets, g, u, h, dyp, out=None):
+    """moe_grouped_ffn_bwd_mxp with MXFP8 on the data gradients only: dg, du
+    and dxp as there, the weight gradients from the bf16 operands."""
+    return _ffn_bwd_pack("moe_grouped_ffn_bwd_mxp_bf16w", xp, pack, offsets, g, u, h, dyp, out)
+
+
+def _ffn_bwd_pack(name, xp, pack, offsets, g, u, h, dyp, out):
     _need_cuda(xp, offsets, g, u, h, dyp, pack.data)
     R = xp.shape[0]
     E, d, F = pack.E, pack.d, pack.F
     dev = xp.device
-    context(dev.index).ensure_ffn_bwd_workspace(E, R, d, F, MOE_MXFP8)
+    context(dev.index).ensure_mx_workspace(E, R, d, F)
     if out is None:
         bf = torch.bfloat16
         out = dict(dg=torch.empty(R, F, dtype=bf, device=dev), du=torch.empty(R, F, dtype=bf, device=dev),
                    dxp=torch.empty(R, d, dtype=bf, device=dev), dw_gate=torch.empty(E, d, F, dtype=bf, device=dev),
                    dw_up=torch.empty(E, d, F, dtype=bf, device=dev),
                    dw_down=torch.empty(E, F, d, dtype=bf, device=dev))
-    context(dev.index).call("moe_grouped_ffn_bwd_mxp", _p(xp), _p(pack.data), pack.data.numel(), _p(offsets),
+    context(dev.index).call(name, _p(xp), _p(pack.data), pack.data.numel(), _p(offsets),
                             _p(g), _p(u), _p(h), _p(dyp), E, R, d, F, _p(out["dg"]), _p(out["du"]),
                             _p(out["dxp"]), _p(out["dw_gate"]), _p(out["dw_up"]), _p(out["dw_down"]))
     return out
@@ -719,7 +731,7 @@ def layer_forward(x, w_router, w_gate, w_up, w_down, k, buf: LayerBuffers, logit
 
 
 def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxfp8=False, shared=None,
-                   recompute=False, aux_alpha=None):
+                   recompute=False, aux_alpha=None, mx_wgrad=True):
     """combine_bwd -> route_bwd -> grouped FFN bwd -> permute_bwd (+router
     dgrad) -> router wgrad.  In bf16 the router's input-gradient term is
     folded into the gate/up dgrad (moe_grouped_ffn_bwd_router) and the
@@ -731,8 +743,11 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxf
     expert's too) are recomputed by the gate/up GEMM before they are used,
     so the forward need not keep them.  aux_alpha (the balance-loss weight)
     adds the gradient of that loss, taken at the router's scores with this
-    step's counts, to dx and dW_r (moe_aux_loss_bwd, moe_router_dense_bwd)."""
+    step's counts, to dx and dW_r (moe_aux_loss_bwd, moe_router_dense_bwd).
+    mx_wgrad=False (with mxfp8): MXFP8 on the data gradients only, the weight
+    gradients from the bf16 operands (moe_grouped_ffn_bwd_mxp_bf16w)."""
     r = buf.route
+    ffn_bwd_pack = moe_grouped_ffn_bwd_mxp if mx_wgrad else moe_grouped_ffn_bwd_mxp_bf16w
     if recompute:
         moe_permute(x, r["row_of"], buf.xp)
         if mxfp8:
@@ -752,8 +767,7 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxf
     else:
         moe_route_bwd(r["gates"], buf.dgates, buf.dlogits_sel)
     if mxfp8:
-        moe_grouped_ffn_bwd_mxp(buf.xp, buf.wpack, r["offsets"], buf.ffn["g"], buf.ffn["u"], buf.ffn["h"],
-                                buf.dyp, buf.bwd)
+        ffn_bwd_pack(buf.xp, buf.wpack, r["offsets"], buf.ffn["g"], buf.ffn["u"], buf.ffn["h"], buf.dyp, buf.bwd)
     else:
         moe_grouped_ffn_bwd(buf.xp, w_gate, w_up, w_down, r["offsets"], buf.ffn["g"], buf.ffn["u"],
                             buf.ffn["h"], buf.dyp, buf.bwd, router=(buf.dl_rows, w_router) if fold else None)
@@ -761,8 +775,8 @@ def layer_backward(dy, x, w_router, w_gate, w_up, w_down, buf: LayerBuffers, mxf
     if shared is not None:
         sh = buf.shared
         if mxfp8:
-            moe_grouped_ffn_bwd_mxp(x, sh["wpack"], sh["offsets"], sh["ffn"]["g"], sh["ffn"]["u"], sh["ffn"]["h"],
-                                    dy, sh["bwd"])
+            ffn_bwd_pack(x, sh["wpack"], sh["offsets"], sh["ffn"]["g"], sh["ffn"]["u"], sh["ffn"]["h"], dy,
+                         sh["bwd"])
         else:
             moe_grouped_ffn_bwd(x, *shared, sh["offsets"], sh["ffn"]["g"], sh["ffn"]["u"], sh["ffn"]["h"], dy,
                                 sh["bwd"])

@@ -785,7 +785,7 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
                                    const int32_t* offsets, const bf16_t* g, const bf16_t* u,
                                    const bf16_t* h, const bf16_t* dyp, int E, int R, int d, int F,
                                    bf16_t* dg, bf16_t* du, bf16_t* dxp, bf16_t* dwg, bf16_t* dwu,
-                                   bf16_t* dwd);
+                                   bf16_t* dwd, bool wgrad_bf16);
 size_t moe_internal_mx_pack_layout(int E, int d, int F, uint8_t* base, MxWeights* w);
 moe_status moe_internal_mx_quantize_weights(moe_ctx* ctx, const bf16_t* wg, const bf16_t* wu,
                                             const bf16_t* wd, int E, int d, int F, uint8_t* pack);
@@ -878,6 +878,144 @@ static hipError_t split_reduce(const float* part, int E, int S, size_t n, bf16_t
   return hipGetLastError();
 }
 
+// The two bf16 weight gradients (K-ragged over each expert's rows).  plan_*:
+// the XCD range table of the launch (planned: filled from the routed counts
+// before this launch, else equal tile counts per XCD); split_part and
+// split_voff: the split-K workspace (wgrad_split_bytes).
+static moe_status run_wgrad_down(moe_ctx* ctx, const void* h, const void* dyp, const int32_t* offsets,
+                                 int E, int R, int d, int F, void* dw_down, int32_t* plan_dn, bool planned,
+                                 float* split_part, int32_t* split_voff) {
+  const int dn_per_e = ((d + BN - 1) / BN) * ((F + CfgWD::BM - 1) / CfgWD::BM);
+  hipError_t e;
+  {
+    // down wgrad: dWd[e] = h_e^T dyp_e (M = F, N = d, K = rows of e)
+    Params p{};
+    p.a0 = (const bf16_t*)h;
+    p.lda = F;
+    p.b0 = (const bf16_t*)dyp;
+    p.ldb = d;
+    p.c0 = dw_down;
+    p.ldc = d;
+    p.c_gstride = (long long)F * d;
+    p.offsets = offsets;
+    p.E = E;
+    p.M = F;
+    p.N = d;
+    p.ntiles = (d + BN - 1) / BN;
+    p.mtiles = (F + CfgWD::BM - 1) / CfgWD::BM;
+    {
+      moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
+      const int S = wgrad_splits(E, R, E * p.ntiles * p.mtiles);
+      if (S == 1) {
+        p.xr = planned ? plan_dn : nullptr;
+        e = launch<WGRAD_DOWN, CfgWD::BM, CfgWD::S, CfgWD::BK, CfgWD::OCC, CfgWD::NW>(p, E * p.ntiles * p.mtiles,
+                                                                      ctx->stream);
+      } else {
+        split_offsets_kernel<<<(E * S + 256) / 256, 256, 0, ctx->stream>>>(offsets, E, S, split_voff);
+        xcd_plan_kernel<<<1, 512, 0, ctx->stream>>>(split_voff, E * S, dn_per_e, plan_dn);
+        Params q = p;
+        q.offsets = split_voff;
+        q.E = E * S;
+        q.xr = plan_dn;
+        q.c0 = split_part;
+        q.part = 1;
+        e = launch<WGRAD_DOWN, CfgWD::BM, CfgWD::S, CfgWD::BK, CfgWD::OCC, CfgWD::NW>(q, q.E * q.ntiles * q.mtiles,
+                                                                      ctx->stream);
+        if (e == hipSuccess) e = split_reduce(split_part, E, S, (size_t)F * d, (bf16_t*)dw_down, ctx->stream);
+      }
+    }
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down wgrad: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+static moe_status run_wgrad_up(moe_ctx* ctx, const void* xp, const void* dg, const void* du,
+                               const int32_t* offsets, int E, int R, int d, int F, void* dw_gate, void* dw_up,
+                               int32_t* plan_up, bool planned, float* split_part, int32_t* split_voff) {
+  const int up_per_e = ((F + 127) / 128) * ((d + CfgWU::BM - 1) / CfgWU::BM);
+  hipError_t e;
+  {
+    // gate/up wgrad: dWg[e] = xp_e^T dg_e, dWu[e] = xp_e^T du_e (M = d, N = F each)
+    Params p{};
+    p.a0 = (const bf16_t*)xp;
+    p.lda = d;
+    p.b0 = (const bf16_t*)dg;
+    p.b1 = (const bf16_t*)du;
+    p.ldb = F;
+    p.c0 = dw_gate;
+    p.c1 = dw_up;
+    p.ldc = F;
+    p.c_gstride = (long long)d * F;
+    p.offsets = offsets;
+    p.E = E;
+    p.M = d;
+    p.N = F;
+    p.ntiles = (F + 127) / 128;
+    p.mtiles = (d + CfgWU::BM - 1) / CfgWU::BM;
+    {
+      moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
+      const int S = wgrad_splits(E, R, E * p.ntiles * p.mtiles);
+      if (S == 1) {
+        p.xr = planned ? plan_up : nullptr;
+        e = launch<WGRAD_UP, CfgWU::BM, CfgWU::S, CfgWU::BK, CfgWU::OCC, CfgWU::NW>(p, E * p.ntiles * p.mtiles,
+                                                                    ctx->stream);
+      } else {
+        split_offsets_kernel<<<(E * S + 256) / 256, 256, 0, ctx->stream>>>(offsets, E, S, split_voff);
+        xcd_plan_kernel<<<1, 512, 0, ctx->stream>>>(split_voff, E * S, up_per_e, plan_up);
+        Params q = p;
+        q.offsets = split_voff;
+        q.E = E * S;
+        q.xr = plan_up;
+        q.c0 = split_part;
+        q.c1 = split_part + (size_t)E * S * d * F;
+        q.part = 1;
+        e = launch<WGRAD_UP, CfgWU::BM, CfgWU::S, CfgWU::BK, CfgWU::OCC, CfgWU::NW>(q, q.E * q.ntiles * q.mtiles,
+                                                                    ctx->stream);
+        if (e == hipSuccess) e = split_reduce(split_part, E, S, (size_t)d * F, (bf16_t*)dw_gate, ctx->stream);
+        if (e == hipSuccess)
+          e = split_reduce(split_part + (size_t)E * S * d * F, E, S, (size_t)d * F, (bf16_t*)dw_up,
+                           ctx->stream);
+      }
+    }
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up wgrad: %s", hipGetErrorString(e));
+  }
+  return MOE_OK;
+}
+
+size_t moe_internal_wgrads_bf16_bytes(int E, int R, int d, int F) {
+  size_t part = 0;
+  return kPlanBytes + wgrad_split_bytes(E, R, d, F, &part);
+}
+
+// Both bf16 weight gradients after data gradients computed elsewhere (the
+// MXFP8 backward with bf16 weight gradients): the XCD range tables come from
+// the routed counts (one small launch), then the two launches as in the bf16
+// backward.  ws: moe_internal_wgrads_bf16_bytes(E, R, d, F) bytes.
+moe_status moe_internal_wgrads_bf16(moe_ctx* ctx, const bf16_t* xp, const int32_t* offsets,
+                                    const bf16_t* dg, const bf16_t* du, const bf16_t* h,
+                                    const bf16_t* dyp, int E, int R, int d, int F, bf16_t* dwg,
+                                    bf16_t* dwu, bf16_t* dwd, void* ws) {
+  size_t part_bytes = 0;
+  wgrad_split_bytes(E, R, d, F, &part_bytes);
+  int32_t* plan_dn = (int32_t*)ws;
+  int32_t* plan_up = plan_dn + 16;
+  float* split_part = (float*)((char*)ws + kPlanBytes);
+  int32_t* split_voff = (int32_t*)((char*)ws + kPlanBytes + part_bytes);
+  const bool planned = R > 0;
+  if (planned) {
+    static_assert(CfgWD::BK == kWgradBK && CfgWU::BK == kWgradBK, "weight-gradient plans use kWgradBK");
+    const int dn_per_e = ((d + BN - 1) / BN) * ((F + CfgWD::BM - 1) / CfgWD::BM);
+    const int up_per_e = ((F + 127) / 128) * ((d + CfgWU::BM - 1) / CfgWU::BM);
+    xcd_plan_kernel<<<1, 512, 0, ctx->stream>>>(offsets, E, dn_per_e, plan_dn);
+    xcd_plan_kernel<<<1, 512, 0, ctx->stream>>>(offsets, E, up_per_e, plan_up);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "weight-gradient plan: %s", hipGetErrorString(e));
+  }
+  moe_status st = run_wgrad_down(ctx, h, dyp, offsets, E, R, d, F, dwd, plan_dn, planned, split_part, split_voff);
+  if (st != MOE_OK) return st;
+  return run_wgrad_up(ctx, xp, dg, du, offsets, E, R, d, F, dwg, dwu, plan_up, planned, split_part, split_voff);
+}
+
 static moe_status ffn_validate(moe_ctx* ctx, int E, int R, int d, int F, moe_dtype dtype,
                                const char* what) {
   MOE_REQUIRE(ctx, dtype == MOE_F32 || dtype == MOE_BF16 || dtype == MOE_MXFP8,
@@ -900,7 +1038,10 @@ moe_status moe_mx_workspace_size(moe_ctx* ctx, int E, int R, int d, int F, size_
   MOE_REQUIRE(ctx, bytes != nullptr, "bytes is null");
   moe_status st = ffn_validate(ctx, E, R, d, F, MOE_MXFP8, "moe_mx_workspace_size");
   if (st != MOE_OK) return st;
-  const size_t a = moe_internal_mx_fwd_bytes(E, R, d, F), b = moe_internal_mx_bwd_bytes(E, R, d, F);
+  // (the backward with bf16 weight gradients keeps their workspace after the
+  // MXFP8 layout)
+  const size_t a = moe_internal_mx_fwd_bytes(E, R, d, F),
+               b = moe_internal_mx_bwd_bytes(E, R, d, F) + moe_internal_wgrads_bf16_bytes(E, R, d, F);
   *bytes = a > b ? a : b;
   return MOE_OK;
 }
@@ -1136,7 +1277,42 @@ moe_status moe_grouped_ffn_bwd_mxp(moe_ctx* ctx, const void* xp, const void* pac
   return moe_internal_ffn_bwd_mx(ctx, (const bf16_t*)xp, nullptr, nullptr, nullptr, &w, offsets,
                                  (const bf16_t*)g, (const bf16_t*)u, (const bf16_t*)h,
                                  (const bf16_t*)dyp, E, R, d, F, (bf16_t*)dg, (bf16_t*)du,
-                                 (bf16_t*)dxp, (bf16_t*)dw_gate, (bf16_t*)dw_up, (bf16_t*)dw_down);
+                                 (bf16_t*)dxp, (bf16_t*)dw_gate, (bf16_t*)dw_up, (bf16_t*)dw_down, false);
+}
+
+moe_status moe_grouped_ffn_bwd_mxp_bf16w(moe_ctx* ctx, const void* xp, const void* pack,
+                                         size_t pack_bytes, const int32_t* offsets, const void* g,
+                                         const void* u, const void* h, const void* dyp, int E, int R,
+                                         int d, int F, void* dg, void* du, void* dxp, void* dw_gate,
+                                         void* dw_up, void* dw_down) {
+  MOE_CHECK_CTX(ctx);
+  moe_status st = ffn_validate(ctx, E, R, d, F, MOE_MXFP8, "moe_grouped_ffn_bwd_mxp_bf16w");
+  if (st != MOE_OK) return st;
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, xp, R == 0);
+  MOE_REQUIRE_PTR(ctx, offsets);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, g, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, u, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, h, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dyp, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dg, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, du, R == 0);
+  MOE_REQUIRE_PTR_OR_EMPTY(ctx, dxp, R == 0);
+  MOE_REQUIRE_PTR(ctx, dw_gate);
+  MOE_REQUIRE_PTR(ctx, dw_up);
+  MOE_REQUIRE_PTR(ctx, dw_down);
+  {
+    const size_t rf = (size_t)R * F * 2, w = (size_t)E * d * F * 2;
+    MOE_REQUIRE_DISJOINT(ctx, "moe_grouped_ffn_bwd_mxp_bf16w", {dg, rf, "dg"}, {du, rf, "du"},
+                         {dxp, (size_t)R * d * 2, "dxp"}, {dw_gate, w, "dw_gate"}, {dw_up, w, "dw_up"},
+                         {dw_down, w, "dw_down"});
+  }
+  MxWeights w;
+  st = pack_regions(ctx, pack, pack_bytes, E, d, F, "moe_grouped_ffn_bwd_mxp_bf16w", &w);
+  if (st != MOE_OK) return st;
+  return moe_internal_ffn_bwd_mx(ctx, (const bf16_t*)xp, nullptr, nullptr, nullptr, &w, offsets,
+                                 (const bf16_t*)g, (const bf16_t*)u, (const bf16_t*)h,
+                                 (const bf16_t*)dyp, E, R, d, F, (bf16_t*)dg, (bf16_t*)du,
+                                 (bf16_t*)dxp, (bf16_t*)dw_gate, (bf16_t*)dw_up, (bf16_t*)dw_down, true);
 }
 
 static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
@@ -1175,7 +1351,7 @@ static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
                                    (const bf16_t*)g, (const bf16_t*)u, (const bf16_t*)h,
                                    (const bf16_t*)dyp, E, R, d, F, (bf16_t*)dg, (bf16_t*)du,
                                    (bf16_t*)dxp, (bf16_t*)dw_gate, (bf16_t*)dw_up,
-                                   (bf16_t*)dw_down);
+                                   (bf16_t*)dw_down, false);
   if (dtype == MOE_F32)
     return moe_internal_ffn_bwd_f32(ctx, (const float*)xp, (const float*)w_gate,
                                     (const float*)w_up, (const float*)w_down, offsets,
@@ -1227,45 +1403,8 @@ static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down dgrad: %s", hipGetErrorString(e));
   }
-  {
-    // down wgrad: dWd[e] = h_e^T dyp_e (M = F, N = d, K = rows of e)
-    Params p{};
-    p.a0 = (const bf16_t*)h;
-    p.lda = F;
-    p.b0 = (const bf16_t*)dyp;
-    p.ldb = d;
-    p.c0 = dw_down;
-    p.ldc = d;
-    p.c_gstride = (long long)F * d;
-    p.offsets = offsets;
-    p.E = E;
-    p.M = F;
-    p.N = d;
-    p.ntiles = (d + BN - 1) / BN;
-    p.mtiles = (F + CfgWD::BM - 1) / CfgWD::BM;
-    {
-      moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_DOWN);
-      const int S = wgrad_splits(E, R, E * p.ntiles * p.mtiles);
-      if (S == 1) {
-        p.xr = planned ? plan_dn : nullptr;
-        e = launch<WGRAD_DOWN, CfgWD::BM, CfgWD::S, CfgWD::BK, CfgWD::OCC, CfgWD::NW>(p, E * p.ntiles * p.mtiles,
-                                                                      ctx->stream);
-      } else {
-        split_offsets_kernel<<<(E * S + 256) / 256, 256, 0, ctx->stream>>>(offsets, E, S, split_voff);
-        xcd_plan_kernel<<<1, 512, 0, ctx->stream>>>(split_voff, E * S, dn_per_e, plan_dn);
-        Params q = p;
-        q.offsets = split_voff;
-        q.E = E * S;
-        q.xr = plan_dn;
-        q.c0 = split_part;
-        q.part = 1;
-        e = launch<WGRAD_DOWN, CfgWD::BM, CfgWD::S, CfgWD::BK, CfgWD::OCC, CfgWD::NW>(q, q.E * q.ntiles * q.mtiles,
-                                                                      ctx->stream);
-        if (e == hipSuccess) e = split_reduce(split_part, E, S, (size_t)F * d, (bf16_t*)dw_down, ctx->stream);
-      }
-    }
-    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "down wgrad: %s", hipGetErrorString(e));
-  }
+  st = run_wgrad_down(ctx, h, dyp, offsets, E, R, d, F, dw_down, plan_dn, planned, split_part, split_voff);
+  if (st != MOE_OK) return st;
   if (R > 0) {
     // gate/up dgrad: dxp = dg Wg^T + du Wu^T (K = 2F in two segments)
     Params p{};
@@ -1292,52 +1431,8 @@ static moe_status ffn_bwd_impl(moe_ctx* ctx, const void* xp, const void* w_gate,
     }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up dgrad: %s", hipGetErrorString(e));
   }
-  {
-    // gate/up wgrad: dWg[e] = xp_e^T dg_e, dWu[e] = xp_e^T du_e (M = d, N = F each)
-    Params p{};
-    p.a0 = (const bf16_t*)xp;
-    p.lda = d;
-    p.b0 = (const bf16_t*)dg;
-    p.b1 = (const bf16_t*)du;
-    p.ldb = F;
-    p.c0 = dw_gate;
-    p.c1 = dw_up;
-    p.ldc = F;
-    p.c_gstride = (long long)d * F;
-    p.offsets = offsets;
-    p.E = E;
-    p.M = d;
-    p.N = F;
-    p.ntiles = (F + 127) / 128;
-    p.mtiles = (d + CfgWU::BM - 1) / CfgWU::BM;
-    {
-      moe_prof_scope ps(ctx, MOE_K_GEMM_WGRAD_UP);
-      const int S = wgrad_splits(E, R, E * p.ntiles * p.mtiles);
-      if (S == 1) {
-        p.xr = planned ? plan_up : nullptr;
-        e = launch<WGRAD_UP, CfgWU::BM, CfgWU::S, CfgWU::BK, CfgWU::OCC, CfgWU::NW>(p, E * p.ntiles * p.mtiles,
-                                                                    ctx->stream);
-      } else {
-        split_offsets_kernel<<<(E * S + 256) / 256, 256, 0, ctx->stream>>>(offsets, E, S, split_voff);
-        xcd_plan_kernel<<<1, 512, 0, ctx->stream>>>(split_voff, E * S, up_per_e, plan_up);
-        Params q = p;
-        q.offsets = split_voff;
-        q.E = E * S;
-        q.xr = plan_up;
-        q.c0 = split_part;
-        q.c1 = split_part + (size_t)E * S * d * F;
-        q.part = 1;
-        e = launch<WGRAD_UP, CfgWU::BM, CfgWU::S, CfgWU::BK, CfgWU::OCC, CfgWU::NW>(q, q.E * q.ntiles * q.mtiles,
-                                                                    ctx->stream);
-        if (e == hipSuccess) e = split_reduce(split_part, E, S, (size_t)d * F, (bf16_t*)dw_gate, ctx->stream);
-        if (e == hipSuccess)
-          e = split_reduce(split_part + (size_t)E * S * d * F, E, S, (size_t)d * F, (bf16_t*)dw_up,
-                           ctx->stream);
-      }
-    }
-    if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "gate/up wgrad: %s", hipGetErrorString(e));
-  }
-  return MOE_OK;
+  return run_wgrad_up(ctx, xp, dg, du, offsets, E, R, d, F, dw_gate, dw_up, plan_up, planned, split_part,
+                      split_voff);
 }
 
 moe_status moe_grouped_ffn_bwd(moe_ctx* ctx, const void* xp, const void* w_gate,

@@ -638,13 +638,24 @@ moe_status moe_internal_ffn_fwd_mx(moe_ctx* ctx, const bf16_t* xp, const uint8_t
   return MOE_OK;
 }
 
+size_t moe_internal_wgrads_bf16_bytes(int E, int R, int d, int F);  // gemm_bf16.hip
+moe_status moe_internal_wgrads_bf16(moe_ctx* ctx, const bf16_t* xp, const int32_t* offsets,
+                                    const bf16_t* dg, const bf16_t* du, const bf16_t* h,
+                                    const bf16_t* dyp, int E, int R, int d, int F, bf16_t* dwg,
+                                    bf16_t* dwu, bf16_t* dwd, void* ws);
+
+// wgrad_bf16: MXFP8 on the two data-gradient GEMMs only; dyp, dg and du are
+// quantised rowwise alone (no column layouts, no Xp or H columns) and the
+// three weight gradients run on the bf16 operands (the bf16 backward's
+// launches, their workspace after the MXFP8 layout).
 moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t* wg,
                                    const bf16_t* wu, const bf16_t* wd, const MxWeights* pw,
                                    const int32_t* offsets, const bf16_t* g, const bf16_t* u,
                                    const bf16_t* h, const bf16_t* dyp, int E, int R, int d, int F,
                                    bf16_t* dg, bf16_t* du, bf16_t* dxp, bf16_t* dwg, bf16_t* dwu,
-                                   bf16_t* dwd) {
-  const size_t need = moe_internal_mx_bwd_bytes(E, R, d, F);
+                                   bf16_t* dwd, bool wgrad_bf16) {
+  const size_t mx_need = moe_internal_mx_bwd_bytes(E, R, d, F);
+  const size_t need = mx_need + (wgrad_bf16 ? moe_internal_wgrads_bf16_bytes(E, R, d, F) : 0);
   if (ctx->ws == nullptr || ctx->ws_bytes < need)
     return fail(ctx, MOE_ERR_WORKSPACE, "MXFP8 backward: workspace %zu bytes < %zu needed",
                 ctx->ws_bytes, need);
@@ -680,7 +691,10 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
     moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
     // dyp in both layouts from one read (rows for the down dgrad, expert
     // column blocks for the down wgrad)
-    e = mx_quantize_both(dyp, R, d, offsets, 0, E, ytq, yts, kp, dyq, dys, s);
+    if (wgrad_bf16)
+      e = mx_quantize_rows(dyp, R, d, dyq, dys, s);
+    else
+      e = mx_quantize_both(dyp, R, d, offsets, 0, E, ytq, yts, kp, dyq, dys, s);
     if (pw) {
       wdq = (uint8_t*)pw->bdq; wds = (uint8_t*)pw->bds;
       wgq = (uint8_t*)pw->bgq; wgs = (uint8_t*)pw->bgs;
@@ -690,11 +704,13 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
       if (e == hipSuccess) e = mx_quantize_rows(wg, E * d, F, wgq, wgs, s);
       if (e == hipSuccess) e = mx_quantize_rows(wu, E * d, F, wuq, wus, s);
     }
-    if (e == hipSuccess) e = mx_quantize_cols(xp, R, d, offsets, 0, E, xtq, xts, kp, s);
-    if (e == hipSuccess) e = mx_quantize_cols(h, R, F, offsets, 0, E, htq, hts, kp, s);
+    if (!wgrad_bf16) {
+      if (e == hipSuccess) e = mx_quantize_cols(xp, R, d, offsets, 0, E, xtq, xts, kp, s);
+      if (e == hipSuccess) e = mx_quantize_cols(h, R, F, offsets, 0, E, htq, hts, kp, s);
+    }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise: %s", hipGetErrorString(e));
   }
-  mx_kbase_kernel<<<1, 1024, 0, s>>>(offsets, E, kbase);
+  if (!wgrad_bf16) mx_kbase_kernel<<<1, 1024, 0, s>>>(offsets, E, kbase);
   if (R > 0) {
     MxParams p{};
     p.a0 = dyq; p.sa0 = dys; p.lda = d;
@@ -706,7 +722,7 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
     e = launch_mx<DGRAD_DOWN, MxDD::BM, MxDD::S, MxDD::NW>(p, (R / MxDD::BM + E) * p.ntiles, s);
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX down dgrad: %s", hipGetErrorString(e));
   }
-  {
+  if (!wgrad_bf16) {
     MxParams p{};
     p.a0 = htq; p.sa0 = hts; p.lda = kp;
     p.b0 = ytq; p.sb0 = yts; p.ldb = kp;
@@ -720,8 +736,13 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
   }
   {
     moe_prof_scope ps(ctx, MOE_K_MX_QUANT);
-    e = mx_quantize_both(dg, R, F, offsets, 0, E, gtq, gts, kp, dgq, dgs, s);
-    if (e == hipSuccess) e = mx_quantize_both(du, R, F, offsets, 0, E, utq, uts, kp, duq, dus, s);
+    if (wgrad_bf16) {
+      e = mx_quantize_rows(dg, R, F, dgq, dgs, s);
+      if (e == hipSuccess) e = mx_quantize_rows(du, R, F, duq, dus, s);
+    } else {
+      e = mx_quantize_both(dg, R, F, offsets, 0, E, gtq, gts, kp, dgq, dgs, s);
+      if (e == hipSuccess) e = mx_quantize_both(du, R, F, offsets, 0, E, utq, uts, kp, duq, dus, s);
+    }
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX quantise dg/du: %s", hipGetErrorString(e));
   }
   if (R > 0) {
@@ -735,6 +756,8 @@ moe_status moe_internal_ffn_bwd_mx(moe_ctx* ctx, const bf16_t* xp, const bf16_t*
     e = launch_mx<DGRAD_UP, MxDU::BM, MxDU::S, MxDU::NW>(p, (R / MxDU::BM + E) * p.ntiles, s);
     if (e != hipSuccess) return fail(ctx, MOE_ERR_HIP, "MX gate/up dgrad: %s", hipGetErrorString(e));
   }
+  if (wgrad_bf16)
+    return moe_internal_wgrads_bf16(ctx, xp, offsets, dg, du, h, dyp, E, R, d, F, dwg, dwu, dwd, ws + mx_need);
   {
     MxParams p{};
     p.a0 = xtq; p.sa0 = xts; p.lda = kp;
