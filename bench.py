@@ -28,7 +28,8 @@ MXFP8 grouped experts (quantisation included) on 65536 pre-routed rows of a
 16-expert, d_model 4096, d_ff 1536 share, `mxfp8_layer` times the main
 workload end to end with quantise-on-permute and MXFP8 expert GEMMs (its
 tokens/s beside the bf16 layer's; for uniform128 also dense8 and zipf128,
-each beside its own bf16 layer), `shared_expert` times the main workload
+each beside its own bf16 layer; each also with MXFP8 on the data-gradient
+GEMMs only and bf16 weight gradients), `shared_expert` times the main workload
 with a shared expert of the routed width added, `recompute` times it with
 activation recompute (the bytes kept from forward to backward beside the
 throughput), and `routing_stats` times the
@@ -418,10 +419,11 @@ def cold_row_movers(ctx, g, buf, reps=10):
 
 
 def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=False, shared_F=0,
-              recompute=False, graph=False, cold_rows=False):
+              recompute=False, graph=False, cold_rows=False, mx_wgrad=True):
     """Time the whole layer forward+backward on one workload (and, with
     `with_stats`, the routing statistics on its last step's buffers).
-    mxfp8: quantise on the permute and run the MXFP8 expert GEMMs.
+    mxfp8: quantise on the permute and run the MXFP8 expert GEMMs (with
+    mx_wgrad False the weight gradients run on the bf16 operands).
     shared_F > 0: add a shared expert of that width."""
     import torch
 
@@ -445,7 +447,7 @@ def layer_leg(cfg, steps, warmup, keep_inputs=False, with_stats=False, mxfp8=Fal
         moe.layer_forward(g["x"], g["wr"], g["wg"], g["wu"], g["wd"], cfg.k, buf, override, mxfp8=mxfp8,
                           shared=shared)
         moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf, mxfp8=mxfp8,
-                           shared=shared, recompute=recompute)
+                           shared=shared, recompute=recompute, mx_wgrad=mx_wgrad)
 
     gpu_ms, wall, prof = time_steps(ctx, step, steps, warmup)
     counts = buf.route["counts"].cpu()
@@ -818,6 +820,12 @@ def main():
                 "vs_bf16_layer": round(ml["tokens_per_s"] / main_leg["tokens_per_s"], 4),
                 "grouped_gemm": magg, "roofline": mroof,
                 "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in ml["prof"].items()}}
+            # MXFP8 on the data-gradient GEMMs only, weight gradients in bf16
+            mw = layer_leg(cfg, args.mx_steps, 3, mxfp8=True, mx_wgrad=False)
+            result["mxfp8_layer"]["bf16_weight_gradients"] = {
+                "tokens_per_s": round(mw["tokens_per_s"], 1), "ms_per_step": round(mw["ms_per_step"], 4),
+                "vs_bf16_layer": round(mw["tokens_per_s"] / main_leg["tokens_per_s"], 4),
+                "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in mw["prof"].items()}}
             if cfg.name == "uniform128":
                 # the other two routed workloads end to end in MXFP8 beside bf16
                 others = {}
@@ -825,9 +833,12 @@ def main():
                     oc = mi.config(name)
                     ob = base if (name == "dense8" and base is not None) else layer_leg(oc, args.mx_steps, 3)
                     om = layer_leg(oc, args.mx_steps, 3, mxfp8=True)
+                    ow = layer_leg(oc, args.mx_steps, 3, mxfp8=True, mx_wgrad=False)
                     others[name] = {"bf16_tokens_per_s": round(ob["tokens_per_s"], 1),
                                     "mxfp8_tokens_per_s": round(om["tokens_per_s"], 1),
                                     "mxfp8_vs_bf16": round(om["tokens_per_s"] / ob["tokens_per_s"], 4),
+                                    "mxfp8_bf16_wgrad_tokens_per_s": round(ow["tokens_per_s"], 1),
+                                    "mxfp8_bf16_wgrad_vs_bf16": round(ow["tokens_per_s"] / ob["tokens_per_s"], 4),
                                     "mxfp8_expert_load": om["load"]}
                 result["mxfp8_layer"]["other_workloads"] = others
     if args.cpu_sample > 0:
