@@ -115,10 +115,10 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_mx_kernel(MxParams p)
   __shared__ int sh[kThreads + 4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane_in = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int wm = wv >> 1, wn = wv & 1;
 
   // ---------------------------------------------------------------- work
   // Row-ragged modes: one tile per block from eight equal-count XCD ranges.
@@ -135,6 +135,13 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_mx_kernel(MxParams p)
     if (!find_mtile<BM>(p.E, p.offsets, p.ntiles, sh, w0)) return;
   }
   for (int L = L0; L < end; L += nslot) {
+  // Blocks of the K-ragged modes walk several tiles.  The lane id is made
+  // opaque at each tile, so the per-lane offsets derived from it are formed
+  // again per tile rather than held through the epilogue: held, they pushed
+  // these kernels past their 256 registers, and the spill reloads inside
+  // the K loop waited for the next stage's loads.
+  int lane = lane_in;
+  if constexpr (TR::kKRAGGED) asm volatile("" : "+v"(lane));
   Work w = w0;
   int kbase = 0;  // K-ragged: first K byte of the expert in the padded layout
   if (TR::kKRAGGED) {
@@ -221,16 +228,19 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_mx_kernel(MxParams p)
     const int n = TR::kDUAL ? w.nt * 128 + (row & 127) : w.nt * BN + row;
     bsoff[j] = n * ldb_s;
   }
-  // one scale load per wave: A rows (wv < AS_TOT) or B rows
+  // One scale load per wave: 64 rows of A (wv < AS_TOT) or of B starting at
+  // the uniform row s_row0, lane l taking row s_row0 + l.  Its per-lane
+  // offset l * ld is formed at each issue from the lane id: kept across the
+  // K loop it was spilled in the K-ragged modes, and its reload before the
+  // load waited for every load in flight.
   [[maybe_unused]] const bool s_is_a = wv < TL::AS_TOT;
-  [[maybe_unused]] const int s_row = (s_is_a ? wv : wv - TL::AS_TOT) * 64 + lane;
+  [[maybe_unused]] int s_row0 = 0;
   if constexpr (TL::SPLIT) {
-    if (s_is_a) {
-      asoff[0] = (TR::kKRAGGED ? (w.m0 + s_row) : s_row) * lda_s;
-    } else {
-      const int n = TR::kDUAL ? w.nt * 128 + (s_row & 127) : w.nt * BN + s_row;
-      bsoff[0] = n * ldb_s;
-    }
+    const int sw = s_is_a ? wv : wv - TL::AS_TOT;
+    if (s_is_a)
+      s_row0 = (TR::kKRAGGED ? w.m0 : 0) + sw * 64;
+    else  // dual: rows 0..127 of the tile from matrix 0, 128..255 from matrix 1
+      s_row0 = TR::kDUAL ? w.nt * 128 + ((sw * 64) & 127) : w.nt * BN + sw * 64;
   }
 
   auto stage_ptr = [&](auto st) -> LDS_AS unsigned char* {
@@ -273,12 +283,18 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_mx_kernel(MxParams p)
                           (wv * TL::BS_INST + j) * 256),
            bsoff[j], kk / 32);
     if constexpr (TL::SPLIT) {
+      const int ld_s = s_is_a ? lda_s : ldb_s;
+      const int lid = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      // the row offset stays in the per-lane offset, which the buffer range
+      // check covers (the scalar offset is not checked): rows past the
+      // operand read as zero
+      const int voff = (s_row0 + lid) * ld_s;
       if (s_is_a)
-        dma4(rsa, (LDS_AS void*)(base + TL::A_BYTES + TL::B_BYTES + wv * 256), asoff[0], kk / 32);
+        dma4(rsa, (LDS_AS void*)(base + TL::A_BYTES + TL::B_BYTES + wv * 256), voff, kk / 32);
       else
         dma4(rsb_split,
              (LDS_AS void*)(base + TL::A_BYTES + TL::B_BYTES + TL::AS_BYTES + (wv - TL::AS_TOT) * 256),
-             bsoff[0], kk / 32);
+             voff, kk / 32);
     }
   };
 
