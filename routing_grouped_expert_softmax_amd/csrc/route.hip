@@ -282,73 +282,60 @@ __global__ void __launch_bounds__(256) expert_scan_kernel(int32_t* __restrict__ 
 // counts with a wave scan) and the stable ranks: the row of (t,j) with
 // e = topk[t,j] is offsets[e] + (rows of e in earlier blocks) + (earlier
 // tokens of this block that chose e).  Experts within a token are distinct,
-// so only earlier tokens matter.
+// so the earlier tokens that chose e are the earlier (token, slot) pairs
+// holding e.  One thread per (token, slot) pair of the block (kRankThreads
+// threads, four waves on the four SIMDs), each counting over the block's
+// earlier pairs read from LDS (the same address in every lane: a broadcast).
+constexpr int kRankThreads = 256;
 template <int KMAX>
-__global__ void __launch_bounds__(kTokBlock) rank_kernel(
+__global__ void __launch_bounds__(kRankThreads) rank_kernel(
     const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ block_counts, int nblk,
     const int32_t* __restrict__ counts, int T_, int E, int k, int32_t* __restrict__ offsets,
     int32_t* __restrict__ row_of, int32_t* __restrict__ src_tk) {
   __shared__ int offs[1025];
   __shared__ int sel[kTokBlock * KMAX];
   const int tid = threadIdx.x;
-  // offsets: each lane owns `per` consecutive experts (per <= 16)
-  const int per = (E + kTokBlock - 1) / kTokBlock;
-  int local = 0;
-  for (int q = 0; q < per; ++q) {
-    const int e = tid * per + q;
-    if (e < E) local += counts[e];
-  }
-  int incl = local;
-#pragma unroll
-  for (int off = 1; off < kTokBlock; off <<= 1) {
-    const int y = __shfl_up(incl, off, kTokBlock);
-    if (tid >= off) incl += y;
-  }
-  const int total = __shfl(incl, kTokBlock - 1, kTokBlock);
-  int run = incl - local;
-  for (int q = 0; q < per; ++q) {
-    const int e = tid * per + q;
-    if (e < E) {
-      offs[e] = run;
-      run += counts[e];
+  if (tid < 64) {
+    // offsets: each lane of wave 0 owns `per` consecutive experts (per <= 16)
+    const int per = (E + 63) / 64;
+    int local = 0;
+    for (int q = 0; q < per; ++q) {
+      const int e = tid * per + q;
+      if (e < E) local += counts[e];
     }
-  }
-  if (tid == 0) offs[E] = total;
-  const int tbase = blockIdx.x * kTokBlock;
-  const int t = tbase + tid;
-  const int ntok = min(kTokBlock, T_ - tbase);
+    int incl = local;
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j)
-    if (j < k) sel[tid * KMAX + j] = (tid < ntok) ? topk_idx[(size_t)t * k + j] : -1;
-  __syncthreads();
-  if (blockIdx.x == 0)
-    for (int e = tid; e <= E; e += kTokBlock) offsets[e] = offs[e];
-  if (tid >= ntok) return;
-  int mine[KMAX], rank[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    mine[j] = (j < k) ? sel[tid * KMAX + j] : -2;
-    rank[j] = 0;
-  }
-  for (int tp = 0; tp < tid; ++tp) {
-#pragma unroll
-    for (int jp = 0; jp < KMAX; ++jp) {
-      if (jp < k) {
-        const int o = sel[tp * KMAX + jp];
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) rank[j] += (o == mine[j]) ? 1 : 0;
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (tid >= off) incl += y;
+    }
+    const int total = __shfl(incl, 63, 64);
+    int run = incl - local;
+    for (int q = 0; q < per; ++q) {
+      const int e = tid * per + q;
+      if (e < E) {
+        offs[e] = run;
+        run += counts[e];
       }
     }
+    if (tid == 0) offs[E] = total;
   }
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
-      const int e = mine[j];
-      const int row = offs[e] + block_counts[(size_t)e * nblk + blockIdx.x] + rank[j];
-      const int flat = t * k + j;
-      row_of[flat] = row;
-      src_tk[row] = flat;
-    }
+  const int tbase = blockIdx.x * kTokBlock;
+  const int ntok = min(kTokBlock, T_ - tbase);
+  const int npair = ntok * k;  // pairs p = t_local * k + j of this block
+  for (int p = tid; p < npair; p += kRankThreads) sel[p] = topk_idx[(size_t)tbase * k + p];
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += kRankThreads) offsets[e] = offs[e];
+  for (int p = tid; p < npair; p += kRankThreads) {
+    const int tl = p / k;  // token within the block
+    const int e = sel[p];
+    int rank = 0;
+    for (int q = 0; q < tl * k; ++q) rank += (sel[q] == e) ? 1 : 0;
+    const int row = offs[e] + block_counts[(size_t)e * nblk + blockIdx.x] + rank;
+    const int flat = tbase * k + p;
+    row_of[flat] = row;
+    src_tk[row] = flat;
   }
 }
 
@@ -367,8 +354,8 @@ void launch_route(const float* logits, int T_, int E, int k, int32_t* topk_idx, 
     expert_scan_kernel<<<E, 256, 0, s>>>(block_counts, nblk, counts);
   }
   moe_prof_scope ps(ctx, MOE_K_RANK);
-  rank_kernel<KMAX><<<nblk, kTokBlock, 0, s>>>(topk_idx, block_counts, nblk, counts, T_, E, k,
-                                               offsets, row_of, src_tk);
+  rank_kernel<KMAX><<<nblk, kRankThreads, 0, s>>>(topk_idx, block_counts, nblk, counts, T_, E, k,
+                                                  offsets, row_of, src_tk);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int n, int v) {
