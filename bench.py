@@ -78,6 +78,25 @@ def row_bytes(name, T, d, k, F, E, esz=2):
     }.get(name)
 
 
+def routing_bytes(name, T, d, k, E, esz=2):
+    """Algorithmic HBM bytes per launch of the routing kernels: every tensor
+    the kernel needs read once and every output written once (int32 indices,
+    fp32 logits and gates; the router weight gradient's minimum reads x once,
+    although its expert-major walk gathers each token row k times)."""
+    nblk = (T + 63) // 64          # 64-token routing blocks
+    pair = T * k * 4               # one int32 or fp32 per (token, slot)
+    hist = E * nblk * 4            # per-block expert counts
+    return {
+        "router_logits": T * d * esz + d * E * esz + T * E * 4,
+        "topk_hist": T * E * 4 + 2 * pair + hist,
+        "expert_scan": 2 * hist + E * 4,
+        "rank": pair + hist + E * 4 + (E + 1) * 4 + 2 * pair,
+        # bf16 layer: gates, dgates, row_of in; dlogits_sel and the expert-row copy out
+        "route_bwd": 3 * pair + 2 * pair,
+        "router_wgrad": T * d * esz + 2 * pair + (E + 1) * 4 + d * E * esz,
+    }.get(name)
+
+
 def _code_only(text):
     """Source text without // comments (outside string literals), trailing
     blanks and empty lines: what the kernel is built from."""
@@ -727,6 +746,20 @@ def main():
                     rows[name]["frac_copy"] = round(gbs / copy_gbs, 3)
     if copies:
         rows["copy_peak_GB/s"] = copies
+    # routing kernels (scores, top-k + histogram, scan, ranks; the routing
+    # backward and the router weight gradient) against HBM, from the same run
+    routing = {}
+    if cfg.dtype == "bf16":
+        for name in ("router_logits", "topk_hist", "expert_scan", "rank", "route_bwd", "router_wgrad"):
+            if name in prof:
+                n, ms = prof[name]
+                nbytes = routing_bytes(name, cfg.T, cfg.d, cfg.k, cfg.E)
+                gbs = nbytes / (ms / n / 1e3) / 1e9
+                routing[name] = {"ms": round(ms / n, 4), "algorithmic_bytes": nbytes, "GB/s": round(gbs, 1),
+                                 "frac_hbm": round(gbs / PEAK_HBM_GBS, 3)}
+        if "router_logits" in routing:
+            tf = 2.0 * cfg.T * cfg.d * cfg.E / (routing["router_logits"]["ms"] / 1e3) / 1e12
+            routing["router_logits"].update({"TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)})
 
     # The timed steps: K replays of the whole step captured in one HIP graph
     # (outputs checked against the eager step), else K eager steps.
@@ -756,6 +789,7 @@ def main():
         "grouped_gemm": agg,
         "mfma_probe": probe,
         "row_movers": rows,
+        "routing_kernels": routing,
         "kernel_ms": {name: round(ms / n, 4) for name, (n, ms) in prof.items()},
         "expert_load": main_leg["load"],
         "timing": timing,
