@@ -4,7 +4,8 @@ recomputes g, u, h with the gate/up GEMM alone is checked two ways.
 
 * Against the CPU oracle: every gradient of the recomputing backward (and the
   shared expert's) within the dtype's bound — fp32 1e-4, bf16 2e-2, MXFP8
-  6e-2 — on the oracle's own chain for the same routing.
+  6e-2 — on the oracle's own chain for the same routing (MXFP8 both with
+  MXFP8 and with bf16 weight gradients).
 * Against the saving backward: bit-identical gradients, after the saved
   tensors are overwritten with NaN, so nothing stale can leak in.
 
@@ -43,6 +44,8 @@ def _grads(buf):
 
 
 def _setup(moe, cfg, inp, Fs, mx):
+    """mx: False (bf16/fp32), True (MXFP8, every GEMM) or "bf16w" (MXFP8
+    forward and data gradients, bf16 weight gradients)."""
     g = {k: inp[k].to(DEV) for k in ("x", "wr", "wg", "wu", "wd", "dy")}
     override = inp["logits"].to(DEV) if "logits" in inp else None
     shared, sw = None, None
@@ -50,15 +53,16 @@ def _setup(moe, cfg, inp, Fs, mx):
         sw = mi.shared_expert_weights(cfg, Fs)
         shared = tuple(sw[k].to(DEV) for k in ("wg_s", "wu_s", "wd_s"))
     dt = torch.float32 if cfg.dtype == "fp32" else torch.bfloat16
-    buf = moe.alloc_layer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, dt, DEV, mxfp8=mx, shared_F=Fs)
+    mxf = bool(mx)
+    buf = moe.alloc_layer(cfg.T, cfg.d, cfg.E, cfg.k, cfg.F, dt, DEV, mxfp8=mxf, shared_F=Fs)
 
     def fwd():
         moe.layer_forward(g["x"], g["wr"], g["wg"], g["wu"], g["wd"], cfg.k, buf, override,
-                          mxfp8=mx, shared=shared)
+                          mxfp8=mxf, shared=shared)
 
     def bwd(recompute):
-        moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf, mxfp8=mx,
-                           shared=shared, recompute=recompute)
+        moe.layer_backward(g["dy"], g["x"], g["wr"], g["wg"], g["wu"], g["wd"], buf, mxfp8=mxf,
+                           shared=shared, recompute=recompute, mx_wgrad=mx != "bf16w")
     return buf, fwd, bwd, sw
 
 
@@ -75,7 +79,8 @@ def _oracle_grads(cfg, inp, r, sw, mx):
     """The oracle's gradients of the layer (+ shared expert) for routing r:
     dx, dgates, dlogits, dW_r, the expert weight gradients and the shared
     expert's.  bf16/fp32: the plain fp64 definition; MXFP8: the oracle's MX
-    chain (each GEMM operand quantised where the GPU quantises it)."""
+    chain (each GEMM operand quantised where the GPU quantises it; with
+    mx == "bf16w" the weight gradients from the bf16 operands)."""
     x, wr, dy = mi.f32(inp["x"]), mi.f32(inp["wr"]), mi.f32(inp["dy"])
     wg, wu, wd = mi.f32(inp["wg"]), mi.f32(inp["wu"]), mi.f32(inp["wd"])
     ws = [mi.f32(sw[k]) for k in ("wg_s", "wu_s", "wd_s")] if sw is not None else None
@@ -93,14 +98,16 @@ def _oracle_grads(cfg, inp, r, sw, mx):
     fw = oracle.mx_expert_fwd(xp, r["offsets"], wg, wu, wd)
     dyp, dgates = oracle.combine_bwd(dy, fw["yp"], r["gates"], r["row_of"])
     dls = oracle.route_bwd(r["gates"], dgates)
-    bw = oracle.mx_expert_bwd(xp, oracle._bf16_round(dyp), r["offsets"], wg, wu, wd, fw["g"], fw["u"], fw["h"])
+    wgrad = "bf16" if mx == "bf16w" else "mx"
+    bw = oracle.mx_expert_bwd(xp, oracle._bf16_round(dyp), r["offsets"], wg, wu, wd, fw["g"], fw["u"], fw["h"],
+                              wgrad=wgrad)
     dx = oracle.permute_bwd(bw["dxp"], r["row_of"], r["topk_idx"], dls, wr)
     out.update(dgates=dgates, dlogits=dls, dw_router=oracle.router_wgrad(x, dls, r["topk_idx"], cfg.E),
                dw_gate=bw["dwg"], dw_up=bw["dwu"], dw_down=bw["dwd"])
     if ws is not None:
         one = np.array([0, cfg.T], dtype=np.int32)
         sf = oracle.mx_expert_fwd(x, one, *ws)
-        sb = oracle.mx_expert_bwd(x, dy, one, *ws, sf["g"], sf["u"], sf["h"])
+        sb = oracle.mx_expert_bwd(x, dy, one, *ws, sf["g"], sf["u"], sf["h"], wgrad=wgrad)
         dx = dx + sb["dxp"]
         out.update(s_dw_gate=sb["dwg"], s_dw_up=sb["dwu"], s_dw_down=sb["dwd"])
     out["dx"] = dx
@@ -111,7 +118,9 @@ CASES = [
     ("tiny", {}, 0, False),
     ("tiny", dict(dtype="bf16", T=700, E=16, k=4, x_std=1.0, routing="uniform"), 0, False),
     ("tiny", dict(dtype="bf16", T=1000, d=256, E=8, k=2, F=384, x_std=1.0, routing="zipf", n_dead=2), 256, False),
-    ("tiny", dict(dtype="bf16", T=512, d=256, E=8, k=2, F=256, x_std=1.0), 256, True)]
+    ("tiny", dict(dtype="bf16", T=512, d=256, E=8, k=2, F=256, x_std=1.0), 256, True),
+    ("tiny", dict(dtype="bf16", T=640, d=256, E=8, k=2, F=256, x_std=1.0, routing="zipf", n_dead=1), 256,
+     "bf16w")]
 
 
 @pytest.mark.parametrize("name,over,Fs,mx", CASES)
