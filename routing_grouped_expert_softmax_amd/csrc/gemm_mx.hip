@@ -358,6 +358,14 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_mx_kernel(MxParams p)
     };
     mstep(std::integral_constant<int, 0>{});
     mstep(std::integral_constant<int, 1>{});
+    // The empty asm takes every accumulator, so all MFMAs of this stage are
+    // issued before the next step's wait for its loads.  Without it the
+    // compiler moved them below that wait, and the wait had nothing to
+    // overlap (one load latency exposed per pair of steps).
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm)
+#pragma unroll
+      for (int sn = 0; sn < 4; ++sn) asm volatile("" : "+v"(acc[sm][sn]));
   };
 
   // ---------------------------------------------------------------- main loop
