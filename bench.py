@@ -213,6 +213,15 @@ def cpu_model():
     return None
 
 
+def quantise_per_step(prof, steps):
+    """MXFP8 quantiser launches per step and their summed time per step (the
+    weight pack, H rowwise, dYp, dG, dU; kernel_ms holds the per-launch mean)."""
+    if "mx_quantize" not in prof:
+        return None
+    n, ms = prof["mx_quantize"]
+    return {"launches": round(n / steps, 2), "ms": round(ms / steps, 4)}
+
+
 def time_steps(ctx, step, steps, warmup):
     """Run `warmup` untimed steps, then time exactly `steps` steps between two
     synchronisations with events on the current stream, per-kernel HIP events
@@ -853,13 +862,15 @@ def main():
                 "tokens_per_s": round(ml["tokens_per_s"], 1), "ms_per_step": round(ml["ms_per_step"], 4),
                 "vs_bf16_layer": round(ml["tokens_per_s"] / main_leg["tokens_per_s"], 4),
                 "grouped_gemm": magg, "roofline": mroof,
-                "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in ml["prof"].items()}}
+                "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in ml["prof"].items()},
+                "quantise_per_step": quantise_per_step(ml["prof"], args.mx_steps)}
             # MXFP8 on the data-gradient GEMMs only, weight gradients in bf16
             mw = layer_leg(cfg, args.mx_steps, 3, mxfp8=True, mx_wgrad=False)
             result["mxfp8_layer"]["bf16_weight_gradients"] = {
                 "tokens_per_s": round(mw["tokens_per_s"], 1), "ms_per_step": round(mw["ms_per_step"], 4),
                 "vs_bf16_layer": round(mw["tokens_per_s"] / main_leg["tokens_per_s"], 4),
-                "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in mw["prof"].items()}}
+                "kernel_ms": {n: round(ms / c, 4) for n, (c, ms) in mw["prof"].items()},
+                "quantise_per_step": quantise_per_step(mw["prof"], args.mx_steps)}
             if cfg.name == "uniform128":
                 # the other two routed workloads end to end in MXFP8 beside bf16
                 others = {}
