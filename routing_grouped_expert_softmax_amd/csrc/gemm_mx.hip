@@ -285,9 +285,7 @@ __global__ void __launch_bounds__(64 * NW, 1) grouped_gemm_mx_kernel(MxParams p)
     if constexpr (TL::SPLIT) {
       const int ld_s = s_is_a ? lda_s : ldb_s;
       const int lid = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-      // the row offset stays in the per-lane offset, which the buffer range
-      // check covers (the scalar offset is not checked): rows past the
-      // operand read as zero
+      // rows past the operand fail the buffer range check and read as zero
       const int voff = (s_row0 + lid) * ld_s;
       if (s_is_a)
         dma4(rsa, (LDS_AS void*)(base + TL::A_BYTES + TL::B_BYTES + wv * 256), voff, kk / 32);
