@@ -11,7 +11,8 @@
 //    64 x 128 sub-tile of 32x32 MFMA tiles (128 accumulator registers, at
 //    most 256 registers per wave).  The forward GEMMs and the wgrads run
 //    128 x 256 x 32 tiles, four waves, two resident blocks per CU; the dgrads
-//    run 256 x 256 x 64 tiles, eight waves, one block per CU (see the tile
+//    run 288 x 256 x 64 tiles, eight waves, one block per CU: 256 rows as
+//    above plus a 32-row strip of one 32x32 MFMA tile per wave (see the tile
 //    configurations below).
 //  * Tiles move HBM -> LDS with buffer loads that write LDS directly (16 bytes
 //    per lane), S stages deep, one static LDS array per stage, explicit vmcnt
@@ -112,10 +113,16 @@ __device__ __forceinline__ int kc_half(int row, int h) { return h ^ ((row >> 3) 
 __device__ __forceinline__ int swz_mn(int k) { return (k & 3) << 2; }
 
 // Tile geometry of one pipeline stage.
+// BM is a multiple of 64 (BMAIN rows, NW/2 waves down) plus an optional
+// 32-row strip (XR = 32): the strip's 32 x 256 outputs are spread over the NW
+// waves as one 32x32 MFMA tile each, so an expert of up to 2 * BM rows takes
+// two row tiles where 256-row tiles would need a third, nearly empty one.
 template <int MODE, int BM, int BK, int NW = 4>
 struct Tile {
   using TR = Traits<MODE>;
-  static constexpr int WM = BM / (NW / 2);  // wave tile rows (M): NW/2 waves down, 2 across
+  static constexpr int XR = BM % 64;        // rows of the extra strip (0 or 32)
+  static constexpr int BMAIN = BM - XR;
+  static constexpr int WM = BMAIN / (NW / 2);  // wave tile rows (M): NW/2 waves down, 2 across
   static constexpr int SM = WM / 32;  // 32-row subtiles per wave
   static constexpr int GROUP = 16 * BK;     // bytes of one 8-row K-contiguous group
   static constexpr int SLICES = BK / 16;    // 16-deep K slices per stage
@@ -123,7 +130,8 @@ struct Tile {
   static constexpr int A_BYTES = BM * BK * 2;
   static constexpr int B_BYTES = BN * BK * 2;
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_INST = A_BYTES / 1024 / NW;  // 1 KiB direct loads per wave
+  static constexpr int A_INST = BMAIN * BK * 2 / 1024 / NW;  // 1 KiB direct loads per wave
+  static constexpr int XA_INST = XR * BK * 2 / 1024;  // strip loads: one each for waves 0..XA_INST-1
   static constexpr int B_INST = B_BYTES / 1024 / NW;
   static constexpr int A_PITCH = TR::kA_KCONTIG ? 128 : BM * 2;  // LDS row pitch (bytes)
   // B: K-contiguous [256][64]; N-contiguous [64][256]; dual: two [64][128]
@@ -136,6 +144,9 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   using TR = Traits<MODE>;
   using TL = Tile<MODE, BM, BK, NW>;
   constexpr int SM = TL::SM;
+  static_assert(TL::XR == 0 || (TL::XR == 32 && S == 2 && NW == 8 && TL::GPI == 1 && TR::kA_KCONTIG &&
+                                TR::kB_KCONTIG && !TR::kKRAGGED && !TR::kDUAL && TL::XA_INST <= NW),
+                "the 32-row strip is built for the eight-wave, two-stage, K-contiguous dgrad tiles");
   // One LDS array per pipeline stage: distinct objects let the compiler see
   // that fragment reads of one stage never alias the loads landing in another.
   __shared__ __attribute__((aligned(1024))) unsigned char lds0[TL::STAGE];
@@ -148,7 +159,7 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   __shared__ float rrow[MODE == DGRAD_UP ? BM : 1];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
+  const int lane0 = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -167,12 +178,12 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
         if (wv == 0) {
           int f0, f1;
           kragged_xcd_range<kWgradBK>(p.offsets, p.E, p.xr_pe0, bid, f0, f1);
-          if (lane == 0) {
+          if (lane0 == 0) {
             p.xr_out0[2 * bid] = f0;
             p.xr_out0[2 * bid + 1] = f1;
           }
           kragged_xcd_range<kWgradBK>(p.offsets, p.E, p.xr_pe1, bid, f0, f1);
-          if (lane == 0) {
+          if (lane0 == 0) {
             p.xr_out1[2 * bid] = f0;
             p.xr_out1[2 * bid + 1] = f1;
           }
@@ -223,6 +234,11 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   for (int L = L0; L < end; L += nslot) {
   // the previous tile's epilogue has finished with the LDS stage buffers
   if (L != L0) lds_barrier();
+  // With the strip, registers are short: the lane id is made opaque per tile
+  // so lane-derived addresses are recomputed in each tile, not held (and
+  // spilled) across the whole tile loop.
+  int lane = lane0;
+  if constexpr (TL::XR > 0) asm volatile("" : "+v"(lane));
   Work w;
   if (TR::kKRAGGED) {
     // expert-major, then m-tile, then n-tile (n fastest: the blocks of one
@@ -321,6 +337,15 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
       boff[j] = (k * p.ldb + w.nt * BN + ((pc ^ swz_mn(k)) << 3)) * (int)esz;
     }
   }
+  // The strip's A rows (BMAIN..BM-1): 1 KiB instruction A_INST * NW + wave,
+  // one for each of the first XA_INST waves, same group layout as the rest.
+  int aoffx = 0;
+  if constexpr (TL::XR > 0) {
+    const int q = TL::A_INST * NW + wv;
+    const int kk = (lane >> 4) % TL::SLICES;
+    const int row = q * 8 + ((lane & 15) >> 1), hp = lane & 1;
+    aoffx = (row * p.lda + (kk * 2 + kc_half(row, hp)) * 8) * (int)esz;
+  }
 
   // Issue the direct loads of K step kt into stage buffer `st`.
   auto stage_ptr = [&](auto st) -> LDS_AS unsigned char* {
@@ -351,6 +376,10 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
       for (int j = 0; j < TL::A_INST; ++j)
         dma16(r, (LDS_AS void*)(base + (wv * TL::A_INST + j) * 1024), aoff[j % PA],
               soff + (j / PA) * astep);
+      if constexpr (TL::XR > 0) {
+        if (wv < TL::XA_INST)
+          dma16(r, (LDS_AS void*)(base + (TL::A_INST * NW + wv) * 1024), aoffx, soff);
+      }
     }
     // B
     {
@@ -409,10 +438,14 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // the wave's 32x32 tile of the strip: rows BMAIN.., columns wn*128 + wm*32..
+  f32x16 accx[1][1];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) accx[0][0][r] = 0.f;
 
   // Fragments of one 16-deep K slice.
   struct Frags {
-    bf16x8 xb[4], ya[SM];
+    bf16x8 xb[4], ya[SM], xbx, yx;
   };
   // 32-row subtiles of this wave that hold at least one valid row: fewer
   // than SM only in an expert's last row tile, whose empty subtiles then
@@ -442,6 +475,10 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
       else
         f.ya[sm] = frag_mn(As, TL::A_PITCH, wm * TL::WM + sm * 32, kk);
     }
+    if constexpr (TL::XR > 0 && decltype(full)::value == 2) {
+      f.yx = frag_kc(As, TL::BMAIN, kk);
+      f.xbx = frag_kc(Bs, wn * 128 + wm * 32, kk);
+    }
   };
   auto mma = [&](const Frags& f, auto full) {
 #pragma unroll
@@ -451,7 +488,10 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
       for (int sn = 0; sn < 4; ++sn)
         acc[sm][sn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.xb[sn], f.ya[sm], acc[sm][sn], 0, 0, 0);
     }
+    if constexpr (TL::XR > 0 && decltype(full)::value == 2)
+      accx[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.xbx, f.yx, accx[0][0], 0, 0, 0);
   };
+
   // One stage: the fragments of slice kk+1 are read while the MFMAs of slice
   // kk run (the compiler interleaves the two).
   auto compute = [&](auto st, auto full) {
@@ -468,6 +508,7 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
     }
     mma(f1, full);
   };
+
 
   // ---------------------------------------------------------------- main loop
   // S-stage pipeline: at the top of step kt the wave waits for its own loads
@@ -546,10 +587,22 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
       if (kt + 2 < nk) step(kt + 2, I2{}, I1{}, full);
     }
   };
-  if (TR::kKRAGGED || nvsm == SM)
-    main_loop(std::true_type{});
-  else
-    main_loop(std::false_type{});
+  // full tiles run branch-free; a tile reaching into the strip runs the strip
+  // MFMAs as well (its main subtiles are then all valid)
+  const bool strip = TL::XR > 0 && w.rows > TL::BMAIN;
+  if constexpr (TL::XR > 0) {
+    if (strip)
+      main_loop(std::integral_constant<int, 2>{});
+    else if (nvsm == SM)
+      main_loop(std::true_type{});
+    else
+      main_loop(std::false_type{});
+  } else {
+    if (TR::kKRAGGED || nvsm == SM)
+      main_loop(std::true_type{});
+    else
+      main_loop(std::false_type{});
+  }
   // all waves are done with the stage buffers before the block exits
   asm volatile("s_barrier" ::: "memory");
 
@@ -563,18 +616,48 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
       for (int sm = 0; sm < SM; ++sm) dlv[sm] = rrow[wm * TL::WM + sm * 32 + (lane & 31)];
       const int ncol4 = 4 * (lane >> 5);
 #pragma unroll
-      for (int sn = 0; sn < 4; ++sn)
+      for (int sn = 0; sn < 4; ++sn) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float wv = rcol[wn * 128 + sn * 32 + 8 * (r >> 2) + ncol4 + (r & 3)];
 #pragma unroll
           for (int sm = 0; sm < SM; ++sm) acc[sm][sn][r] += dlv[sm] * wv;
         }
+        // one column subtile at a time: its 16 W_r values are all that is live
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (TL::XR > 0) {
+        if (strip) {
+          const float dlx = rrow[TL::BMAIN + (lane & 31)];
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            accx[0][0][r] += dlx * rcol[wn * 128 + wm * 32 + 8 * (r >> 2) + ncol4 + (r & 3)];
+        }
+      }
     }
   }
 
   // ---------------------------------------------------------------- epilogue
   EpiArgs ea{p.c0, p.c1, p.c2, p.ldc, p.c_gstride, p.aux0, p.aux1, p.N, p.M};
+  // The strip's 32x32 tile of this wave (rows BMAIN.., columns wn*128 +
+  // wm*32.. of the block tile).  The down dgrad stores it first, straight
+  // from the accumulators (its SwiGLU backward needs them in fp32); the
+  // gate/up dgrad rounds it to bf16 here and stores it after the main
+  // epilogue, so only eight registers stay live through that.
+  [[maybe_unused]] uint32_t xpk[8];
+  if constexpr (TL::XR > 0) {
+    if (strip) {
+      if constexpr (MODE == DGRAD_DOWN) {
+        Work ws = w;
+        ws.row0 = w.row0 + TL::BMAIN;
+        ws.rows = w.rows - TL::BMAIN;
+        store_tile_direct<MODE, BM, 1, false, 1, 32>(accx, ea, ws, lane, 0, wn * 4 + wm);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xpk[i] = pack2bf(accx[0][0][2 * i], accx[0][0][2 * i + 1]);
+      }
+    }
+  }
   if constexpr (TR::kKRAGGED) {
     if (p.part) {
       store_partial_f32<MODE, BM, SM>(acc, ea, w, lane, wm, wn);
@@ -591,9 +674,22 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
     LDS_AS unsigned char* wbuf =
         (sel == 0 ? (LDS_AS unsigned char*)lds0 : sel == 1 ? (LDS_AS unsigned char*)lds1
          : sel == 2 ? (LDS_AS unsigned char*)lds2 : (LDS_AS unsigned char*)lds3) + (wave % PER) * REG;
-    store_tile<MODE, BM, SM, false, CH, NCS>(acc, ea, w, lane, wm, wn, wbuf);
+    store_tile<MODE, BM, SM, false, CH, NCS, (TL::XR > 0)>(acc, ea, w, lane, wm, wn, wbuf);
   } else {
     store_tile_direct<MODE, BM, SM, false>(acc, ea, w, lane, wm, wn);
+  }
+  if constexpr (TL::XR > 0 && MODE != DGRAD_DOWN) {
+    // lane holds row BMAIN + (lane & 31), columns 8*g + 4*(lane >> 5) + 0..3
+    if (strip && (lane & 31) < w.rows - TL::BMAIN) {
+      const size_t crow = (size_t)(w.row0 + TL::BMAIN + (lane & 31));
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int col = w.nt * BN + wn * 128 + wm * 32 + 8 * g4 + 4 * (lane >> 5);
+        if (col < p.N)
+          *reinterpret_cast<uint2*>((bf16_t*)p.c0 + crow * p.ldc + col) =
+              make_uint2(xpk[2 * g4], xpk[2 * g4 + 1]);
+      }
+    }
   }
   }  // tiles of this block
 #endif
@@ -616,7 +712,14 @@ hipError_t launch(const Params& p, int blocks, hipStream_t s) {
 // dgrads instead run one 256x256 block per CU with eight waves (64x128 wave
 // tiles, two waves per SIMD) and 64-deep K steps in two 64 KiB stages: a
 // third less L2->LDS traffic per FLOP and half the barriers, which outweighs
-// the lost overlap there.  In the forward GEMMs, whose epilogues are heavier,
+// the lost overlap there.  Their tiles carry the 32-row strip (288 rows, two
+// 68 KiB stages): with a few hundred routed rows per expert, an expert just
+// past 512 rows then takes two row tiles instead of two plus a nearly empty
+// third that would still stream the whole weight tile (uniform top-4 over 128
+// experts, 454-564 rows each: down dgrad 0.45 -> 0.41 ms, gate/up dgrad
+// 0.69 -> 0.65 ms; on Zipf-skewed counts both run about 6 % slower, on 8192
+// rows per expert the down dgrad is 10 % faster and the gate/up dgrad 7 %
+// slower).  In the forward GEMMs, whose epilogues are heavier,
 // 256-row tiles lose: at a few hundred rows per expert an expert's last
 // 256-row tile is often nearly empty yet loads a full weight tile (measured
 // per mode on routed counts).  (The down dgrad's epilogue, which also streams
@@ -632,10 +735,10 @@ hipError_t launch(const Params& p, int blocks, hipStream_t s) {
 #define GEMM_DN_CFG GEMM_M_CFG     // forward down
 #endif
 #ifndef GEMM_DU_CFG
-#define GEMM_DU_CFG 256, 2, 64, 1, 8  // gate/up dgrad
+#define GEMM_DU_CFG 288, 2, 64, 1, 8  // gate/up dgrad
 #endif
 #ifndef GEMM_DD_CFG
-#define GEMM_DD_CFG 256, 2, 64, 1, 8  // down dgrad
+#define GEMM_DD_CFG 288, 2, 64, 1, 8  // down dgrad
 #endif
 #ifndef GEMM_W_CFG
 #define GEMM_W_CFG 128, 3, 32, 2   // both wgrads

@@ -563,10 +563,14 @@ constexpr int epi_chunk(int stage_bytes, int stages) {
 // columns.  SWIGLU_FROM_BF16: the forward's h (and the dgrad's silu terms)
 // are computed from the bf16-rounded g and u instead of the fp32 sums.
 // wbuf: this wave's staging region, epi_region_bytes<MODE>(CH, NCS) bytes.
-template <int MODE, int BM, int SM, bool SWIGLU_FROM_BF16, int CH, int NCS = 1>
+// OPAQUE: recompute the lane's staging addresses per tile instead of letting
+// the compiler keep them live through the main loop (where registers are
+// short they would be spilled and reloaded before every staged row).
+template <int MODE, int BM, int SM, bool SWIGLU_FROM_BF16, int CH, int NCS = 1, bool OPAQUE = false>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[SM][4], const EpiArgs& a,
                                            const Work& w, int lane, int wm, int wn,
                                            LDS_AS unsigned char* wbuf) {
+  if constexpr (OPAQUE) asm volatile("" : "+v"(lane));
   constexpr int WM = SM * 32;  // wave tile rows
   const int ncol4 = 4 * (lane >> 5);
   if constexpr (MODE == ROUTER) {
