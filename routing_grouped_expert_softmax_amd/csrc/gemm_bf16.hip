@@ -605,6 +605,9 @@ __global__ void __launch_bounds__(64 * NW, OCC) grouped_gemm_kernel(Params p) {
   }
   // all waves are done with the stage buffers before the block exits
   asm volatile("s_barrier" ::: "memory");
+  // with the strip, the epilogue's lane-derived addresses are formed here,
+  // not before the loop (where they would take the loop's registers)
+  if constexpr (TL::XR > 0) asm volatile("" : "+v"(lane));
 
   if constexpr (MODE == DGRAD_UP) {
     if (p.rdl != nullptr) {
