@@ -239,13 +239,18 @@ __device__ void kragged_xcd_range(const int32_t* offsets, int E, int per_e, int 
 // Tile table of a row-ragged launch: expert e owns ceil(n_e / BM) * ntiles
 // logical tiles, m-tile fastest, experts in order.  Each thread keeps the
 // exclusive scan of the tile counts of its (up to four) experts.
-template <int BM>
+// NFAST: an expert's tiles in m-major order (the n-tiles of one row tile
+// consecutive); otherwise n-major (the row tiles sharing one weight tile
+// consecutive).
+template <int BM, bool NFAST = false>
 struct MTileSched {
   int cnt[4], til[4];
   int run;    // first logical tile of this thread's experts
   int per;    // experts per thread
   int total;  // tiles of the launch (block-uniform)
+  int ntiles_;
   __device__ void init(int E, const int32_t* offsets, int ntiles, int* sh) {
+    ntiles_ = ntiles;
     // threads past kThreads (larger blocks) hold no experts
     const int tid = threadIdx.x;
     per = (E + kThreads - 1) / kThreads;  // <= 4
@@ -276,8 +281,14 @@ struct MTileSched {
         const int mt_e = (cnt[q] + BM - 1) / BM;
         const int local_t = L - r;
         sh[kThreads] = e;
-        sh[kThreads + 1] = local_t % mt_e;  // m-tile
-        sh[kThreads + 2] = local_t / mt_e;  // n-tile
+        if (NFAST) {
+          const int nt = ntiles_;
+          sh[kThreads + 1] = local_t / nt;  // m-tile
+          sh[kThreads + 2] = local_t % nt;  // n-tile
+        } else {
+          sh[kThreads + 1] = local_t % mt_e;  // m-tile
+          sh[kThreads + 2] = local_t / mt_e;  // n-tile
+        }
       }
       r += til[q];
     }
