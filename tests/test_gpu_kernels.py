@@ -167,6 +167,9 @@ FFN_CASES = [
     ("bf16", 256, 256, [4096]),
     ("bf16", 256, 384, [3000, 5, 0, 2500]),
     ("bf16", 128, 256, [2049]),
+    # around the dgrads' 288-row tiles (256 rows plus a 32-row strip): strips
+    # full, partly filled (257..287 rows) and absent, in first and second tiles
+    ("bf16", 256, 256, [288, 289, 575, 576, 577, 270, 256, 32, 0, 544]),
     # many small experts: the tile schedulers' threads hold 2 and 4 experts each
     ("bf16", 128, 128, [(i * 37) % 23 for i in range(300)]),
     ("bf16", 128, 128, [(i * 13) % 7 for i in range(1000)]),
